@@ -1,0 +1,91 @@
+"""Brute force on tiny inputs: scalar Python loops vs the oracle.
+
+The oracle computes attention with float64 matrix products, scores with array
+reductions and selection by sorting.  Here every attention weight is a scalar
+loop with math.exp, scores are accumulated pair by pair, and the kept set is
+decided by counting, for each candidate, how many candidates outrank it.  The
+rotated Q and K come from the oracle (RoPE has its own pins).
+"""
+import math
+
+import numpy as np
+
+from kv_cache_compression_statekv_amd.workload import CONFIGS, FrameStream
+from oracle import CompressedState, LayerConfig, OracleStream, frame_step
+
+
+def _brute(cfg, state, q_rot, k_rot, v, n):
+    T, Hq, Hkv, d = cfg.tokens_per_frame, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    G = Hq // Hkv
+    k0 = state.count
+    P = k0 + T
+    pos = [int(p) for p in state.pos] + [n * T + i for i in range(T)]
+
+    def key(g, j):
+        return state.K[g, j] if j < k0 else k_rot[j - k0, g]
+
+    def val(g, j):
+        return state.V[g, j] if j < k0 else v[j - k0, g]
+
+    sigma = 1.0 / math.sqrt(d)      # alpha = 1 in every brute-force case
+    out = np.zeros((T, Hq, d))
+    score = [0.0] * P
+    for h in range(Hq):
+        g = h // G
+        for i in range(T):
+            vis = [j for j in range(P) if pos[j] <= n * T + i]
+            logit = {j: sigma * sum(float(a) * float(b) for a, b in zip(q_rot[i, h], key(g, j)))
+                     for j in vis}
+            mx = max(logit.values())
+            w = {j: math.exp(logit[j] - mx) for j in vis}
+            tot = sum(w.values())
+            for j in vis:
+                p = w[j] / tot
+                score[j] += p
+                out[i, h] += p * val(g, j)
+    score = [s / (Hq * T) for s in score]
+    s32 = [float(np.float32(s)) for s in score]
+    if P <= cfg.budget:
+        keep = list(range(P))
+    else:
+        keep = []
+        for j in range(P):
+            better = sum(1 for m in range(P)
+                         if s32[m] > s32[j] or (s32[m] == s32[j] and pos[m] < pos[j]))
+            if better < cfg.budget:
+                keep.append(j)
+    return out, score, keep
+
+
+def test_tiny_stream_matches_brute_force():
+    wl = CONFIGS["tiny"]
+    cfg = LayerConfig(n_q_heads=wl.n_q_heads, n_kv_heads=wl.n_kv_heads,
+                      head_dim=wl.head_dim, tokens_per_frame=wl.tokens_per_frame,
+                      budget=wl.budget, dtype=wl.dtype, rope_base=wl.rope_base)
+    stream = FrameStream(wl)
+    orc = OracleStream(cfg)
+    for n in range(wl.n_frames):
+        before = orc.state
+        res = orc.step(*stream.frame(n))
+        out, score, keep = _brute(cfg, before, res.Q_rot, res.K_rot, res.V, n)
+        assert np.max(np.abs(res.O_exact - out)) < 1e-12
+        assert np.max(np.abs(res.scores - np.array(score))) < 1e-14
+        assert res.keep.tolist() == keep
+
+
+def test_gqa_bf16_frames_match_brute_force():
+    cfg = LayerConfig(n_q_heads=6, n_kv_heads=2, head_dim=16, tokens_per_frame=5,
+                      budget=7, dtype="bf16", rope_base=1e4)
+    rng = np.random.default_rng(11)
+    orc = OracleStream(cfg)
+    for n in range(4):
+        f = lambda *s: rng.standard_normal(s).astype(np.float32)
+        Q, K, V = f(5, 6, 16), f(5, 2, 16), f(5, 2, 16)
+        from kv_cache_compression_statekv_amd.workload import round_to_bf16
+        Q, K, V = round_to_bf16(Q), round_to_bf16(K), round_to_bf16(V)
+        before = orc.state
+        res = orc.step(Q, K, V)
+        out, score, keep = _brute(cfg, before, res.Q_rot, res.K_rot, res.V, n)
+        assert np.max(np.abs(res.O_exact - out)) < 1e-12
+        assert np.max(np.abs(res.scores - np.array(score))) < 1e-14
+        assert res.keep.tolist() == keep
