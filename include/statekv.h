@@ -1,0 +1,188 @@
+/*
+ * statekv.h - C ABI of the StateKV streaming-prefill frame step on AMD MI355X
+ * (gfx950).
+ *
+ * The operation is the per-layer, per-frame step of the paper note "Linear
+ * Scaling Video VLMs for Long Video Understanding" (papernotes.org, ECCV 2026),
+ * section 方法详解:
+ *   - 整体框架 / 关键设计 1: each layer keeps a compressed state C (capacity B)
+ *     and a detailed state D holding every processed token; the queries of
+ *     frame n attend only over [Kbar_{n-1}; K_n] and the result goes to the
+ *     next layer;
+ *   - 关键设计 2: the candidate pool is the old state plus the frame's T tokens;
+ *     each candidate is scored by the average attention the frame's queries
+ *     pay to it; the B best form the next state;
+ *   - 关键设计 3: RoPE angles use the virtual stream position L_n = nT and one
+ *     global scaling factor alpha fixed before the stream starts.
+ *
+ * Readings taken where the text is silent (equations are missing from it):
+ *   - attention is softmax(sigma * Q K^T) V, causal inside the frame, with the
+ *     whole compressed state visible;
+ *   - a candidate's score is its attention weight averaged over all T queries
+ *     and all Hq query heads of the layer (masked pairs count as zero), kept
+ *     as fp32; one index set per layer is shared by all KV heads;
+ *   - Top-B orders by (score descending, position ascending): ties keep the
+ *     older token; the new state lists its tokens in ascending position;
+ *   - alpha > 1 applies the YaRN frequency ramp (original window
+ *     rope_orig_ctx) and the logit scale sigma = (0.1 ln alpha + 1)^2/sqrt(d);
+ *   - K and D store keys after RoPE (positions never change); V has no RoPE.
+ *
+ * Conventions (all entry points):
+ *   - Return 0 on success or a negative STATEKV_E* code.  Arguments are
+ *     checked before anything is enqueued, so a failed call leaves the state
+ *     unchanged.  Errors reported by the HIP runtime return STATEKV_EDEVICE.
+ *   - Device pointers are HIP device memory on the state's device.  Tensors
+ *     are dense, row-major, in the element type of the configuration
+ *     (bf16 as raw 16-bit words, or fp32).
+ *   - A state belongs to one HIP stream (statekv_set_stream); its work is
+ *     asynchronous on that stream.  Calls on one state are not thread-safe.
+ */
+#ifndef STATEKV_H
+#define STATEKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define STATEKV_OK          0
+#define STATEKV_EINVAL     -1  /* a null pointer, bad size or unsupported shape */
+#define STATEKV_EORDER     -2  /* n is not the next frame of the stream */
+#define STATEKV_ECAPACITY  -3  /* the detailed cache is full (max_frames reached) */
+#define STATEKV_ENOMEM     -4  /* device allocation failed */
+#define STATEKV_EDEVICE    -5  /* the HIP runtime reported an error */
+#define STATEKV_ENONFINITE -6  /* an input frame held NaN or Inf */
+
+#define STATEKV_DTYPE_BF16  1
+#define STATEKV_DTYPE_F32   2
+
+/* Shape and RoPE parameters of one layer. */
+typedef struct statekv_layer_cfg {
+  int32_t n_q_heads;        /* Hq >= 1 */
+  int32_t n_kv_heads;       /* Hkv >= 1, Hq % Hkv == 0; query head h uses KV head h / (Hq/Hkv) */
+  int32_t head_dim;         /* d: 64 or 128 */
+  int32_t tokens_per_frame; /* T >= 1 */
+  int32_t max_frames;       /* frames the detailed cache holds (N_max >= 1) */
+  int32_t dtype;            /* STATEKV_DTYPE_BF16 or STATEKV_DTYPE_F32 */
+  double  rope_base;        /* RoPE base (> 1) */
+  int32_t rope_orig_ctx;    /* original context of the YaRN ramp (>= 1) */
+} statekv_layer_cfg;
+
+typedef struct statekv_state statekv_state;
+
+/* A non-owning window on device memory held by the state. */
+typedef struct statekv_view {
+  const void*    k;            /* keys after RoPE */
+  const void*    v;            /* values */
+  const int32_t* pos;          /* [count] absolute stream positions, ascending
+                                  (compressed view); NULL for the detailed view */
+  int64_t        count;        /* tokens in the view */
+  int64_t        head_stride;  /* elements between consecutive KV heads */
+  int64_t        token_stride; /* elements between consecutive tokens */
+  int32_t        n_kv_heads;
+  int32_t        head_dim;
+  int32_t        dtype;
+  int32_t        frames_done;  /* frames processed so far */
+} statekv_view;
+
+/* Scores and selection of the most recent frame that computed them. */
+typedef struct statekv_scores_view {
+  const float*   scores;    /* [pool] fp32 mean attention of each candidate */
+  const int32_t* pool_pos;  /* [pool] positions of the candidates (old state, then frame) */
+  const int32_t* keep;      /* [kept] indices into the pool that were kept, ascending */
+  int32_t        pool;      /* candidates: min(B, n*T) + T */
+  int32_t        kept;      /* min(B, pool) */
+  int32_t        frame;     /* frame index, or -1 if no frame has computed scores */
+} statekv_scores_view;
+
+/*
+ * Create the per-layer state: compressed state of capacity B (empty), the
+ * detailed cache for cfg->max_frames * T tokens, and all scratch buffers, on
+ * the current HIP device.  Everything is allocated here; later calls do not
+ * allocate.  alpha >= 1 is the global RoPE scaling factor (关键设计 3), fixed
+ * for the life of the state.  Requires B >= 1 and B + T <= 32768.
+ * On success *out receives the state; the caller releases it with
+ * statekv_destroy.  Errors: EINVAL, ENOMEM, EDEVICE.
+ */
+int statekv_create(const statekv_layer_cfg* cfg, int32_t budget_B, float alpha,
+                   statekv_state** out);
+
+/* Launch subsequent work on hip_stream (a hipStream_t; NULL = default stream). */
+int statekv_set_stream(statekv_state* s, void* hip_stream);
+
+/*
+ * One StateKV step of frame n (0-based; page frame n+1) for this layer.
+ *   Q [T][Hq][d], K [T][Hkv][d], V [T][Hkv][d]: projected, pre-RoPE inputs
+ *     (device, caller-owned, read only);
+ *   O [T][Hq][d]: attention output (device, caller-owned, written).
+ * Rotates Q and K at positions nT..nT+T-1, attends over [compressed state;
+ * frame], appends the rotated K and V to the detailed cache, scores the pool
+ * and keeps min(B, pool) candidates as the next compressed state.
+ * n must equal the number of frames already processed (EORDER otherwise);
+ * ECAPACITY once max_frames frames are done.  Asynchronous: O and the views
+ * are valid after the stream reaches this point.  A NaN or Inf in Q, K or V is
+ * detected on the device and reported by the next view call (ENONFINITE).
+ */
+int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K,
+                          const void* V, int32_t n, void* O);
+
+/*
+ * Compressed state C after the last frame: k, v are [Hkv][count][d] with
+ * head_stride = (B+T)*d and token_stride = d; pos[count] ascending.
+ * Synchronises the state's stream.  Valid until the next prefill_frame or
+ * destroy.  Returns ENONFINITE if an input frame held NaN or Inf.
+ */
+int statekv_compressed_view(const statekv_state* s, statekv_view* out);
+
+/*
+ * Detailed state D: k, v are [frames_done*T][Hkv][d] (token_stride = Hkv*d,
+ * head_stride = d), row p holding the token at stream position p.  Synchronises
+ * the state's stream.  Valid until destroy.  Returns ENONFINITE as above.
+ */
+int statekv_detailed_view(const statekv_state* s, statekv_view* out);
+
+/*
+ * Scores, pool positions and kept indices of the last frame that computed
+ * them (frames whose pool does not exceed B skip scoring unless
+ * STATEKV_FLAG_ALWAYS_SCORE is set).  Synchronises the stream; valid until the
+ * next prefill_frame or destroy.
+ */
+int statekv_scores(const statekv_state* s, statekv_scores_view* out);
+
+#define STATEKV_FLAG_ALWAYS_SCORE  1u  /* score the pool even while it fits in B */
+#define STATEKV_FLAG_KERNEL_TIMING 2u  /* time each kernel with HIP events */
+
+/* Set option flags (STATEKV_FLAG_*).  Takes effect from the next frame. */
+int statekv_set_flags(statekv_state* s, uint32_t flags);
+
+/* Kernels of one step, in launch order, as indexed by statekv_kernel_times. */
+#define STATEKV_K_ROPE     0  /* virtual-position RoPE + append to D */
+#define STATEKV_K_ATTN     1  /* fused attention, pass 1 (split over keys) */
+#define STATEKV_K_COMBINE  2  /* merge of key splits, output O and row stats */
+#define STATEKV_K_SCORE    3  /* recompute pass: per-key column sums */
+#define STATEKV_K_SELECT   4  /* Top-B select and compaction list */
+#define STATEKV_K_GATHER   5  /* gather of the kept rows into the next state */
+#define STATEKV_K_COUNT    6
+
+/*
+ * With STATEKV_FLAG_KERNEL_TIMING set, per-kernel device time (HIP events on
+ * the state's stream) is summed over frames.  Copies up to n_kernels sums in
+ * milliseconds into ms[] and launch counts into launches[] (either may be
+ * NULL), synchronising the stream; reset != 0 clears the sums afterwards.
+ */
+int statekv_kernel_times(statekv_state* s, float* ms, int32_t* launches,
+                         int32_t n_kernels, int32_t reset);
+
+/* Release every device buffer of the state.  Accepts NULL. */
+void statekv_destroy(statekv_state* s);
+
+/* Static description of an error code. */
+const char* statekv_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* STATEKV_H */

@@ -1,0 +1,552 @@
+// Host runtime and C ABI of the StateKV frame step (see include/statekv.h).
+//
+// State layout in HBM (one layer):
+//   kbuf[2], vbuf[2]  [Hkv][cap][d], cap = B + T: the compressed state in rows
+//                     [0, count) followed by the current frame's rows; two
+//                     buffers, the Top-B gather writes the other one.
+//   pos[2]            [cap] absolute positions of those rows.
+//   dk, dv            [max_frames*T][Hkv][d]: the detailed cache D.
+//   qrot              [Hkv][G*T][d]: the frame's rotated queries, rows grouped
+//                     by KV head (row = token*G + head-in-group).
+//   opart/mpart/lpart split-over-keys partials of attention pass 1.
+//   row_m/row_rinv    final row max and 1/row sum, read by the score pass.
+//   colpart           [row splits][Hkv][cap] per-key column sums (fp64).
+//   scores, keep      fp32 scores of the pool and the kept pool indices.
+// Everything is allocated in statekv_create; a frame step only launches.
+#include "statekv.h"
+#include "statekv_internal.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+
+using namespace statekv;
+
+struct statekv_state {
+  statekv_layer_cfg cfg;
+  int32_t B;
+  float alpha;
+  Dt dt;
+  int esize, Hq, Hkv, D, T, G, R, cap;
+  int device;
+  hipStream_t stream;
+
+  // launch geometry
+  int attn_tiles, attn_splits_max;
+  int score_rsplits_max;
+
+  void* kbuf[2];
+  void* vbuf[2];
+  int32_t* pos[2];
+  void* dk;
+  void* dv;
+  void* qrot;
+  float* opart;
+  float* mpart;
+  double* lpart;
+  float* row_m;
+  float* row_rinv;
+  double* colpart;
+  float* scores;
+  int32_t* keep;
+  double* inv_freq;
+  int32_t* nonfinite;
+
+  float c_hi, c_lo;  // softmax scale times log2(e), as a float pair
+
+  int cur;           // buffer holding the compressed state
+  int count;         // tokens in the compressed state
+  int frames_done;
+
+  // scores of the last frame that computed them
+  int score_frame, score_pool, score_kept, score_buf;
+
+  uint32_t flags;
+  // Kernel timing: a ring of (start, stop) event pairs per kernel, drained
+  // lazily so that recording never waits for the device.
+  static constexpr int kRing = 64;
+  hipEvent_t ev[kRing][STATEKV_K_COUNT][2];
+  bool ev_pending[kRing][STATEKV_K_COUNT];
+  int ev_slot;
+  bool ev_ok;
+  float ktime_ms[STATEKV_K_COUNT];
+  int32_t klaunch[STATEKV_K_COUNT];
+};
+
+namespace {
+
+int check(hipError_t e) { return e == hipSuccess ? STATEKV_OK : STATEKV_EDEVICE; }
+
+template <class P>
+int alloc(P** p, size_t bytes) {
+  *p = nullptr;
+  if (bytes == 0) bytes = 16;
+  hipError_t e = hipMalloc((void**)p, bytes);
+  if (e != hipSuccess) {
+    *p = nullptr;
+    return e == hipErrorOutOfMemory ? STATEKV_ENOMEM : STATEKV_EDEVICE;
+  }
+  return STATEKV_OK;
+}
+
+void release(statekv_state* s) {
+  void* bufs[] = {s->kbuf[0], s->kbuf[1], s->vbuf[0], s->vbuf[1], s->pos[0], s->pos[1],
+                  s->dk, s->dv, s->qrot, s->opart, s->mpart, s->lpart, s->row_m,
+                  s->row_rinv, s->colpart, s->scores, s->keep, s->inv_freq, s->nonfinite};
+  for (void* b : bufs)
+    if (b) (void)hipFree(b);
+  for (auto& ring : s->ev)
+    for (auto& e : ring) {
+      if (e[0]) (void)hipEventDestroy(e[0]);
+      if (e[1]) (void)hipEventDestroy(e[1]);
+    }
+}
+
+// Add a finished (start, stop) pair of ring slot r, kernel k to the sums.
+void drain_slot(statekv_state* s, int r, int k) {
+  if (!s->ev_pending[r][k]) return;
+  s->ev_pending[r][k] = false;
+  if (hipEventSynchronize(s->ev[r][k][1]) != hipSuccess) return;
+  float ms = 0.f;
+  if (hipEventElapsedTime(&ms, s->ev[r][k][0], s->ev[r][k][1]) == hipSuccess) {
+    s->ktime_ms[k] += ms;
+    s->klaunch[k] += 1;
+  }
+}
+
+// Frequencies of the rotation pairs: theta_k = base^(-2k/d), and under a
+// fixed scaling factor alpha > 1 the YaRN ramp over r_k = L_orig theta_k / 2pi:
+// gamma = clamp((r - 1) / 31, 0, 1), theta'_k = (1 - gamma) theta_k / alpha + gamma theta_k.
+void scaled_inv_freq(int d, double base, double alpha, int orig_ctx, double* out) {
+  for (int k = 0; k < d / 2; ++k) {
+    const double kk = (double)k;
+    const double th = pow(base, -2.0 * kk / (double)d);
+    if (alpha == 1.0) {
+      out[k] = th;
+      continue;
+    }
+    const double r = (double)orig_ctx * th / (2.0 * M_PI);
+    const double gamma = std::min(std::max((r - 1.0) / (32.0 - 1.0), 0.0), 1.0);
+    out[k] = (1.0 - gamma) * th / alpha + gamma * th;
+  }
+}
+
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+constexpr int kTargetWGs = 512;  // about two work-groups per compute unit
+
+// Key splits of pass 1 for a pool of P keys: enough work-groups to fill the
+// chip, at least 4 blocks of 64 keys per split.
+void attn_geometry(const statekv_state* s, int P, int* splits, int* kps) {
+  const int base = s->attn_tiles * s->Hkv;
+  int sp = std::max(1, std::min(ceil_div(kTargetWGs, base), ceil_div(P, 4 * kAttnBN)));
+  sp = std::min(sp, s->attn_splits_max);
+  int k = ceil_div(ceil_div(P, sp), kAttnBN) * kAttnBN;
+  *splits = ceil_div(P, k);
+  *kps = k;
+}
+
+void score_geometry(const statekv_state* s, int P, int* key_blocks, int* rsplits, int* rps) {
+  const int kb = ceil_div(P, score_keys_per_wg(s->dt));
+  const int base = kb * s->Hkv;
+  int rs = std::max(1, std::min(ceil_div(kTargetWGs, base), ceil_div(s->R, 128)));
+  rs = std::min(rs, s->score_rsplits_max);
+  const int r = ceil_div(ceil_div(s->R, rs), 32) * 32;
+  *key_blocks = kb;
+  *rsplits = ceil_div(s->R, r);
+  *rps = r;
+}
+
+struct KernelTimer {
+  statekv_state* s;
+  int k;
+  bool on;
+  KernelTimer(statekv_state* st, int kernel)
+      : s(st), k(kernel), on((st->flags & STATEKV_FLAG_KERNEL_TIMING) && st->ev_ok) {
+    if (!on) return;
+    drain_slot(s, s->ev_slot, k);  // the pair recorded kRing frames ago
+    (void)hipEventRecord(s->ev[s->ev_slot][k][0], s->stream);
+  }
+  void done() {
+    if (!on) return;
+    (void)hipEventRecord(s->ev[s->ev_slot][k][1], s->stream);
+    s->ev_pending[s->ev_slot][k] = true;
+  }
+};
+
+int read_nonfinite(const statekv_state* s) {
+  int32_t h = 0;
+  if (hipMemcpy(&h, s->nonfinite, sizeof(h), hipMemcpyDeviceToHost) != hipSuccess)
+    return STATEKV_EDEVICE;
+  return h ? STATEKV_ENONFINITE : STATEKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* statekv_strerror(int code) {
+  switch (code) {
+    case STATEKV_OK: return "ok";
+    case STATEKV_EINVAL: return "invalid argument";
+    case STATEKV_EORDER: return "frame index is not the next frame of the stream";
+    case STATEKV_ECAPACITY: return "detailed cache is full";
+    case STATEKV_ENOMEM: return "device memory allocation failed";
+    case STATEKV_EDEVICE: return "HIP runtime error";
+    case STATEKV_ENONFINITE: return "an input frame held NaN or Inf";
+    default: return "unknown error";
+  }
+}
+
+int statekv_create(const statekv_layer_cfg* cfg, int32_t budget_B, float alpha,
+                   statekv_state** out) {
+  if (!cfg || !out) return STATEKV_EINVAL;
+  *out = nullptr;
+  const statekv_layer_cfg c = *cfg;
+  if (c.n_q_heads < 1 || c.n_kv_heads < 1 || c.n_q_heads % c.n_kv_heads != 0) return STATEKV_EINVAL;
+  if (c.head_dim != 64 && c.head_dim != 128) return STATEKV_EINVAL;
+  if (c.tokens_per_frame < 1 || c.max_frames < 1) return STATEKV_EINVAL;
+  if (c.dtype != STATEKV_DTYPE_BF16 && c.dtype != STATEKV_DTYPE_F32) return STATEKV_EINVAL;
+  if (!(c.rope_base > 1.0) || !isfinite(c.rope_base) || c.rope_orig_ctx < 1) return STATEKV_EINVAL;
+  if (!(alpha >= 1.0f) || !isfinite(alpha)) return STATEKV_EINVAL;
+  if (budget_B < 1 || (int64_t)budget_B + c.tokens_per_frame > kMaxPool) return STATEKV_EINVAL;
+  const int64_t positions = (int64_t)c.max_frames * c.tokens_per_frame;
+  if (positions > INT32_MAX) return STATEKV_EINVAL;
+  const int64_t rows = (int64_t)c.n_q_heads * c.tokens_per_frame;
+  if (rows > INT32_MAX / 128) return STATEKV_EINVAL;
+
+  statekv_state* s = (statekv_state*)calloc(1, sizeof(statekv_state));
+  if (!s) return STATEKV_ENOMEM;
+  s->cfg = c;
+  s->B = budget_B;
+  s->alpha = alpha;
+  s->dt = c.dtype == STATEKV_DTYPE_BF16 ? Dt::BF16 : Dt::F32;
+  s->esize = c.dtype == STATEKV_DTYPE_BF16 ? 2 : 4;
+  s->Hq = c.n_q_heads;
+  s->Hkv = c.n_kv_heads;
+  s->D = c.head_dim;
+  s->T = c.tokens_per_frame;
+  s->G = s->Hq / s->Hkv;
+  s->R = s->G * s->T;
+  s->cap = budget_B + s->T;
+  s->stream = nullptr;
+  s->score_frame = -1;
+
+  int rc = check(hipGetDevice(&s->device));
+  if (rc) {
+    free(s);
+    return rc;
+  }
+
+  s->attn_tiles = ceil_div(s->R, attn_rows_per_wg(s->dt));
+  s->attn_splits_max = std::max(1, ceil_div(s->cap, 4 * kAttnBN));
+  s->score_rsplits_max = std::max(1, ceil_div(s->R, 128));
+
+  const size_t E = s->esize, D = s->D;
+  const size_t pool_bytes = (size_t)s->Hkv * s->cap * D * E;
+  const size_t det_bytes = (size_t)positions * s->Hkv * D * E;
+  const size_t rows_all = (size_t)s->Hkv * s->R;
+  const size_t S = s->attn_splits_max;
+  for (int i = 0; i < 2 && !rc; ++i) {
+    rc = alloc(&s->kbuf[i], pool_bytes);
+    if (!rc) rc = alloc(&s->vbuf[i], pool_bytes);
+    if (!rc) rc = alloc(&s->pos[i], (size_t)s->cap * sizeof(int32_t));
+  }
+  if (!rc) rc = alloc(&s->dk, det_bytes);
+  if (!rc) rc = alloc(&s->dv, det_bytes);
+  if (!rc) rc = alloc(&s->qrot, rows_all * D * E);
+  if (!rc) rc = alloc(&s->opart, S * rows_all * D * sizeof(float));
+  if (!rc) rc = alloc(&s->mpart, S * rows_all * sizeof(float));
+  if (!rc) rc = alloc(&s->lpart, S * rows_all * sizeof(double));
+  if (!rc) rc = alloc(&s->row_m, rows_all * sizeof(float));
+  if (!rc) rc = alloc(&s->row_rinv, rows_all * sizeof(float));
+  if (!rc) rc = alloc(&s->colpart, (size_t)s->score_rsplits_max * s->Hkv * s->cap * sizeof(double));
+  if (!rc) rc = alloc(&s->scores, (size_t)s->cap * sizeof(float));
+  if (!rc) rc = alloc(&s->keep, (size_t)s->cap * sizeof(int32_t));
+  if (!rc) rc = alloc(&s->inv_freq, D / 2 * sizeof(double));
+  if (!rc) rc = alloc(&s->nonfinite, sizeof(int32_t));
+  if (!rc) {
+    double table[64];
+    scaled_inv_freq(s->D, c.rope_base, (double)alpha, c.rope_orig_ctx, table);
+    rc = check(hipMemcpy(s->inv_freq, table, D / 2 * sizeof(double), hipMemcpyHostToDevice));
+  }
+  if (!rc) rc = check(hipMemset(s->nonfinite, 0, sizeof(int32_t)));
+  if (!rc) rc = check(hipMemset(s->keep, 0, (size_t)s->cap * sizeof(int32_t)));
+  if (!rc) rc = check(hipMemset(s->pos[0], 0, (size_t)s->cap * sizeof(int32_t)));
+  if (!rc) rc = check(hipMemset(s->pos[1], 0, (size_t)s->cap * sizeof(int32_t)));
+  if (!rc) {
+    s->ev_ok = true;
+    for (auto& ring : s->ev)
+      for (auto& e : ring)
+        if (s->ev_ok && (hipEventCreate(&e[0]) != hipSuccess || hipEventCreate(&e[1]) != hipSuccess))
+          s->ev_ok = false;
+  }
+  if (rc) {
+    release(s);
+    free(s);
+    return rc;
+  }
+  // Softmax scale: sigma = mscale^2 / sqrt(d), mscale = 0.1 ln(alpha) + 1 (1 when
+  // alpha = 1), applied as 2^(sigma log2(e) x) with the constant split in two
+  // floats so that it carries fp64 accuracy.
+  const double mscale = alpha <= 1.0f ? 1.0 : 0.1 * log((double)alpha) + 1.0;
+  const double cexp = mscale * mscale / sqrt((double)s->D) * M_LOG2E;
+  s->c_hi = (float)cexp;
+  s->c_lo = (float)(cexp - (double)s->c_hi);
+  *out = s;
+  return STATEKV_OK;
+}
+
+int statekv_set_stream(statekv_state* s, void* hip_stream) {
+  if (!s) return STATEKV_EINVAL;
+  s->stream = (hipStream_t)hip_stream;
+  return STATEKV_OK;
+}
+
+int statekv_set_flags(statekv_state* s, uint32_t flags) {
+  if (!s) return STATEKV_EINVAL;
+  if (flags & ~(STATEKV_FLAG_ALWAYS_SCORE | STATEKV_FLAG_KERNEL_TIMING)) return STATEKV_EINVAL;
+  s->flags = flags;
+  return STATEKV_OK;
+}
+
+int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const void* V,
+                          int32_t n, void* O) {
+  if (!s || !Q || !K || !V || !O) return STATEKV_EINVAL;
+  if (n != s->frames_done) return STATEKV_EORDER;
+  if (n >= s->cfg.max_frames) return STATEKV_ECAPACITY;
+  int rc = check(hipSetDevice(s->device));
+  if (rc) return rc;
+
+  const int k0 = s->count;
+  const int P = k0 + s->T;
+  const int cur = s->cur;
+  const hipStream_t st = s->stream;
+
+  {
+    KernelTimer tm(s, STATEKV_K_ROPE);
+    RopeArgs a{};
+    a.q = Q;
+    a.k = K;
+    a.v = V;
+    a.inv_freq = s->inv_freq;
+    a.qrot = s->qrot;
+    a.kpool = s->kbuf[cur];
+    a.vpool = s->vbuf[cur];
+    a.pool_pos = s->pos[cur];
+    a.dk = s->dk;
+    a.dv = s->dv;
+    a.nonfinite = s->nonfinite;
+    a.n = n;
+    a.T = s->T;
+    a.Hq = s->Hq;
+    a.Hkv = s->Hkv;
+    a.G = s->G;
+    a.cap = s->cap;
+    a.k0 = k0;
+    rc = check(launch_rope(s->dt, s->D, a, st));
+    tm.done();
+    if (rc) return rc;
+  }
+  int splits, kps;
+  attn_geometry(s, P, &splits, &kps);
+  {
+    KernelTimer tm(s, STATEKV_K_ATTN);
+    AttnArgs a{};
+    a.qrot = s->qrot;
+    a.kpool = s->kbuf[cur];
+    a.vpool = s->vbuf[cur];
+    a.opart = s->opart;
+    a.mpart = s->mpart;
+    a.lpart = s->lpart;
+    a.c_hi = s->c_hi;
+    a.c_lo = s->c_lo;
+    a.R = s->R;
+    a.G = s->G;
+    a.cap = s->cap;
+    a.P = P;
+    a.k0 = k0;
+    a.kps = kps;
+    a.Hkv = s->Hkv;
+    rc = check(launch_attn(s->dt, s->D, a, s->attn_tiles, splits, st));
+    tm.done();
+    if (rc) return rc;
+  }
+  {
+    KernelTimer tm(s, STATEKV_K_COMBINE);
+    CombineArgs a{};
+    a.opart = s->opart;
+    a.mpart = s->mpart;
+    a.lpart = s->lpart;
+    a.out = O;
+    a.row_m = s->row_m;
+    a.row_rinv = s->row_rinv;
+    a.R = s->R;
+    a.G = s->G;
+    a.Hq = s->Hq;
+    a.Hkv = s->Hkv;
+    a.S = splits;
+    rc = check(launch_combine(s->dt, s->D, a, st));
+    tm.done();
+    if (rc) return rc;
+  }
+
+  const bool evict = P > s->B;
+  if (evict || (s->flags & STATEKV_FLAG_ALWAYS_SCORE)) {
+    int key_blocks, rsplits, rps;
+    score_geometry(s, P, &key_blocks, &rsplits, &rps);
+    {
+      KernelTimer tm(s, STATEKV_K_SCORE);
+      ScoreArgs a{};
+      a.qrot = s->qrot;
+      a.kpool = s->kbuf[cur];
+      a.row_m = s->row_m;
+      a.row_rinv = s->row_rinv;
+      a.colpart = s->colpart;
+      a.c_hi = s->c_hi;
+      a.c_lo = s->c_lo;
+      a.R = s->R;
+      a.G = s->G;
+      a.cap = s->cap;
+      a.P = P;
+      a.k0 = k0;
+      a.rps = rps;
+      a.Hkv = s->Hkv;
+      rc = check(launch_score(s->dt, s->D, a, key_blocks, rsplits, st));
+      tm.done();
+      if (rc) return rc;
+    }
+    {
+      KernelTimer tm(s, STATEKV_K_SELECT);
+      SelectArgs a{};
+      a.colpart = s->colpart;
+      a.scores = s->scores;
+      a.keep = s->keep;
+      a.nparts = rsplits * s->Hkv;
+      a.cap = s->cap;
+      a.P = P;
+      a.B = s->B;
+      a.denom = (double)s->Hq * (double)s->T;
+      rc = check(launch_select(a, st));
+      tm.done();
+      if (rc) return rc;
+    }
+    s->score_frame = n;
+    s->score_pool = P;
+    s->score_kept = std::min(P, (int)s->B);
+    s->score_buf = cur;
+  }
+  if (evict) {
+    KernelTimer tm(s, STATEKV_K_GATHER);
+    GatherArgs a{};
+    a.kcur = s->kbuf[cur];
+    a.vcur = s->vbuf[cur];
+    a.pcur = s->pos[cur];
+    a.knext = s->kbuf[cur ^ 1];
+    a.vnext = s->vbuf[cur ^ 1];
+    a.pnext = s->pos[cur ^ 1];
+    a.keep = s->keep;
+    a.Hkv = s->Hkv;
+    a.cap = s->cap;
+    a.B = s->B;
+    a.row_bytes = s->D * s->esize;
+    rc = check(launch_gather(a, st));
+    tm.done();
+    if (rc) return rc;
+    s->cur = cur ^ 1;
+    s->count = s->B;
+  } else {
+    s->count = P;
+  }
+  s->frames_done = n + 1;
+  s->ev_slot = (s->ev_slot + 1) % statekv_state::kRing;
+  return STATEKV_OK;
+}
+
+int statekv_compressed_view(const statekv_state* s, statekv_view* out) {
+  if (!s || !out) return STATEKV_EINVAL;
+  if (hipSetDevice(s->device) != hipSuccess || hipStreamSynchronize(s->stream) != hipSuccess)
+    return STATEKV_EDEVICE;
+  const int nf = read_nonfinite(s);
+  if (nf) return nf;
+  memset(out, 0, sizeof(*out));
+  out->k = s->kbuf[s->cur];
+  out->v = s->vbuf[s->cur];
+  out->pos = s->pos[s->cur];
+  out->count = s->count;
+  out->head_stride = (int64_t)s->cap * s->D;
+  out->token_stride = s->D;
+  out->n_kv_heads = s->Hkv;
+  out->head_dim = s->D;
+  out->dtype = s->cfg.dtype;
+  out->frames_done = s->frames_done;
+  return STATEKV_OK;
+}
+
+int statekv_detailed_view(const statekv_state* s, statekv_view* out) {
+  if (!s || !out) return STATEKV_EINVAL;
+  if (hipSetDevice(s->device) != hipSuccess || hipStreamSynchronize(s->stream) != hipSuccess)
+    return STATEKV_EDEVICE;
+  const int nf = read_nonfinite(s);
+  if (nf) return nf;
+  memset(out, 0, sizeof(*out));
+  out->k = s->dk;
+  out->v = s->dv;
+  out->pos = nullptr;
+  out->count = (int64_t)s->frames_done * s->T;
+  out->head_stride = s->D;
+  out->token_stride = (int64_t)s->Hkv * s->D;
+  out->n_kv_heads = s->Hkv;
+  out->head_dim = s->D;
+  out->dtype = s->cfg.dtype;
+  out->frames_done = s->frames_done;
+  return STATEKV_OK;
+}
+
+int statekv_scores(const statekv_state* s, statekv_scores_view* out) {
+  if (!s || !out) return STATEKV_EINVAL;
+  if (hipSetDevice(s->device) != hipSuccess || hipStreamSynchronize(s->stream) != hipSuccess)
+    return STATEKV_EDEVICE;
+  memset(out, 0, sizeof(*out));
+  out->frame = s->score_frame;
+  if (s->score_frame < 0) return STATEKV_OK;
+  // The pool of the scored frame stays intact until the next frame: the
+  // gather writes the other buffer.
+  out->scores = s->scores;
+  out->pool_pos = s->pos[s->score_buf];
+  out->keep = s->keep;
+  out->pool = s->score_pool;
+  out->kept = s->score_kept;
+  return STATEKV_OK;
+}
+
+int statekv_kernel_times(statekv_state* s, float* ms, int32_t* launches, int32_t n_kernels,
+                         int32_t reset) {
+  if (!s || n_kernels < 0) return STATEKV_EINVAL;
+  if (hipSetDevice(s->device) != hipSuccess || hipStreamSynchronize(s->stream) != hipSuccess)
+    return STATEKV_EDEVICE;
+  for (int r = 0; r < statekv_state::kRing; ++r)
+    for (int k = 0; k < STATEKV_K_COUNT; ++k) drain_slot(s, r, k);
+  const int n = std::min<int>(n_kernels, STATEKV_K_COUNT);
+  for (int k = 0; k < n; ++k) {
+    if (ms) ms[k] = s->ktime_ms[k];
+    if (launches) launches[k] = s->klaunch[k];
+  }
+  if (reset) {
+    memset(s->ktime_ms, 0, sizeof(s->ktime_ms));
+    memset(s->klaunch, 0, sizeof(s->klaunch));
+  }
+  return STATEKV_OK;
+}
+
+void statekv_destroy(statekv_state* s) {
+  if (!s) return;
+  (void)hipSetDevice(s->device);
+  (void)hipStreamSynchronize(s->stream);
+  release(s);
+  free(s);
+}
+
+}  // extern "C"

@@ -1,0 +1,70 @@
+"""The C ABI library loads and exports what include/statekv.h declares; host-side
+argument checks reject bad calls before touching the device.  No compute."""
+import ctypes
+import math
+
+import pytest
+
+import kv_cache_compression_statekv_amd as skv
+
+
+def test_every_declared_function_is_exported():
+    lib = skv.load_library()
+    names = skv.declared_functions()
+    assert {"statekv_create", "statekv_prefill_frame", "statekv_compressed_view",
+            "statekv_detailed_view", "statekv_destroy"} <= set(names)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_error_strings():
+    for code in range(0, -7, -1):
+        assert skv.error_string(code) and skv.error_string(code) != "unknown error"
+    assert skv.error_string(-99) == "unknown error"
+
+
+def _cfg(**kw):
+    base = dict(n_q_heads=4, n_kv_heads=2, head_dim=64, tokens_per_frame=16, max_frames=4,
+                dtype=skv.DTYPE_BF16, rope_base=1e6, rope_orig_ctx=32768)
+    base.update(kw)
+    return skv.LayerCfg(**base)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(n_q_heads=0), dict(n_kv_heads=0), dict(n_q_heads=6, n_kv_heads=4),
+    dict(head_dim=96), dict(head_dim=32), dict(tokens_per_frame=0), dict(max_frames=0),
+    dict(dtype=7), dict(rope_base=1.0), dict(rope_base=math.inf), dict(rope_orig_ctx=0),
+])
+def test_create_rejects_bad_config(bad):
+    lib = skv.load_library()
+    h = ctypes.c_void_p()
+    cfg = _cfg(**bad)
+    assert lib.statekv_create(ctypes.byref(cfg), 64, 1.0, ctypes.byref(h)) == skv.STATEKV_EINVAL
+    assert not h.value
+
+
+@pytest.mark.parametrize("budget,alpha", [(0, 1.0), (-5, 1.0), (32768, 1.0), (64, 0.5),
+                                          (64, math.nan), (64, math.inf)])
+def test_create_rejects_bad_budget_or_alpha(budget, alpha):
+    lib = skv.load_library()
+    h = ctypes.c_void_p()
+    cfg = _cfg()
+    assert lib.statekv_create(ctypes.byref(cfg), budget, alpha, ctypes.byref(h)) == skv.STATEKV_EINVAL
+
+
+def test_null_arguments_are_rejected():
+    lib = skv.load_library()
+    h = ctypes.c_void_p()
+    assert lib.statekv_create(None, 64, 1.0, ctypes.byref(h)) == skv.STATEKV_EINVAL
+    cfg = _cfg()
+    assert lib.statekv_create(ctypes.byref(cfg), 64, 1.0, None) == skv.STATEKV_EINVAL
+    assert lib.statekv_prefill_frame(None, None, None, None, 0, None) == skv.STATEKV_EINVAL
+    v = skv.View()
+    assert lib.statekv_compressed_view(None, ctypes.byref(v)) == skv.STATEKV_EINVAL
+    assert lib.statekv_detailed_view(None, ctypes.byref(v)) == skv.STATEKV_EINVAL
+    sv = skv.ScoresView()
+    assert lib.statekv_scores(None, ctypes.byref(sv)) == skv.STATEKV_EINVAL
+    assert lib.statekv_set_flags(None, 0) == skv.STATEKV_EINVAL
+    assert lib.statekv_set_stream(None, None) == skv.STATEKV_EINVAL
+    assert lib.statekv_kernel_times(None, None, None, 0, 0) == skv.STATEKV_EINVAL
+    lib.statekv_destroy(None)

@@ -1,0 +1,188 @@
+"""HIP path vs the CPU oracle on the same seeded frames (needs an MI355X).
+
+Every checked frame is teacher-forced: the oracle starts from the GPU's own
+compressed state before that frame.  Bars:
+  * O: max over (token, head) of ||O - O_ref||_inf / ||O_ref||_inf below 2e-2
+    (bf16) or 1e-5 (fp32);
+  * rotated K and V appended to D, and every kept state row: bit-exact;
+  * kept index sets: identical except candidates whose oracle score is within
+    1e-6 relative of the B-th score;
+  * scores (when computed): relative error below 1e-5, summing to 1.
+"""
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_compression_statekv_amd as skv
+from kv_cache_compression_statekv_amd.workload import CONFIGS, FrameStream, StreamConfig
+from gpu_helpers import (StepCheck, assert_step_ok, gpu_state_as_oracle, make_state,
+                         oracle_cfg, output_error, to_device, to_f64)
+from oracle import OracleStream, frame_step
+
+pytestmark = pytest.mark.gpu
+
+
+def _small(name, cid, **kw):
+    base = dict(name=name, config_id=cid, dtype="bf16", n_q_heads=8, n_kv_heads=2,
+                head_dim=64, tokens_per_frame=200, budget=700, n_frames=6, n_layers=1,
+                rope_base=1e6, alpha=1.0, n_sinks=4)
+    base.update(kw)
+    return StreamConfig(**base)
+
+
+SMALL = {
+    "tiny": CONFIGS["tiny"],
+    # rows 800 = 3 full 256-row tiles + 32, pool 900 = 14 key blocks + 4
+    "ragged_bf16_d64": _small("ragged_bf16_d64", 101),
+    "ragged_bf16_d128_yarn": _small("ragged_bf16_d128_yarn", 102, n_q_heads=12, n_kv_heads=4,
+                                    head_dim=128, tokens_per_frame=96, budget=333, n_frames=7,
+                                    alpha=4.0, n_sinks=2),
+    "f32_d128_mha": _small("f32_d128_mha", 103, dtype="f32", n_q_heads=3, n_kv_heads=3,
+                           head_dim=128, tokens_per_frame=33, budget=50, n_frames=5,
+                           rope_base=1e4, alpha=2.0, n_sinks=1),
+    "bf16_t1_b1": _small("bf16_t1_b1", 104, n_q_heads=2, n_kv_heads=1, tokens_per_frame=1,
+                         budget=1, n_frames=6, n_sinks=0),
+    "bf16_g16_b_lt_t": _small("bf16_g16_b_lt_t", 105, n_q_heads=16, n_kv_heads=1,
+                              tokens_per_frame=130, budget=97, n_frames=4, n_sinks=3),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_stream_every_frame(name):
+    wl = SMALL[name]
+    chk = StepCheck(wl, flags=skv.FLAG_ALWAYS_SCORE)
+    for _ in range(wl.n_frames):
+        rep = chk.step(check=True)
+        print(rep, flush=True)
+        assert_step_ok(rep, wl.dtype)
+
+
+# Full per-frame sizes of the five workloads, teacher-forced on sampled frames
+# (the fill boundary, the first evicting frames, later frames).
+FULL = [
+    ("tiny", 0, 8, [0, 1, 2, 3, 7]),
+    ("ivl3_1b", 0, 64, [0, 15, 16, 17, 40, 63]),
+    ("ivl3_2b", 0, 512, [15, 16, 17, 300, 511]),
+    ("ivl3_2b", 27, 24, [16, 23]),
+    ("qwen3vl_2b", 0, 40, [0, 3, 4, 5, 21, 39]),
+    ("qwen3vl_2b", 27, 8, [4, 7]),
+    ("stress", 0, 70, [0, 63, 64, 65, 69]),
+]
+
+
+@pytest.mark.parametrize("name,layer,frames,check", FULL,
+                         ids=[f"{c[0]}-L{c[1]}" for c in FULL])
+def test_full_size_sampled_frames(name, layer, frames, check):
+    wl = CONFIGS[name]
+    chk = StepCheck(wl, layer=layer)
+    worst = {}
+    for n in range(frames):
+        rep = chk.step(check=n in check)
+        if rep is not None:
+            print(name, layer, rep, flush=True)
+            assert_step_ok(rep, wl.dtype)
+            for key in ("out_err", "score_rel_max"):
+                if key in rep:
+                    worst[key] = max(worst.get(key, 0.0), rep[key])
+    print("worst", name, layer, worst, flush=True)
+
+
+def test_bursts_are_exercised():
+    wl = CONFIGS["qwen3vl_2b"]
+    fs = FrameStream(wl, 0)
+    assert any(fs.is_burst_frame(n) for n in range(4, 40))
+
+
+def test_no_eviction_stream_reduces_to_full_attention():
+    """B >= N*T: the GPU stream equals the oracle, which equals causal SDPA over
+    all tokens (pinned on the CPU)."""
+    wl = SMALL["ragged_bf16_d64"].replace(budget=6 * 200 + 5, n_frames=6)
+    chk = StepCheck(wl)
+    for _ in range(wl.n_frames):
+        rep = chk.step(check=True)
+        assert_step_ok(rep, wl.dtype)
+    _, _, pos = chk.st.compressed_view()
+    assert pos.cpu().numpy().tolist() == list(range(6 * 200))
+
+
+def test_exact_ties_keep_the_oldest():
+    """All-zero queries: every state key and the frame's first key tie bit-exactly;
+    with one slot too few the newest of them is evicted, exactly as the oracle."""
+    wl = _small("ties", 106, n_q_heads=2, n_kv_heads=1, tokens_per_frame=8, budget=13,
+                n_frames=3, n_sinks=0)
+    st = make_state(wl)
+    cfg = oracle_cfg(wl)
+    fs = FrameStream(wl)
+    for n in range(2):
+        st.prefill_frame(*[to_device(x, wl.dtype) for x in fs.frame(n)], n=n)
+    Q, K, V = fs.frame(2)
+    Q = np.zeros_like(Q)
+    before = gpu_state_as_oracle(st)
+    st.prefill_frame(*[to_device(x, wl.dtype) for x in (Q, K, V)], n=2)
+    res = frame_step(cfg, before, Q, K, V, 2)
+    _, _, pos = st.compressed_view()
+    assert pos.cpu().numpy().tolist() == res.state.pos.tolist()
+    sc = st.scores()
+    s = sc["scores"].cpu().numpy()
+    assert len(set(s[:14].tolist())) == 1          # 13 state keys + frame key 0
+    assert res.state.pos.tolist() == before.pos.tolist()
+
+
+def test_two_runs_are_bitwise_identical():
+    wl = SMALL["ragged_bf16_d128_yarn"]
+    outs = []
+    for _ in range(2):
+        st = make_state(wl)
+        fs = FrameStream(wl)
+        os_ = [st.prefill_frame(*[to_device(x, wl.dtype) for x in fs.frame(n)], n=n).cpu()
+               for n in range(wl.n_frames)]
+        k, v, pos = st.compressed_view()
+        sc = st.scores()
+        outs.append((os_, k.cpu(), v.cpu(), pos.cpu(), sc["scores"].cpu()))
+        st.close()
+    a, b = outs
+    for x, y in zip(a[0], b[0]):
+        assert torch.equal(x, y)
+    for x, y in zip(a[1:], b[1:]):
+        assert torch.equal(x, y)
+
+
+def test_out_of_order_and_capacity_errors_leave_state_unchanged():
+    wl = SMALL["tiny"].replace(n_frames=2)
+    st = make_state(wl)
+    fs = FrameStream(wl)
+    f0 = [to_device(x, wl.dtype) for x in fs.frame(0)]
+    with pytest.raises(skv.StateKVError) as e:
+        st.prefill_frame(*f0, n=1)
+    assert e.value.code == skv.STATEKV_EORDER
+    st.prefill_frame(*f0, n=0)
+    st.prefill_frame(*[to_device(x, wl.dtype) for x in fs.frame(1)], n=1)
+    with pytest.raises(skv.StateKVError) as e:
+        st.prefill_frame(*f0, n=2)
+    assert e.value.code == skv.STATEKV_ECAPACITY
+    _, _, pos = st.compressed_view()
+    assert pos.numel() == 32
+
+
+def test_nonfinite_input_is_reported():
+    wl = SMALL["tiny"]
+    st = make_state(wl)
+    Q, K, V = FrameStream(wl).frame(0)
+    K = K.copy()
+    K[3, 0, 5] = np.nan
+    st.prefill_frame(*[to_device(x, wl.dtype) for x in (Q, K, V)], n=0)
+    with pytest.raises(skv.StateKVError) as e:
+        st.compressed_view()
+    assert e.value.code == skv.STATEKV_ENONFINITE
+
+
+def test_binding_rejects_bad_tensors():
+    wl = SMALL["tiny"]
+    st = make_state(wl)
+    Q, K, V = [to_device(x, wl.dtype) for x in FrameStream(wl).frame(0)]
+    with pytest.raises(ValueError):
+        st.prefill_frame(Q.to(torch.bfloat16), K, V, n=0)
+    with pytest.raises(ValueError):
+        st.prefill_frame(Q[:, :1], K, V, n=0)
+    with pytest.raises(ValueError):
+        st.prefill_frame(Q.cpu(), K, V, n=0)
