@@ -1,0 +1,240 @@
+#!/usr/bin/env python3
+"""Benchmark of the StateKV frame step on one MI355X (gfx950).
+
+A step is one StateKV frame step of one layer (virtual-position RoPE, append
+to D, attention over [compressed state; frame], scores, Top-B, gather) on one
+frame of the synthetic stream.  Default workload: the InternVL3-1B-like layer
+(bf16, 14 query / 2 KV heads, d = 64, T = 256, B = 4096); the stream generator
+is the seeded one of the tests, extended past its 64 frames when more steps
+are asked for.  All frames are resident in HBM before timing starts; W
+warm-up frames (the first B/T = 16 fill the state) precede K timed steps, so
+every timed step evicts T tokens (constant work per frame).
+
+Printed: one JSON line with frames/s (value), the roofline of the dominant
+kernel (attention pass 1) from HIP events on the library's stream, per-kernel
+times, per-step latency statistics, and the CPU oracle timed on the host
+cores on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "frames/s per layer StateKV step at B=4096,T=256; MFMA % of bf16 peak"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "kv_cache_compression_statekv_amd", "csrc", "statekv_kernels.hip")
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=512, help="timed frame steps (K)")
+    p.add_argument("--warmup", type=int, default=16, help="untimed frames before timing (W)")
+    p.add_argument("--workload", default="ivl3_1b")
+    p.add_argument("--distinct-frames", type=int, default=128,
+                   help="frames drawn from the generator; later steps reuse them cyclically")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="bounded CPU work for the oracle baseline (0 disables it)")
+    p.add_argument("--no-kernel-timing", action="store_true")
+    return p.parse_args()
+
+
+def pair_count(T: int, kept: int) -> int:
+    """Query-key pairs of one head in a frame step: T*kept state pairs + causal frame pairs."""
+    return T * kept + T * (T + 1) // 2
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def load_traffic(kernel: str, workload: str):
+    """HBM bytes per launch measured by rocprofv3 counters, if taken on the current source."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures the StateKV frame step on one GPU only; "
+              f"--gpus {args.gpus} (WORLD_SIZE={world}) is not supported: the step has no "
+              "multi-GPU path in this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import kv_cache_compression_statekv_amd as skv
+    from kv_cache_compression_statekv_amd.workload import CONFIGS, FrameStream
+
+    wl = CONFIGS[args.workload]
+    T, Hq, Hkv, d, B = wl.tokens_per_frame, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.budget
+    fill = math.ceil(B / T)
+    W = max(args.warmup, fill)
+    K = args.steps
+    timing_pass = 0 if args.no_kernel_timing else K
+    total = W + K + timing_pass
+    tdtype = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    # Inputs resident in HBM before timing.
+    fs = FrameStream(wl, 0)
+    distinct = min(total, args.distinct_frames)
+    frames = []
+    for n in range(distinct):
+        q, k, v = fs.frame(n)
+        frames.append(tuple(torch.from_numpy(x).to(tdtype).to(dev).contiguous() for x in (q, k, v)))
+    out = torch.empty((T, Hq, d), dtype=tdtype, device=dev)
+    torch.cuda.synchronize()
+
+    st = skv.StateKV(n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, tokens_per_frame=T,
+                     max_frames=total, budget=B, alpha=wl.alpha, dtype=wl.dtype,
+                     rope_base=wl.rope_base, rope_orig_ctx=wl.rope_orig_ctx)
+    lib, h = st._lib, st._h
+    ptrs = [tuple(t.data_ptr() for t in f) for f in frames]
+    optr = out.data_ptr()
+
+    def step(n):
+        q, k, v = ptrs[n % distinct]
+        rc = lib.statekv_prefill_frame(h, q, k, v, n, optr)
+        if rc:
+            raise skv.StateKVError(rc, f"statekv_prefill_frame({n})")
+
+    for n in range(W):
+        step(n)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for n in range(W, W + K):
+        step(n)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    elapsed = t1 - t0
+    fps = K / elapsed
+
+    # Second pass: per-kernel HIP events (library stream) and per-step events.
+    kernels = {}
+    lat = []
+    if timing_pass:
+        st.set_flags(skv.FLAG_KERNEL_TIMING)
+        st.kernel_times(reset=True)
+        stream = torch.cuda.current_stream()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(timing_pass + 1)]
+        evs[0].record(stream)
+        for i, n in enumerate(range(W + K, W + K + timing_pass)):
+            step(n)
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        lat = [evs[i].elapsed_time(evs[i + 1]) for i in range(timing_pass)]
+        for name, (ms, cnt) in st.kernel_times().items():
+            kernels[name] = {"avg_us": 1e3 * ms / cnt if cnt else None, "launches": cnt}
+        st.set_flags(0)
+
+    pairs = pair_count(T, B)
+    attn_flops = 4.0 * Hq * d * pairs                 # QK^T + PV, causal-counted
+    executed_flops = 6.0 * Hq * d * pairs             # + QK^T recomputed by the score pass
+    roofline = None
+    extra = {}
+    if kernels.get("attn_fwd", {}).get("avg_us"):
+        t_attn = kernels["attn_fwd"]["avg_us"] * 1e-6
+        achieved = attn_flops / t_attn / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                    "traffic": load_traffic("attn_fwd", args.workload)}
+        t_passes = sum(kernels[k]["avg_us"] for k in ("attn_fwd", "attn_score")
+                       if kernels[k]["avg_us"]) * 1e-6
+        extra["attention_passes_mfma_frac"] = round(executed_flops / t_passes / 1e12 / PEAK_BF16_TFLOPS, 4)
+        t_step_kernels = sum(v["avg_us"] for v in kernels.values() if v["avg_us"]) * 1e-6
+        extra["kernel_sum_us_per_step"] = round(t_step_kernels * 1e6, 2)
+    if lat:
+        lat_a = np.array(lat)
+        idx = np.arange(lat_a.size)
+        slope = float(np.polyfit(idx, lat_a, 1)[0]) if lat_a.size > 1 else 0.0
+        q = max(1, lat_a.size // 8)
+        extra["step_latency_us"] = {
+            "median": round(float(np.median(lat_a)) * 1e3, 2),
+            "p99": round(float(np.quantile(lat_a, 0.99)) * 1e3, 2),
+            "slope_us_per_frame": round(slope * 1e3, 5),
+            "last_over_first_median": round(float(np.median(lat_a[-q:]) / np.median(lat_a[:q])), 4),
+        }
+
+    # CPU baseline: the oracle, started from the GPU's state, on the next frames.
+    cpu = None
+    if args.cpu_seconds > 0:
+        from oracle import CompressedState, LayerConfig, frame_step
+        try:
+            from threadpoolctl import threadpool_info
+            blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                                if i.get("user_api") == "blas"] or [1])
+        except Exception:
+            blas_threads = 1
+        cfg = LayerConfig(n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, tokens_per_frame=T,
+                          budget=B, dtype=wl.dtype, rope_base=wl.rope_base, alpha=wl.alpha,
+                          rope_orig_ctx=wl.rope_orig_ctx)
+        kk, vv, pp = st.compressed_view()
+        ostate = CompressedState(kk.float().cpu().numpy().astype(np.float64),
+                                 vv.float().cpu().numpy().astype(np.float64),
+                                 pp.cpu().numpy().astype(np.int64))
+        n0 = total
+        done, tc = 0, 0.0
+        while tc < args.cpu_seconds and done < 64:
+            q, k, v = fs.frame(n0 + done)
+            c0 = time.perf_counter()
+            ostate = frame_step(cfg, ostate, q, k, v, n0 + done).state
+            tc += time.perf_counter() - c0
+            done += 1
+        cpu = {"value": round(done / tc, 4), "unit": "frames/s", "cores": blas_threads,
+               "kind": "oracle",
+               "sample": f"{done} steady-state frames of the same stream (n={n0}..{n0 + done - 1}), "
+                         f"float64 numpy oracle, {tc:.1f} s; cores = BLAS threads of its matrix "
+                         "products (element-wise steps run on one thread)"}
+
+    st.close()
+    rec = {
+        "metric": METRIC,
+        "value": round(fps, 2),
+        "unit": "frames/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(1e3 * elapsed / K, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: 1 layer, Hq={Hq}, Hkv={Hkv}, d={d}, T={T}, B={B}, "
+                               f"alpha={wl.alpha:g}, seeded Gaussian frames with {wl.n_sinks} "
+                               f"drifting sink keys per frame",
+                   "tokens_per_frame": T, "budget": B, "layers": 1},
+        "tokens_per_s": round(fps * T, 1),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        **extra,
+        "attn_fwd_algorithmic_gflop": round(attn_flops / 1e9, 4),
+        "executed_gflop_attention_passes": round(executed_flops / 1e9, 4),
+    }
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()

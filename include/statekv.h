@@ -22,7 +22,9 @@
  *     and all Hq query heads of the layer (masked pairs count as zero), kept
  *     as fp32; one index set per layer is shared by all KV heads;
  *   - Top-B orders by (score descending, position ascending): ties keep the
- *     older token; the new state lists its tokens in ascending position;
+ *     older token.  The state keeps its slots: kept frame tokens take the
+ *     slots of evicted ones, so the state is a set in slot order (not sorted
+ *     by position);
  *   - alpha > 1 applies the YaRN frequency ramp (original window
  *     rope_orig_ctx) and the logit scale sigma = (0.1 ln alpha + 1)^2/sqrt(d);
  *   - K and D store keys after RoPE (positions never change); V has no RoPE.
@@ -76,7 +78,7 @@ typedef struct statekv_state statekv_state;
 typedef struct statekv_view {
   const void*    k;            /* keys after RoPE */
   const void*    v;            /* values */
-  const int32_t* pos;          /* [count] absolute stream positions, ascending
+  const int32_t* pos;          /* [count] absolute stream positions in slot order
                                   (compressed view); NULL for the detailed view */
   int64_t        count;        /* tokens in the view */
   int64_t        head_stride;  /* elements between consecutive KV heads */
@@ -90,8 +92,8 @@ typedef struct statekv_view {
 /* Scores and selection of the most recent frame that computed them. */
 typedef struct statekv_scores_view {
   const float*   scores;    /* [pool] fp32 mean attention of each candidate */
-  const int32_t* pool_pos;  /* [pool] positions of the candidates (old state, then frame) */
-  const int32_t* keep;      /* [kept] indices into the pool that were kept, ascending */
+  const int32_t* pool_pos;  /* [pool] positions of the candidates (state slots, then frame) */
+  const int32_t* keep_flag; /* [pool] 1 if the candidate stayed in the state, else 0 */
   int32_t        pool;      /* candidates: min(B, n*T) + T */
   int32_t        kept;      /* min(B, pool) */
   int32_t        frame;     /* frame index, or -1 if no frame has computed scores */
@@ -130,7 +132,8 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K,
 
 /*
  * Compressed state C after the last frame: k, v are [Hkv][count][d] with
- * head_stride = (B+T)*d and token_stride = d; pos[count] ascending.
+ * head_stride = (B+T)*d and token_stride = d; pos[count] gives each slot's
+ * stream position (slot order; sort by position for a sequence view).
  * Synchronises the state's stream.  Valid until the next prefill_frame or
  * destroy.  Returns ENONFINITE if an input frame held NaN or Inf.
  */
@@ -160,11 +163,10 @@ int statekv_set_flags(statekv_state* s, uint32_t flags);
 /* Kernels of one step, in launch order, as indexed by statekv_kernel_times. */
 #define STATEKV_K_ROPE     0  /* virtual-position RoPE + append to D */
 #define STATEKV_K_ATTN     1  /* fused attention, pass 1 (split over keys) */
-#define STATEKV_K_COMBINE  2  /* merge of key splits, output O and row stats */
-#define STATEKV_K_SCORE    3  /* recompute pass: per-key column sums */
-#define STATEKV_K_SELECT   4  /* Top-B select and compaction list */
-#define STATEKV_K_GATHER   5  /* gather of the kept rows into the next state */
-#define STATEKV_K_COUNT    6
+#define STATEKV_K_SCORE    2  /* recompute pass: per-key column sums */
+#define STATEKV_K_SELECT   3  /* Top-B decision; merge of the key splits into O */
+#define STATEKV_K_MOVES    4  /* kept frame rows move into the evicted slots */
+#define STATEKV_K_COUNT    5
 
 /*
  * With STATEKV_FLAG_KERNEL_TIMING set, per-kernel device time (HIP events on

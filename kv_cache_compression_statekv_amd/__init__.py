@@ -33,7 +33,7 @@ DTYPE_F32 = 2
 FLAG_ALWAYS_SCORE = 1
 FLAG_KERNEL_TIMING = 2
 
-KERNEL_NAMES = ["rope_append", "attn_fwd", "attn_combine", "attn_score", "topb_select", "gather"]
+KERNEL_NAMES = ["rope_append", "attn_fwd", "attn_score", "select_merge", "moves"]
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
                       "include", "statekv.h")
@@ -71,7 +71,7 @@ class ScoresView(ctypes.Structure):
     _fields_ = [
         ("scores", ctypes.c_void_p),
         ("pool_pos", ctypes.c_void_p),
-        ("keep", ctypes.c_void_p),
+        ("keep_flag", ctypes.c_void_p),
         ("pool", ctypes.c_int32),
         ("kept", ctypes.c_int32),
         ("frame", ctypes.c_int32),
@@ -229,7 +229,7 @@ class StateKV:
 
     # -- views (copied into new tensors) ------------------------------------------
     def compressed_view(self):
-        """(Kbar [Hkv][count][d], Vbar [Hkv][count][d], pos [count] int32), copies."""
+        """(Kbar [Hkv][count][d], Vbar [Hkv][count][d], pos [count] int32), copies in slot order."""
         v = View()
         self._check(self._lib.statekv_compressed_view(self._h, ctypes.byref(v)),
                     "statekv_compressed_view")
@@ -249,7 +249,7 @@ class StateKV:
                 _copy_to_tensor(v.v, shape, self.torch_dtype, self.device))
 
     def scores(self):
-        """dict(frame, scores [pool] f32, pool_pos [pool] i32, keep [kept] i32) or None."""
+        """dict(frame, scores [pool] f32, pool_pos [pool] i32, keep_flag [pool] i32) or None."""
         sv = ScoresView()
         self._check(self._lib.statekv_scores(self._h, ctypes.byref(sv)), "statekv_scores")
         if sv.frame < 0:
@@ -258,7 +258,7 @@ class StateKV:
             "frame": sv.frame,
             "scores": _copy_to_tensor(sv.scores, (sv.pool,), torch.float32, self.device),
             "pool_pos": _copy_to_tensor(sv.pool_pos, (sv.pool,), torch.int32, self.device),
-            "keep": _copy_to_tensor(sv.keep, (sv.kept,), torch.int32, self.device),
+            "keep_flag": _copy_to_tensor(sv.keep_flag, (sv.pool,), torch.int32, self.device),
         }
 
     def kernel_times(self, reset: bool = False):

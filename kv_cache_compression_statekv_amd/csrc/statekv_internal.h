@@ -8,12 +8,34 @@ namespace statekv {
 
 enum class Dt : int { BF16 = 1, F32 = 2 };
 
+constexpr int kAttnThreads = 256;
+constexpr int kAttnBN = 64;          // keys per LDS block in attention pass 1
+constexpr int kMaxSplits = 24;       // key splits of pass 1 (merges unroll over them)
+constexpr int kScoreMaxRows = 512;   // rows of one score work-group (row statistics in LDS)
+constexpr int kSelectThreads = 1024;
+constexpr int kMaxPool = 32768;      // B + T limit of the single-work-group select
+constexpr int kSelectBins = 4096;
+constexpr int kSelCand = 1024;       // boundary candidates resolved by rank counting
+// Column sums are accumulated as unsigned 64-bit fixed point with this many
+// fractional bits: integer addition is associative, so the sum does not depend
+// on the order in which work-groups add their partials.  A sum is at most
+// Hq*T (every weight 1), which stays below 2^63 for Hq*T <= 2^22.
+constexpr int kScoreFracBits = 40;
+constexpr int64_t kMaxRowsTimesHeads = 1 << 22;
+
+// Cos / sin table of the scaled RoPE angles, built once per state.
+struct RopeTableArgs {
+  const double* inv_freq;  // [d/2] scaled frequencies
+  float2* table;           // [npos][d/2] (cos, sin) rounded to fp32
+  int32_t npos, half;
+};
+
 // Per-frame arguments of the RoPE + append kernel.
 struct RopeArgs {
   const void* q;          // [T][Hq][d]
   const void* k;          // [T][Hkv][d]
   const void* v;          // [T][Hkv][d]
-  const double* inv_freq; // [d/2] scaled RoPE frequencies
+  const float2* table;    // [max_frames*T][d/2]
   void* qrot;             // [Hkv][G*T][d], row r = token*G + head-in-group
   void* kpool;            // [Hkv][cap][d]: state rows, then this frame's rows
   void* vpool;            // [Hkv][cap][d]
@@ -25,72 +47,74 @@ struct RopeArgs {
 };
 
 // Attention pass 1: one work-group per (row tile, KV head, key split).
+// Per split and row it leaves (m_s, l_s, O_s) with m_s an integer (log2 units)
+// so that merging splits scales by exact powers of two.
 struct AttnArgs {
   const void* qrot;       // [Hkv][R][d]
   const void* kpool;      // [Hkv][cap][d]
   const void* vpool;      // [Hkv][cap][d]
   float* opart;           // [S][Hkv][R][d] unnormalised partial outputs
-  float* mpart;           // [S][Hkv][R] partial row maxima (scaled, log2 units)
-  double* lpart;          // [S][Hkv][R] partial row sums of exp2
-  float c_hi, c_lo;       // sigma * log2(e) split into two floats
+  float* mpart;           // [S][Hkv][R] reference maxima (integers, -inf if empty)
+  double* lpart;          // [S][Hkv][R] partial row sums of 2^(x*c - m_s)
+  float c_hi;             // sigma * log2(e) rounded to fp32
   int32_t R, G, cap, P, k0, kps, Hkv;
-};
-
-struct CombineArgs {
-  const float* opart;
-  const float* mpart;
-  const double* lpart;
-  void* out;              // [T][Hq][d]
-  float* row_m;           // [Hkv][R] final row maxima
-  float* row_rinv;        // [Hkv][R] 1 / row sums
-  int32_t R, G, Hq, Hkv, S;
 };
 
 // Score pass: one work-group per (key block, KV head, row split).
 struct ScoreArgs {
   const void* qrot;
   const void* kpool;
-  const float* row_m;
-  const float* row_rinv;
-  double* colpart;        // [RS][Hkv][cap] per-key column sums
-  float c_hi, c_lo;
-  int32_t R, G, cap, P, k0, rps, Hkv;
+  const float* mpart;
+  const double* lpart;
+  unsigned long long* colsum;  // [cap] column sums, fixed point (2^-kScoreFracBits units)
+  float c_hi, c_lo;            // sigma * log2(e) = c_hi + c_lo
+  int32_t R, G, cap, P, k0, rps, Hkv, S;
 };
 
+// Work-group 0: scores and the Top-B decision; work-groups 1..: the merge of
+// the key splits of pass 1 into O (independent of the selection).
 struct SelectArgs {
-  const double* colpart;  // [nparts][cap]
-  float* scores;          // [P]
-  int32_t* keep;          // [B]
-  int32_t nparts, cap, P, B;
-  double denom;           // Hq * T
+  unsigned long long* colsum;  // [cap] fixed-point column sums; cleared after reading
+  const int32_t* pool_pos;     // [cap] positions of the pool rows
+  float* scores;               // [P] out: fp32 scores
+  int32_t* score_pos;          // [P] out: positions of the scored pool
+  int32_t* keep_flag;          // [P] out: 1 if the candidate stays in the state
+  int32_t* move_dst;           // [T] out: evicted state slots (< B), ascending
+  int32_t* move_src;           // [T] out: kept rows beyond B, ascending
+  int32_t* move_count;         // [1] out
+  int32_t P, B, mode;          // mode: kSelMerge, kSelScores or kSelEvict
+  double denom;                // Hq * T
+  const float* opart;
+  const float* mpart;
+  const double* lpart;
+  void* out;                   // [T][Hq][d]
+  int32_t Hkv, R, G, Hq, S;
 };
+constexpr int kSelMerge = 0;   // merge only (the pool fits in B and is not scored)
+constexpr int kSelScores = 1;  // scores, everything kept
+constexpr int kSelEvict = 2;   // scores and Top-B
 
-struct GatherArgs {
-  const void* kcur;
-  const void* vcur;
-  const int32_t* pcur;
-  void* knext;
-  void* vnext;
-  int32_t* pnext;
-  const int32_t* keep;
-  int32_t Hkv, cap, B, row_bytes;
+// Applies the moves of the selection: row move_src[i] -> slot move_dst[i] of
+// every KV head, and its position.
+struct MovesArgs {
+  void* kpool;
+  void* vpool;
+  int32_t* pool_pos;
+  const int32_t* move_dst;
+  const int32_t* move_src;
+  const int32_t* move_count;
+  int32_t Hkv, cap, B, row_bytes, max_moves;
 };
-
-constexpr int kAttnThreads = 256;
-constexpr int kAttnBN = 64;          // keys per block in pass 1
-constexpr int kSelectThreads = 1024;
-constexpr int kMaxPool = 32768;      // B + T limit of the single-work-group select
-constexpr int kSelectBins = 4096;
 
 // Rows handled by one pass-1 work-group / keys by one score work-group.
-int attn_rows_per_wg(Dt dt);
+int attn_rows_per_wg(Dt dt, int d);
 int score_keys_per_wg(Dt dt);
 
+hipError_t launch_rope_table(const RopeTableArgs& a, hipStream_t s);
 hipError_t launch_rope(Dt dt, int d, const RopeArgs& a, hipStream_t s);
 hipError_t launch_attn(Dt dt, int d, const AttnArgs& a, int row_tiles, int splits, hipStream_t s);
-hipError_t launch_combine(Dt dt, int d, const CombineArgs& a, hipStream_t s);
 hipError_t launch_score(Dt dt, int d, const ScoreArgs& a, int key_blocks, int rsplits, hipStream_t s);
-hipError_t launch_select(const SelectArgs& a, hipStream_t s);
-hipError_t launch_gather(const GatherArgs& a, hipStream_t s);
+hipError_t launch_select(Dt dt, int d, const SelectArgs& a, hipStream_t s);
+hipError_t launch_moves(const MovesArgs& a, hipStream_t s);
 
 }  // namespace statekv

@@ -6,14 +6,16 @@
 //                       fixed scaled frequencies; 整体框架 / flowchart node E:
 //                       the frame's K, V are appended to the detailed cache D.
 //   attn_fwd_kernel     关键设计 1: the frame's queries attend over
-//   combine_kernel      [Kbar_{n-1}; K_n] (bf16 MFMA, online softmax, split
-//                       over keys, then merged).
+//                       [Kbar_{n-1}; K_n] (bf16 MFMA, online softmax, split
+//                       over keys; the splits are merged by select_kernel).
 //   attn_score_kernel   关键设计 2: score of candidate j = attention weight paid
 //                       to j averaged over the frame's queries and query heads;
 //                       recomputed with the final row max / sum of pass 1.
-//   topb_select_kernel  关键设计 2: TopK({s_j}, B), ties kept toward the older
-//                       token, emitted in ascending position.
-//   gather_kernel       关键设计 2: build C_n from the kept candidates.
+//   select_kernel       关键设计 2: TopK({s_j}, B), ties kept toward the older
+//                       token; its other work-groups merge the key splits of
+//                       the attention output.
+//   moves_kernel        关键设计 2: build C_n from the kept candidates (kept
+//                       frame rows move into the evicted slots).
 //
 // Matrix-core tiles use v_mfma_f32_32x32x16_bf16 (bf16 storage) or
 // v_mfma_f32_32x32x2_f32 (fp32 storage).  Accumulator layout of a 32x32 tile:
@@ -23,6 +25,7 @@
 #include "statekv_internal.h"
 
 #include <math.h>
+#include <stdlib.h>
 
 namespace statekv {
 namespace {
@@ -110,85 +113,147 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 // ---------------------------------------------------------------------------
 // RoPE at virtual positions + append to the detailed cache.
-// One thread per (token, group of 4 rotation pairs), looping over all heads so
-// that each cos/sin is evaluated once.  Rotation of the pair (x1, x2) =
-// (x[k], x[k + d/2]) is computed in fp64 with one fused multiply-add per
-// output (the other product is exact in fp64) and rounded once to storage.
+// Every (token, head, 8 rotation pairs) has its own thread: x1 = x[k..k+8),
+// x2 = x[k+d/2..k+d/2+8) are rotated by the table's fp32 cos / sin of
+// position nT + i in fp64, with one fused multiply-add per output (the other
+// product is exact in fp64), and rounded once to storage.  Rotated queries go
+// to the grouped query buffer; rotated keys and the values go to the pool's
+// frame rows and to D.
 // ---------------------------------------------------------------------------
+template <class E> struct Vec8;
+template <> struct Vec8<BF16> {
+  static __device__ __forceinline__ void load(const uint16_t* p, float* x) {
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[2 * j] = __uint_as_float(v[j] << 16);
+      x[2 * j + 1] = __uint_as_float(v[j] & 0xffff0000u);
+    }
+  }
+  static __device__ __forceinline__ void store(uint16_t* p, const uint16_t* y) {
+    u32x4_t v;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = (uint32_t)y[2 * j] | ((uint32_t)y[2 * j + 1] << 16);
+    *reinterpret_cast<u32x4_t*>(p) = v;
+  }
+};
+template <> struct Vec8<F32> {
+  static __device__ __forceinline__ void load(const float* p, float* x) {
+    const f32x4_t a = *reinterpret_cast<const f32x4_t*>(p);
+    const f32x4_t b = *reinterpret_cast<const f32x4_t*>(p + 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[j] = a[j];
+      x[4 + j] = b[j];
+    }
+  }
+  static __device__ __forceinline__ void store(float* p, const float* y) {
+    *reinterpret_cast<f32x4_t*>(p) = f32x4_t{y[0], y[1], y[2], y[3]};
+    *reinterpret_cast<f32x4_t*>(p + 4) = f32x4_t{y[4], y[5], y[6], y[7]};
+  }
+};
+
+// cos / sin of (p * theta_k) for every stream position p and frequency k,
+// evaluated in fp64 and rounded to fp32; built once when the state is created.
+__global__ __launch_bounds__(256) void rope_table_kernel(RopeTableArgs a) {
+  const size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= (size_t)a.npos * a.half) return;
+  const int p = (int)(t / a.half), k = (int)(t - (size_t)p * a.half);
+  double sn, cs;
+  sincos((double)p * a.inv_freq[k], &sn, &cs);
+  a.table[t] = float2{(float)cs, (float)sn};
+}
+
+constexpr int kRopeTokensPerWG = 4;
+
 template <class E, int D>
 __global__ __launch_bounds__(256) void rope_append_kernel(RopeArgs a) {
   typedef typename E::T T;
   constexpr int HALF = D / 2;
-  constexpr int PPT = 4;
-  constexpr int TPT = HALF / PPT;
-  const int gt = blockIdx.x * blockDim.x + threadIdx.x;
-  const int tok = gt / TPT;
-  if (tok >= a.T) return;
-  const int k = (gt - tok * TPT) * PPT;
-  const int pos = a.n * a.T + tok;
-
-  double c[PPT], s[PPT];
-#pragma unroll
-  for (int j = 0; j < PPT; ++j) {
-    double sn, cs;
-    sincos((double)pos * a.inv_freq[k + j], &sn, &cs);
-    c[j] = (double)(float)cs;
-    s[j] = (double)(float)sn;
-  }
+  constexpr int TPW = kRopeTokensPerWG;
+  constexpr int CH = HALF / 8;  // 8-pair chunks per head
+  const int tid = threadIdx.x;
+  const int tok0 = blockIdx.x * TPW;
   bool finite = true;
-
-  auto rotate = [&](const T* src, T* dst0, T* dst1) {
-#pragma unroll
-    for (int j = 0; j < PPT; ++j) {
-      const float x1f = Store<E>::load(src + k + j);
-      const float x2f = Store<E>::load(src + k + j + HALF);
-      finite &= isfinite(x1f) && isfinite(x2f);
-      const double x1 = x1f, x2 = x2f;
-      const T y1 = Store<E>::from_f64(fma(x1, c[j], -(x2 * s[j])));
-      const T y2 = Store<E>::from_f64(fma(x2, c[j], x1 * s[j]));
-      dst0[k + j] = y1;
-      dst0[k + j + HALF] = y2;
-      if (dst1) {
-        dst1[k + j] = y1;
-        dst1[k + j + HALF] = y2;
-      }
-    }
-  };
-
+  const int nh = a.Hq + a.Hkv;
   const size_t rows_per_group = (size_t)a.G * a.T;
-  for (int h = 0; h < a.Hq; ++h) {
-    const int g = h / a.G;
-    const int hl = h - g * a.G;
-    const T* src = (const T*)a.q + ((size_t)tok * a.Hq + h) * D;
-    T* dst = (T*)a.qrot + ((size_t)g * rows_per_group + (size_t)tok * a.G + hl) * D;
-    rotate(src, dst, nullptr);
-  }
-  for (int g = 0; g < a.Hkv; ++g) {
-    const T* src = (const T*)a.k + ((size_t)tok * a.Hkv + g) * D;
-    T* pool = (T*)a.kpool + ((size_t)g * a.cap + a.k0 + tok) * D;
-    T* det = (T*)a.dk + ((size_t)pos * a.Hkv + g) * D;
-    rotate(src, pool, det);
-    const T* vs = (const T*)a.v + ((size_t)tok * a.Hkv + g) * D;
-    T* vpool = (T*)a.vpool + ((size_t)g * a.cap + a.k0 + tok) * D;
-    T* vdet = (T*)a.dv + ((size_t)pos * a.Hkv + g) * D;
+  for (int t = tid; t < TPW * nh * CH; t += 256) {
+    const int c = t % CH;
+    const int rest = t / CH;
+    const int hd = rest % nh;
+    const int lt = rest / nh;
+    const int tok = tok0 + lt;
+    if (tok >= a.T) continue;
+    const int k = c * 8;
+    const int pos = a.n * a.T + tok;
+    const T* src;
+    T* dst0;
+    T* dst1 = nullptr;
+    if (hd < a.Hq) {
+      const int g = hd / a.G, hl = hd - g * a.G;
+      src = (const T*)a.q + ((size_t)tok * a.Hq + hd) * D;
+      dst0 = (T*)a.qrot + ((size_t)g * rows_per_group + (size_t)tok * a.G + hl) * D;
+    } else {
+      const int g = hd - a.Hq;
+      src = (const T*)a.k + ((size_t)tok * a.Hkv + g) * D;
+      dst0 = (T*)a.kpool + ((size_t)g * a.cap + a.k0 + tok) * D;
+      dst1 = (T*)a.dk + ((size_t)pos * a.Hkv + g) * D;
+    }
+    float x1[8], x2[8];
+    Vec8<E>::load(src + k, x1);
+    Vec8<E>::load(src + k + HALF, x2);
+    const f32x4_t* tb = reinterpret_cast<const f32x4_t*>(a.table + (size_t)pos * HALF + k);
+    f32x4_t cs4[4];
 #pragma unroll
-    for (int j = 0; j < PPT; ++j) {
-      const T v1 = vs[k + j], v2 = vs[k + j + HALF];
-      finite &= isfinite(Store<E>::load(&v1)) && isfinite(Store<E>::load(&v2));
-      vpool[k + j] = v1;
-      vpool[k + j + HALF] = v2;
-      vdet[k + j] = v1;
-      vdet[k + j + HALF] = v2;
+    for (int j = 0; j < 4; ++j) cs4[j] = tb[j];   // (cos, sin) of pairs k+2j, k+2j+1
+    T y1[8], y2[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      finite &= isfinite(x1[j]) && isfinite(x2[j]);
+      const double cc = cs4[j >> 1][2 * (j & 1)], ss = cs4[j >> 1][2 * (j & 1) + 1];
+      const double u = x1[j], v = x2[j];
+      y1[j] = Store<E>::from_f64(fma(u, cc, -(v * ss)));
+      y2[j] = Store<E>::from_f64(fma(v, cc, u * ss));
+    }
+    Vec8<E>::store(dst0 + k, y1);
+    Vec8<E>::store(dst0 + k + HALF, y2);
+    if (dst1) {
+      Vec8<E>::store(dst1 + k, y1);
+      Vec8<E>::store(dst1 + k + HALF, y2);
     }
   }
-  if (k == 0) a.pool_pos[a.k0 + tok] = pos;
+  // Values: copied unrotated to the pool and to D, 16 bytes per task.
+  constexpr int VEC = 16 / (int)sizeof(T);
+  constexpr int VCH = D / VEC;
+  for (int t = tid; t < TPW * a.Hkv * VCH; t += 256) {
+    const int c = t % VCH;
+    const int rest = t / VCH;
+    const int g = rest % a.Hkv;
+    const int lt = rest / a.Hkv;
+    const int tok = tok0 + lt;
+    if (tok >= a.T) continue;
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>((const T*)a.v + ((size_t)tok * a.Hkv + g) * D + c * VEC);
+    if constexpr (sizeof(T) == 2) {
+      float x[8];
+      Vec8<BF16>::load(reinterpret_cast<const uint16_t*>(&v), x);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) finite &= isfinite(x[j]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) finite &= isfinite(__uint_as_float(v[j]));
+    }
+    *reinterpret_cast<u32x4_t*>((T*)a.vpool + ((size_t)g * a.cap + a.k0 + tok) * D + c * VEC) = v;
+    *reinterpret_cast<u32x4_t*>((T*)a.dv + ((size_t)(a.n * a.T + tok) * a.Hkv + g) * D + c * VEC) = v;
+  }
+  if (tid < TPW && tok0 + tid < a.T) a.pool_pos[a.k0 + tok0 + tid] = a.n * a.T + tok0 + tid;
   if (!finite) atomicOr(a.nonfinite, 1);
 }
 
 // ---------------------------------------------------------------------------
-// Attention pass 1.  Work-group = 4 waves; each wave owns QT tiles of 32 query
+// Attention pass 1.  Work-group = NW waves; each wave owns QT tiles of 32 query
 // rows of one KV group (rows r = token*G + head-in-group) and the work-group
-// walks its key split in blocks of 64 keys staged in LDS.
+// walks its key split in blocks of 64 keys, double-buffered in LDS: the next
+// block's global loads are in flight while the current block is computed.
 //
 // S^T = K Q^T puts one query per lane column, so row max / row sum reduce
 // inside the lane plus one exchange with lane l^32.  O^T = V^T P^T reuses the
@@ -196,20 +261,186 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeArgs a) {
 // supplies to one instruction are keys {16m + 8(t/4) + 4(l/32) + t%4}, so V^T
 // is written to LDS with bits 2 and 3 of the key index swapped inside each
 // group of 16, which makes those eight keys contiguous (one 16-byte read).
+//
+// Visibility: key j is visible to a query of token i iff j < k0 + i + 1 (all
+// state keys, the frame's keys causally) and j lies in this split.  Blocks
+// that every row of the work-group sees in full take the unmasked path.
+// Exponent: p = 2^(x*c_hi - m) with c_hi = sigma*log2(e) rounded to fp32; the
+// row sum l only needs the weights near the maximum, whose exponent error
+// c_lo*x is common to them, so it stays within about 1e-7 of the exact sum.
 // ---------------------------------------------------------------------------
-template <class E, int D, int QT>
-__global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
+template <class E, int D, int NT>
+struct AttnStage {
+  typedef typename E::T T;
+  static constexpr int BN = kAttnBN;
+  static constexpr int EPV = 16 / (int)sizeof(T);
+  static constexpr int KSTR = D + EPV;
+  static constexpr int VSTR = BN + EPV;
+  static constexpr int KCH = BN * (D / EPV) / NT;          // 16-byte K chunks / thread
+  // bf16 V^T: tasks of KG consecutive keys x 8 dims
+  static constexpr int KG = (BN / 4) * (D / 8) >= NT ? 4 : 2;
+  static constexpr int VTASKS = (BN / KG) * (D / 8);
+  static constexpr int VT_PER = (VTASKS + NT - 1) / NT;
+  static constexpr int VCH = sizeof(T) == 2 ? KG * VT_PER : KCH;
+  static_assert(KCH >= 1 && (BN * (D / EPV)) % NT == 0, "K staging shape");
+
+  u32x4_t kr[KCH];
+  u32x4_t vr[VCH];
+
+  __device__ __forceinline__ void load(const T* kbase, const T* vbase, int kb, int kend, int tid) {
+    constexpr int CPR = D / EPV;
+#pragma unroll
+    for (int j = 0; j < KCH; ++j) {
+      const int t = tid + j * NT;
+      const int rr = t / CPR, cc = t - rr * CPR;
+      const int key = kb + rr;
+      kr[j] = u32x4_t{0u, 0u, 0u, 0u};
+      if (key < kend) kr[j] = *reinterpret_cast<const u32x4_t*>(kbase + (size_t)key * D + cc * EPV);
+    }
+    if constexpr (sizeof(T) == 2) {
+      constexpr int NKQ = BN / KG;
+#pragma unroll
+      for (int u = 0; u < VT_PER; ++u) {
+        const int t = tid + u * NT;
+        const int kq = t % NKQ, dc = t / NKQ;
+#pragma unroll
+        for (int j = 0; j < KG; ++j) {
+          const int key = kb + kq * KG + j;
+          vr[u * KG + j] = u32x4_t{0u, 0u, 0u, 0u};
+          if (t < VTASKS && key < kend)
+            vr[u * KG + j] = *reinterpret_cast<const u32x4_t*>(vbase + (size_t)key * D + dc * 8);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < VCH; ++j) {
+        const int t = tid + j * NT;
+        const int rr = t % BN, cc = t / BN;
+        const int key = kb + rr;
+        vr[j] = u32x4_t{0u, 0u, 0u, 0u};
+        if (key < kend) vr[j] = *reinterpret_cast<const u32x4_t*>(vbase + (size_t)key * D + cc * 4);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(T* Ks, T* Vt, int tid) const {
+    constexpr int CPR = D / EPV;
+#pragma unroll
+    for (int j = 0; j < KCH; ++j) {
+      const int t = tid + j * NT;
+      const int rr = t / CPR, cc = t - rr * CPR;
+      *reinterpret_cast<u32x4_t*>(&Ks[rr * KSTR + cc * EPV]) = kr[j];
+    }
+    if constexpr (sizeof(T) == 2) {
+      constexpr int NKQ = BN / KG;
+#pragma unroll
+      for (int u = 0; u < VT_PER; ++u) {
+        const int t = tid + u * NT;
+        if (t >= VTASKS) continue;
+        const int kq = t % NKQ, dc = t / NKQ;
+        const int kk = kq * KG;
+        const int slot = (kk & ~12) | ((kk & 4) << 1) | ((kk & 8) >> 1);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          uint32_t w[KG];
+#pragma unroll
+          for (int j = 0; j < KG; ++j) w[j] = vr[u * KG + j][e >> 1];
+          if constexpr (KG == 4) {
+            uint32_t lo, hi;
+            if (e & 1) {
+              lo = (w[0] >> 16) | (w[1] & 0xffff0000u);
+              hi = (w[2] >> 16) | (w[3] & 0xffff0000u);
+            } else {
+              lo = (w[0] & 0xffffu) | (w[1] << 16);
+              hi = (w[2] & 0xffffu) | (w[3] << 16);
+            }
+            *reinterpret_cast<u32x2_t*>(&Vt[(dc * 8 + e) * VSTR + slot]) = u32x2_t{lo, hi};
+          } else {
+            const uint32_t lo = (e & 1) ? ((w[0] >> 16) | (w[1] & 0xffff0000u))
+                                        : ((w[0] & 0xffffu) | (w[1] << 16));
+            *reinterpret_cast<uint32_t*>(&Vt[(dc * 8 + e) * VSTR + slot]) = lo;
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < VCH; ++j) {
+        const int t = tid + j * NT;
+        const int rr = t % BN, cc = t / BN;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Vt[(cc * 4 + e) * VSTR + rr] = __uint_as_float(vr[j][e]);
+      }
+    }
+  }
+};
+
+// Online softmax over one 32-key sub-tile (S^T accumulators: 16 keys per lane
+// for the lane's query, the other 16 in lane l^32).  Overwrites the scores
+// with p = 2^(x*c_hi - m) and returns in alpha the factor that rescales the
+// earlier output.  The reference m is an integer (log2 units) that moves only
+// when the row maximum exceeds it by more than kLazyRescale, to ceil(max): the
+// weights stay below 2^kLazyRescale, rescaling is rare and every rescale or
+// merge factor 2^(m_old - m_new) is an exact power of two.
+constexpr float kLazyRescale = 8.f;
+
+template <int QT, bool MASK>
+__device__ __forceinline__ void online_softmax(f32x16_t (&sacc)[QT], float (&m_run)[QT],
+                                               double (&l_run)[QT], float (&alpha)[QT],
+                                               const int (&lim)[QT], int kb, int hh,
+                                               float c_hi) {
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if constexpr (MASK) {
+        const int key = kb + 8 * (i >> 2) + 4 * hh + (i & 3);
+        sacc[qt][i] = key < lim[qt] ? sacc[qt][i] : -INFINITY;
+      }
+      mx = fmaxf(mx, sacc[qt][i]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * c_hi;
+    alpha[qt] = 1.f;
+    if (__ballot(mx > m_run[qt] + kLazyRescale)) {   // rare after the first sub-tile
+      if (mx > m_run[qt] + kLazyRescale) {
+        const float m_new = ceilf(mx);
+        if (m_run[qt] == -INFINITY) {
+          alpha[qt] = 0.f;
+          l_run[qt] = 0.0;
+        } else {
+          const int dm = (int)(m_run[qt] - m_new);
+          alpha[qt] = ldexpf(1.f, dm);
+          l_run[qt] = ldexp(l_run[qt], dm);
+        }
+        m_run[qt] = m_new;
+      }
+    }
+    const float m_use = m_run[qt] == -INFINITY ? 0.f : m_run[qt];
+    float rs = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float p = fast_exp2(fmaf(sacc[qt][i], c_hi, -m_use));
+      sacc[qt][i] = p;
+      rs += p;
+    }
+    l_run[qt] += (double)rs;
+  }
+}
+
+template <class E, int D, int QT, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void attn_fwd_kernel(AttnArgs a) {
   typedef typename E::T T;
   typedef Mma<E> M;
+  constexpr int NT = 64 * NW;
+  typedef AttnStage<E, D, NT> Stage;
   constexpr int BN = kAttnBN;
-  constexpr int EPV = 16 / (int)sizeof(T);  // elements per 16-byte vector
-  constexpr int KSTR = D + EPV;              // LDS pitch of K rows
-  constexpr int VSTR = BN + EPV;             // LDS pitch of V^T rows
+  constexpr int KSTR = Stage::KSTR;
+  constexpr int VSTR = Stage::VSTR;
   constexpr int NKS = D / M::KS;
   constexpr int NDT = D / 32;
-  constexpr int BM = 4 * 32 * QT;
-  __shared__ __attribute__((aligned(16))) T Ks[BN * KSTR];
-  __shared__ __attribute__((aligned(16))) T Vt[D * VSTR];
+  constexpr int BM = NW * 32 * QT;
+  __shared__ __attribute__((aligned(16))) T Ks[2][BN * KSTR];
+  __shared__ __attribute__((aligned(16))) T Vt[2][D * VSTR];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -221,18 +452,20 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
   const int need_end = a.k0 + row_last / a.G + 1;  // keys beyond are masked for every row
   const int kbeg = split * a.kps;
   const int kend = min(min(kbeg + a.kps, need_end), a.P);
+  // Blocks ending at or before this key are visible to every row of the work-group.
+  const int full_end = min(kend, a.k0 + tok_min + 1);
 
   const T* qbase = (const T*)a.qrot + (size_t)g * a.R * D;
   const T* kbase = (const T*)a.kpool + (size_t)g * a.cap * D;
   const T* vbase = (const T*)a.vpool + (size_t)g * a.cap * D;
 
   typename M::Frag qf[QT][NKS];
-  int qrow[QT], qtok[QT];
+  int qrow[QT], lim[QT];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     const int r = row_wg + (wave * QT + qt) * 32 + col;
     qrow[qt] = r;
-    qtok[qt] = r < a.R ? r / a.G : -1;
+    lim[qt] = min(kend, a.k0 + (r < a.R ? r / a.G : -1) + 1);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
       qf[qt][ks] = r < a.R ? M::ld(qbase + (size_t)r * D + ks * M::KS + hh * M::KL) : M::zero();
@@ -249,163 +482,79 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
     l_run[qt] = 0.0;
   }
 
-  for (int kb = kbeg; kb < kend; kb += BN) {
-    __syncthreads();
-    // Stage K rows [kb, kb + BN) (zero past the split end).
-    {
-      constexpr int CPR = D / EPV;
-      for (int t = tid; t < BN * CPR; t += kAttnThreads) {
-        const int rr = t / CPR, cc = t - rr * CPR;
-        const int key = kb + rr;
-        u32x4_t v = {0u, 0u, 0u, 0u};
-        if (key < kend) v = *reinterpret_cast<const u32x4_t*>(kbase + (size_t)key * D + cc * EPV);
-        *reinterpret_cast<u32x4_t*>(&Ks[rr * KSTR + cc * EPV]) = v;
-      }
-    }
-    // Stage V^T.
-    if constexpr (sizeof(T) == 2) {
-      constexpr int NKQ = BN / 4;  // key quads
-      for (int t = tid; t < NKQ * (D / 8); t += kAttnThreads) {
-        const int kq = t % NKQ, dc = t / NKQ;
-        const int key0 = kb + kq * 4;
-        u32x4_t r4[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          r4[j] = u32x4_t{0u, 0u, 0u, 0u};
-          if (key0 + j < kend)
-            r4[j] = *reinterpret_cast<const u32x4_t*>(vbase + (size_t)(key0 + j) * D + dc * 8);
-        }
-        const int kk = kq * 4;
-        const int slot = (kk & ~12) | ((kk & 4) << 1) | ((kk & 8) >> 1);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t w0 = r4[0][e >> 1], w1 = r4[1][e >> 1];
-          const uint32_t w2 = r4[2][e >> 1], w3 = r4[3][e >> 1];
-          uint32_t lo, hi;
-          if (e & 1) {
-            lo = (w0 >> 16) | (w1 & 0xffff0000u);
-            hi = (w2 >> 16) | (w3 & 0xffff0000u);
-          } else {
-            lo = (w0 & 0xffffu) | (w1 << 16);
-            hi = (w2 & 0xffffu) | (w3 << 16);
-          }
-          *reinterpret_cast<u32x2_t*>(&Vt[(dc * 8 + e) * VSTR + slot]) = u32x2_t{lo, hi};
-        }
-      }
-    } else {
-      for (int t = tid; t < BN * (D / 4); t += kAttnThreads) {
-        const int rr = t % BN, cc = t / BN;
-        const int key = kb + rr;
-        f32x4_t v = {0.f, 0.f, 0.f, 0.f};
-        if (key < kend) v = *reinterpret_cast<const f32x4_t*>(vbase + (size_t)key * D + cc * 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) Vt[(cc * 4 + e) * VSTR + rr] = v[e];
-      }
-    }
-    __syncthreads();
+  Stage stage;
+  const int nblk = kend > kbeg ? (kend - kbeg + BN - 1) / BN : 0;
+  if (nblk > 0) {
+    stage.load(kbase, vbase, kbeg, kend, tid);
+    stage.store(Ks[0], Vt[0], tid);
+  }
+  __syncthreads();
 
-    // S^T tiles: 2 sub-tiles of 32 keys x QT tiles of 32 queries.
-    f32x16_t sacc[2][QT];
+  for (int b = 0; b < nblk; ++b) {
+    const int kb = kbeg + b * BN;
+    const int buf = b & 1;
+    if (b + 1 < nblk) stage.load(kbase, vbase, kb + BN, kend, tid);
+    const T* ks_ = Ks[buf];
+    const T* vt_ = Vt[buf];
+
+    // Two sub-tiles of 32 keys: S^T = K Q^T, softmax, O^T += V^T P^T.
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
+      const int ksub = kb + sub * 32;
+      f32x16_t sacc[QT];
 #pragma unroll
-      for (int qt = 0; qt < QT; ++qt) sacc[sub][qt] = f32x16_t{};
+      for (int qt = 0; qt < QT; ++qt) sacc[qt] = f32x16_t{};
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const typename M::Frag af = M::ld(&Ks[(sub * 32 + col) * KSTR + ks * M::KS + hh * M::KL]);
+        const typename M::Frag af = M::ld(&ks_[(sub * 32 + col) * KSTR + ks * M::KS + hh * M::KL]);
 #pragma unroll
-        for (int qt = 0; qt < QT; ++qt) sacc[sub][qt] = M::mma(af, qf[qt][ks], sacc[sub][qt]);
+        for (int qt = 0; qt < QT; ++qt) sacc[qt] = M::mma(af, qf[qt][ks], sacc[qt]);
       }
-    }
 
-    // Online softmax, one query per lane column.
-    const bool need_mask = (kb + BN > a.k0 + tok_min) || (kb + BN > kend);
-    float pv[QT][2][16];
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float x = sacc[sub][qt][i];
-          bool vis = true;
-          if (need_mask) {
-            const int key = kb + sub * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-            vis = key < kend && (key < a.k0 || key - a.k0 <= qtok[qt]);
-          }
-          mx = vis ? fmaxf(mx, x) : mx;
-        }
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      float m_new = m_run[qt];
-      if (mx != -INFINITY) m_new = fmaxf(m_new, mx * a.c_hi);
-      float rs = 0.f;
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float x = sacc[sub][qt][i];
-          float p = 0.f;
-          if (m_new != -INFINITY) p = fast_exp2(fmaf(x, a.c_lo, fmaf(x, a.c_hi, -m_new)));
-          if (need_mask) {
-            const int key = kb + sub * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-            const bool vis = key < kend && (key < a.k0 || key - a.k0 <= qtok[qt]);
-            p = vis ? p : 0.f;
-          }
-          pv[qt][sub][i] = p;
-          rs += p;
-        }
-      }
-      float alpha = 1.f;
-      if (m_new != m_run[qt]) {
-        const double al = exp2((double)m_run[qt] - (double)m_new);
-        l_run[qt] *= al;
-        alpha = (float)al;
-      }
-      l_run[qt] += (double)rs;
-      m_run[qt] = m_new;
-      if (__ballot(alpha != 1.f)) {
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) o[qt][dt] *= alpha;
-      }
-    }
-
-    // O^T += V^T P^T.
-    if constexpr (sizeof(T) == 2) {
-      bf16x8_t pf[QT][2][2];
+      float alpha[QT];
+      if (ksub + 32 > full_end)
+        online_softmax<QT, true>(sacc, m_run, l_run, alpha, lim, ksub, hh, a.c_hi);
+      else
+        online_softmax<QT, false>(sacc, m_run, l_run, alpha, lim, ksub, hh, a.c_hi);
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt)
+        if (__ballot(alpha[qt] != 1.f)) {
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub)
+          for (int dt = 0; dt < NDT; ++dt) o[qt][dt] *= alpha[qt];
+        }
+
+      if constexpr (sizeof(T) == 2) {
+        // Each 16-key slice of P is packed to bf16 right before its MFMAs.
 #pragma unroll
-          for (int mm = 0; mm < 2; ++mm)
+        for (int mm = 0; mm < 2; ++mm) {
+          bf16x8_t pf[QT];
 #pragma unroll
-            for (int t = 0; t < 8; ++t) pf[qt][sub][mm][t] = (__bf16)pv[qt][sub][8 * mm + t];
+          for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
+            for (int t = 0; t < 8; ++t) pf[qt][t] = (__bf16)sacc[qt][8 * mm + t];
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-          for (int mm = 0; mm < 2; ++mm) {
+          for (int dt = 0; dt < NDT; ++dt) {
             const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(
-                &Vt[(dt * 32 + col) * VSTR + sub * 32 + mm * 16 + hh * 8]);
+                &vt_[(dt * 32 + col) * VSTR + sub * 32 + mm * 16 + hh * 8]);
 #pragma unroll
-            for (int qt = 0; qt < QT; ++qt) o[qt][dt] = M::mma(af, pf[qt][sub][mm], o[qt][dt]);
+            for (int qt = 0; qt < QT; ++qt) o[qt][dt] = M::mma(af, pf[qt], o[qt][dt]);
           }
-    } else {
+        }
+      } else {
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub)
+        for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
           for (int t = 0; t < 16; ++t) {
             const int kin = sub * 32 + 8 * (t >> 2) + 4 * hh + (t & 3);
-            const float af = Vt[(dt * 32 + col) * VSTR + kin];
+            const float af = vt_[(dt * 32 + col) * VSTR + kin];
 #pragma unroll
-            for (int qt = 0; qt < QT; ++qt) o[qt][dt] = M::mma(af, pv[qt][sub][t], o[qt][dt]);
+            for (int qt = 0; qt < QT; ++qt) o[qt][dt] = M::mma(af, sacc[qt][t], o[qt][dt]);
           }
+      }
     }
+
+    if (b + 1 < nblk) stage.store(Ks[buf ^ 1], Vt[buf ^ 1], tid);
+    __syncthreads();
   }
 
   // Partial results of this key split.
@@ -435,54 +584,17 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Merge of the key splits: O = sum_s 2^(m_s - m) O_s / l, l = sum_s 2^(m_s - m) l_s.
-// Writes O in [T][Hq][d] and the row statistics used by the score pass.
-// ---------------------------------------------------------------------------
-template <class E, int D>
-__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
-  typedef typename E::T T;
-  constexpr int CPR = D / 4;
-  const size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const size_t total = (size_t)a.Hkv * a.R * CPR;
-  if (t >= total) return;
-  const int c = (int)(t % CPR);
-  const size_t gr = t / CPR;
-  const int r = (int)(gr % a.R);
-  const int g = (int)(gr / a.R);
-  const size_t stride = (size_t)a.Hkv * a.R;
-  const size_t base = (size_t)g * a.R + r;
-  float m = -INFINITY;
-  for (int s = 0; s < a.S; ++s) m = fmaxf(m, a.mpart[s * stride + base]);
-  double l = 0.0;
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < a.S; ++s) {
-    const float ms = a.mpart[s * stride + base];
-    if (ms == -INFINITY) continue;
-    const double w = exp2((double)ms - (double)m);
-    l += a.lpart[s * stride + base] * w;
-    const f32x4_t os = *reinterpret_cast<const f32x4_t*>(a.opart + (s * stride + base) * D + c * 4);
-    acc += (float)w * os;
-  }
-  const float inv = (float)(1.0 / l);
-  const int tok = r / a.G;
-  const int h = g * a.G + (r - tok * a.G);
-  T* out = (T*)a.out + ((size_t)tok * a.Hq + h) * D + c * 4;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) out[e] = Store<E>::from_f32(acc[e] * inv);
-  if (c == 0) {
-    a.row_m[base] = m;
-    a.row_rinv[base] = inv;
-  }
-}
-
-// ---------------------------------------------------------------------------
 // Score pass.  Work-group = 4 waves; each wave keeps KT tiles of 32 keys in
 // registers (the B operand of S = Q K^T) and all waves stream the same
-// 32-row Q tiles through LDS.  With queries as rows, a lane holds 16 rows of
-// one key column, so the column sum of P = 2^(s*c - m) / l is accumulated in
-// the lane: fp32 over the tile's 16 rows, then fp64 across tiles; the two lane
-// halves are added at the end.  The order of every sum is fixed, so the
-// result is deterministic.
+// 32-row Q tiles through double-buffered LDS (the next tile is loaded while
+// the current one is computed).  The row statistics of the work-group's rows
+// (reference max m and row sum l) are formed once, up front, from the
+// key-split partials of pass 1.  With queries as rows, a lane holds 16 rows of one key
+// column, so the column sum of P = 2^(x*c - m) / l is accumulated
+// in the lane: fp32 over the tile's 16 rows, then fp64 across tiles; the two
+// lane halves are added at the end and the work-group's sum is added to the
+// key's fixed-point total.  Every sum has a fixed order (or is an integer
+// sum), so the scores are deterministic.
 // ---------------------------------------------------------------------------
 template <class E, int D, int KT>
 __global__ __launch_bounds__(256, 1) void attn_score_kernel(ScoreArgs a) {
@@ -493,10 +605,12 @@ __global__ __launch_bounds__(256, 1) void attn_score_kernel(ScoreArgs a) {
   constexpr int QSTR = D + EPV;
   constexpr int NKS = D / M::KS;
   constexpr int BNK = 4 * 32 * KT;
-  __shared__ __attribute__((aligned(16))) T Qs[RT * QSTR];
-  __shared__ __attribute__((aligned(16))) float sm[RT];
-  __shared__ __attribute__((aligned(16))) float sr[RT];
-  __shared__ int stok[RT];
+  constexpr int CPR = D / EPV;                       // 16-byte chunks per Q row
+  constexpr int QCH = (RT * CPR + kAttnThreads - 1) / kAttnThreads;
+  __shared__ __attribute__((aligned(16))) T Qs[2][RT * QSTR];
+  __shared__ __attribute__((aligned(16))) float sm[kScoreMaxRows];
+  __shared__ __attribute__((aligned(16))) float sr[kScoreMaxRows];
+  __shared__ __attribute__((aligned(16))) int slim[kScoreMaxRows];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -507,8 +621,9 @@ __global__ __launch_bounds__(256, 1) void attn_score_kernel(ScoreArgs a) {
 
   const T* qbase = (const T*)a.qrot + (size_t)g * a.R * D;
   const T* kbase = (const T*)a.kpool + (size_t)g * a.cap * D;
-  const float* mbase = a.row_m + (size_t)g * a.R;
-  const float* rbase = a.row_rinv + (size_t)g * a.R;
+  const size_t sstride = (size_t)a.Hkv * a.R;   // split stride of the pass-1 partials
+  const float* mbase = a.mpart + (size_t)g * a.R;
+  const double* lbase = a.lpart + (size_t)g * a.R;
 
   typename M::Frag kf[KT][NKS];
 #pragma unroll
@@ -527,27 +642,67 @@ __global__ __launch_bounds__(256, 1) void attn_score_kernel(ScoreArgs a) {
   // Rows whose token precedes every frame key of this work-group see none of them.
   int rstart = r0;
   if (key_wg >= a.k0) rstart = max(r0, (key_wg - a.k0) * a.G);
+  const int nrow = r1 - rstart;
+  const int ntile = nrow > 0 ? (nrow + RT - 1) / RT : 0;
 
-  for (int rt = rstart; rt < r1; rt += RT) {
-    __syncthreads();
-    {
-      constexpr int CPR = D / EPV;
-      for (int t = tid; t < RT * CPR; t += kAttnThreads) {
-        const int rr = t / CPR, cc = t - rr * CPR;
-        const int r = rt + rr;
-        u32x4_t v = {0u, 0u, 0u, 0u};
-        if (r < r1) v = *reinterpret_cast<const u32x4_t*>(qbase + (size_t)r * D + cc * EPV);
-        *reinterpret_cast<u32x4_t*>(&Qs[rr * QSTR + cc * EPV]) = v;
+  // Row statistics of the work-group's rows (padded to whole tiles), from the
+  // key-split partials of pass 1: m = max_s m_s, l = sum_s 2^(m_s - m) l_s
+  // (exact powers of two, fp64 sum).  Padding rows get 1/l = 0.
+  for (int i = tid; i < ntile * RT; i += kAttnThreads) {
+    const int r = rstart + i;
+    float m = 0.f, rinv = 0.f;
+    int lim = 0;
+    if (r < r1) {
+      float ms[kMaxSplits];
+      double ls[kMaxSplits];
+      m = -INFINITY;
+#pragma unroll
+      for (int sp = 0; sp < kMaxSplits; ++sp) {
+        ms[sp] = sp < a.S ? mbase[sp * sstride + r] : -INFINITY;
+        ls[sp] = sp < a.S ? lbase[sp * sstride + r] : 0.0;
+        m = fmaxf(m, ms[sp]);
       }
-      if (tid < RT) {
-        const int r = rt + tid;
-        const bool ok = r < r1;
-        sm[tid] = ok ? mbase[r] : 0.f;
-        sr[tid] = ok ? rbase[r] : 0.f;
-        stok[tid] = ok ? r / a.G : -1;
-      }
+      double l = 0.0;
+#pragma unroll
+      for (int sp = 0; sp < kMaxSplits; ++sp)
+        if (ms[sp] != -INFINITY) l += ldexp(ls[sp], (int)(ms[sp] - m));
+      rinv = (float)(1.0 / l);
+      lim = a.k0 + r / a.G + 1;   // keys below this are visible to row r
     }
-    __syncthreads();
+    sm[i] = m;
+    sr[i] = rinv;
+    slim[i] = lim;
+  }
+
+  u32x4_t qr[QCH];
+  auto load_tile = [&](int rt) {
+#pragma unroll
+    for (int j = 0; j < QCH; ++j) {
+      const int t = tid + j * kAttnThreads;
+      const int rr = t / CPR, cc = t - rr * CPR;
+      const int r = rt + rr;
+      qr[j] = u32x4_t{0u, 0u, 0u, 0u};
+      if (t < RT * CPR && r < r1) qr[j] = *reinterpret_cast<const u32x4_t*>(qbase + (size_t)r * D + cc * EPV);
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < QCH; ++j) {
+      const int t = tid + j * kAttnThreads;
+      const int rr = t / CPR, cc = t - rr * CPR;
+      if (t < RT * CPR) *reinterpret_cast<u32x4_t*>(&Qs[buf][rr * QSTR + cc * EPV]) = qr[j];
+    }
+  };
+
+  if (ntile > 0) {
+    load_tile(rstart);
+    store_tile(0);
+  }
+  __syncthreads();
+  for (int it = 0; it < ntile; ++it) {
+    const int buf = it & 1;
+    const int ro = it * RT;   // tile offset inside the statistics arrays
+    if (it + 1 < ntile) load_tile(rstart + (it + 1) * RT);
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
       const int key_t0 = key_w + kt * 32;
@@ -555,44 +710,69 @@ __global__ __launch_bounds__(256, 1) void attn_score_kernel(ScoreArgs a) {
       f32x16_t acc = f32x16_t{};
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const typename M::Frag af = M::ld(&Qs[col * QSTR + ks * M::KS + hh * M::KL]);
+        const typename M::Frag af = M::ld(&Qs[buf][col * QSTR + ks * M::KS + hh * M::KL]);
         acc = M::mma(af, kf[kt][ks], acc);
       }
-      const bool causal = key_t0 + 31 >= a.k0;
-      const int ktok = key_t0 + col - a.k0;
+      const int key = key_t0 + col;
       float sum = 0.f;
+      if (key_t0 + 31 >= a.k0) {  // tile holds frame keys: causal visibility per row
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4_t mv = *reinterpret_cast<const f32x4_t*>(&sm[8 * j + 4 * hh]);
-        const f32x4_t rv = *reinterpret_cast<const f32x4_t*>(&sr[8 * j + 4 * hh]);
+        for (int j = 0; j < 4; ++j) {
+          const f32x4_t mv = *reinterpret_cast<const f32x4_t*>(&sm[ro + 8 * j + 4 * hh]);
+          const f32x4_t rv = *reinterpret_cast<const f32x4_t*>(&sr[ro + 8 * j + 4 * hh]);
+          const int4 lv = *reinterpret_cast<const int4*>(&slim[ro + 8 * j + 4 * hh]);
+          const int lvv[4] = {lv.x, lv.y, lv.z, lv.w};
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float x = acc[4 * j + q];
-          float p = fast_exp2(fmaf(x, a.c_lo, fmaf(x, a.c_hi, -mv[q]))) * rv[q];
-          if (causal && ktok > stok[8 * j + 4 * hh + q]) p = 0.f;
-          sum += p;
+          for (int q = 0; q < 4; ++q) {
+            const float x = acc[4 * j + q];
+            const float p = fast_exp2(fmaf(x, a.c_lo, fmaf(x, a.c_hi, -mv[q]))) * rv[q];
+            sum += key < lvv[q] ? p : 0.f;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x4_t mv = *reinterpret_cast<const f32x4_t*>(&sm[ro + 8 * j + 4 * hh]);
+          const f32x4_t rv = *reinterpret_cast<const f32x4_t*>(&sr[ro + 8 * j + 4 * hh]);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float x = acc[4 * j + q];
+            sum += fast_exp2(fmaf(x, a.c_lo, fmaf(x, a.c_hi, -mv[q]))) * rv[q];
+          }
         }
       }
       cs[kt] += (double)sum;
     }
+    if (it + 1 < ntile) store_tile(buf ^ 1);
+    __syncthreads();
   }
 #pragma unroll
   for (int kt = 0; kt < KT; ++kt) {
     const double tot = cs[kt] + __shfl_xor(cs[kt], 32);
     const int key = key_w + kt * 32 + col;
-    if (hh == 0 && key < a.P) a.colpart[((size_t)rsplit * a.Hkv + g) * a.cap + key] = tot;
+    if (hh == 0 && key < a.P && tot > 0.0) {
+      const unsigned long long fx =
+          (unsigned long long)(tot * (double)(1ull << kScoreFracBits) + 0.5);
+      atomicAdd(&a.colsum[key], fx);
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Top-B selection in one work-group of 1024 threads.
-// Scores s_j = (sum of the column partials in fixed order) / (Hq*T), rounded
-// to fp32.  Non-negative fp32 values order like their bit patterns, so the
-// B-th largest bit pattern tau is found by refining a value range [lo, hi]:
-// histogram the candidates in [lo, hi] into up to 4096 equal-width buckets,
-// pick the bucket holding the B-th largest, repeat until lo == hi.  Then keep
-// every score > tau and, among scores == tau, the lowest pool indices (the
-// older tokens).  The keep list is written in ascending pool index.
+// Top-B selection (work-group 0 of select_kernel, 1024 threads).
+// Scores s_j = (fixed-point column sum) / (Hq*T), rounded to fp32.  The pool
+// keeps its B best under (score descending, position ascending), i.e. it
+// evicts the E = P - B smallest 64-bit keys
+//     key_j = (bits of s_j) << 32 | ~pos_j
+// (non-negative fp32 values order like their bit patterns; among equal scores
+// the newer token has the smaller key).  The keys are distinct, so the evicted
+// set is unique.  The E-th smallest key is bracketed by refining a key range
+// [lo, hi] with a histogram of up to 4096 power-of-two-wide buckets until the
+// boundary bucket holds at most kSelCand candidates (usually after one round);
+// each candidate is then ranked by counting the candidates below it.
+// The state keeps its slots: evicted slots below B receive, in ascending
+// order, the kept rows at or beyond B (the frame's tail), so at most T rows
+// move per KV head; the move list is built with one block-wide scan.
 // ---------------------------------------------------------------------------
 __device__ int block_excl_scan(int v, int* sh, int* total) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -624,86 +804,89 @@ __device__ int block_excl_scan(int v, int* sh, int* total) {
 
 constexpr int kSelMaxPerThread = kMaxPool / kSelectThreads;  // 32
 
-__global__ __launch_bounds__(1024, 1) void topb_select_kernel(SelectArgs a) {
-  __shared__ uint32_t sbits[kMaxPool];
+__device__ void select_top_b(const SelectArgs& a) {
   __shared__ int hist[kSelectBins];
+  __shared__ unsigned long long cand_key[kSelCand];
+  __shared__ int cand_idx[kSelCand];
+  __shared__ uint8_t evict[kMaxPool];
   __shared__ int scan_sh[kSelectThreads / 64 + 1];
-  __shared__ uint32_t red_lo[kSelectThreads / 64], red_hi[kSelectThreads / 64];
-  __shared__ int s_bucket, s_above;
+  __shared__ unsigned long long red_lo[kSelectThreads / 64], red_hi[kSelectThreads / 64];
+  __shared__ int s_bucket, s_below, s_cnt, s_ncand;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int j = tid; j < a.P; j += kSelectThreads) {
-    double s = 0.0;
-    for (int q = 0; q < a.nparts; ++q) s += a.colpart[(size_t)q * a.cap + j];
-    const float f = (float)(s / a.denom);
-    a.scores[j] = f;
-    sbits[j] = __float_as_uint(f);
-  }
-  __syncthreads();
-
-  if (a.P <= a.B) {
-    for (int j = tid; j < a.P; j += kSelectThreads) a.keep[j] = j;
-    return;
-  }
-
   const int C = (a.P + kSelectThreads - 1) / kSelectThreads;
   const int i0 = tid * C;
   const int cnt = max(0, min(C, a.P - i0));
-  uint32_t b[kSelMaxPerThread];
-  uint32_t lo = 0xffffffffu, hi = 0u;
+  unsigned long long key[kSelMaxPerThread];
+  unsigned long long lo = ~0ull, hi = 0ull;
 #pragma unroll
   for (int j = 0; j < kSelMaxPerThread; ++j) {
-    b[j] = 0u;
+    key[j] = 0ull;
     if (j < cnt) {
-      b[j] = sbits[i0 + j];
-      lo = min(lo, b[j]);
-      hi = max(hi, b[j]);
+      const int idx = i0 + j;
+      const unsigned long long fx = a.colsum[idx];
+      a.colsum[idx] = 0ull;  // ready for the next frame's score pass
+      const double sc = (double)fx * (1.0 / (double)(1ull << kScoreFracBits));
+      const float f = (float)(sc / a.denom);
+      const int p = a.pool_pos[idx];
+      a.scores[idx] = f;
+      a.score_pos[idx] = p;
+      key[j] = ((unsigned long long)__float_as_uint(f) << 32) | (unsigned long long)(~(uint32_t)p);
+      lo = min(lo, key[j]);
+      hi = max(hi, key[j]);
     }
   }
-  // block min / max
+  if (a.mode != kSelEvict) {
+#pragma unroll
+    for (int j = 0; j < kSelMaxPerThread; ++j)
+      if (j < cnt) a.keep_flag[i0 + j] = 1;
+    if (tid == 0) *a.move_count = 0;
+    return;
+  }
+
+  // block min / max of the keys
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
-    lo = min(lo, (uint32_t)__shfl_xor((int)lo, o));
-    hi = max(hi, (uint32_t)__shfl_xor((int)hi, o));
+    lo = min(lo, (unsigned long long)__shfl_xor((long long)lo, o));
+    hi = max(hi, (unsigned long long)__shfl_xor((long long)hi, o));
   }
   if (lane == 0) {
     red_lo[wave] = lo;
     red_hi[wave] = hi;
   }
   __syncthreads();
-  lo = 0xffffffffu;
-  hi = 0u;
+  lo = ~0ull;
+  hi = 0ull;
+#pragma unroll
   for (int w = 0; w < kSelectThreads / 64; ++w) {
     lo = min(lo, red_lo[w]);
     hi = max(hi, red_hi[w]);
   }
 
-  int need = a.B;
-  while (lo < hi) {
-    const uint64_t range = (uint64_t)hi - lo + 1u;
-    const int nb = (int)(range < (uint64_t)kSelectBins ? range : (uint64_t)kSelectBins);
+  int need = a.P - a.B;  // keys still to evict inside [lo, hi]
+  for (;;) {
+    const unsigned long long span = hi - lo;
+    const int bits = span ? 64 - __clzll((long long)span) : 0;
+    const int sh = bits > 12 ? bits - 12 : 0;
+    const int nb = (int)(span >> sh) + 1;
     for (int x = tid; x < nb; x += kSelectThreads) hist[x] = 0;
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < kSelMaxPerThread; ++j) {
-      if (j < cnt && b[j] >= lo && b[j] <= hi) {
-        const int bk = (int)(((uint64_t)(b[j] - lo) * (uint64_t)nb) / range);
-        atomicAdd(&hist[bk], 1);
-      }
-    }
+    for (int j = 0; j < kSelMaxPerThread; ++j)
+      if (j < cnt && key[j] >= lo && key[j] <= hi) atomicAdd(&hist[(int)((key[j] - lo) >> sh)], 1);
     __syncthreads();
-    // Walk buckets from the top: position q holds bucket nb-1-q.
     int c4[4];
     int s4 = 0;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int q = tid * 4 + u;
-      c4[u] = q < nb ? hist[nb - 1 - q] : 0;
+      c4[u] = q < nb ? hist[q] : 0;
       s4 += c4[u];
     }
     if (tid == 0) {
       s_bucket = 0;
-      s_above = 0;
+      s_below = 0;
+      s_cnt = 0;
     }
     int total;
     int run = block_excl_scan(s4, scan_sh, &total);
@@ -711,74 +894,150 @@ __global__ __launch_bounds__(1024, 1) void topb_select_kernel(SelectArgs a) {
     for (int u = 0; u < 4; ++u) {
       const int q = tid * 4 + u;
       if (q < nb && run < need && need <= run + c4[u]) {
-        s_bucket = nb - 1 - q;
-        s_above = run;
+        s_bucket = q;
+        s_below = run;
+        s_cnt = c4[u];
       }
       run += c4[u];
     }
     __syncthreads();
-    const uint64_t x = (uint64_t)s_bucket;
-    need -= s_above;
-    const uint64_t off_lo = (x * range + nb - 1) / nb;
-    const uint64_t off_hi = ((x + 1) * range + nb - 1) / nb - 1;
-    hi = lo + (uint32_t)off_hi;
-    lo = lo + (uint32_t)off_lo;
+    need -= s_below;
+    const unsigned long long blo = lo + ((unsigned long long)s_bucket << sh);
+    const unsigned long long width_m1 = sh ? ((1ull << sh) - 1ull) : 0ull;
+    const unsigned long long bhi = (hi - blo > width_m1) ? blo + width_m1 : hi;
+    lo = blo;
+    hi = bhi;
+    const int ncnt = s_cnt;
     __syncthreads();
+    if (ncnt <= kSelCand) break;
   }
-  const uint32_t tau = lo;
 
-  int my_eq = 0;
-#pragma unroll
-  for (int j = 0; j < kSelMaxPerThread; ++j) my_eq += (j < cnt && b[j] == tau) ? 1 : 0;
-  int eq_total;
-  int eqr = block_excl_scan(my_eq, scan_sh, &eq_total);
-  uint32_t keepmask = 0u;
-  int my_keep = 0;
+  // Keys below lo are evicted; the candidates in [lo, hi] are ranked.
+  if (tid == 0) s_ncand = 0;
+  __syncthreads();
 #pragma unroll
   for (int j = 0; j < kSelMaxPerThread; ++j) {
     if (j < cnt) {
-      bool k = b[j] > tau;
-      if (b[j] == tau) {
-        k = eqr < need;
-        ++eqr;
-      }
-      if (k) {
-        keepmask |= 1u << j;
-        ++my_keep;
+      evict[i0 + j] = key[j] < lo ? 1 : 0;
+      if (key[j] >= lo && key[j] <= hi) {
+        const int slot = atomicAdd(&s_ncand, 1);
+        cand_key[slot] = key[j];
+        cand_idx[slot] = i0 + j;
       }
     }
   }
-  int kept_total;
-  int out = block_excl_scan(my_keep, scan_sh, &kept_total);
+  __syncthreads();
+  const int nc = s_ncand;
+  if (tid < nc) {
+    const unsigned long long mine = cand_key[tid];
+    int rank = 0;
+    for (int c = 0; c < nc; ++c) rank += cand_key[c] < mine ? 1 : 0;
+    evict[cand_idx[tid]] = rank < need ? 1 : 0;
+  }
+  __syncthreads();
+
+  // Keep flags and the move list (holes below B, movers at or beyond B).
+  int holes = 0, movers = 0;
 #pragma unroll
-  for (int j = 0; j < kSelMaxPerThread; ++j)
-    if ((keepmask >> j) & 1u) a.keep[out++] = i0 + j;
+  for (int j = 0; j < kSelMaxPerThread; ++j) {
+    if (j < cnt) {
+      const int idx = i0 + j;
+      const int ev = evict[idx];
+      a.keep_flag[idx] = 1 - ev;
+      holes += (idx < a.B && ev) ? 1 : 0;
+      movers += (idx >= a.B && !ev) ? 1 : 0;
+    }
+  }
+  int total;
+  const int base = block_excl_scan(holes | (movers << 16), scan_sh, &total);
+  int bh = base & 0xffff, bm = base >> 16;
+#pragma unroll
+  for (int j = 0; j < kSelMaxPerThread; ++j) {
+    if (j < cnt) {
+      const int idx = i0 + j;
+      const int ev = evict[idx];
+      if (idx < a.B && ev) a.move_dst[bh++] = idx;
+      if (idx >= a.B && !ev) a.move_src[bm++] = idx;
+    }
+  }
+  if (tid == 0) *a.move_count = total & 0xffff;
 }
 
-// ---------------------------------------------------------------------------
-// Gather of the kept rows (K, V of every KV head, and positions) into the
-// other state buffer, 16 bytes per thread, consecutive threads on
-// consecutive bytes of a row.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
+// Merge of the key splits of pass 1:
+//   m = max_s m_s,  l = sum_s 2^(m_s - m) l_s,  O = sum_s 2^(m_s - m) O_s / l,
+// one thread per (row, 4 dims), written to O [T][Hq][d].  The factors are
+// exact powers of two (the m_s are integers).  Partials of splits that saw no
+// key of a row were never written, so they are selected out, not multiplied.
+template <class E, int D>
+__device__ void merge_splits(const SelectArgs& a, size_t t) {
+  typedef typename E::T T;
+  constexpr int CPR = D / 4;
+  const size_t nrows = (size_t)a.Hkv * a.R;
+  if (t >= nrows * CPR) return;
+  const size_t base = t / CPR;   // = g*R + r
+  const int c = (int)(t - base * CPR);
+  const size_t stride = nrows;
+  float ms[kMaxSplits];
+  float m = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) {
+    ms[s] = s < a.S ? a.mpart[s * stride + base] : -INFINITY;
+    m = fmaxf(m, ms[s]);
+  }
+  float l = 0.f;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) {
+    if (s < a.S) {
+      const f32x4_t os = *reinterpret_cast<const f32x4_t*>(a.opart + (s * stride + base) * D + c * 4);
+      const double ls = a.lpart[s * stride + base];
+      const bool live = ms[s] != -INFINITY;
+      const float w = live ? ldexpf(1.f, (int)(ms[s] - m)) : 0.f;
+      l += live ? w * (float)ls : 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = live ? fmaf(w, os[e], acc[e]) : acc[e];
+    }
+  }
+  const float inv = 1.f / l;
+  const int g = (int)(base / a.R), r = (int)(base - (size_t)g * a.R);
+  const int tok = r / a.G;
+  const int h = g * a.G + (r - tok * a.G);
+  T* out = (T*)a.out + ((size_t)tok * a.Hq + h) * D + c * 4;
+  if constexpr (sizeof(T) == 2) {
+    const u32x2_t v = {(uint32_t)f32_to_bf16(acc[0] * inv) | ((uint32_t)f32_to_bf16(acc[1] * inv) << 16),
+                       (uint32_t)f32_to_bf16(acc[2] * inv) | ((uint32_t)f32_to_bf16(acc[3] * inv) << 16)};
+    *reinterpret_cast<u32x2_t*>(out) = v;
+  } else {
+    *reinterpret_cast<f32x4_t*>(out) = acc * inv;
+  }
+}
+
+template <class E, int D>
+__global__ __launch_bounds__(kSelectThreads, 1) void select_kernel(SelectArgs a) {
+  if (blockIdx.x > 0) {
+    merge_splits<E, D>(a, (size_t)(blockIdx.x - 1) * kSelectThreads + threadIdx.x);
+    return;
+  }
+  if (a.mode != kSelMerge) select_top_b(a);
+}
+
+// Moves of the selection, 16 bytes per thread: K and V of every KV head.
+__global__ __launch_bounds__(256) void moves_kernel(MovesArgs a) {
   const int cpr = a.row_bytes / 16;
   const size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const size_t total = (size_t)a.Hkv * a.B * cpr;
-  if (t >= total) return;
-  const int c = (int)(t % cpr);
-  const size_t gr = t / cpr;
-  const int r = (int)(gr % a.B);
-  const int g = (int)(gr / a.B);
-  // keep[] holds pool indices; clamping only guards the copy against a
-  // malformed list, it never changes a valid one.
-  const int src = min(max(a.keep[r], 0), a.cap - 1);
+  const int i = (int)(t / ((size_t)a.Hkv * cpr));
+  if (i >= min(*a.move_count, a.max_moves)) return;
+  const int rem = (int)(t - (size_t)i * a.Hkv * cpr);
+  const int g = rem / cpr, c = rem - g * cpr;
+  // The move list holds slots below B and rows in [B, cap); clamping only
+  // guards the copy against a malformed list.
+  const int dst = min(max(a.move_dst[i], 0), a.B - 1);
+  const int src = min(max(a.move_src[i], a.B), a.cap - 1);
   const size_t so = ((size_t)g * a.cap + src) * a.row_bytes + (size_t)c * 16;
-  const size_t dof = ((size_t)g * a.cap + r) * a.row_bytes + (size_t)c * 16;
-  *reinterpret_cast<u32x4_t*>((char*)a.knext + dof) =
-      *reinterpret_cast<const u32x4_t*>((const char*)a.kcur + so);
-  *reinterpret_cast<u32x4_t*>((char*)a.vnext + dof) =
-      *reinterpret_cast<const u32x4_t*>((const char*)a.vcur + so);
-  if (g == 0 && c == 0) a.pnext[r] = a.pcur[src];
+  const size_t dof = ((size_t)g * a.cap + dst) * a.row_bytes + (size_t)c * 16;
+  *reinterpret_cast<u32x4_t*>((char*)a.kpool + dof) = *reinterpret_cast<const u32x4_t*>((const char*)a.kpool + so);
+  *reinterpret_cast<u32x4_t*>((char*)a.vpool + dof) = *reinterpret_cast<const u32x4_t*>((const char*)a.vpool + so);
+  if (g == 0 && c == 0) a.pool_pos[dst] = a.pool_pos[src];
 }
 
 }  // namespace
@@ -786,17 +1045,35 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
-static constexpr int kQtBf16 = 2;  // query tiles per wave in pass 1 (bf16)
-static constexpr int kQtF32 = 1;
 static constexpr int kKtBf16 = 2;  // key tiles per wave in the score pass
 static constexpr int kKtF32 = 1;
 
-int attn_rows_per_wg(Dt dt) { return 4 * 32 * (dt == Dt::BF16 ? kQtBf16 : kQtF32); }
+// Pass-1 shape: bf16 uses 8 waves of one 32-query tile each (two waves per
+// SIMD, so one wave's matrix work overlaps the other's softmax); fp32 (tiny
+// shapes) uses 4 waves.  STATEKV_ATTN_WAVES=4 selects 4 waves of two tiles.
+static int attn_variant() {
+  static int v = -1;
+  if (v < 0) {
+    const char* e = getenv("STATEKV_ATTN_WAVES");
+    v = (e && atoi(e) == 4) ? 4 : 8;
+  }
+  return v;
+}
+
+int attn_rows_per_wg(Dt dt, int) {
+  if (dt != Dt::BF16) return 4 * 32;
+  return attn_variant() == 4 ? 4 * 32 * 2 : 8 * 32;
+}
 int score_keys_per_wg(Dt dt) { return 4 * 32 * (dt == Dt::BF16 ? kKtBf16 : kKtF32); }
 
+hipError_t launch_rope_table(const RopeTableArgs& a, hipStream_t s) {
+  const size_t total = (size_t)a.npos * a.half;
+  hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_rope(Dt dt, int d, const RopeArgs& a, hipStream_t s) {
-  const int tpt = d / 8;
-  const int blocks = (a.T * tpt + 255) / 256;
+  const int blocks = (a.T + kRopeTokensPerWG - 1) / kRopeTokensPerWG;
   if (dt == Dt::BF16) {
     if (d == 64) hipLaunchKernelGGL((rope_append_kernel<BF16, 64>), dim3(blocks), dim3(256), 0, s, a);
     else hipLaunchKernelGGL((rope_append_kernel<BF16, 128>), dim3(blocks), dim3(256), 0, s, a);
@@ -808,26 +1085,18 @@ hipError_t launch_rope(Dt dt, int d, const RopeArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_attn(Dt dt, int d, const AttnArgs& a, int row_tiles, int splits, hipStream_t s) {
-  const dim3 grid(row_tiles, a.Hkv, splits), block(kAttnThreads);
+  const dim3 grid(row_tiles, a.Hkv, splits);
   if (dt == Dt::BF16) {
-    if (d == 64) hipLaunchKernelGGL((attn_fwd_kernel<BF16, 64, kQtBf16>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((attn_fwd_kernel<BF16, 128, kQtBf16>), grid, block, 0, s, a);
+    if (attn_variant() == 4) {
+      if (d == 64) hipLaunchKernelGGL((attn_fwd_kernel<BF16, 64, 2, 4>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((attn_fwd_kernel<BF16, 128, 2, 4>), grid, dim3(256), 0, s, a);
+    } else {
+      if (d == 64) hipLaunchKernelGGL((attn_fwd_kernel<BF16, 64, 1, 8>), grid, dim3(512), 0, s, a);
+      else hipLaunchKernelGGL((attn_fwd_kernel<BF16, 128, 1, 8>), grid, dim3(512), 0, s, a);
+    }
   } else {
-    if (d == 64) hipLaunchKernelGGL((attn_fwd_kernel<F32, 64, kQtF32>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((attn_fwd_kernel<F32, 128, kQtF32>), grid, block, 0, s, a);
-  }
-  return hipGetLastError();
-}
-
-hipError_t launch_combine(Dt dt, int d, const CombineArgs& a, hipStream_t s) {
-  const size_t total = (size_t)a.Hkv * a.R * (d / 4);
-  const dim3 grid((unsigned)((total + 255) / 256)), block(256);
-  if (dt == Dt::BF16) {
-    if (d == 64) hipLaunchKernelGGL((combine_kernel<BF16, 64>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((combine_kernel<BF16, 128>), grid, block, 0, s, a);
-  } else {
-    if (d == 64) hipLaunchKernelGGL((combine_kernel<F32, 64>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((combine_kernel<F32, 128>), grid, block, 0, s, a);
+    if (d == 64) hipLaunchKernelGGL((attn_fwd_kernel<F32, 64, 1, 4>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((attn_fwd_kernel<F32, 128, 1, 4>), grid, dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }
@@ -844,14 +1113,22 @@ hipError_t launch_score(Dt dt, int d, const ScoreArgs& a, int key_blocks, int rs
   return hipGetLastError();
 }
 
-hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(topb_select_kernel, dim3(1), dim3(kSelectThreads), 0, s, a);
+hipError_t launch_select(Dt dt, int d, const SelectArgs& a, hipStream_t s) {
+  const size_t mthreads = (size_t)a.Hkv * a.R * (d / 4);
+  const dim3 grid((unsigned)(1 + (mthreads + kSelectThreads - 1) / kSelectThreads)), block(kSelectThreads);
+  if (dt == Dt::BF16) {
+    if (d == 64) hipLaunchKernelGGL((select_kernel<BF16, 64>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((select_kernel<BF16, 128>), grid, block, 0, s, a);
+  } else {
+    if (d == 64) hipLaunchKernelGGL((select_kernel<F32, 64>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((select_kernel<F32, 128>), grid, block, 0, s, a);
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_gather(const GatherArgs& a, hipStream_t s) {
-  const size_t total = (size_t)a.Hkv * a.B * (a.row_bytes / 16);
-  hipLaunchKernelGGL(gather_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a);
+hipError_t launch_moves(const MovesArgs& a, hipStream_t s) {
+  const size_t total = (size_t)a.max_moves * a.Hkv * (a.row_bytes / 16);
+  hipLaunchKernelGGL(moves_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -1,17 +1,24 @@
 // Host runtime and C ABI of the StateKV frame step (see include/statekv.h).
 //
 // State layout in HBM (one layer):
-//   kbuf[2], vbuf[2]  [Hkv][cap][d], cap = B + T: the compressed state in rows
-//                     [0, count) followed by the current frame's rows; two
-//                     buffers, the Top-B gather writes the other one.
-//   pos[2]            [cap] absolute positions of those rows.
+//   kpool, vpool      [Hkv][cap][d], cap = B + T.  Rows [0, count) hold the
+//                     compressed state (one slot per token, in slot order);
+//                     the current frame is written to rows [count, count+T).
+//                     After the Top-B decision the kept frame rows at or
+//                     beyond B move into the evicted slots below B, so at
+//                     most T rows move per KV head and frame.
+//   ppos              [cap] absolute stream positions of those rows.
 //   dk, dv            [max_frames*T][Hkv][d]: the detailed cache D.
 //   qrot              [Hkv][G*T][d]: the frame's rotated queries, rows grouped
 //                     by KV head (row = token*G + head-in-group).
-//   opart/mpart/lpart split-over-keys partials of attention pass 1.
-//   row_m/row_rinv    final row max and 1/row sum, read by the score pass.
-//   colpart           [row splits][Hkv][cap] per-key column sums (fp64).
-//   scores, keep      fp32 scores of the pool and the kept pool indices.
+//   opart/mpart/lpart split-over-keys partials of attention pass 1 (merged
+//                     into O by the select kernel's merge work-groups; the
+//                     score pass forms its row statistics from mpart/lpart).
+//   rope_tab          [max_frames*T][d/2] fp32 (cos, sin) of the scaled angles.
+//   colsum            [cap] per-key column sums, 64-bit fixed point; the select
+//                     kernel reads and clears them.
+//   scores, score_pos, keep_flag   scores of the last scored pool.
+//   move_dst, move_src, move_count the moves of the last selection.
 // Everything is allocated in statekv_create; a frame step only launches.
 #include "statekv.h"
 #include "statekv_internal.h"
@@ -37,31 +44,33 @@ struct statekv_state {
   int attn_tiles, attn_splits_max;
   int score_rsplits_max;
 
-  void* kbuf[2];
-  void* vbuf[2];
-  int32_t* pos[2];
+  void* kpool;
+  void* vpool;
+  int32_t* ppos;
   void* dk;
   void* dv;
   void* qrot;
   float* opart;
   float* mpart;
   double* lpart;
-  float* row_m;
-  float* row_rinv;
-  double* colpart;
+  float2* rope_tab;
+  unsigned long long* colsum;
   float* scores;
-  int32_t* keep;
+  int32_t* score_pos;
+  int32_t* keep_flag;
+  int32_t* move_dst;
+  int32_t* move_src;
+  int32_t* move_count;
   double* inv_freq;
   int32_t* nonfinite;
 
   float c_hi, c_lo;  // softmax scale times log2(e), as a float pair
 
-  int cur;           // buffer holding the compressed state
   int count;         // tokens in the compressed state
   int frames_done;
 
   // scores of the last frame that computed them
-  int score_frame, score_pool, score_kept, score_buf;
+  int score_frame, score_pool;
 
   uint32_t flags;
   // Kernel timing: a ring of (start, stop) event pairs per kernel, drained
@@ -92,9 +101,9 @@ int alloc(P** p, size_t bytes) {
 }
 
 void release(statekv_state* s) {
-  void* bufs[] = {s->kbuf[0], s->kbuf[1], s->vbuf[0], s->vbuf[1], s->pos[0], s->pos[1],
-                  s->dk, s->dv, s->qrot, s->opart, s->mpart, s->lpart, s->row_m,
-                  s->row_rinv, s->colpart, s->scores, s->keep, s->inv_freq, s->nonfinite};
+  void* bufs[] = {s->kpool, s->vpool, s->ppos, s->dk, s->dv, s->qrot, s->opart, s->mpart,
+                  s->lpart, s->rope_tab, s->colsum, s->scores, s->score_pos, s->keep_flag,
+                  s->move_dst, s->move_src, s->move_count, s->inv_freq, s->nonfinite};
   for (void* b : bufs)
     if (b) (void)hipFree(b);
   for (auto& ring : s->ev)
@@ -153,6 +162,7 @@ void score_geometry(const statekv_state* s, int P, int* key_blocks, int* rsplits
   const int base = kb * s->Hkv;
   int rs = std::max(1, std::min(ceil_div(kTargetWGs, base), ceil_div(s->R, 128)));
   rs = std::min(rs, s->score_rsplits_max);
+  rs = std::max(rs, ceil_div(s->R, kScoreMaxRows));  // rows per work-group fit the LDS statistics
   const int r = ceil_div(ceil_div(s->R, rs), 32) * 32;
   *key_blocks = kb;
   *rsplits = ceil_div(s->R, r);
@@ -181,6 +191,12 @@ int read_nonfinite(const statekv_state* s) {
   if (hipMemcpy(&h, s->nonfinite, sizeof(h), hipMemcpyDeviceToHost) != hipSuccess)
     return STATEKV_EDEVICE;
   return h ? STATEKV_ENONFINITE : STATEKV_OK;
+}
+
+int sync_state(const statekv_state* s) {
+  if (hipSetDevice(s->device) != hipSuccess || hipStreamSynchronize(s->stream) != hipSuccess)
+    return STATEKV_EDEVICE;
+  return STATEKV_OK;
 }
 
 }  // namespace
@@ -215,7 +231,7 @@ int statekv_create(const statekv_layer_cfg* cfg, int32_t budget_B, float alpha,
   const int64_t positions = (int64_t)c.max_frames * c.tokens_per_frame;
   if (positions > INT32_MAX) return STATEKV_EINVAL;
   const int64_t rows = (int64_t)c.n_q_heads * c.tokens_per_frame;
-  if (rows > INT32_MAX / 128) return STATEKV_EINVAL;
+  if (rows > kMaxRowsTimesHeads) return STATEKV_EINVAL;
 
   statekv_state* s = (statekv_state*)calloc(1, sizeof(statekv_state));
   if (!s) return STATEKV_ENOMEM;
@@ -240,31 +256,42 @@ int statekv_create(const statekv_layer_cfg* cfg, int32_t budget_B, float alpha,
     return rc;
   }
 
-  s->attn_tiles = ceil_div(s->R, attn_rows_per_wg(s->dt));
-  s->attn_splits_max = std::max(1, ceil_div(s->cap, 4 * kAttnBN));
-  s->score_rsplits_max = std::max(1, ceil_div(s->R, 128));
+  s->attn_tiles = ceil_div(s->R, attn_rows_per_wg(s->dt, s->D));
+  s->attn_splits_max = std::min(kMaxSplits, std::max(1, ceil_div(s->cap, 4 * kAttnBN)));
+  s->score_rsplits_max = std::max(ceil_div(s->R, kScoreMaxRows), ceil_div(s->R, 128));
+  // Tuning overrides (launch geometry only; the result does not depend on them).
+  if (const char* e = getenv("STATEKV_ATTN_SPLITS")) {
+    const int v = atoi(e);
+    if (v >= 1) s->attn_splits_max = std::min(v, s->attn_splits_max);
+  }
+  if (const char* e = getenv("STATEKV_SCORE_RSPLITS")) {
+    const int v = atoi(e);
+    if (v >= 1)
+      s->score_rsplits_max = std::max(ceil_div(s->R, kScoreMaxRows), std::min(v, s->score_rsplits_max));
+  }
 
   const size_t E = s->esize, D = s->D;
   const size_t pool_bytes = (size_t)s->Hkv * s->cap * D * E;
   const size_t det_bytes = (size_t)positions * s->Hkv * D * E;
   const size_t rows_all = (size_t)s->Hkv * s->R;
   const size_t S = s->attn_splits_max;
-  for (int i = 0; i < 2 && !rc; ++i) {
-    rc = alloc(&s->kbuf[i], pool_bytes);
-    if (!rc) rc = alloc(&s->vbuf[i], pool_bytes);
-    if (!rc) rc = alloc(&s->pos[i], (size_t)s->cap * sizeof(int32_t));
-  }
+  rc = alloc(&s->kpool, pool_bytes);
+  if (!rc) rc = alloc(&s->vpool, pool_bytes);
+  if (!rc) rc = alloc(&s->ppos, (size_t)s->cap * sizeof(int32_t));
   if (!rc) rc = alloc(&s->dk, det_bytes);
   if (!rc) rc = alloc(&s->dv, det_bytes);
   if (!rc) rc = alloc(&s->qrot, rows_all * D * E);
   if (!rc) rc = alloc(&s->opart, S * rows_all * D * sizeof(float));
   if (!rc) rc = alloc(&s->mpart, S * rows_all * sizeof(float));
   if (!rc) rc = alloc(&s->lpart, S * rows_all * sizeof(double));
-  if (!rc) rc = alloc(&s->row_m, rows_all * sizeof(float));
-  if (!rc) rc = alloc(&s->row_rinv, rows_all * sizeof(float));
-  if (!rc) rc = alloc(&s->colpart, (size_t)s->score_rsplits_max * s->Hkv * s->cap * sizeof(double));
+  if (!rc) rc = alloc(&s->rope_tab, (size_t)positions * (D / 2) * sizeof(float2));
+  if (!rc) rc = alloc(&s->colsum, (size_t)s->cap * sizeof(unsigned long long));
   if (!rc) rc = alloc(&s->scores, (size_t)s->cap * sizeof(float));
-  if (!rc) rc = alloc(&s->keep, (size_t)s->cap * sizeof(int32_t));
+  if (!rc) rc = alloc(&s->score_pos, (size_t)s->cap * sizeof(int32_t));
+  if (!rc) rc = alloc(&s->keep_flag, (size_t)s->cap * sizeof(int32_t));
+  if (!rc) rc = alloc(&s->move_dst, (size_t)s->T * sizeof(int32_t));
+  if (!rc) rc = alloc(&s->move_src, (size_t)s->T * sizeof(int32_t));
+  if (!rc) rc = alloc(&s->move_count, sizeof(int32_t));
   if (!rc) rc = alloc(&s->inv_freq, D / 2 * sizeof(double));
   if (!rc) rc = alloc(&s->nonfinite, sizeof(int32_t));
   if (!rc) {
@@ -272,10 +299,19 @@ int statekv_create(const statekv_layer_cfg* cfg, int32_t budget_B, float alpha,
     scaled_inv_freq(s->D, c.rope_base, (double)alpha, c.rope_orig_ctx, table);
     rc = check(hipMemcpy(s->inv_freq, table, D / 2 * sizeof(double), hipMemcpyHostToDevice));
   }
+  if (!rc) {
+    RopeTableArgs ta{};
+    ta.inv_freq = s->inv_freq;
+    ta.table = s->rope_tab;
+    ta.npos = (int32_t)positions;
+    ta.half = s->D / 2;
+    rc = check(launch_rope_table(ta, nullptr));
+  }
   if (!rc) rc = check(hipMemset(s->nonfinite, 0, sizeof(int32_t)));
-  if (!rc) rc = check(hipMemset(s->keep, 0, (size_t)s->cap * sizeof(int32_t)));
-  if (!rc) rc = check(hipMemset(s->pos[0], 0, (size_t)s->cap * sizeof(int32_t)));
-  if (!rc) rc = check(hipMemset(s->pos[1], 0, (size_t)s->cap * sizeof(int32_t)));
+  if (!rc) rc = check(hipMemset(s->colsum, 0, (size_t)s->cap * sizeof(unsigned long long)));
+  if (!rc) rc = check(hipMemset(s->ppos, 0, (size_t)s->cap * sizeof(int32_t)));
+  if (!rc) rc = check(hipMemset(s->move_count, 0, sizeof(int32_t)));
+  if (!rc) rc = check(hipDeviceSynchronize());
   if (!rc) {
     s->ev_ok = true;
     for (auto& ring : s->ev)
@@ -290,7 +326,7 @@ int statekv_create(const statekv_layer_cfg* cfg, int32_t budget_B, float alpha,
   }
   // Softmax scale: sigma = mscale^2 / sqrt(d), mscale = 0.1 ln(alpha) + 1 (1 when
   // alpha = 1), applied as 2^(sigma log2(e) x) with the constant split in two
-  // floats so that it carries fp64 accuracy.
+  // floats so that the score pass carries it to fp64 accuracy.
   const double mscale = alpha <= 1.0f ? 1.0 : 0.1 * log((double)alpha) + 1.0;
   const double cexp = mscale * mscale / sqrt((double)s->D) * M_LOG2E;
   s->c_hi = (float)cexp;
@@ -322,8 +358,9 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const 
 
   const int k0 = s->count;
   const int P = k0 + s->T;
-  const int cur = s->cur;
   const hipStream_t st = s->stream;
+  const bool evict = P > s->B;
+  const bool scored = evict || (s->flags & STATEKV_FLAG_ALWAYS_SCORE);
 
   {
     KernelTimer tm(s, STATEKV_K_ROPE);
@@ -331,11 +368,11 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const 
     a.q = Q;
     a.k = K;
     a.v = V;
-    a.inv_freq = s->inv_freq;
+    a.table = s->rope_tab;
     a.qrot = s->qrot;
-    a.kpool = s->kbuf[cur];
-    a.vpool = s->vbuf[cur];
-    a.pool_pos = s->pos[cur];
+    a.kpool = s->kpool;
+    a.vpool = s->vpool;
+    a.pool_pos = s->ppos;
     a.dk = s->dk;
     a.dv = s->dv;
     a.nonfinite = s->nonfinite;
@@ -356,13 +393,12 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const 
     KernelTimer tm(s, STATEKV_K_ATTN);
     AttnArgs a{};
     a.qrot = s->qrot;
-    a.kpool = s->kbuf[cur];
-    a.vpool = s->vbuf[cur];
+    a.kpool = s->kpool;
+    a.vpool = s->vpool;
     a.opart = s->opart;
     a.mpart = s->mpart;
     a.lpart = s->lpart;
     a.c_hi = s->c_hi;
-    a.c_lo = s->c_lo;
     a.R = s->R;
     a.G = s->G;
     a.cap = s->cap;
@@ -374,92 +410,81 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const 
     tm.done();
     if (rc) return rc;
   }
+  if (scored) {
+    int key_blocks, rsplits, rps;
+    score_geometry(s, P, &key_blocks, &rsplits, &rps);
+    KernelTimer tm(s, STATEKV_K_SCORE);
+    ScoreArgs a{};
+    a.qrot = s->qrot;
+    a.kpool = s->kpool;
+    a.mpart = s->mpart;
+    a.lpart = s->lpart;
+    a.S = splits;
+    a.colsum = s->colsum;
+    a.c_hi = s->c_hi;
+    a.c_lo = s->c_lo;
+    a.R = s->R;
+    a.G = s->G;
+    a.cap = s->cap;
+    a.P = P;
+    a.k0 = k0;
+    a.rps = rps;
+    a.Hkv = s->Hkv;
+    rc = check(launch_score(s->dt, s->D, a, key_blocks, rsplits, st));
+    tm.done();
+    if (rc) return rc;
+  }
   {
-    KernelTimer tm(s, STATEKV_K_COMBINE);
-    CombineArgs a{};
+    KernelTimer tm(s, STATEKV_K_SELECT);
+    SelectArgs a{};
+    a.colsum = s->colsum;
+    a.pool_pos = s->ppos;
+    a.scores = s->scores;
+    a.score_pos = s->score_pos;
+    a.keep_flag = s->keep_flag;
+    a.move_dst = s->move_dst;
+    a.move_src = s->move_src;
+    a.move_count = s->move_count;
+    a.P = P;
+    a.B = s->B;
+    a.mode = evict ? kSelEvict : (scored ? kSelScores : kSelMerge);
+    a.denom = (double)s->Hq * (double)s->T;
     a.opart = s->opart;
     a.mpart = s->mpart;
     a.lpart = s->lpart;
     a.out = O;
-    a.row_m = s->row_m;
-    a.row_rinv = s->row_rinv;
+    a.Hkv = s->Hkv;
     a.R = s->R;
     a.G = s->G;
     a.Hq = s->Hq;
-    a.Hkv = s->Hkv;
     a.S = splits;
-    rc = check(launch_combine(s->dt, s->D, a, st));
+    rc = check(launch_select(s->dt, s->D, a, st));
     tm.done();
     if (rc) return rc;
   }
-
-  const bool evict = P > s->B;
-  if (evict || (s->flags & STATEKV_FLAG_ALWAYS_SCORE)) {
-    int key_blocks, rsplits, rps;
-    score_geometry(s, P, &key_blocks, &rsplits, &rps);
-    {
-      KernelTimer tm(s, STATEKV_K_SCORE);
-      ScoreArgs a{};
-      a.qrot = s->qrot;
-      a.kpool = s->kbuf[cur];
-      a.row_m = s->row_m;
-      a.row_rinv = s->row_rinv;
-      a.colpart = s->colpart;
-      a.c_hi = s->c_hi;
-      a.c_lo = s->c_lo;
-      a.R = s->R;
-      a.G = s->G;
-      a.cap = s->cap;
-      a.P = P;
-      a.k0 = k0;
-      a.rps = rps;
-      a.Hkv = s->Hkv;
-      rc = check(launch_score(s->dt, s->D, a, key_blocks, rsplits, st));
-      tm.done();
-      if (rc) return rc;
-    }
-    {
-      KernelTimer tm(s, STATEKV_K_SELECT);
-      SelectArgs a{};
-      a.colpart = s->colpart;
-      a.scores = s->scores;
-      a.keep = s->keep;
-      a.nparts = rsplits * s->Hkv;
-      a.cap = s->cap;
-      a.P = P;
-      a.B = s->B;
-      a.denom = (double)s->Hq * (double)s->T;
-      rc = check(launch_select(a, st));
-      tm.done();
-      if (rc) return rc;
-    }
-    s->score_frame = n;
-    s->score_pool = P;
-    s->score_kept = std::min(P, (int)s->B);
-    s->score_buf = cur;
-  }
   if (evict) {
-    KernelTimer tm(s, STATEKV_K_GATHER);
-    GatherArgs a{};
-    a.kcur = s->kbuf[cur];
-    a.vcur = s->vbuf[cur];
-    a.pcur = s->pos[cur];
-    a.knext = s->kbuf[cur ^ 1];
-    a.vnext = s->vbuf[cur ^ 1];
-    a.pnext = s->pos[cur ^ 1];
-    a.keep = s->keep;
+    KernelTimer tm(s, STATEKV_K_MOVES);
+    MovesArgs a{};
+    a.kpool = s->kpool;
+    a.vpool = s->vpool;
+    a.pool_pos = s->ppos;
+    a.move_dst = s->move_dst;
+    a.move_src = s->move_src;
+    a.move_count = s->move_count;
     a.Hkv = s->Hkv;
     a.cap = s->cap;
     a.B = s->B;
     a.row_bytes = s->D * s->esize;
-    rc = check(launch_gather(a, st));
+    a.max_moves = std::min(P - (int)s->B, (int)s->B);
+    rc = check(launch_moves(a, st));
     tm.done();
     if (rc) return rc;
-    s->cur = cur ^ 1;
-    s->count = s->B;
-  } else {
-    s->count = P;
   }
+  if (scored) {
+    s->score_frame = n;
+    s->score_pool = P;
+  }
+  s->count = evict ? (int)s->B : P;
   s->frames_done = n + 1;
   s->ev_slot = (s->ev_slot + 1) % statekv_state::kRing;
   return STATEKV_OK;
@@ -467,14 +492,13 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const 
 
 int statekv_compressed_view(const statekv_state* s, statekv_view* out) {
   if (!s || !out) return STATEKV_EINVAL;
-  if (hipSetDevice(s->device) != hipSuccess || hipStreamSynchronize(s->stream) != hipSuccess)
-    return STATEKV_EDEVICE;
-  const int nf = read_nonfinite(s);
-  if (nf) return nf;
+  int rc = sync_state(s);
+  if (!rc) rc = read_nonfinite(s);
+  if (rc) return rc;
   memset(out, 0, sizeof(*out));
-  out->k = s->kbuf[s->cur];
-  out->v = s->vbuf[s->cur];
-  out->pos = s->pos[s->cur];
+  out->k = s->kpool;
+  out->v = s->vpool;
+  out->pos = s->ppos;
   out->count = s->count;
   out->head_stride = (int64_t)s->cap * s->D;
   out->token_stride = s->D;
@@ -487,10 +511,9 @@ int statekv_compressed_view(const statekv_state* s, statekv_view* out) {
 
 int statekv_detailed_view(const statekv_state* s, statekv_view* out) {
   if (!s || !out) return STATEKV_EINVAL;
-  if (hipSetDevice(s->device) != hipSuccess || hipStreamSynchronize(s->stream) != hipSuccess)
-    return STATEKV_EDEVICE;
-  const int nf = read_nonfinite(s);
-  if (nf) return nf;
+  int rc = sync_state(s);
+  if (!rc) rc = read_nonfinite(s);
+  if (rc) return rc;
   memset(out, 0, sizeof(*out));
   out->k = s->dk;
   out->v = s->dv;
@@ -507,26 +530,24 @@ int statekv_detailed_view(const statekv_state* s, statekv_view* out) {
 
 int statekv_scores(const statekv_state* s, statekv_scores_view* out) {
   if (!s || !out) return STATEKV_EINVAL;
-  if (hipSetDevice(s->device) != hipSuccess || hipStreamSynchronize(s->stream) != hipSuccess)
-    return STATEKV_EDEVICE;
+  const int rc = sync_state(s);
+  if (rc) return rc;
   memset(out, 0, sizeof(*out));
   out->frame = s->score_frame;
   if (s->score_frame < 0) return STATEKV_OK;
-  // The pool of the scored frame stays intact until the next frame: the
-  // gather writes the other buffer.
   out->scores = s->scores;
-  out->pool_pos = s->pos[s->score_buf];
-  out->keep = s->keep;
+  out->pool_pos = s->score_pos;
+  out->keep_flag = s->keep_flag;
   out->pool = s->score_pool;
-  out->kept = s->score_kept;
+  out->kept = std::min(s->score_pool, (int)s->B);
   return STATEKV_OK;
 }
 
 int statekv_kernel_times(statekv_state* s, float* ms, int32_t* launches, int32_t n_kernels,
                          int32_t reset) {
   if (!s || n_kernels < 0) return STATEKV_EINVAL;
-  if (hipSetDevice(s->device) != hipSuccess || hipStreamSynchronize(s->stream) != hipSuccess)
-    return STATEKV_EDEVICE;
+  const int rc = sync_state(s);
+  if (rc) return rc;
   for (int r = 0; r < statekv_state::kRing; ++r)
     for (int k = 0; k < STATEKV_K_COUNT; ++k) drain_slot(s, r, k);
   const int n = std::min<int>(n_kernels, STATEKV_K_COUNT);

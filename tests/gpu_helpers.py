@@ -100,7 +100,8 @@ class StepCheck:
         pos_new = pos_new.cpu().numpy().astype(np.int64)
         rep["state_size"] = (int(pos_new.size), int(res.state.count))
         rep["violations"] = selection_violations(res, pos_new, wl.budget)
-        rep["ascending"] = bool(np.all(np.diff(pos_new) > 0))
+        # The state is a set of slots: positions are unique (slot order is free).
+        rep["unique"] = bool(np.unique(pos_new).size == pos_new.size)
         # Every kept row equals the pool row at its position (bit-exact).
         K_pool = np.concatenate([before.K, res.K_rot.transpose(1, 0, 2)], axis=1)
         V_pool = np.concatenate([before.V, res.V.transpose(1, 0, 2)], axis=1)
@@ -117,6 +118,8 @@ class StepCheck:
             rep["score_rel_p99"] = float(np.quantile(rel, 0.99))
             rep["score_sum"] = float(s_gpu.sum())
             rep["pool_pos_exact"] = bool(np.array_equal(sc["pool_pos"].cpu().numpy(), res.pool_pos))
+            kept = sc["pool_pos"].cpu().numpy()[sc["keep_flag"].cpu().numpy() == 1]
+            rep["keep_flag_matches_state"] = sorted(kept.tolist()) == sorted(pos_new.tolist())
         self.report.append(rep)
         return rep
 
@@ -125,9 +128,9 @@ def assert_step_ok(rep, dtype: str, score_tol: float = 1e-5):
     assert rep["out_err"] <= OUT_TOL[dtype], rep
     assert rep["d_k_exact"] and rep["d_v_exact"], rep
     assert rep["state_size"][0] == rep["state_size"][1], rep
-    assert rep["ascending"] and rep["rows_exact"], rep
+    assert rep["unique"] and rep["rows_exact"], rep
     assert not rep["violations"], rep
     if "score_rel_max" in rep:
         assert rep["score_rel_max"] <= score_tol, rep
         assert abs(rep["score_sum"] - 1.0) < 1e-4, rep
-        assert rep["pool_pos_exact"], rep
+        assert rep["pool_pos_exact"] and rep["keep_flag_matches_state"], rep

@@ -102,7 +102,7 @@ def test_no_eviction_stream_reduces_to_full_attention():
         rep = chk.step(check=True)
         assert_step_ok(rep, wl.dtype)
     _, _, pos = chk.st.compressed_view()
-    assert pos.cpu().numpy().tolist() == list(range(6 * 200))
+    assert pos.cpu().numpy().tolist() == list(range(6 * 200))   # nothing evicted or moved
 
 
 def test_exact_ties_keep_the_oldest():
@@ -121,11 +121,11 @@ def test_exact_ties_keep_the_oldest():
     st.prefill_frame(*[to_device(x, wl.dtype) for x in (Q, K, V)], n=2)
     res = frame_step(cfg, before, Q, K, V, 2)
     _, _, pos = st.compressed_view()
-    assert pos.cpu().numpy().tolist() == res.state.pos.tolist()
+    assert sorted(pos.cpu().numpy().tolist()) == sorted(res.state.pos.tolist())
     sc = st.scores()
     s = sc["scores"].cpu().numpy()
     assert len(set(s[:14].tolist())) == 1          # 13 state keys + frame key 0
-    assert res.state.pos.tolist() == before.pos.tolist()
+    assert sorted(res.state.pos.tolist()) == sorted(before.pos.tolist())
 
 
 def test_two_runs_are_bitwise_identical():
