@@ -45,6 +45,13 @@ def parse_args():
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="bounded CPU work for the oracle baseline (0 disables it)")
     p.add_argument("--no-kernel-timing", action="store_true")
+    p.add_argument("--copy-calibration-mb", type=int, default=0,
+                   help="first run one device-to-device copy of this many MiB (a kernel of known "
+                        "traffic that rocprofv3 counters are scaled by)")
+    p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="no GPU work: turn two rocprofv3 --pmc counter_collection.csv files "
+                        "(FETCH_SIZE, WRITE_SIZE) of a run with --copy-calibration-mb into "
+                        "profiles/attn_fwd_<workload>_traffic.json")
     return p.parse_args()
 
 
@@ -70,8 +77,50 @@ def load_traffic(kernel: str, workload: str):
     return rec.get("bytes_per_launch")
 
 
+def summarize_pmc(fetch_csv: str, write_csv: str, workload: str, copy_mb: int) -> dict:
+    """HBM bytes per attn_fwd launch, scaled by the counters of a known copy."""
+    import csv
+    import statistics
+
+    def per_kernel(path, counter):
+        """Median over attn_fwd dispatches; the largest copy dispatch (the calibration copy)."""
+        attn, copies = [], []
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            v = float(r["Counter_Value"]) * 1024.0  # KiB -> bytes
+            if "attn_fwd_kernel" in r["Kernel_Name"]:
+                attn.append(v)
+            elif "copyBuffer" in r["Kernel_Name"]:
+                copies.append((int(r["Grid_Size"]), v))
+        return {"attn_fwd": statistics.median(attn), "copy": max(copies)[1]}
+
+    f = per_kernel(fetch_csv, "FETCH_SIZE")
+    w = per_kernel(write_csv, "WRITE_SIZE")
+    copy_bytes = copy_mb * (1 << 20)
+    f_scale = copy_bytes / f["copy"]
+    w_scale = copy_bytes / w["copy"]
+    rec = {
+        "kernel": "attn_fwd", "workload": workload,
+        "source_sha256": kernel_source_hash(),
+        "fetch_bytes_raw": f["attn_fwd"], "write_bytes_raw": w["attn_fwd"],
+        "copy_calibration_bytes": copy_bytes,
+        "copy_fetch_raw": f["copy"], "copy_write_raw": w["copy"],
+        "fetch_scale": f_scale, "write_scale": w_scale,
+        "bytes_per_launch": f["attn_fwd"] * f_scale + w["attn_fwd"] * w_scale,
+    }
+    path = os.path.join(ROOT, "profiles", f"attn_fwd_{workload}_traffic.json")
+    with open(path, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    return rec
+
+
 def main():
     args = parse_args()
+    if args.summarize_pmc:
+        print(json.dumps(summarize_pmc(*args.summarize_pmc, args.workload,
+                                       args.copy_calibration_mb or 256)))
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures the StateKV frame step on one GPU only; "
@@ -95,6 +144,14 @@ def main():
     tdtype = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.copy_calibration_mb:
+        n = args.copy_calibration_mb * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # Inputs resident in HBM before timing.
     fs = FrameStream(wl, 0)
@@ -195,7 +252,7 @@ def main():
                                  pp.cpu().numpy().astype(np.int64))
         n0 = total
         done, tc = 0, 0.0
-        while tc < args.cpu_seconds and done < 64:
+        while tc < args.cpu_seconds and done < 512:
             q, k, v = fs.frame(n0 + done)
             c0 = time.perf_counter()
             ostate = frame_step(cfg, ostate, q, k, v, n0 + done).state
