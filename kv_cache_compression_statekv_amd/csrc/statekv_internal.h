@@ -77,13 +77,12 @@ struct SelectArgs {
   unsigned long long* colsum;  // [cap] fixed-point column sums; cleared after reading
   const int32_t* pool_pos;     // [cap] positions of the pool rows
   float* scores;               // [P] out: fp32 scores
-  int32_t* score_pos;          // [P] out: positions of the scored pool
   int32_t* keep_flag;          // [P] out: 1 if the candidate stays in the state
   int32_t* move_dst;           // [T] out: evicted state slots (< B), ascending
   int32_t* move_src;           // [T] out: kept rows beyond B, ascending
   int32_t* move_count;         // [1] out
   int32_t P, B, mode;          // mode: kSelMerge, kSelScores or kSelEvict
-  double denom;                // Hq * T
+  double score_scale;          // 2^-kScoreFracBits / (Hq * T)
   const float* opart;
   const float* mpart;
   const double* lpart;
@@ -100,6 +99,7 @@ struct MovesArgs {
   void* kpool;
   void* vpool;
   int32_t* pool_pos;
+  int32_t* evicted_pos;        // [max_moves] out: positions the moves overwrite
   const int32_t* move_dst;
   const int32_t* move_src;
   const int32_t* move_count;
@@ -116,5 +116,9 @@ hipError_t launch_attn(Dt dt, int d, const AttnArgs& a, int row_tiles, int split
 hipError_t launch_score(Dt dt, int d, const ScoreArgs& a, int key_blocks, int rsplits, hipStream_t s);
 hipError_t launch_select(Dt dt, int d, const SelectArgs& a, hipStream_t s);
 hipError_t launch_moves(const MovesArgs& a, hipStream_t s);
+// score_pos[move_dst[i]] = evicted_pos[i] for i < min(*move_count, max_moves).
+hipError_t launch_restore_positions(int32_t* score_pos, const int32_t* evicted_pos,
+                                    const int32_t* move_dst, const int32_t* move_count,
+                                    int max_moves, int B, hipStream_t s);
 
 }  // namespace statekv

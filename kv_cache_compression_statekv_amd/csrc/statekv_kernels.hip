@@ -766,196 +766,284 @@ __global__ __launch_bounds__(256, 1) void attn_score_kernel(ScoreArgs a) {
 //     key_j = (bits of s_j) << 32 | ~pos_j
 // (non-negative fp32 values order like their bit patterns; among equal scores
 // the newer token has the smaller key).  The keys are distinct, so the evicted
-// set is unique.  The E-th smallest key is bracketed by refining a key range
-// [lo, hi] with a histogram of up to 4096 power-of-two-wide buckets until the
-// boundary bucket holds at most kSelCand candidates (usually after one round);
-// each candidate is then ranked by counting the candidates below it.
-// The state keeps its slots: evicted slots below B receive, in ascending
-// order, the kept rows at or beyond B (the frame's tail), so at most T rows
-// move per KV head; the move list is built with one block-wide scan.
+// set is unique.  The score bits live in LDS.  The E-th smallest key is
+// bracketed by refining a range of score bits with histograms of up to 4096
+// power-of-two-wide buckets until the boundary bucket holds at most kSelCand
+// candidates (usually after one round).  If the boundary is a single score
+// shared by more candidates (exact ties), the same refinement runs over ~pos
+// of the tied rows.  The candidates are then ranked by their keys; positions
+// are read only for candidates whose score bits tie.  The state keeps its
+// slots: evicted slots below B receive, in ascending order, the kept rows at
+// or beyond B (the frame's tail), so at most T rows move per KV head; the move
+// list is built with one block-wide scan.
 // ---------------------------------------------------------------------------
-__device__ int block_excl_scan(int v, int* sh, int* total) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) sh[wave] = x;
-  __syncthreads();
-  if (wave == 0) {
-    const int w = lane < kSelectThreads / 64 ? sh[lane] : 0;
-    int xs = w;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(xs, o);
-      if (lane >= o) xs += y;
-    }
-    if (lane < kSelectThreads / 64) sh[lane] = xs - w;
-    if (lane == kSelectThreads / 64 - 1) sh[kSelectThreads / 64] = xs;
-  }
-  __syncthreads();
-  const int res = sh[wave] + x - v;
-  *total = sh[kSelectThreads / 64];
-  __syncthreads();
-  return res;
+
+// Inclusive prefix sum over the 64 lanes of a wave (row shifts within rows of
+// 16 lanes, then the row broadcasts of lanes 15 and 31).
+__device__ __forceinline__ int wave_incl_sum(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
 }
 
-constexpr int kSelMaxPerThread = kMaxPool / kSelectThreads;  // 32
+// Minimum / maximum of the wave, valid in lane 63 (same lane pattern).
+__device__ __forceinline__ uint32_t wave_min_last(uint32_t x) {
+  const int id = -1;
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)x, 0x111, 0xf, 0xf, false));
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)x, 0x112, 0xf, 0xf, false));
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)x, 0x114, 0xf, 0xf, false));
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)x, 0x118, 0xf, 0xf, false));
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)x, 0x142, 0xa, 0xf, false));
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)x, 0x143, 0xc, 0xf, false));
+  return x;
+}
+__device__ __forceinline__ uint32_t wave_max_last(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false));
+  return x;
+}
 
-__device__ void select_top_b(const SelectArgs& a) {
-  __shared__ int hist[kSelectBins];
-  __shared__ unsigned long long cand_key[kSelCand];
-  __shared__ int cand_idx[kSelCand];
-  __shared__ uint8_t evict[kMaxPool];
-  __shared__ int scan_sh[kSelectThreads / 64 + 1];
-  __shared__ unsigned long long red_lo[kSelectThreads / 64], red_hi[kSelectThreads / 64];
-  __shared__ int s_bucket, s_below, s_cnt, s_ncand;
-
+// Exclusive prefix sum over the work-group; *total receives the sum.  One
+// barrier; sh[] must not be written again before the caller's next barrier.
+__device__ int block_excl_scan(int v, int* sh, int* total) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int C = (a.P + kSelectThreads - 1) / kSelectThreads;
-  const int i0 = tid * C;
-  const int cnt = max(0, min(C, a.P - i0));
-  unsigned long long key[kSelMaxPerThread];
-  unsigned long long lo = ~0ull, hi = 0ull;
-#pragma unroll
-  for (int j = 0; j < kSelMaxPerThread; ++j) {
-    key[j] = 0ull;
-    if (j < cnt) {
-      const int idx = i0 + j;
-      const unsigned long long fx = a.colsum[idx];
-      a.colsum[idx] = 0ull;  // ready for the next frame's score pass
-      const double sc = (double)fx * (1.0 / (double)(1ull << kScoreFracBits));
-      const float f = (float)(sc / a.denom);
-      const int p = a.pool_pos[idx];
-      a.scores[idx] = f;
-      a.score_pos[idx] = p;
-      key[j] = ((unsigned long long)__float_as_uint(f) << 32) | (unsigned long long)(~(uint32_t)p);
-      lo = min(lo, key[j]);
-      hi = max(hi, key[j]);
-    }
-  }
-  if (a.mode != kSelEvict) {
-#pragma unroll
-    for (int j = 0; j < kSelMaxPerThread; ++j)
-      if (j < cnt) a.keep_flag[i0 + j] = 1;
-    if (tid == 0) *a.move_count = 0;
-    return;
-  }
-
-  // block min / max of the keys
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    lo = min(lo, (unsigned long long)__shfl_xor((long long)lo, o));
-    hi = max(hi, (unsigned long long)__shfl_xor((long long)hi, o));
-  }
-  if (lane == 0) {
-    red_lo[wave] = lo;
-    red_hi[wave] = hi;
-  }
+  const int inc = wave_incl_sum(v);
+  if (lane == 63) sh[wave] = inc;
   __syncthreads();
-  lo = ~0ull;
-  hi = 0ull;
+  int before = 0, tot = 0;
 #pragma unroll
   for (int w = 0; w < kSelectThreads / 64; ++w) {
-    lo = min(lo, red_lo[w]);
-    hi = max(hi, red_hi[w]);
+    const int x = sh[w];
+    before += w < wave ? x : 0;
+    tot += x;
   }
+  *total = tot;
+  return before + inc - v;
+}
 
-  int need = a.P - a.B;  // keys still to evict inside [lo, hi]
-  for (;;) {
-    const unsigned long long span = hi - lo;
-    const int bits = span ? 64 - __clzll((long long)span) : 0;
-    const int sh = bits > 12 ? bits - 12 : 0;
-    const int nb = (int)(span >> sh) + 1;
-    for (int x = tid; x < nb; x += kSelectThreads) hist[x] = 0;
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < kSelMaxPerThread; ++j)
-      if (j < cnt && key[j] >= lo && key[j] <= hi) atomicAdd(&hist[(int)((key[j] - lo) >> sh)], 1);
-    __syncthreads();
-    int c4[4];
-    int s4 = 0;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int q = tid * 4 + u;
-      c4[u] = q < nb ? hist[q] : 0;
-      s4 += c4[u];
-    }
-    if (tid == 0) {
-      s_bucket = 0;
-      s_below = 0;
-      s_cnt = 0;
-    }
-    int total;
-    int run = block_excl_scan(s4, scan_sh, &total);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int q = tid * 4 + u;
-      if (q < nb && run < need && need <= run + c4[u]) {
-        s_bucket = q;
-        s_below = run;
-        s_cnt = c4[u];
-      }
-      run += c4[u];
-    }
-    __syncthreads();
-    need -= s_below;
-    const unsigned long long blo = lo + ((unsigned long long)s_bucket << sh);
-    const unsigned long long width_m1 = sh ? ((1ull << sh) - 1ull) : 0ull;
-    const unsigned long long bhi = (hi - blo > width_m1) ? blo + width_m1 : hi;
-    lo = blo;
-    hi = bhi;
-    const int ncnt = s_cnt;
-    __syncthreads();
-    if (ncnt <= kSelCand) break;
-  }
+struct SelectShared {
+  uint32_t val[kMaxPool];  // score bits of the pool rows; bit 31 = evicted
+  int hist[kSelectBins];
+  uint32_t cand_v[kSelCand];
+  uint32_t cand_np[kSelCand];
+  int cand_idx[kSelCand];
+  int scan[kSelectThreads / 64];
+  uint32_t red_lo[kSelectThreads / 64], red_hi[kSelectThreads / 64];
+  int bucket, below, cnt, ncand, any_tie;
+};
 
-  // Keys below lo are evicted; the candidates in [lo, hi] are ranked.
-  if (tid == 0) s_ncand = 0;
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < kSelMaxPerThread; ++j) {
-    if (j < cnt) {
-      evict[i0 + j] = key[j] < lo ? 1 : 0;
-      if (key[j] >= lo && key[j] <= hi) {
-        const int slot = atomicAdd(&s_ncand, 1);
-        cand_key[slot] = key[j];
-        cand_idx[slot] = i0 + j;
-      }
-    }
+// One refinement of the boundary: histogram of the values get(idx) in
+// [lo, hi] (get returns false for rows outside the set), then the bucket
+// holding the need-th smallest becomes the new [lo, hi].  Returns that
+// bucket's count.
+template <class Get>
+__device__ int refine_boundary(SelectShared& sh, int P, uint32_t& lo, uint32_t& hi, int& need, Get get) {
+  const int tid = threadIdx.x;
+  const uint32_t span = hi - lo;
+  const int bits = span ? 32 - __clz((int)span) : 0;
+  const int shift = bits > 12 ? bits - 12 : 0;
+  const int nb = (int)(span >> shift) + 1;
+  for (int x = tid; x < nb; x += kSelectThreads) sh.hist[x] = 0;
+  if (tid == 0) {
+    sh.bucket = 0;
+    sh.below = 0;
+    sh.cnt = 0;
   }
   __syncthreads();
-  const int nc = s_ncand;
-  if (tid < nc) {
-    const unsigned long long mine = cand_key[tid];
-    int rank = 0;
-    for (int c = 0; c < nc; ++c) rank += cand_key[c] < mine ? 1 : 0;
-    evict[cand_idx[tid]] = rank < need ? 1 : 0;
+  for (int idx = tid; idx < P; idx += kSelectThreads) {
+    uint32_t v;
+    if (get(idx, v) && v >= lo && v <= hi) atomicAdd(&sh.hist[(int)((v - lo) >> shift)], 1);
   }
   __syncthreads();
-
-  // Keep flags and the move list (holes below B, movers at or beyond B).
-  int holes = 0, movers = 0;
+  int c4[4];
+  int s4 = 0;
 #pragma unroll
-  for (int j = 0; j < kSelMaxPerThread; ++j) {
-    if (j < cnt) {
-      const int idx = i0 + j;
-      const int ev = evict[idx];
-      a.keep_flag[idx] = 1 - ev;
-      holes += (idx < a.B && ev) ? 1 : 0;
-      movers += (idx >= a.B && !ev) ? 1 : 0;
-    }
+  for (int u = 0; u < 4; ++u) {
+    const int q = tid * 4 + u;
+    c4[u] = q < nb ? sh.hist[q] : 0;
+    s4 += c4[u];
   }
   int total;
-  const int base = block_excl_scan(holes | (movers << 16), scan_sh, &total);
-  int bh = base & 0xffff, bm = base >> 16;
+  int run = block_excl_scan(s4, sh.scan, &total);
 #pragma unroll
-  for (int j = 0; j < kSelMaxPerThread; ++j) {
-    if (j < cnt) {
-      const int idx = i0 + j;
-      const int ev = evict[idx];
+  for (int u = 0; u < 4; ++u) {
+    const int q = tid * 4 + u;
+    if (q < nb && run < need && need <= run + c4[u]) {
+      sh.bucket = q;
+      sh.below = run;
+      sh.cnt = c4[u];
+    }
+    run += c4[u];
+  }
+  __syncthreads();
+  need -= sh.below;
+  const uint32_t blo = lo + ((uint32_t)sh.bucket << shift);
+  const uint32_t width_m1 = (uint32_t)((1ull << shift) - 1ull);
+  hi = (hi - blo > width_m1) ? blo + width_m1 : hi;
+  lo = blo;
+  const int cnt = sh.cnt;
+  __syncthreads();
+  return cnt;
+}
+
+__device__ void select_top_b(const SelectArgs& a) {
+  __shared__ SelectShared sh;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // Row j*kSelectThreads + tid of the pool belongs to thread tid, so that every
+  // global access of a wave is contiguous.  No global store precedes a
+  // barrier (a barrier waits for the wave's outstanding stores): the outputs
+  // are written after the last one.
+  const int C = (a.P + kSelectThreads - 1) / kSelectThreads;
+  constexpr int kChunk = 8;
+  uint32_t flo = ~0u, fhi = 0u;
+  for (int j0 = 0; j0 < C; j0 += kChunk) {
+    unsigned long long fx[kChunk];
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) {
+      const int idx = (j0 + j) * kSelectThreads + tid;
+      fx[j] = idx < a.P ? a.colsum[idx] : 0ull;
+    }
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) {
+      const int idx = (j0 + j) * kSelectThreads + tid;
+      if (idx < a.P) {
+        const uint32_t fb = __float_as_uint((float)((double)fx[j] * a.score_scale));
+        sh.val[idx] = fb;
+        flo = min(flo, fb);
+        fhi = max(fhi, fb);
+      }
+    }
+  }
+
+  if (a.mode == kSelEvict) {
+    // Range of the score bits.
+    flo = wave_min_last(flo);
+    fhi = wave_max_last(fhi);
+    if (lane == 63) {
+      sh.red_lo[wave] = flo;
+      sh.red_hi[wave] = fhi;
+    }
+    __syncthreads();
+    uint32_t lo = ~0u, hi = 0u;
+#pragma unroll
+    for (int w = 0; w < kSelectThreads / 64; ++w) {
+      lo = min(lo, sh.red_lo[w]);
+      hi = max(hi, sh.red_hi[w]);
+    }
+
+    int need = a.P - a.B;  // keys still to evict inside the boundary range
+    int cnt;
+    do {
+      cnt = refine_boundary(sh, a.P, lo, hi, need, [&](int idx, uint32_t& v) {
+        v = sh.val[idx];
+        return true;
+      });
+    } while (cnt > kSelCand && lo != hi);
+
+    // Exact ties beyond kSelCand at one score: refine over ~pos of the tied rows.
+    uint32_t plo = 0u, phi = ~0u;
+    const bool tie_stage = cnt > kSelCand;
+    if (tie_stage) {
+      const uint32_t tied = lo;
+      do {
+        cnt = refine_boundary(sh, a.P, plo, phi, need, [&](int idx, uint32_t& v) {
+          if (sh.val[idx] != tied) return false;
+          v = ~(uint32_t)a.pool_pos[idx];
+          return true;
+        });
+      } while (cnt > kSelCand && plo != phi);
+    }
+
+    // Rows below the boundary are evicted (bit 31 of their entry); the
+    // candidates are collected.
+    if (tid == 0) {
+      sh.ncand = 0;
+      sh.any_tie = 0;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < a.P; idx += kSelectThreads) {
+      const uint32_t v = sh.val[idx];
+      bool ev = v < lo;
+      bool cand = v >= lo && v <= hi;
+      if (cand && tie_stage) {
+        const uint32_t np = ~(uint32_t)a.pool_pos[idx];
+        ev = np < plo;
+        cand = np >= plo && np <= phi;
+      }
+      if (cand) {
+        const int slot = atomicAdd(&sh.ncand, 1);
+        sh.cand_v[slot] = v;
+        sh.cand_idx[slot] = idx;
+      }
+      if (ev) sh.val[idx] = v | 0x80000000u;
+    }
+    __syncthreads();
+    // Rank of each candidate among the candidates: by score bits, and by ~pos
+    // among equal score bits (read only when such ties exist).
+    const int nc = sh.ncand;
+    int rank = 0, eq = 0;
+    uint32_t mine = 0u;
+    if (tid < nc) {
+      mine = sh.cand_v[tid];
+      for (int c = 0; c < nc; ++c) {
+        const uint32_t o = sh.cand_v[c];
+        rank += o < mine ? 1 : 0;
+        eq += o == mine ? 1 : 0;
+      }
+      if (eq == 1 && rank < need) sh.val[sh.cand_idx[tid]] |= 0x80000000u;
+      if (eq > 1) sh.any_tie = 1;
+    }
+    __syncthreads();
+    if (sh.any_tie) {
+      uint32_t np = 0u;
+      if (tid < nc && eq > 1) {
+        np = ~(uint32_t)a.pool_pos[sh.cand_idx[tid]];
+        sh.cand_np[tid] = np;
+      }
+      __syncthreads();
+      if (tid < nc && eq > 1) {
+        for (int c = 0; c < nc; ++c)
+          rank += (sh.cand_v[c] == mine && sh.cand_np[c] < np) ? 1 : 0;
+        if (rank < need) sh.val[sh.cand_idx[tid]] |= 0x80000000u;
+      }
+      __syncthreads();
+    }
+  }
+
+  // Move list from the flags: every thread scans a contiguous range of rows so
+  // that holes (evicted slots below B) and movers (kept rows at or beyond B)
+  // come out ascending.
+  const int i0 = tid * C;
+  const int i1 = min(a.P, i0 + C);
+  int holes = 0, movers = 0;
+  for (int idx = i0; idx < i1; ++idx) {
+    const uint32_t ev = sh.val[idx] >> 31;
+    holes += (idx < a.B && ev) ? 1 : 0;
+    movers += (idx >= a.B && !ev) ? 1 : 0;
+  }
+  int total;
+  const int base = block_excl_scan(holes | (movers << 16), sh.scan, &total);
+
+  // Outputs (the positions of the scored pool are rebuilt on request from the
+  // pool positions and the positions the moves overwrite).
+  for (int idx = tid; idx < a.P; idx += kSelectThreads) {
+    const uint32_t v = sh.val[idx];
+    a.scores[idx] = __uint_as_float(v & 0x7fffffffu);
+    a.keep_flag[idx] = (int)(1u - (v >> 31));
+    a.colsum[idx] = 0ull;  // ready for the next frame's score pass
+  }
+  if (holes | movers) {
+    int bh = base & 0xffff, bm = base >> 16;
+    for (int idx = i0; idx < i1; ++idx) {
+      const uint32_t ev = sh.val[idx] >> 31;
       if (idx < a.B && ev) a.move_dst[bh++] = idx;
       if (idx >= a.B && !ev) a.move_src[bm++] = idx;
     }
@@ -1037,7 +1125,20 @@ __global__ __launch_bounds__(256) void moves_kernel(MovesArgs a) {
   const size_t dof = ((size_t)g * a.cap + dst) * a.row_bytes + (size_t)c * 16;
   *reinterpret_cast<u32x4_t*>((char*)a.kpool + dof) = *reinterpret_cast<const u32x4_t*>((const char*)a.kpool + so);
   *reinterpret_cast<u32x4_t*>((char*)a.vpool + dof) = *reinterpret_cast<const u32x4_t*>((const char*)a.vpool + so);
-  if (g == 0 && c == 0) a.pool_pos[dst] = a.pool_pos[src];
+  if (g == 0 && c == 0) {
+    a.evicted_pos[i] = a.pool_pos[dst];
+    a.pool_pos[dst] = a.pool_pos[src];
+  }
+}
+
+// Positions of the scored pool in the slots that the moves overwrote.
+__global__ __launch_bounds__(256) void restore_positions_kernel(int32_t* score_pos, const int32_t* evicted_pos,
+                                                                const int32_t* move_dst,
+                                                                const int32_t* move_count, int max_moves,
+                                                                int B) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= min(*move_count, max_moves)) return;
+  score_pos[min(max(move_dst[i], 0), B - 1)] = evicted_pos[i];
 }
 
 }  // namespace
@@ -1129,6 +1230,14 @@ hipError_t launch_select(Dt dt, int d, const SelectArgs& a, hipStream_t s) {
 hipError_t launch_moves(const MovesArgs& a, hipStream_t s) {
   const size_t total = (size_t)a.max_moves * a.Hkv * (a.row_bytes / 16);
   hipLaunchKernelGGL(moves_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_restore_positions(int32_t* score_pos, const int32_t* evicted_pos,
+                                    const int32_t* move_dst, const int32_t* move_count,
+                                    int max_moves, int B, hipStream_t s) {
+  hipLaunchKernelGGL(restore_positions_kernel, dim3((unsigned)((max_moves + 255) / 256)), dim3(256), 0, s,
+                     score_pos, evicted_pos, move_dst, move_count, max_moves, B);
   return hipGetLastError();
 }
 

@@ -17,8 +17,11 @@
 //   rope_tab          [max_frames*T][d/2] fp32 (cos, sin) of the scaled angles.
 //   colsum            [cap] per-key column sums, 64-bit fixed point; the select
 //                     kernel reads and clears them.
-//   scores, score_pos, keep_flag   scores of the last scored pool.
+//   scores, keep_flag              scores of the last scored pool.
 //   move_dst, move_src, move_count the moves of the last selection.
+//   evicted_pos                    positions the last moves overwrote.
+//   score_pos                      positions of the last scored pool, rebuilt
+//                                  on request by statekv_scores.
 // Everything is allocated in statekv_create; a frame step only launches.
 #include "statekv.h"
 #include "statekv_internal.h"
@@ -61,6 +64,7 @@ struct statekv_state {
   int32_t* move_dst;
   int32_t* move_src;
   int32_t* move_count;
+  int32_t* evicted_pos;
   double* inv_freq;
   int32_t* nonfinite;
 
@@ -70,7 +74,7 @@ struct statekv_state {
   int frames_done;
 
   // scores of the last frame that computed them
-  int score_frame, score_pool;
+  int score_frame, score_pool, score_moves_max;
 
   uint32_t flags;
   // Kernel timing: a ring of (start, stop) event pairs per kernel, drained
@@ -103,7 +107,8 @@ int alloc(P** p, size_t bytes) {
 void release(statekv_state* s) {
   void* bufs[] = {s->kpool, s->vpool, s->ppos, s->dk, s->dv, s->qrot, s->opart, s->mpart,
                   s->lpart, s->rope_tab, s->colsum, s->scores, s->score_pos, s->keep_flag,
-                  s->move_dst, s->move_src, s->move_count, s->inv_freq, s->nonfinite};
+                  s->move_dst, s->move_src, s->move_count, s->evicted_pos, s->inv_freq,
+                  s->nonfinite};
   for (void* b : bufs)
     if (b) (void)hipFree(b);
   for (auto& ring : s->ev)
@@ -292,6 +297,7 @@ int statekv_create(const statekv_layer_cfg* cfg, int32_t budget_B, float alpha,
   if (!rc) rc = alloc(&s->move_dst, (size_t)s->T * sizeof(int32_t));
   if (!rc) rc = alloc(&s->move_src, (size_t)s->T * sizeof(int32_t));
   if (!rc) rc = alloc(&s->move_count, sizeof(int32_t));
+  if (!rc) rc = alloc(&s->evicted_pos, (size_t)s->T * sizeof(int32_t));
   if (!rc) rc = alloc(&s->inv_freq, D / 2 * sizeof(double));
   if (!rc) rc = alloc(&s->nonfinite, sizeof(int32_t));
   if (!rc) {
@@ -440,7 +446,6 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const 
     a.colsum = s->colsum;
     a.pool_pos = s->ppos;
     a.scores = s->scores;
-    a.score_pos = s->score_pos;
     a.keep_flag = s->keep_flag;
     a.move_dst = s->move_dst;
     a.move_src = s->move_src;
@@ -448,7 +453,7 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const 
     a.P = P;
     a.B = s->B;
     a.mode = evict ? kSelEvict : (scored ? kSelScores : kSelMerge);
-    a.denom = (double)s->Hq * (double)s->T;
+    a.score_scale = 1.0 / ((double)(1ull << kScoreFracBits) * (double)s->Hq * (double)s->T);
     a.opart = s->opart;
     a.mpart = s->mpart;
     a.lpart = s->lpart;
@@ -468,6 +473,7 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const 
     a.kpool = s->kpool;
     a.vpool = s->vpool;
     a.pool_pos = s->ppos;
+    a.evicted_pos = s->evicted_pos;
     a.move_dst = s->move_dst;
     a.move_src = s->move_src;
     a.move_count = s->move_count;
@@ -483,6 +489,7 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const 
   if (scored) {
     s->score_frame = n;
     s->score_pool = P;
+    s->score_moves_max = evict ? std::min(P - (int)s->B, (int)s->B) : 0;
   }
   s->count = evict ? (int)s->B : P;
   s->frames_done = n + 1;
@@ -530,11 +537,20 @@ int statekv_detailed_view(const statekv_state* s, statekv_view* out) {
 
 int statekv_scores(const statekv_state* s, statekv_scores_view* out) {
   if (!s || !out) return STATEKV_EINVAL;
-  const int rc = sync_state(s);
+  int rc = sync_state(s);
   if (rc) return rc;
   memset(out, 0, sizeof(*out));
   out->frame = s->score_frame;
   if (s->score_frame < 0) return STATEKV_OK;
+  // Positions at scoring time: the pool positions, except in the slots the
+  // moves overwrote.
+  rc = check(hipMemcpyAsync(s->score_pos, s->ppos, (size_t)s->score_pool * sizeof(int32_t),
+                            hipMemcpyDeviceToDevice, s->stream));
+  if (!rc && s->score_moves_max > 0)
+    rc = check(launch_restore_positions(s->score_pos, s->evicted_pos, s->move_dst, s->move_count,
+                                        s->score_moves_max, s->B, s->stream));
+  if (!rc) rc = check(hipStreamSynchronize(s->stream));
+  if (rc) return rc;
   out->scores = s->scores;
   out->pool_pos = s->score_pos;
   out->keep_flag = s->keep_flag;

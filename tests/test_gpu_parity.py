@@ -105,27 +105,31 @@ def test_no_eviction_stream_reduces_to_full_attention():
     assert pos.cpu().numpy().tolist() == list(range(6 * 200))   # nothing evicted or moved
 
 
-def test_exact_ties_keep_the_oldest():
+@pytest.mark.parametrize("T,B,before", [(8, 13, 2), (64, 1500, 24)], ids=["b13", "b1500"])
+def test_exact_ties_keep_the_oldest(T, B, before):
     """All-zero queries: every state key and the frame's first key tie bit-exactly;
-    with one slot too few the newest of them is evicted, exactly as the oracle."""
-    wl = _small("ties", 106, n_q_heads=2, n_kv_heads=1, tokens_per_frame=8, budget=13,
-                n_frames=3, n_sinks=0)
+    with one slot too few the newest of them is evicted, exactly as the oracle.
+    With B = 1500 the tie (1501 keys) is larger than the selection's candidate
+    buffer, so the tie is broken by the refinement over positions."""
+    wl = _small("ties", 106, n_q_heads=2, n_kv_heads=1, tokens_per_frame=T, budget=B,
+                n_frames=before + 1, n_sinks=0)
     st = make_state(wl)
     cfg = oracle_cfg(wl)
     fs = FrameStream(wl)
-    for n in range(2):
+    for n in range(before):
         st.prefill_frame(*[to_device(x, wl.dtype) for x in fs.frame(n)], n=n)
-    Q, K, V = fs.frame(2)
+    Q, K, V = fs.frame(before)
     Q = np.zeros_like(Q)
-    before = gpu_state_as_oracle(st)
-    st.prefill_frame(*[to_device(x, wl.dtype) for x in (Q, K, V)], n=2)
-    res = frame_step(cfg, before, Q, K, V, 2)
+    prior = gpu_state_as_oracle(st)
+    assert prior.pos.size == B
+    st.prefill_frame(*[to_device(x, wl.dtype) for x in (Q, K, V)], n=before)
+    res = frame_step(cfg, prior, Q, K, V, before)
     _, _, pos = st.compressed_view()
     assert sorted(pos.cpu().numpy().tolist()) == sorted(res.state.pos.tolist())
     sc = st.scores()
     s = sc["scores"].cpu().numpy()
-    assert len(set(s[:14].tolist())) == 1          # 13 state keys + frame key 0
-    assert sorted(res.state.pos.tolist()) == sorted(before.pos.tolist())
+    assert len(set(s[:B + 1].tolist())) == 1       # B state keys + frame key 0
+    assert sorted(res.state.pos.tolist()) == sorted(prior.pos.tolist())
 
 
 def test_two_runs_are_bitwise_identical():
