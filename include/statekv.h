@@ -161,12 +161,13 @@ int statekv_scores(const statekv_state* s, statekv_scores_view* out);
 int statekv_set_flags(statekv_state* s, uint32_t flags);
 
 /* Kernels of one step, in launch order, as indexed by statekv_kernel_times. */
-#define STATEKV_K_ROPE     0  /* virtual-position RoPE + append to D */
+#define STATEKV_K_ROPE     0  /* virtual-position RoPE + append to D; the
+                                 previous frame's moves of kept rows into
+                                 evicted slots */
 #define STATEKV_K_ATTN     1  /* fused attention, pass 1 (split over keys) */
 #define STATEKV_K_SCORE    2  /* recompute pass: per-key column sums */
 #define STATEKV_K_SELECT   3  /* Top-B decision; merge of the key splits into O */
-#define STATEKV_K_MOVES    4  /* kept frame rows move into the evicted slots */
-#define STATEKV_K_COUNT    5
+#define STATEKV_K_COUNT    4
 
 /*
  * With STATEKV_FLAG_KERNEL_TIMING set, per-kernel device time (HIP events on

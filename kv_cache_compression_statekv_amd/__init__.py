@@ -33,7 +33,7 @@ DTYPE_F32 = 2
 FLAG_ALWAYS_SCORE = 1
 FLAG_KERNEL_TIMING = 2
 
-KERNEL_NAMES = ["rope_append", "attn_fwd", "attn_score", "select_merge", "moves"]
+KERNEL_NAMES = ["rope_append", "attn_fwd", "attn_score", "select_merge"]
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
                       "include", "statekv.h")

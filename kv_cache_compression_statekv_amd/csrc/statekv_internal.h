@@ -30,21 +30,42 @@ struct RopeTableArgs {
   int32_t npos, half;
 };
 
-// Per-frame arguments of the RoPE + append kernel.
+// Moves of a selection: row move_src[i] (a frame row at or beyond B) ->
+// slot move_dst[i] (< B) of every KV head, with its position; the position
+// the slot held is saved in evicted_pos[slot].
+struct MovesArgs {
+  void* kpool;
+  void* vpool;
+  int32_t* pool_pos;
+  int32_t* evicted_pos;        // [B] out
+  const int32_t* move_dst;
+  const int32_t* move_src;
+  const int32_t* move_count;
+  int32_t Hkv, cap, B, row_bytes, max_moves;
+};
+
+// Per-frame arguments of the RoPE + append kernel.  Work-groups at or beyond
+// rope_blocks apply the previous frame's moves (mv.max_moves > 0): they touch
+// state slots below B and the previous frame's rows, never this frame's.
 struct RopeArgs {
   const void* q;          // [T][Hq][d]
   const void* k;          // [T][Hkv][d]
   const void* v;          // [T][Hkv][d]
   const float2* table;    // [max_frames*T][d/2]
   void* qrot;             // [Hkv][G*T][d], row r = token*G + head-in-group
-  void* kpool;            // [Hkv][cap][d]: state rows, then this frame's rows
+  void* kpool;            // [Hkv][cap][d]: state rows; this frame's rows at frame_base
   void* vpool;            // [Hkv][cap][d]
-  int32_t* pool_pos;      // [cap]
+  int32_t* pool_pos;      // [cap] position of every row
   void* dk;               // [max_frames*T][Hkv][d]
   void* dv;               // [max_frames*T][Hkv][d]
   int32_t* nonfinite;     // set to 1 when an input element is NaN or Inf
-  int32_t n, T, Hq, Hkv, G, cap, k0;
+  int32_t n, T, Hq, Hkv, G, cap, frame_base, rope_blocks;
+  MovesArgs mv;
 };
+
+// Pool index j (state slots, then the frame's tokens) -> row of the pool
+// arrays: the frame's tokens sit at frame_base = k0 + foff.
+__host__ __device__ inline int pool_row(int j, int k0, int foff) { return j < k0 ? j : j + foff; }
 
 // Attention pass 1: one work-group per (row tile, KV head, key split).
 // Per split and row it leaves (m_s, l_s, O_s) with m_s an integer (log2 units)
@@ -57,7 +78,7 @@ struct AttnArgs {
   float* mpart;           // [S][Hkv][R] reference maxima (integers, -inf if empty)
   double* lpart;          // [S][Hkv][R] partial row sums of 2^(x*c - m_s)
   float c_hi;             // sigma * log2(e) rounded to fp32
-  int32_t R, G, cap, P, k0, kps, Hkv;
+  int32_t R, G, cap, P, k0, foff, kps, Hkv;
 };
 
 // Score pass: one work-group per (key block, KV head, row split).
@@ -68,20 +89,21 @@ struct ScoreArgs {
   const double* lpart;
   unsigned long long* colsum;  // [cap] column sums, fixed point (2^-kScoreFracBits units)
   float c_hi, c_lo;            // sigma * log2(e) = c_hi + c_lo
-  int32_t R, G, cap, P, k0, rps, Hkv, S;
+  int32_t R, G, cap, P, k0, foff, rps, Hkv, S;
 };
 
 // Work-group 0: scores and the Top-B decision; work-groups 1..: the merge of
 // the key splits of pass 1 into O (independent of the selection).
 struct SelectArgs {
   unsigned long long* colsum;  // [cap] fixed-point column sums; cleared after reading
-  const int32_t* pool_pos;     // [cap] positions of the pool rows
+  const int32_t* pool_pos;     // [cap] positions of the pool rows (by row)
   float* scores;               // [P] out: fp32 scores
   int32_t* keep_flag;          // [P] out: 1 if the candidate stays in the state
   int32_t* move_dst;           // [T] out: evicted state slots (< B), ascending
-  int32_t* move_src;           // [T] out: kept rows beyond B, ascending
+  int32_t* move_src;           // [T] out: rows of the kept frame tokens at or beyond B, ascending
   int32_t* move_count;         // [1] out
   int32_t P, B, mode;          // mode: kSelMerge, kSelScores or kSelEvict
+  int32_t k0, foff;            // pool index -> row
   double score_scale;          // 2^-kScoreFracBits / (Hq * T)
   const float* opart;
   const float* mpart;
@@ -93,22 +115,11 @@ constexpr int kSelMerge = 0;   // merge only (the pool fits in B and is not scor
 constexpr int kSelScores = 1;  // scores, everything kept
 constexpr int kSelEvict = 2;   // scores and Top-B
 
-// Applies the moves of the selection: row move_src[i] -> slot move_dst[i] of
-// every KV head, and its position.
-struct MovesArgs {
-  void* kpool;
-  void* vpool;
-  int32_t* pool_pos;
-  int32_t* evicted_pos;        // [max_moves] out: positions the moves overwrite
-  const int32_t* move_dst;
-  const int32_t* move_src;
-  const int32_t* move_count;
-  int32_t Hkv, cap, B, row_bytes, max_moves;
-};
-
 // Rows handled by one pass-1 work-group / keys by one score work-group.
 int attn_rows_per_wg(Dt dt, int d);
 int score_keys_per_wg(Dt dt);
+// Work-groups of the RoPE part of the RoPE kernel for T tokens.
+int rope_blocks(int T);
 
 hipError_t launch_rope_table(const RopeTableArgs& a, hipStream_t s);
 hipError_t launch_rope(Dt dt, int d, const RopeArgs& a, hipStream_t s);
@@ -116,9 +127,10 @@ hipError_t launch_attn(Dt dt, int d, const AttnArgs& a, int row_tiles, int split
 hipError_t launch_score(Dt dt, int d, const ScoreArgs& a, int key_blocks, int rsplits, hipStream_t s);
 hipError_t launch_select(Dt dt, int d, const SelectArgs& a, hipStream_t s);
 hipError_t launch_moves(const MovesArgs& a, hipStream_t s);
-// score_pos[move_dst[i]] = evicted_pos[i] for i < min(*move_count, max_moves).
-hipError_t launch_restore_positions(int32_t* score_pos, const int32_t* evicted_pos,
-                                    const int32_t* move_dst, const int32_t* move_count,
-                                    int max_moves, int B, hipStream_t s);
+// Positions of a scored pool of P candidates: the position of its row, or
+// for an evicted slot below B that a move has since filled, the saved one.
+hipError_t launch_score_positions(int32_t* score_pos, const int32_t* pool_pos,
+                                  const int32_t* evicted_pos, const int32_t* keep_flag, int P,
+                                  int B, int k0, int foff, bool moved, hipStream_t s);
 
 }  // namespace statekv

@@ -164,6 +164,27 @@ __global__ __launch_bounds__(256) void rope_table_kernel(RopeTableArgs a) {
   a.table[t] = float2{(float)cs, (float)sn};
 }
 
+// One 16-byte chunk of a move: task t = (move i, KV head g, chunk c); K and V.
+// The move list holds slots below B and rows in [B, cap); clamping only
+// guards the copy against a malformed list.
+__device__ __forceinline__ void apply_move_chunk(const MovesArgs& a, size_t t) {
+  const int cpr = a.row_bytes / 16;
+  const int i = (int)(t / ((size_t)a.Hkv * cpr));
+  if (i >= min(*a.move_count, a.max_moves)) return;
+  const int rem = (int)(t - (size_t)i * a.Hkv * cpr);
+  const int g = rem / cpr, c = rem - g * cpr;
+  const int dst = min(max(a.move_dst[i], 0), a.B - 1);
+  const int src = min(max(a.move_src[i], a.B), a.cap - 1);
+  const size_t so = ((size_t)g * a.cap + src) * a.row_bytes + (size_t)c * 16;
+  const size_t dof = ((size_t)g * a.cap + dst) * a.row_bytes + (size_t)c * 16;
+  *reinterpret_cast<u32x4_t*>((char*)a.kpool + dof) = *reinterpret_cast<const u32x4_t*>((const char*)a.kpool + so);
+  *reinterpret_cast<u32x4_t*>((char*)a.vpool + dof) = *reinterpret_cast<const u32x4_t*>((const char*)a.vpool + so);
+  if (g == 0 && c == 0) {
+    a.evicted_pos[dst] = a.pool_pos[dst];
+    a.pool_pos[dst] = a.pool_pos[src];
+  }
+}
+
 constexpr int kRopeTokensPerWG = 4;
 
 template <class E, int D>
@@ -173,6 +194,10 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeArgs a) {
   constexpr int TPW = kRopeTokensPerWG;
   constexpr int CH = HALF / 8;  // 8-pair chunks per head
   const int tid = threadIdx.x;
+  if ((int)blockIdx.x >= a.rope_blocks) {   // the previous frame's moves
+    apply_move_chunk(a.mv, (size_t)(blockIdx.x - a.rope_blocks) * 256 + tid);
+    return;
+  }
   const int tok0 = blockIdx.x * TPW;
   bool finite = true;
   const int nh = a.Hq + a.Hkv;
@@ -196,7 +221,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeArgs a) {
     } else {
       const int g = hd - a.Hq;
       src = (const T*)a.k + ((size_t)tok * a.Hkv + g) * D;
-      dst0 = (T*)a.kpool + ((size_t)g * a.cap + a.k0 + tok) * D;
+      dst0 = (T*)a.kpool + ((size_t)g * a.cap + a.frame_base + tok) * D;
       dst1 = (T*)a.dk + ((size_t)pos * a.Hkv + g) * D;
     }
     float x1[8], x2[8];
@@ -242,10 +267,10 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) finite &= isfinite(__uint_as_float(v[j]));
     }
-    *reinterpret_cast<u32x4_t*>((T*)a.vpool + ((size_t)g * a.cap + a.k0 + tok) * D + c * VEC) = v;
+    *reinterpret_cast<u32x4_t*>((T*)a.vpool + ((size_t)g * a.cap + a.frame_base + tok) * D + c * VEC) = v;
     *reinterpret_cast<u32x4_t*>((T*)a.dv + ((size_t)(a.n * a.T + tok) * a.Hkv + g) * D + c * VEC) = v;
   }
-  if (tid < TPW && tok0 + tid < a.T) a.pool_pos[a.k0 + tok0 + tid] = a.n * a.T + tok0 + tid;
+  if (tid < TPW && tok0 + tid < a.T) a.pool_pos[a.frame_base + tok0 + tid] = a.n * a.T + tok0 + tid;
   if (!finite) atomicOr(a.nonfinite, 1);
 }
 
@@ -287,7 +312,8 @@ struct AttnStage {
   u32x4_t kr[KCH];
   u32x4_t vr[VCH];
 
-  __device__ __forceinline__ void load(const T* kbase, const T* vbase, int kb, int kend, int tid) {
+  __device__ __forceinline__ void load(const T* kbase, const T* vbase, int kb, int kend, int k0,
+                                       int foff, int tid) {
     constexpr int CPR = D / EPV;
 #pragma unroll
     for (int j = 0; j < KCH; ++j) {
@@ -295,7 +321,8 @@ struct AttnStage {
       const int rr = t / CPR, cc = t - rr * CPR;
       const int key = kb + rr;
       kr[j] = u32x4_t{0u, 0u, 0u, 0u};
-      if (key < kend) kr[j] = *reinterpret_cast<const u32x4_t*>(kbase + (size_t)key * D + cc * EPV);
+      if (key < kend)
+        kr[j] = *reinterpret_cast<const u32x4_t*>(kbase + (size_t)pool_row(key, k0, foff) * D + cc * EPV);
     }
     if constexpr (sizeof(T) == 2) {
       constexpr int NKQ = BN / KG;
@@ -308,7 +335,7 @@ struct AttnStage {
           const int key = kb + kq * KG + j;
           vr[u * KG + j] = u32x4_t{0u, 0u, 0u, 0u};
           if (t < VTASKS && key < kend)
-            vr[u * KG + j] = *reinterpret_cast<const u32x4_t*>(vbase + (size_t)key * D + dc * 8);
+            vr[u * KG + j] = *reinterpret_cast<const u32x4_t*>(vbase + (size_t)pool_row(key, k0, foff) * D + dc * 8);
         }
       }
     } else {
@@ -318,7 +345,8 @@ struct AttnStage {
         const int rr = t % BN, cc = t / BN;
         const int key = kb + rr;
         vr[j] = u32x4_t{0u, 0u, 0u, 0u};
-        if (key < kend) vr[j] = *reinterpret_cast<const u32x4_t*>(vbase + (size_t)key * D + cc * 4);
+        if (key < kend)
+          vr[j] = *reinterpret_cast<const u32x4_t*>(vbase + (size_t)pool_row(key, k0, foff) * D + cc * 4);
       }
     }
   }
@@ -485,7 +513,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fwd_kernel(AttnArgs a) {
   Stage stage;
   const int nblk = kend > kbeg ? (kend - kbeg + BN - 1) / BN : 0;
   if (nblk > 0) {
-    stage.load(kbase, vbase, kbeg, kend, tid);
+    stage.load(kbase, vbase, kbeg, kend, a.k0, a.foff, tid);
     stage.store(Ks[0], Vt[0], tid);
   }
   __syncthreads();
@@ -493,7 +521,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fwd_kernel(AttnArgs a) {
   for (int b = 0; b < nblk; ++b) {
     const int kb = kbeg + b * BN;
     const int buf = b & 1;
-    if (b + 1 < nblk) stage.load(kbase, vbase, kb + BN, kend, tid);
+    if (b + 1 < nblk) stage.load(kbase, vbase, kb + BN, kend, a.k0, a.foff, tid);
     const T* ks_ = Ks[buf];
     const T* vt_ = Vt[buf];
 
@@ -631,7 +659,8 @@ __global__ __launch_bounds__(256, 1) void attn_score_kernel(ScoreArgs a) {
     const int key = key_w + kt * 32 + col;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
-      kf[kt][ks] = key < a.P ? M::ld(kbase + (size_t)key * D + ks * M::KS + hh * M::KL) : M::zero();
+      kf[kt][ks] = key < a.P ? M::ld(kbase + (size_t)pool_row(key, a.k0, a.foff) * D + ks * M::KS + hh * M::KL)
+                             : M::zero();
   }
   double cs[KT];
 #pragma unroll
@@ -956,7 +985,7 @@ __device__ void select_top_b(const SelectArgs& a) {
       do {
         cnt = refine_boundary(sh, a.P, plo, phi, need, [&](int idx, uint32_t& v) {
           if (sh.val[idx] != tied) return false;
-          v = ~(uint32_t)a.pool_pos[idx];
+          v = ~(uint32_t)a.pool_pos[pool_row(idx, a.k0, a.foff)];
           return true;
         });
       } while (cnt > kSelCand && plo != phi);
@@ -974,7 +1003,7 @@ __device__ void select_top_b(const SelectArgs& a) {
       bool ev = v < lo;
       bool cand = v >= lo && v <= hi;
       if (cand && tie_stage) {
-        const uint32_t np = ~(uint32_t)a.pool_pos[idx];
+        const uint32_t np = ~(uint32_t)a.pool_pos[pool_row(idx, a.k0, a.foff)];
         ev = np < plo;
         cand = np >= plo && np <= phi;
       }
@@ -1005,7 +1034,7 @@ __device__ void select_top_b(const SelectArgs& a) {
     if (sh.any_tie) {
       uint32_t np = 0u;
       if (tid < nc && eq > 1) {
-        np = ~(uint32_t)a.pool_pos[sh.cand_idx[tid]];
+        np = ~(uint32_t)a.pool_pos[pool_row(sh.cand_idx[tid], a.k0, a.foff)];
         sh.cand_np[tid] = np;
       }
       __syncthreads();
@@ -1033,7 +1062,7 @@ __device__ void select_top_b(const SelectArgs& a) {
   const int base = block_excl_scan(holes | (movers << 16), sh.scan, &total);
 
   // Outputs (the positions of the scored pool are rebuilt on request from the
-  // pool positions and the positions the moves overwrite).
+  // row positions and the positions the moves overwrite).
   for (int idx = tid; idx < a.P; idx += kSelectThreads) {
     const uint32_t v = sh.val[idx];
     a.scores[idx] = __uint_as_float(v & 0x7fffffffu);
@@ -1045,7 +1074,7 @@ __device__ void select_top_b(const SelectArgs& a) {
     for (int idx = i0; idx < i1; ++idx) {
       const uint32_t ev = sh.val[idx] >> 31;
       if (idx < a.B && ev) a.move_dst[bh++] = idx;
-      if (idx >= a.B && !ev) a.move_src[bm++] = idx;
+      if (idx >= a.B && !ev) a.move_src[bm++] = pool_row(idx, a.k0, a.foff);
     }
   }
   if (tid == 0) *a.move_count = total & 0xffff;
@@ -1109,36 +1138,21 @@ __global__ __launch_bounds__(kSelectThreads, 1) void select_kernel(SelectArgs a)
   if (a.mode != kSelMerge) select_top_b(a);
 }
 
-// Moves of the selection, 16 bytes per thread: K and V of every KV head.
+// Moves of a selection outside a frame step (before a view), 16 bytes per
+// thread: K and V of every KV head.
 __global__ __launch_bounds__(256) void moves_kernel(MovesArgs a) {
-  const int cpr = a.row_bytes / 16;
-  const size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int i = (int)(t / ((size_t)a.Hkv * cpr));
-  if (i >= min(*a.move_count, a.max_moves)) return;
-  const int rem = (int)(t - (size_t)i * a.Hkv * cpr);
-  const int g = rem / cpr, c = rem - g * cpr;
-  // The move list holds slots below B and rows in [B, cap); clamping only
-  // guards the copy against a malformed list.
-  const int dst = min(max(a.move_dst[i], 0), a.B - 1);
-  const int src = min(max(a.move_src[i], a.B), a.cap - 1);
-  const size_t so = ((size_t)g * a.cap + src) * a.row_bytes + (size_t)c * 16;
-  const size_t dof = ((size_t)g * a.cap + dst) * a.row_bytes + (size_t)c * 16;
-  *reinterpret_cast<u32x4_t*>((char*)a.kpool + dof) = *reinterpret_cast<const u32x4_t*>((const char*)a.kpool + so);
-  *reinterpret_cast<u32x4_t*>((char*)a.vpool + dof) = *reinterpret_cast<const u32x4_t*>((const char*)a.vpool + so);
-  if (g == 0 && c == 0) {
-    a.evicted_pos[i] = a.pool_pos[dst];
-    a.pool_pos[dst] = a.pool_pos[src];
-  }
+  apply_move_chunk(a, (size_t)blockIdx.x * blockDim.x + threadIdx.x);
 }
 
-// Positions of the scored pool in the slots that the moves overwrote.
-__global__ __launch_bounds__(256) void restore_positions_kernel(int32_t* score_pos, const int32_t* evicted_pos,
-                                                                const int32_t* move_dst,
-                                                                const int32_t* move_count, int max_moves,
-                                                                int B) {
+// Positions of the scored pool: row position, or the saved position of an
+// evicted slot below B that a move has filled since.
+__global__ __launch_bounds__(256) void score_positions_kernel(int32_t* score_pos, const int32_t* pool_pos,
+                                                              const int32_t* evicted_pos,
+                                                              const int32_t* keep_flag, int P, int B,
+                                                              int k0, int foff, int moved) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= min(*move_count, max_moves)) return;
-  score_pos[min(max(move_dst[i], 0), B - 1)] = evicted_pos[i];
+  if (i >= P) return;
+  score_pos[i] = (moved && i < B && keep_flag[i] == 0) ? evicted_pos[i] : pool_pos[pool_row(i, k0, foff)];
 }
 
 }  // namespace
@@ -1173,8 +1187,11 @@ hipError_t launch_rope_table(const RopeTableArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+int rope_blocks(int T) { return (T + kRopeTokensPerWG - 1) / kRopeTokensPerWG; }
+
 hipError_t launch_rope(Dt dt, int d, const RopeArgs& a, hipStream_t s) {
-  const int blocks = (a.T + kRopeTokensPerWG - 1) / kRopeTokensPerWG;
+  const size_t move_tasks = a.mv.max_moves > 0 ? (size_t)a.mv.max_moves * a.Hkv * (a.mv.row_bytes / 16) : 0;
+  const int blocks = a.rope_blocks + (int)((move_tasks + 255) / 256);
   if (dt == Dt::BF16) {
     if (d == 64) hipLaunchKernelGGL((rope_append_kernel<BF16, 64>), dim3(blocks), dim3(256), 0, s, a);
     else hipLaunchKernelGGL((rope_append_kernel<BF16, 128>), dim3(blocks), dim3(256), 0, s, a);
@@ -1233,11 +1250,11 @@ hipError_t launch_moves(const MovesArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_restore_positions(int32_t* score_pos, const int32_t* evicted_pos,
-                                    const int32_t* move_dst, const int32_t* move_count,
-                                    int max_moves, int B, hipStream_t s) {
-  hipLaunchKernelGGL(restore_positions_kernel, dim3((unsigned)((max_moves + 255) / 256)), dim3(256), 0, s,
-                     score_pos, evicted_pos, move_dst, move_count, max_moves, B);
+hipError_t launch_score_positions(int32_t* score_pos, const int32_t* pool_pos,
+                                  const int32_t* evicted_pos, const int32_t* keep_flag, int P,
+                                  int B, int k0, int foff, bool moved, hipStream_t s) {
+  hipLaunchKernelGGL(score_positions_kernel, dim3((unsigned)((P + 255) / 256)), dim3(256), 0, s, score_pos,
+                     pool_pos, evicted_pos, keep_flag, P, B, k0, foff, moved ? 1 : 0);
   return hipGetLastError();
 }
 

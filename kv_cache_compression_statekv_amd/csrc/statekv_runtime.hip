@@ -1,12 +1,16 @@
 // Host runtime and C ABI of the StateKV frame step (see include/statekv.h).
 //
 // State layout in HBM (one layer):
-//   kpool, vpool      [Hkv][cap][d], cap = B + T.  Rows [0, count) hold the
-//                     compressed state (one slot per token, in slot order);
-//                     the current frame is written to rows [count, count+T).
-//                     After the Top-B decision the kept frame rows at or
-//                     beyond B move into the evicted slots below B, so at
-//                     most T rows move per KV head and frame.
+//   kpool, vpool      [Hkv][cap][d], cap = B + 2T.  Rows [0, count) hold the
+//                     compressed state (one slot per token, in slot order).
+//                     While the state fills, frame n is written right after
+//                     it (rows [count, count+T)); once frames evict, they
+//                     alternate between rows [B, B+T) and [B+T, B+2T).  After
+//                     the Top-B decision the kept frame rows at or beyond B
+//                     move into the evicted slots below B (at most T rows per
+//                     KV head); the next frame's RoPE kernel performs these
+//                     moves, as its own rows lie in the other region.  A view
+//                     of the state performs pending moves first.
 //   ppos              [cap] absolute stream positions of those rows.
 //   dk, dv            [max_frames*T][Hkv][d]: the detailed cache D.
 //   qrot              [Hkv][G*T][d]: the frame's rotated queries, rows grouped
@@ -19,7 +23,7 @@
 //                     kernel reads and clears them.
 //   scores, keep_flag              scores of the last scored pool.
 //   move_dst, move_src, move_count the moves of the last selection.
-//   evicted_pos                    positions the last moves overwrote.
+//   evicted_pos                    [B] positions the last moves overwrote, by slot.
 //   score_pos                      positions of the last scored pool, rebuilt
 //                                  on request by statekv_scores.
 // Everything is allocated in statekv_create; a frame step only launches.
@@ -73,8 +77,14 @@ struct statekv_state {
   int count;         // tokens in the compressed state
   int frames_done;
 
+  // rows of the last frame; moves of its selection not yet performed
+  int frame_base;
+  mutable bool moves_pending;
+  int pending_max_moves;
+
   // scores of the last frame that computed them
-  int score_frame, score_pool, score_moves_max;
+  int score_frame, score_pool, score_k0, score_foff;
+  bool score_evicted;
 
   uint32_t flags;
   // Kernel timing: a ring of (start, stop) event pairs per kernel, drained
@@ -191,6 +201,31 @@ struct KernelTimer {
   }
 };
 
+MovesArgs moves_args(const statekv_state* s, int max_moves) {
+  MovesArgs a{};
+  a.kpool = s->kpool;
+  a.vpool = s->vpool;
+  a.pool_pos = s->ppos;
+  a.evicted_pos = s->evicted_pos;
+  a.move_dst = s->move_dst;
+  a.move_src = s->move_src;
+  a.move_count = s->move_count;
+  a.Hkv = s->Hkv;
+  a.cap = s->cap;
+  a.B = s->B;
+  a.row_bytes = s->D * s->esize;
+  a.max_moves = max_moves;
+  return a;
+}
+
+// Performs the moves of the last selection if no frame step has yet.
+int apply_pending_moves(const statekv_state* s) {
+  if (!s->moves_pending) return STATEKV_OK;
+  const int rc = check(launch_moves(moves_args(s, s->pending_max_moves), s->stream));
+  if (!rc) s->moves_pending = false;
+  return rc;
+}
+
 int read_nonfinite(const statekv_state* s) {
   int32_t h = 0;
   if (hipMemcpy(&h, s->nonfinite, sizeof(h), hipMemcpyDeviceToHost) != hipSuccess)
@@ -251,7 +286,7 @@ int statekv_create(const statekv_layer_cfg* cfg, int32_t budget_B, float alpha,
   s->T = c.tokens_per_frame;
   s->G = s->Hq / s->Hkv;
   s->R = s->G * s->T;
-  s->cap = budget_B + s->T;
+  s->cap = budget_B + 2 * s->T;
   s->stream = nullptr;
   s->score_frame = -1;
 
@@ -297,7 +332,7 @@ int statekv_create(const statekv_layer_cfg* cfg, int32_t budget_B, float alpha,
   if (!rc) rc = alloc(&s->move_dst, (size_t)s->T * sizeof(int32_t));
   if (!rc) rc = alloc(&s->move_src, (size_t)s->T * sizeof(int32_t));
   if (!rc) rc = alloc(&s->move_count, sizeof(int32_t));
-  if (!rc) rc = alloc(&s->evicted_pos, (size_t)s->T * sizeof(int32_t));
+  if (!rc) rc = alloc(&s->evicted_pos, (size_t)s->B * sizeof(int32_t));
   if (!rc) rc = alloc(&s->inv_freq, D / 2 * sizeof(double));
   if (!rc) rc = alloc(&s->nonfinite, sizeof(int32_t));
   if (!rc) {
@@ -367,6 +402,10 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const 
   const hipStream_t st = s->stream;
   const bool evict = P > s->B;
   const bool scored = evict || (s->flags & STATEKV_FLAG_ALWAYS_SCORE);
+  // Rows of this frame: right after the state, or, while the previous
+  // frame's moves are pending, the region its rows do not occupy.
+  const int F = s->moves_pending ? (s->frame_base == (int)s->B + s->T ? (int)s->B : (int)s->B + s->T) : k0;
+  const int foff = F - k0;
 
   {
     KernelTimer tm(s, STATEKV_K_ROPE);
@@ -388,7 +427,9 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const 
     a.Hkv = s->Hkv;
     a.G = s->G;
     a.cap = s->cap;
-    a.k0 = k0;
+    a.frame_base = F;
+    a.rope_blocks = rope_blocks(s->T);
+    a.mv = moves_args(s, s->moves_pending ? s->pending_max_moves : 0);
     rc = check(launch_rope(s->dt, s->D, a, st));
     tm.done();
     if (rc) return rc;
@@ -410,6 +451,7 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const 
     a.cap = s->cap;
     a.P = P;
     a.k0 = k0;
+    a.foff = foff;
     a.kps = kps;
     a.Hkv = s->Hkv;
     rc = check(launch_attn(s->dt, s->D, a, s->attn_tiles, splits, st));
@@ -434,6 +476,7 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const 
     a.cap = s->cap;
     a.P = P;
     a.k0 = k0;
+    a.foff = foff;
     a.rps = rps;
     a.Hkv = s->Hkv;
     rc = check(launch_score(s->dt, s->D, a, key_blocks, rsplits, st));
@@ -452,6 +495,8 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const 
     a.move_count = s->move_count;
     a.P = P;
     a.B = s->B;
+    a.k0 = k0;
+    a.foff = foff;
     a.mode = evict ? kSelEvict : (scored ? kSelScores : kSelMerge);
     a.score_scale = 1.0 / ((double)(1ull << kScoreFracBits) * (double)s->Hq * (double)s->T);
     a.opart = s->opart;
@@ -467,29 +512,15 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const 
     tm.done();
     if (rc) return rc;
   }
-  if (evict) {
-    KernelTimer tm(s, STATEKV_K_MOVES);
-    MovesArgs a{};
-    a.kpool = s->kpool;
-    a.vpool = s->vpool;
-    a.pool_pos = s->ppos;
-    a.evicted_pos = s->evicted_pos;
-    a.move_dst = s->move_dst;
-    a.move_src = s->move_src;
-    a.move_count = s->move_count;
-    a.Hkv = s->Hkv;
-    a.cap = s->cap;
-    a.B = s->B;
-    a.row_bytes = s->D * s->esize;
-    a.max_moves = std::min(P - (int)s->B, (int)s->B);
-    rc = check(launch_moves(a, st));
-    tm.done();
-    if (rc) return rc;
-  }
+  s->moves_pending = evict;
+  s->pending_max_moves = evict ? std::min(P - (int)s->B, (int)s->B) : 0;
+  s->frame_base = F;
   if (scored) {
     s->score_frame = n;
     s->score_pool = P;
-    s->score_moves_max = evict ? std::min(P - (int)s->B, (int)s->B) : 0;
+    s->score_k0 = k0;
+    s->score_foff = foff;
+    s->score_evicted = evict;
   }
   s->count = evict ? (int)s->B : P;
   s->frames_done = n + 1;
@@ -499,7 +530,9 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const 
 
 int statekv_compressed_view(const statekv_state* s, statekv_view* out) {
   if (!s || !out) return STATEKV_EINVAL;
-  int rc = sync_state(s);
+  int rc = check(hipSetDevice(s->device));
+  if (!rc) rc = apply_pending_moves(s);
+  if (!rc) rc = sync_state(s);
   if (!rc) rc = read_nonfinite(s);
   if (rc) return rc;
   memset(out, 0, sizeof(*out));
@@ -537,18 +570,19 @@ int statekv_detailed_view(const statekv_state* s, statekv_view* out) {
 
 int statekv_scores(const statekv_state* s, statekv_scores_view* out) {
   if (!s || !out) return STATEKV_EINVAL;
-  int rc = sync_state(s);
+  int rc = check(hipSetDevice(s->device));
+  if (!rc) rc = sync_state(s);
   if (rc) return rc;
   memset(out, 0, sizeof(*out));
   out->frame = s->score_frame;
   if (s->score_frame < 0) return STATEKV_OK;
-  // Positions at scoring time: the pool positions, except in the slots the
-  // moves overwrote.
-  rc = check(hipMemcpyAsync(s->score_pos, s->ppos, (size_t)s->score_pool * sizeof(int32_t),
-                            hipMemcpyDeviceToDevice, s->stream));
-  if (!rc && s->score_moves_max > 0)
-    rc = check(launch_restore_positions(s->score_pos, s->evicted_pos, s->move_dst, s->move_count,
-                                        s->score_moves_max, s->B, s->stream));
+  // Positions at scoring time: those of the pool rows, except in the slots
+  // that the selection's moves have filled since.
+  rc = apply_pending_moves(s);
+  if (!rc)
+    rc = check(launch_score_positions(s->score_pos, s->ppos, s->evicted_pos, s->keep_flag,
+                                      s->score_pool, s->B, s->score_k0, s->score_foff,
+                                      s->score_evicted, s->stream));
   if (!rc) rc = check(hipStreamSynchronize(s->stream));
   if (rc) return rc;
   out->scores = s->scores;

@@ -110,6 +110,12 @@ class StepCheck:
         rep["rows_exact"] = (min(sel) >= 0
                              and bool(np.array_equal(to_f64(k_new), K_pool[:, sel]))
                              and bool(np.array_equal(to_f64(v_new), V_pool[:, sel])))
+        # Independent of teacher forcing: every state row is the detailed-cache
+        # row of its token, so moves done in earlier (unchecked) frames are
+        # verified too.
+        pos_t = torch.from_numpy(pos_new).to(dk.device)
+        rep["state_matches_D"] = (bool(torch.equal(k_new, dk[pos_t].transpose(0, 1)))
+                                  and bool(torch.equal(v_new, dv[pos_t].transpose(0, 1))))
         sc = self.st.scores()
         if sc is not None and sc["frame"] == n:
             s_gpu = sc["scores"].cpu().numpy().astype(np.float64)
@@ -128,7 +134,7 @@ def assert_step_ok(rep, dtype: str, score_tol: float = 1e-5):
     assert rep["out_err"] <= OUT_TOL[dtype], rep
     assert rep["d_k_exact"] and rep["d_v_exact"], rep
     assert rep["state_size"][0] == rep["state_size"][1], rep
-    assert rep["unique"] and rep["rows_exact"], rep
+    assert rep["unique"] and rep["rows_exact"] and rep["state_matches_D"], rep
     assert not rep["violations"], rep
     if "score_rel_max" in rep:
         assert rep["score_rel_max"] <= score_tol, rep
