@@ -164,6 +164,13 @@ __global__ __launch_bounds__(256) void rope_table_kernel(RopeTableArgs a) {
   a.table[t] = float2{(float)cs, (float)sn};
 }
 
+// Partial outputs of pass 1 are stored in groups of 32 flat rows (flat row =
+// (split*Hkv + g)*R + r): inside a group, quad q of the dims of flat row ri is
+// f32x4 number q*32 + ri%32, so that a wave's store instruction writes 1 KB
+// contiguous.  Returns the f32x4 index of the group of flat row ri.  The
+// buffer holds whole groups.
+__host__ __device__ inline size_t opart_group(size_t ri, int D) { return (ri >> 5) * (size_t)(D / 4) * 32; }
+
 // One 16-byte chunk of a move: task t = (move i, KV head g, chunk c); K and V.
 // The move list holds slots below B and rows in [B, cap); clamping only
 // guards the copy against a malformed list.
@@ -597,14 +604,15 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fwd_kernel(AttnArgs a) {
         a.lpart[ri] = lt;
       }
       if (m_run[qt] != -INFINITY) {
-        float* op = a.opart + ri * D;
+        // Lane-order layout: one store instruction writes 1 KB contiguous.
+        f32x4_t* op = reinterpret_cast<f32x4_t*>(a.opart) + opart_group(ri, D) + (ri & 31);
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             f32x4_t v = {o[qt][dt][4 * j], o[qt][dt][4 * j + 1], o[qt][dt][4 * j + 2],
                          o[qt][dt][4 * j + 3]};
-            *reinterpret_cast<f32x4_t*>(op + dt * 32 + 8 * j + 4 * hh) = v;
+            op[(dt * 8 + 2 * j + hh) * 32] = v;
           }
       }
     }
@@ -1082,23 +1090,25 @@ __device__ void select_top_b(const SelectArgs& a) {
 
 // Merge of the key splits of pass 1:
 //   m = max_s m_s,  l = sum_s 2^(m_s - m) l_s,  O = sum_s 2^(m_s - m) O_s / l,
-// one thread per (row, 4 dims), written to O [T][Hq][d].  The factors are
-// exact powers of two (the m_s are integers).  Partials of splits that saw no
-// key of a row were never written, so they are selected out, not multiplied.
+// one thread per (row, 4 dims), written to O [T][Hq][d].  Threads take rows
+// fastest inside groups of 32, matching the lane-order layout of the
+// partials.  The factors are exact powers of two (the m_s are integers).
+// Partials of splits that saw no key of a row were never written, so they
+// are selected out, not multiplied.
 template <class E, int D>
 __device__ void merge_splits(const SelectArgs& a, size_t t) {
   typedef typename E::T T;
   constexpr int CPR = D / 4;
   const size_t nrows = (size_t)a.Hkv * a.R;
-  if (t >= nrows * CPR) return;
-  const size_t base = t / CPR;   // = g*R + r
-  const int c = (int)(t - base * CPR);
-  const size_t stride = nrows;
+  const size_t grp = (t >> 5) / CPR;
+  const int c = (int)((t >> 5) - grp * CPR);
+  const size_t base = grp * 32 + (t & 31);   // = g*R + r
+  if (base >= nrows) return;
   float ms[kMaxSplits];
   float m = -INFINITY;
 #pragma unroll
   for (int s = 0; s < kMaxSplits; ++s) {
-    ms[s] = s < a.S ? a.mpart[s * stride + base] : -INFINITY;
+    ms[s] = s < a.S ? a.mpart[s * nrows + base] : -INFINITY;
     m = fmaxf(m, ms[s]);
   }
   float l = 0.f;
@@ -1106,8 +1116,9 @@ __device__ void merge_splits(const SelectArgs& a, size_t t) {
 #pragma unroll
   for (int s = 0; s < kMaxSplits; ++s) {
     if (s < a.S) {
-      const f32x4_t os = *reinterpret_cast<const f32x4_t*>(a.opart + (s * stride + base) * D + c * 4);
-      const double ls = a.lpart[s * stride + base];
+      const size_t ri = s * nrows + base;
+      const f32x4_t os = reinterpret_cast<const f32x4_t*>(a.opart)[opart_group(ri, D) + (size_t)c * 32 + (ri & 31)];
+      const double ls = a.lpart[ri];
       const bool live = ms[s] != -INFINITY;
       const float w = live ? ldexpf(1.f, (int)(ms[s] - m)) : 0.f;
       l += live ? w * (float)ls : 0.f;
@@ -1232,7 +1243,7 @@ hipError_t launch_score(Dt dt, int d, const ScoreArgs& a, int key_blocks, int rs
 }
 
 hipError_t launch_select(Dt dt, int d, const SelectArgs& a, hipStream_t s) {
-  const size_t mthreads = (size_t)a.Hkv * a.R * (d / 4);
+  const size_t mthreads = ((size_t)a.Hkv * a.R + 31) / 32 * 32 * (d / 4);   // whole 32-row groups
   const dim3 grid((unsigned)(1 + (mthreads + kSelectThreads - 1) / kSelectThreads)), block(kSelectThreads);
   if (dt == Dt::BF16) {
     if (d == 64) hipLaunchKernelGGL((select_kernel<BF16, 64>), grid, block, 0, s, a);

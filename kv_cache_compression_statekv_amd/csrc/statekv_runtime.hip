@@ -321,7 +321,7 @@ int statekv_create(const statekv_layer_cfg* cfg, int32_t budget_B, float alpha,
   if (!rc) rc = alloc(&s->dk, det_bytes);
   if (!rc) rc = alloc(&s->dv, det_bytes);
   if (!rc) rc = alloc(&s->qrot, rows_all * D * E);
-  if (!rc) rc = alloc(&s->opart, S * rows_all * D * sizeof(float));
+  if (!rc) rc = alloc(&s->opart, (S * rows_all + 31) / 32 * 32 * D * sizeof(float));  // whole 32-row groups
   if (!rc) rc = alloc(&s->mpart, S * rows_all * sizeof(float));
   if (!rc) rc = alloc(&s->lpart, S * rows_all * sizeof(double));
   if (!rc) rc = alloc(&s->rope_tab, (size_t)positions * (D / 2) * sizeof(float2));

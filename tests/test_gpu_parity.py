@@ -44,6 +44,9 @@ SMALL = {
                          budget=1, n_frames=6, n_sinks=0),
     "bf16_g16_b_lt_t": _small("bf16_g16_b_lt_t", 105, n_q_heads=16, n_kv_heads=1,
                               tokens_per_frame=130, budget=97, n_frames=4, n_sinks=3),
+    # G*T = 99 rows per KV head (not a multiple of 32) with several key splits
+    "bf16_rows99_splits": _small("bf16_rows99_splits", 107, n_q_heads=6, n_kv_heads=2,
+                                 tokens_per_frame=33, budget=700, n_frames=24, n_sinks=2),
 }
 
 
