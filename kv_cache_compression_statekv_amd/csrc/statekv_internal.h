@@ -74,7 +74,9 @@ struct AttnArgs {
   const void* qrot;       // [Hkv][R][d]
   const void* kpool;      // [Hkv][cap][d]
   const void* vpool;      // [Hkv][cap][d]
-  float* opart;           // [S][Hkv][R][d] unnormalised partial outputs
+  void* opart;            // [S][Hkv][R][d] unnormalised partial outputs, lane-order groups
+                          // of 32 rows: fp16 scaled by 2^-e_s for bf16 streams, else fp32
+  int8_t* epart;          // [S][Hkv][R] e_s of the fp16 partials
   float* mpart;           // [S][Hkv][R] reference maxima (integers, -inf if empty)
   double* lpart;          // [S][Hkv][R] partial row sums of 2^(x*c - m_s)
   float c_hi;             // sigma * log2(e) rounded to fp32
@@ -105,7 +107,8 @@ struct SelectArgs {
   int32_t P, B, mode;          // mode: kSelMerge, kSelScores or kSelEvict
   int32_t k0, foff;            // pool index -> row
   double score_scale;          // 2^-kScoreFracBits / (Hq * T)
-  const float* opart;
+  const void* opart;
+  const int8_t* epart;
   const float* mpart;
   const double* lpart;
   void* out;                   // [T][Hq][d]

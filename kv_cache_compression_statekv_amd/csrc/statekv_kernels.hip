@@ -31,6 +31,7 @@ namespace statekv {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -163,6 +164,28 @@ __global__ __launch_bounds__(256) void rope_table_kernel(RopeTableArgs a) {
   sincos((double)p * a.inv_freq[k], &sn, &cs);
   a.table[t] = float2{(float)cs, (float)sn};
 }
+
+// Partial outputs of pass 1.  bf16 streams store each row of O_s as fp16
+// scaled by a power of two 2^-e_s (e_s per row, so that the row's largest
+// magnitude is below 1): relative rounding 2^-11, half the bytes of fp32.  The
+// merge folds 2^e_s into its exact power-of-two weight.  fp32 streams store
+// fp32 with e_s = 0.
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+template <class E> struct PartialOut;
+template <> struct PartialOut<BF16> {
+  typedef f16x4_t V;
+  static __device__ __forceinline__ V pack(float a, float b, float c, float d, float sc) {
+    return V{(_Float16)(a * sc), (_Float16)(b * sc), (_Float16)(c * sc), (_Float16)(d * sc)};
+  }
+  static __device__ __forceinline__ f32x4_t unpack(V v) {
+    return f32x4_t{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+  }
+};
+template <> struct PartialOut<F32> {
+  typedef f32x4_t V;
+  static __device__ __forceinline__ V pack(float a, float b, float c, float d, float) { return V{a, b, c, d}; }
+  static __device__ __forceinline__ f32x4_t unpack(V v) { return v; }
+};
 
 // Partial outputs of pass 1 are stored in groups of 32 flat rows (flat row =
 // (split*Hkv + g)*R + r): inside a group, quad q of the dims of flat row ri is
@@ -604,16 +627,28 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fwd_kernel(AttnArgs a) {
         a.lpart[ri] = lt;
       }
       if (m_run[qt] != -INFINITY) {
-        // Lane-order layout: one store instruction writes 1 KB contiguous.
-        f32x4_t* op = reinterpret_cast<f32x4_t*>(a.opart) + opart_group(ri, D) + (ri & 31);
+        int e = 0;
+        if constexpr (sizeof(T) == 2) {
+          float amax = 0.f;
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(o[qt][dt][i]));
+          amax = fmaxf(amax, __shfl_xor(amax, 32));
+          (void)frexpf(amax, &e);   // amax < 2^e
+          if (hh == 0) a.epart[ri] = (int8_t)max(-127, min(127, e));
+        }
+        const float sc = ldexpf(1.f, -e);
+        // Lane-order layout: one store instruction writes 512 B (fp16) or
+        // 1 KB (fp32) contiguous.
+        typedef typename PartialOut<E>::V PV;
+        PV* op = reinterpret_cast<PV*>(a.opart) + opart_group(ri, D) + (ri & 31);
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            f32x4_t v = {o[qt][dt][4 * j], o[qt][dt][4 * j + 1], o[qt][dt][4 * j + 2],
-                         o[qt][dt][4 * j + 3]};
-            op[(dt * 8 + 2 * j + hh) * 32] = v;
-          }
+          for (int j = 0; j < 4; ++j)
+            op[(dt * 8 + 2 * j + hh) * 32] = PartialOut<E>::pack(o[qt][dt][4 * j], o[qt][dt][4 * j + 1],
+                                                                o[qt][dt][4 * j + 2], o[qt][dt][4 * j + 3], sc);
       }
     }
   }
@@ -1117,13 +1152,17 @@ __device__ void merge_splits(const SelectArgs& a, size_t t) {
   for (int s = 0; s < kMaxSplits; ++s) {
     if (s < a.S) {
       const size_t ri = s * nrows + base;
-      const f32x4_t os = reinterpret_cast<const f32x4_t*>(a.opart)[opart_group(ri, D) + (size_t)c * 32 + (ri & 31)];
+      typedef typename PartialOut<E>::V PV;
+      const f32x4_t os = PartialOut<E>::unpack(
+          reinterpret_cast<const PV*>(a.opart)[opart_group(ri, D) + (size_t)c * 32 + (ri & 31)]);
       const double ls = a.lpart[ri];
       const bool live = ms[s] != -INFINITY;
+      const int es = sizeof(T) == 2 ? (int)a.epart[ri] : 0;
       const float w = live ? ldexpf(1.f, (int)(ms[s] - m)) : 0.f;
+      const float wo = live ? ldexpf(1.f, (int)(ms[s] - m) + es) : 0.f;
       l += live ? w * (float)ls : 0.f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = live ? fmaf(w, os[e], acc[e]) : acc[e];
+      for (int e = 0; e < 4; ++e) acc[e] = live ? fmaf(wo, os[e], acc[e]) : acc[e];
     }
   }
   const float inv = 1.f / l;

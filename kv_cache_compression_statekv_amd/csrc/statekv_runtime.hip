@@ -57,7 +57,8 @@ struct statekv_state {
   void* dk;
   void* dv;
   void* qrot;
-  float* opart;
+  void* opart;
+  int8_t* epart;
   float* mpart;
   double* lpart;
   float2* rope_tab;
@@ -115,7 +116,7 @@ int alloc(P** p, size_t bytes) {
 }
 
 void release(statekv_state* s) {
-  void* bufs[] = {s->kpool, s->vpool, s->ppos, s->dk, s->dv, s->qrot, s->opart, s->mpart,
+  void* bufs[] = {s->kpool, s->vpool, s->ppos, s->dk, s->dv, s->qrot, s->opart, s->epart, s->mpart,
                   s->lpart, s->rope_tab, s->colsum, s->scores, s->score_pos, s->keep_flag,
                   s->move_dst, s->move_src, s->move_count, s->evicted_pos, s->inv_freq,
                   s->nonfinite};
@@ -321,7 +322,8 @@ int statekv_create(const statekv_layer_cfg* cfg, int32_t budget_B, float alpha,
   if (!rc) rc = alloc(&s->dk, det_bytes);
   if (!rc) rc = alloc(&s->dv, det_bytes);
   if (!rc) rc = alloc(&s->qrot, rows_all * D * E);
-  if (!rc) rc = alloc(&s->opart, (S * rows_all + 31) / 32 * 32 * D * sizeof(float));  // whole 32-row groups
+  if (!rc) rc = alloc(&s->opart, (S * rows_all + 31) / 32 * 32 * D * E);  // whole 32-row groups
+  if (!rc) rc = alloc(&s->epart, S * rows_all * sizeof(int8_t));
   if (!rc) rc = alloc(&s->mpart, S * rows_all * sizeof(float));
   if (!rc) rc = alloc(&s->lpart, S * rows_all * sizeof(double));
   if (!rc) rc = alloc(&s->rope_tab, (size_t)positions * (D / 2) * sizeof(float2));
@@ -443,6 +445,7 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const 
     a.kpool = s->kpool;
     a.vpool = s->vpool;
     a.opart = s->opart;
+    a.epart = s->epart;
     a.mpart = s->mpart;
     a.lpart = s->lpart;
     a.c_hi = s->c_hi;
@@ -500,6 +503,7 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const 
     a.mode = evict ? kSelEvict : (scored ? kSelScores : kSelMerge);
     a.score_scale = 1.0 / ((double)(1ull << kScoreFracBits) * (double)s->Hq * (double)s->T);
     a.opart = s->opart;
+    a.epart = s->epart;
     a.mpart = s->mpart;
     a.lpart = s->lpart;
     a.out = O;
