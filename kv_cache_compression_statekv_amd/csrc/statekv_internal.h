@@ -77,8 +77,9 @@ struct AttnArgs {
   void* opart;            // [S][Hkv][R][d] unnormalised partial outputs, lane-order groups
                           // of 32 rows: fp16 scaled by 2^-e_s for bf16 streams, else fp32
   int8_t* epart;          // [S][Hkv][R] e_s of the fp16 partials
-  float* mpart;           // [S][Hkv][R] reference maxima (integers, -inf if empty)
-  double* lpart;          // [S][Hkv][R] partial row sums of 2^(x*c - m_s)
+  float* mpart;           // reference maxima (integers, -inf if empty) and partial row
+  double* lpart;          // sums of 2^(x*c - m_s), per (row, split): split-major inside
+                          // groups of 32 rows
   float c_hi;             // sigma * log2(e) rounded to fp32
   int32_t R, G, cap, P, k0, foff, kps, Hkv;
 };

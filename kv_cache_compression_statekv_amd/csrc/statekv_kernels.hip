@@ -194,6 +194,36 @@ template <> struct PartialOut<F32> {
 // buffer holds whole groups.
 __host__ __device__ inline size_t opart_group(size_t ri, int D) { return (ri >> 5) * (size_t)(D / 4) * 32; }
 
+// Split statistics of pass 1 are stored split-major inside groups of 32 rows
+// (row = g*R + r): a wave's store is 32 consecutive values, and the
+// statistics of one row are 32 elements apart.
+__host__ __device__ inline size_t stat_index(size_t row, int split) {
+  return ((row >> 5) * kMaxSplits + split) * 32 + (row & 31);
+}
+__device__ __forceinline__ void load_split_stats(const float* mpart, const double* lpart, size_t row, int S,
+                                                 float (&ms)[kMaxSplits], double (&ls)[kMaxSplits]) {
+  const float* mrow = mpart + stat_index(row, 0);
+  const double* lrow = lpart + stat_index(row, 0);
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplits; ++sp) {
+    ms[sp] = sp < S ? mrow[sp * 32] : -INFINITY;
+    ls[sp] = sp < S ? lrow[sp * 32] : 0.0;
+  }
+}
+
+// m = max_s m_s, l = sum_s 2^(m_s - m) l_s: exact powers of two, fp64 sum in
+// split order; splits that saw no key of the row (m_s = -inf) are skipped.
+__device__ __forceinline__ void merge_split_stats(const float (&ms)[kMaxSplits], const double (&ls)[kMaxSplits],
+                                                  float& m, double& l) {
+  m = -INFINITY;
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplits; ++sp) m = fmaxf(m, ms[sp]);
+  l = 0.0;
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplits; ++sp)
+    if (ms[sp] != -INFINITY) l += ldexp(ls[sp], (int)(ms[sp] - m));
+}
+
 // One 16-byte chunk of a move: task t = (move i, KV head g, chunk c); K and V.
 // The move list holds slots below B and rows in [B, cap); clamping only
 // guards the copy against a malformed list.
@@ -623,8 +653,9 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fwd_kernel(AttnArgs a) {
     if (r < a.R) {
       const size_t ri = ((size_t)split * a.Hkv + g) * a.R + r;
       if (hh == 0) {
-        a.mpart[ri] = m_run[qt];
-        a.lpart[ri] = lt;
+        const size_t si = stat_index((size_t)g * a.R + r, split);
+        a.mpart[si] = m_run[qt];
+        a.lpart[si] = lt;
       }
       if (m_run[qt] != -INFINITY) {
         int e = 0;
@@ -692,9 +723,6 @@ __global__ __launch_bounds__(256, 1) void attn_score_kernel(ScoreArgs a) {
 
   const T* qbase = (const T*)a.qrot + (size_t)g * a.R * D;
   const T* kbase = (const T*)a.kpool + (size_t)g * a.cap * D;
-  const size_t sstride = (size_t)a.Hkv * a.R;   // split stride of the pass-1 partials
-  const float* mbase = a.mpart + (size_t)g * a.R;
-  const double* lbase = a.lpart + (size_t)g * a.R;
 
   typename M::Frag kf[KT][NKS];
 #pragma unroll
@@ -727,17 +755,9 @@ __global__ __launch_bounds__(256, 1) void attn_score_kernel(ScoreArgs a) {
     if (r < r1) {
       float ms[kMaxSplits];
       double ls[kMaxSplits];
-      m = -INFINITY;
-#pragma unroll
-      for (int sp = 0; sp < kMaxSplits; ++sp) {
-        ms[sp] = sp < a.S ? mbase[sp * sstride + r] : -INFINITY;
-        ls[sp] = sp < a.S ? lbase[sp * sstride + r] : 0.0;
-        m = fmaxf(m, ms[sp]);
-      }
-      double l = 0.0;
-#pragma unroll
-      for (int sp = 0; sp < kMaxSplits; ++sp)
-        if (ms[sp] != -INFINITY) l += ldexp(ls[sp], (int)(ms[sp] - m));
+      load_split_stats(a.mpart, a.lpart, (size_t)g * a.R + r, a.S, ms, ls);
+      double l;
+      merge_split_stats(ms, ls, m, l);
       rinv = (float)(1.0 / l);
       lim = a.k0 + r / a.G + 1;   // keys below this are visible to row r
     }
@@ -966,8 +986,7 @@ __device__ int refine_boundary(SelectShared& sh, int P, uint32_t& lo, uint32_t& 
   return cnt;
 }
 
-__device__ void select_top_b(const SelectArgs& a) {
-  __shared__ SelectShared sh;
+__device__ void select_top_b(const SelectArgs& a, SelectShared& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // Row j*kSelectThreads + tid of the pool belongs to thread tid, so that every
   // global access of a wave is contiguous.  No global store precedes a
@@ -1125,47 +1144,62 @@ __device__ void select_top_b(const SelectArgs& a) {
 
 // Merge of the key splits of pass 1:
 //   m = max_s m_s,  l = sum_s 2^(m_s - m) l_s,  O = sum_s 2^(m_s - m) O_s / l,
-// one thread per (row, 4 dims), written to O [T][Hq][d].  Threads take rows
-// fastest inside groups of 32, matching the lane-order layout of the
-// partials.  The factors are exact powers of two (the m_s are integers).
-// Partials of splits that saw no key of a row were never written, so they
-// are selected out, not multiplied.
+// one thread per (row, 4 dims), written to O [T][Hq][d].  A work-group covers
+// whole groups of 32 rows with rows fastest, matching the lane-order layout
+// of the partials; one thread per row merges the row's split statistics into
+// LDS (weights 2^(m_s - m), exact powers of two, and 1/l), which the row's
+// other threads read.  Partials of splits that saw no key of a row were never
+// written, so they are selected out, not multiplied.
 template <class E, int D>
-__device__ void merge_splits(const SelectArgs& a, size_t t) {
+__device__ void merge_splits(const SelectArgs& a, int wg, float* lds) {
   typedef typename E::T T;
   constexpr int CPR = D / 4;
+  constexpr int GPW = kSelectThreads / (32 * CPR);   // row groups per work-group
+  static_assert(GPW >= 1 && GPW * 32 * CPR == kSelectThreads, "merge work-group shape");
+  float* wts = lds;                                   // [GPW*32][kMaxSplits]
+  float* rinv = lds + GPW * 32 * kMaxSplits;          // [GPW*32]
+  const int tid = threadIdx.x;
   const size_t nrows = (size_t)a.Hkv * a.R;
-  const size_t grp = (t >> 5) / CPR;
-  const int c = (int)((t >> 5) - grp * CPR);
-  const size_t base = grp * 32 + (t & 31);   // = g*R + r
-  if (base >= nrows) return;
-  float ms[kMaxSplits];
-  float m = -INFINITY;
+  const int gsub = (tid >> 5) / CPR;
+  const int c = (tid >> 5) - gsub * CPR;
+  const int lrow = gsub * 32 + (tid & 31);
+  const size_t base = ((size_t)wg * GPW + gsub) * 32 + (tid & 31);   // = g*R + r
+  if (c == 0) {
+    float w[kMaxSplits];
+    float inv = 0.f;
 #pragma unroll
-  for (int s = 0; s < kMaxSplits; ++s) {
-    ms[s] = s < a.S ? a.mpart[s * nrows + base] : -INFINITY;
-    m = fmaxf(m, ms[s]);
+    for (int sp = 0; sp < kMaxSplits; ++sp) w[sp] = 0.f;
+    if (base < nrows) {
+      float ms[kMaxSplits];
+      double ls[kMaxSplits];
+      load_split_stats(a.mpart, a.lpart, base, a.S, ms, ls);
+      float m;
+      double l;
+      merge_split_stats(ms, ls, m, l);
+#pragma unroll
+      for (int sp = 0; sp < kMaxSplits; ++sp) w[sp] = ms[sp] != -INFINITY ? ldexpf(1.f, (int)(ms[sp] - m)) : 0.f;
+      inv = (float)(1.0 / l);
+    }
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplits; ++sp) wts[lrow * kMaxSplits + sp] = w[sp];
+    rinv[lrow] = inv;
   }
-  float l = 0.f;
+  __syncthreads();
+  if (base >= nrows) return;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int s = 0; s < kMaxSplits; ++s) {
-    if (s < a.S) {
+  for (int s = 0; s < a.S; ++s) {
+    const float w = wts[lrow * kMaxSplits + s];
+    if (w != 0.f) {
       const size_t ri = s * nrows + base;
       typedef typename PartialOut<E>::V PV;
       const f32x4_t os = PartialOut<E>::unpack(
           reinterpret_cast<const PV*>(a.opart)[opart_group(ri, D) + (size_t)c * 32 + (ri & 31)]);
-      const double ls = a.lpart[ri];
-      const bool live = ms[s] != -INFINITY;
-      const int es = sizeof(T) == 2 ? (int)a.epart[ri] : 0;
-      const float w = live ? ldexpf(1.f, (int)(ms[s] - m)) : 0.f;
-      const float wo = live ? ldexpf(1.f, (int)(ms[s] - m) + es) : 0.f;
-      l += live ? w * (float)ls : 0.f;
+      const float wo = sizeof(T) == 2 ? ldexpf(w, (int)a.epart[ri]) : w;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = live ? fmaf(wo, os[e], acc[e]) : acc[e];
+      for (int e = 0; e < 4; ++e) acc[e] = fmaf(wo, os[e], acc[e]);
     }
   }
-  const float inv = 1.f / l;
+  const float inv = rinv[lrow];
   const int g = (int)(base / a.R), r = (int)(base - (size_t)g * a.R);
   const int tok = r / a.G;
   const int h = g * a.G + (r - tok * a.G);
@@ -1181,11 +1215,12 @@ __device__ void merge_splits(const SelectArgs& a, size_t t) {
 
 template <class E, int D>
 __global__ __launch_bounds__(kSelectThreads, 1) void select_kernel(SelectArgs a) {
+  __shared__ SelectShared sh;   // the selection's state, or the merge's statistics
   if (blockIdx.x > 0) {
-    merge_splits<E, D>(a, (size_t)(blockIdx.x - 1) * kSelectThreads + threadIdx.x);
+    merge_splits<E, D>(a, blockIdx.x - 1, reinterpret_cast<float*>(sh.val));
     return;
   }
-  if (a.mode != kSelMerge) select_top_b(a);
+  if (a.mode != kSelMerge) select_top_b(a, sh);
 }
 
 // Moves of a selection outside a frame step (before a view), 16 bytes per

@@ -324,8 +324,9 @@ int statekv_create(const statekv_layer_cfg* cfg, int32_t budget_B, float alpha,
   if (!rc) rc = alloc(&s->qrot, rows_all * D * E);
   if (!rc) rc = alloc(&s->opart, (S * rows_all + 31) / 32 * 32 * D * E);  // whole 32-row groups
   if (!rc) rc = alloc(&s->epart, S * rows_all * sizeof(int8_t));
-  if (!rc) rc = alloc(&s->mpart, S * rows_all * sizeof(float));
-  if (!rc) rc = alloc(&s->lpart, S * rows_all * sizeof(double));
+  const size_t stat_rows = (rows_all + 31) / 32 * 32;   // whole groups of 32 rows
+  if (!rc) rc = alloc(&s->mpart, stat_rows * kMaxSplits * sizeof(float));
+  if (!rc) rc = alloc(&s->lpart, stat_rows * kMaxSplits * sizeof(double));
   if (!rc) rc = alloc(&s->rope_tab, (size_t)positions * (D / 2) * sizeof(float2));
   if (!rc) rc = alloc(&s->colsum, (size_t)s->cap * sizeof(unsigned long long));
   if (!rc) rc = alloc(&s->scores, (size_t)s->cap * sizeof(float));
