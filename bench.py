@@ -45,6 +45,10 @@ def parse_args():
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="bounded CPU work for the oracle baseline (0 disables it)")
     p.add_argument("--no-kernel-timing", action="store_true")
+    p.add_argument("--quadratic", action="store_true",
+                   help="also run the quadratic comparison over the workload's full stream: "
+                        "one-shot full causal attention over all N*T tokens, full attention "
+                        "streamed frame by frame (no eviction), and StateKV streamed")
     p.add_argument("--copy-calibration-mb", type=int, default=0,
                    help="first run one device-to-device copy of this many MiB (a kernel of known "
                         "traffic that rocprofv3 counters are scaled by)")
@@ -113,6 +117,74 @@ def summarize_pmc(fetch_csv: str, write_csv: str, workload: str, copy_mb: int) -
     with open(path, "w") as fh:
         json.dump(rec, fh, indent=1)
     return rec
+
+
+def quadratic_comparison(skv, torch, np, wl):
+    """Full causal attention vs StateKV over the same N*T tokens (one layer)."""
+    from kv_cache_compression_statekv_amd.workload import stream_tokens
+
+    N, T = wl.n_frames, wl.tokens_per_frame
+    Hq, Hkv, d = wl.n_q_heads, wl.n_kv_heads, wl.head_dim
+    L = N * T
+    tdtype = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    Q, K, V = (torch.from_numpy(x).to(tdtype).cuda() for x in stream_tokens(wl, N))
+    common = dict(n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, alpha=wl.alpha, dtype=wl.dtype,
+                  rope_base=wl.rope_base, rope_orig_ctx=wl.rope_orig_ctx)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    # (i) one-shot: one frame of all L tokens in a state that never evicts.
+    one_ms = []
+    out = torch.empty((L, Hq, d), dtype=tdtype, device="cuda")
+    for rep_i in range(3):
+        st = skv.StateKV(tokens_per_frame=L, max_frames=1, budget=L, **common)
+        ms = timed(lambda: st.prefill_frame(Q, K, V, 0, out=out))
+        st.close()
+        if rep_i:
+            one_ms.append(ms)
+    causal_pairs = L * (L + 1) / 2
+    one_flops = 4.0 * Hq * d * causal_pairs
+
+    def streamed(budget):
+        st = skv.StateKV(tokens_per_frame=T, max_frames=N, budget=budget, **common)
+        o = torch.empty((T, Hq, d), dtype=tdtype, device="cuda")
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(N + 1)]
+        evs[0].record(stream)
+        for n in range(N):
+            sl = slice(n * T, (n + 1) * T)
+            st.prefill_frame(Q[sl], K[sl], V[sl], n, out=o)
+            evs[n + 1].record(stream)
+        torch.cuda.synchronize()
+        lat = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(N)]) * 1e3
+        st.close()
+        idx = np.arange(N)
+        return {"total_ms": round(float(lat.sum()) / 1e3, 3),
+                "frame_us_first": round(float(lat[0]), 2),
+                "frame_us_median": round(float(np.median(lat)), 2),
+                "frame_us_last": round(float(lat[-1]), 2),
+                "slope_us_per_frame": round(float(np.polyfit(idx, lat, 1)[0]), 4)}
+
+    full_stream = streamed(L)
+    statekv = streamed(wl.budget)
+    one = float(np.median(one_ms))
+    return {
+        "tokens": L, "frames": N, "budget": wl.budget,
+        "full_causal_one_shot_ms": round(one, 3),
+        "full_causal_algorithmic_tflop": round(one_flops / 1e12, 2),
+        "full_causal_tflops": round(one_flops / (one * 1e-3) / 1e12, 1),
+        "full_causal_mfma_frac": round(one_flops / (one * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "full_attention_streamed": full_stream,
+        "statekv_streamed": statekv,
+        "statekv_over_one_shot_time": round(statekv["total_ms"] / one, 4),
+        "statekv_over_full_streamed_time": round(statekv["total_ms"] / full_stream["total_ms"], 4),
+    }
 
 
 def main():
@@ -233,6 +305,8 @@ def main():
             "last_over_first_median": round(float(np.median(lat_a[-q:]) / np.median(lat_a[:q])), 4),
         }
 
+    quadratic = quadratic_comparison(skv, torch, np, wl) if args.quadratic else None
+
     # CPU baseline: the oracle, started from the GPU's state, on the next frames.
     cpu = None
     if args.cpu_seconds > 0:
@@ -287,6 +361,7 @@ def main():
         "cpu_baseline": cpu,
         "kernels": kernels,
         **extra,
+        **({"quadratic": quadratic} if quadratic else {}),
         "attn_fwd_algorithmic_gflop": round(attn_flops / 1e9, 4),
         "executed_gflop_attention_passes": round(executed_flops / 1e9, 4),
     }

@@ -104,7 +104,9 @@ typedef struct statekv_scores_view {
  * detailed cache for cfg->max_frames * T tokens, and all scratch buffers, on
  * the current HIP device.  Everything is allocated here; later calls do not
  * allocate.  alpha >= 1 is the global RoPE scaling factor (关键设计 3), fixed
- * for the life of the state.  Requires B >= 1 and B + T <= 32768.
+ * for the life of the state.  Requires B >= 1 and B + T <= 32768, except
+ * when B >= max_frames * T: such a state never evicts (full causal attention
+ * over the stream, the quadratic baseline) and may hold any number of tokens.
  * On success *out receives the state; the caller releases it with
  * statekv_destroy.  Errors: EINVAL, ENOMEM, EDEVICE.
  */
@@ -123,7 +125,9 @@ int statekv_set_stream(statekv_state* s, void* hip_stream);
  * frame], appends the rotated K and V to the detailed cache, scores the pool
  * and keeps min(B, pool) candidates as the next compressed state.
  * n must equal the number of frames already processed (EORDER otherwise);
- * ECAPACITY once max_frames frames are done.  Asynchronous: O and the views
+ * ECAPACITY once max_frames frames are done; EINVAL for a frame that would
+ * score a pool of more than 32768 candidates (possible only with
+ * STATEKV_FLAG_ALWAYS_SCORE on a state that never evicts).  Asynchronous: O and the views
  * are valid after the stream reaches this point.  A NaN or Inf in Q, K or V is
  * detected on the device and reported by the next view call (ENONFINITE).
  */
@@ -132,7 +136,8 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K,
 
 /*
  * Compressed state C after the last frame: k, v are [Hkv][count][d] with
- * head_stride = (B+T)*d and token_stride = d; pos[count] gives each slot's
+ * head_stride (elements between KV heads: the row capacity times d) and
+ * token_stride = d; pos[count] gives each slot's
  * stream position (slot order; sort by position for a sequence view).
  * Synchronises the state's stream.  Valid until the next prefill_frame or
  * destroy.  Returns ENONFINITE if an input frame held NaN or Inf.

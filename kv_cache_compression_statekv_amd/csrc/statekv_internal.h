@@ -82,6 +82,7 @@ struct AttnArgs {
                           // groups of 32 rows
   float c_hi;             // sigma * log2(e) rounded to fp32
   int32_t R, G, cap, P, k0, foff, kps, Hkv;
+  int32_t ss;             // split stride of the statistics (maximum splits)
 };
 
 // Score pass: one work-group per (key block, KV head, row split).
@@ -92,7 +93,7 @@ struct ScoreArgs {
   const double* lpart;
   unsigned long long* colsum;  // [cap] column sums, fixed point (2^-kScoreFracBits units)
   float c_hi, c_lo;            // sigma * log2(e) = c_hi + c_lo
-  int32_t R, G, cap, P, k0, foff, rps, Hkv, S;
+  int32_t R, G, cap, P, k0, foff, rps, Hkv, S, ss;
 };
 
 // Work-group 0: scores and the Top-B decision; work-groups 1..: the merge of
@@ -113,7 +114,7 @@ struct SelectArgs {
   const float* mpart;
   const double* lpart;
   void* out;                   // [T][Hq][d]
-  int32_t Hkv, R, G, Hq, S;
+  int32_t Hkv, R, G, Hq, S, ss;
 };
 constexpr int kSelMerge = 0;   // merge only (the pool fits in B and is not scored)
 constexpr int kSelScores = 1;  // scores, everything kept

@@ -197,13 +197,14 @@ __host__ __device__ inline size_t opart_group(size_t ri, int D) { return (ri >> 
 // Split statistics of pass 1 are stored split-major inside groups of 32 rows
 // (row = g*R + r): a wave's store is 32 consecutive values, and the
 // statistics of one row are 32 elements apart.
-__host__ __device__ inline size_t stat_index(size_t row, int split) {
-  return ((row >> 5) * kMaxSplits + split) * 32 + (row & 31);
+// ss = splits per group (the maximum number of splits).
+__host__ __device__ inline size_t stat_index(size_t row, int split, int ss) {
+  return ((row >> 5) * ss + split) * 32 + (row & 31);
 }
 __device__ __forceinline__ void load_split_stats(const float* mpart, const double* lpart, size_t row, int S,
-                                                 float (&ms)[kMaxSplits], double (&ls)[kMaxSplits]) {
-  const float* mrow = mpart + stat_index(row, 0);
-  const double* lrow = lpart + stat_index(row, 0);
+                                                 int ss, float (&ms)[kMaxSplits], double (&ls)[kMaxSplits]) {
+  const float* mrow = mpart + stat_index(row, 0, ss);
+  const double* lrow = lpart + stat_index(row, 0, ss);
 #pragma unroll
   for (int sp = 0; sp < kMaxSplits; ++sp) {
     ms[sp] = sp < S ? mrow[sp * 32] : -INFINITY;
@@ -534,7 +535,8 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fwd_kernel(AttnArgs a) {
   const int lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, hh = lane >> 5;
   const int g = blockIdx.y, split = blockIdx.z;
-  const int row_wg = blockIdx.x * BM;
+  // Heaviest row tiles first (later tokens see more keys).
+  const int row_wg = (gridDim.x - 1 - blockIdx.x) * BM;
   const int row_last = min(a.R, row_wg + BM) - 1;
   const int tok_min = row_wg / a.G;
   const int need_end = a.k0 + row_last / a.G + 1;  // keys beyond are masked for every row
@@ -653,7 +655,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fwd_kernel(AttnArgs a) {
     if (r < a.R) {
       const size_t ri = ((size_t)split * a.Hkv + g) * a.R + r;
       if (hh == 0) {
-        const size_t si = stat_index((size_t)g * a.R + r, split);
+        const size_t si = stat_index((size_t)g * a.R + r, split, a.ss);
         a.mpart[si] = m_run[qt];
         a.lpart[si] = lt;
       }
@@ -755,7 +757,7 @@ __global__ __launch_bounds__(256, 1) void attn_score_kernel(ScoreArgs a) {
     if (r < r1) {
       float ms[kMaxSplits];
       double ls[kMaxSplits];
-      load_split_stats(a.mpart, a.lpart, (size_t)g * a.R + r, a.S, ms, ls);
+      load_split_stats(a.mpart, a.lpart, (size_t)g * a.R + r, a.S, a.ss, ms, ls);
       double l;
       merge_split_stats(ms, ls, m, l);
       rinv = (float)(1.0 / l);
@@ -1172,7 +1174,7 @@ __device__ void merge_splits(const SelectArgs& a, int wg, float* lds) {
     if (base < nrows) {
       float ms[kMaxSplits];
       double ls[kMaxSplits];
-      load_split_stats(a.mpart, a.lpart, base, a.S, ms, ls);
+      load_split_stats(a.mpart, a.lpart, base, a.S, a.ss, ms, ls);
       float m;
       double l;
       merge_split_stats(ms, ls, m, l);

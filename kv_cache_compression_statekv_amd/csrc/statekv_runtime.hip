@@ -49,6 +49,7 @@ struct statekv_state {
 
   // launch geometry
   int attn_tiles, attn_splits_max;
+  bool never_evicts;
   int score_rsplits_max;
 
   void* kpool;
@@ -268,9 +269,14 @@ int statekv_create(const statekv_layer_cfg* cfg, int32_t budget_B, float alpha,
   if (c.dtype != STATEKV_DTYPE_BF16 && c.dtype != STATEKV_DTYPE_F32) return STATEKV_EINVAL;
   if (!(c.rope_base > 1.0) || !isfinite(c.rope_base) || c.rope_orig_ctx < 1) return STATEKV_EINVAL;
   if (!(alpha >= 1.0f) || !isfinite(alpha)) return STATEKV_EINVAL;
-  if (budget_B < 1 || (int64_t)budget_B + c.tokens_per_frame > kMaxPool) return STATEKV_EINVAL;
   const int64_t positions = (int64_t)c.max_frames * c.tokens_per_frame;
   if (positions > INT32_MAX) return STATEKV_EINVAL;
+  // The selection runs in one work-group over at most kMaxPool candidates; a
+  // budget that holds every token of the stream never selects (full
+  // attention) and has no such limit.
+  const bool never_evicts = budget_B >= positions;
+  if (budget_B < 1 || (!never_evicts && (int64_t)budget_B + c.tokens_per_frame > kMaxPool))
+    return STATEKV_EINVAL;
   const int64_t rows = (int64_t)c.n_q_heads * c.tokens_per_frame;
   if (rows > kMaxRowsTimesHeads) return STATEKV_EINVAL;
 
@@ -287,7 +293,10 @@ int statekv_create(const statekv_layer_cfg* cfg, int32_t budget_B, float alpha,
   s->T = c.tokens_per_frame;
   s->G = s->Hq / s->Hkv;
   s->R = s->G * s->T;
-  s->cap = budget_B + 2 * s->T;
+  // Rows: the state, then two frame regions (frames alternate once they
+  // evict); a stream that never evicts needs one row per token.
+  s->never_evicts = budget_B >= (int64_t)c.max_frames * c.tokens_per_frame;
+  s->cap = s->never_evicts ? c.max_frames * c.tokens_per_frame : budget_B + 2 * s->T;
   s->stream = nullptr;
   s->score_frame = -1;
 
@@ -298,7 +307,8 @@ int statekv_create(const statekv_layer_cfg* cfg, int32_t budget_B, float alpha,
   }
 
   s->attn_tiles = ceil_div(s->R, attn_rows_per_wg(s->dt, s->D));
-  s->attn_splits_max = std::min(kMaxSplits, std::max(1, ceil_div(s->cap, 4 * kAttnBN)));
+  s->attn_splits_max = std::min(std::min(kMaxSplits, ceil_div(kTargetWGs, s->attn_tiles * s->Hkv)),
+                                std::max(1, ceil_div(s->cap, 4 * kAttnBN)));
   s->score_rsplits_max = std::max(ceil_div(s->R, kScoreMaxRows), ceil_div(s->R, 128));
   // Tuning overrides (launch geometry only; the result does not depend on them).
   if (const char* e = getenv("STATEKV_ATTN_SPLITS")) {
@@ -325,8 +335,8 @@ int statekv_create(const statekv_layer_cfg* cfg, int32_t budget_B, float alpha,
   if (!rc) rc = alloc(&s->opart, (S * rows_all + 31) / 32 * 32 * D * E);  // whole 32-row groups
   if (!rc) rc = alloc(&s->epart, S * rows_all * sizeof(int8_t));
   const size_t stat_rows = (rows_all + 31) / 32 * 32;   // whole groups of 32 rows
-  if (!rc) rc = alloc(&s->mpart, stat_rows * kMaxSplits * sizeof(float));
-  if (!rc) rc = alloc(&s->lpart, stat_rows * kMaxSplits * sizeof(double));
+  if (!rc) rc = alloc(&s->mpart, stat_rows * S * sizeof(float));
+  if (!rc) rc = alloc(&s->lpart, stat_rows * S * sizeof(double));
   if (!rc) rc = alloc(&s->rope_tab, (size_t)positions * (D / 2) * sizeof(float2));
   if (!rc) rc = alloc(&s->colsum, (size_t)s->cap * sizeof(unsigned long long));
   if (!rc) rc = alloc(&s->scores, (size_t)s->cap * sizeof(float));
@@ -405,6 +415,7 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const 
   const hipStream_t st = s->stream;
   const bool evict = P > s->B;
   const bool scored = evict || (s->flags & STATEKV_FLAG_ALWAYS_SCORE);
+  if (scored && P > kMaxPool) return STATEKV_EINVAL;   // beyond the selection's pool limit
   // Rows of this frame: right after the state, or, while the previous
   // frame's moves are pending, the region its rows do not occupy.
   const int F = s->moves_pending ? (s->frame_base == (int)s->B + s->T ? (int)s->B : (int)s->B + s->T) : k0;
@@ -457,6 +468,7 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const 
     a.k0 = k0;
     a.foff = foff;
     a.kps = kps;
+    a.ss = s->attn_splits_max;
     a.Hkv = s->Hkv;
     rc = check(launch_attn(s->dt, s->D, a, s->attn_tiles, splits, st));
     tm.done();
@@ -472,6 +484,7 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const 
     a.mpart = s->mpart;
     a.lpart = s->lpart;
     a.S = splits;
+    a.ss = s->attn_splits_max;
     a.colsum = s->colsum;
     a.c_hi = s->c_hi;
     a.c_lo = s->c_lo;
@@ -513,6 +526,7 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const 
     a.G = s->G;
     a.Hq = s->Hq;
     a.S = splits;
+    a.ss = s->attn_splits_max;
     rc = check(launch_select(s->dt, s->D, a, st));
     tm.done();
     if (rc) return rc;

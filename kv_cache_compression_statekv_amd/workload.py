@@ -175,6 +175,21 @@ class FrameStream:
         return q, k, v
 
 
+def stream_tokens(cfg: StreamConfig, n_frames: int, layer: int = 0):
+    """Q, K, V of frames 0 .. n_frames-1 of one layer's stream, concatenated
+    along tokens: [n_frames*T][H][d] fp32 arrays holding storage values.  The
+    input of one-shot full causal attention over the same tokens."""
+    T, Hq, Hkv, d = cfg.tokens_per_frame, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    L = n_frames * T
+    Q = np.empty((L, Hq, d), dtype=np.float32)
+    K = np.empty((L, Hkv, d), dtype=np.float32)
+    V = np.empty((L, Hkv, d), dtype=np.float32)
+    fs = FrameStream(cfg, layer)
+    for n in range(n_frames):
+        Q[n * T:(n + 1) * T], K[n * T:(n + 1) * T], V[n * T:(n + 1) * T] = fs.frame(n)
+    return Q, K, V
+
+
 def to_storage_bytes(x: np.ndarray, dtype: str) -> np.ndarray:
     """Raw storage of a frame tensor: uint16 bf16 bits or fp32."""
     if dtype == "bf16":

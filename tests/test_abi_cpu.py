@@ -43,13 +43,28 @@ def test_create_rejects_bad_config(bad):
     assert not h.value
 
 
-@pytest.mark.parametrize("budget,alpha", [(0, 1.0), (-5, 1.0), (32768, 1.0), (64, 0.5),
-                                          (64, math.nan), (64, math.inf)])
-def test_create_rejects_bad_budget_or_alpha(budget, alpha):
+@pytest.mark.parametrize("budget,alpha,frames", [(0, 1.0, 4), (-5, 1.0, 4), (64, 0.5, 4),
+                                                 (64, math.nan, 4), (64, math.inf, 4),
+                                                 # evicting stream whose pool exceeds 32768
+                                                 (32768, 1.0, 4096)])
+def test_create_rejects_bad_budget_or_alpha(budget, alpha, frames):
     lib = skv.load_library()
     h = ctypes.c_void_p()
-    cfg = _cfg()
+    cfg = _cfg(max_frames=frames)
     assert lib.statekv_create(ctypes.byref(cfg), budget, alpha, ctypes.byref(h)) == skv.STATEKV_EINVAL
+
+
+def test_create_accepts_full_attention_budget_beyond_pool_limit():
+    """A budget that holds every token never selects, so the 32768-candidate
+    limit of the selection does not apply (here: no GPU, so creation stops at
+    the device, after validation)."""
+    lib = skv.load_library()
+    h = ctypes.c_void_p()
+    cfg = _cfg(max_frames=4096)      # 65536 tokens
+    rc = lib.statekv_create(ctypes.byref(cfg), 65536, 1.0, ctypes.byref(h))
+    assert rc != skv.STATEKV_EINVAL
+    if rc == skv.STATEKV_OK:
+        lib.statekv_destroy(h)
 
 
 def test_null_arguments_are_rejected():
