@@ -587,25 +587,30 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fwd_kernel(AttnArgs a) {
     const T* ks_ = Ks[buf];
     const T* vt_ = Vt[buf];
 
-    // Two sub-tiles of 32 keys: S^T = K Q^T, softmax, O^T += V^T P^T.
+    // Two sub-tiles of 32 keys: S^T = K Q^T, softmax, O^T += V^T P^T.  Both
+    // sub-tiles' QK^T are issued first, so that the softmax of one overlaps
+    // the matrix work of the other (the MFMA pipe runs beside the VALU).
+    f32x16_t sacc[2][QT];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) sacc[sub][qt] = f32x16_t{};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        const typename M::Frag af = M::ld(&ks_[(sub * 32 + col) * KSTR + ks * M::KS + hh * M::KL]);
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) sacc[sub][qt] = M::mma(af, qf[qt][ks], sacc[sub][qt]);
+      }
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       const int ksub = kb + sub * 32;
-      f32x16_t sacc[QT];
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) sacc[qt] = f32x16_t{};
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const typename M::Frag af = M::ld(&ks_[(sub * 32 + col) * KSTR + ks * M::KS + hh * M::KL]);
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) sacc[qt] = M::mma(af, qf[qt][ks], sacc[qt]);
-      }
-
       float alpha[QT];
       if (ksub + 32 > full_end)
-        online_softmax<QT, true>(sacc, m_run, l_run, alpha, lim, ksub, hh, a.c_hi);
+        online_softmax<QT, true>(sacc[sub], m_run, l_run, alpha, lim, ksub, hh, a.c_hi);
       else
-        online_softmax<QT, false>(sacc, m_run, l_run, alpha, lim, ksub, hh, a.c_hi);
+        online_softmax<QT, false>(sacc[sub], m_run, l_run, alpha, lim, ksub, hh, a.c_hi);
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt)
         if (__ballot(alpha[qt] != 1.f)) {
@@ -621,7 +626,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
           for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
-            for (int t = 0; t < 8; ++t) pf[qt][t] = (__bf16)sacc[qt][8 * mm + t];
+            for (int t = 0; t < 8; ++t) pf[qt][t] = (__bf16)sacc[sub][qt][8 * mm + t];
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt) {
             const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(
@@ -638,7 +643,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fwd_kernel(AttnArgs a) {
             const int kin = sub * 32 + 8 * (t >> 2) + 4 * hh + (t & 3);
             const float af = vt_[(dt * 32 + col) * VSTR + kin];
 #pragma unroll
-            for (int qt = 0; qt < QT; ++qt) o[qt][dt] = M::mma(af, sacc[qt][t], o[qt][dt]);
+            for (int qt = 0; qt < QT; ++qt) o[qt][dt] = M::mma(af, sacc[sub][qt][t], o[qt][dt]);
           }
       }
     }
@@ -797,43 +802,49 @@ __global__ __launch_bounds__(256, 1) void attn_score_kernel(ScoreArgs a) {
     const int buf = it & 1;
     const int ro = it * RT;   // tile offset inside the statistics arrays
     if (it + 1 < ntile) load_tile(rstart + (it + 1) * RT);
+    // S = Q K^T for the KT key tiles: Q fragments read once per k-slice and
+    // fed to KT independent accumulation chains.
+    f32x16_t acc[KT];
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) acc[kt] = f32x16_t{};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const typename M::Frag af = M::ld(&Qs[buf][col * QSTR + ks * M::KS + hh * M::KL]);
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) acc[kt] = M::mma(af, kf[kt][ks], acc[kt]);
+    }
+    // Statistics of the lane's 16 rows of this tile.
+    f32x4_t mv[4], rv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      mv[j] = *reinterpret_cast<const f32x4_t*>(&sm[ro + 8 * j + 4 * hh]);
+      rv[j] = *reinterpret_cast<const f32x4_t*>(&sr[ro + 8 * j + 4 * hh]);
+    }
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
       const int key_t0 = key_w + kt * 32;
-      if (key_t0 >= a.P) break;
-      f32x16_t acc = f32x16_t{};
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const typename M::Frag af = M::ld(&Qs[buf][col * QSTR + ks * M::KS + hh * M::KL]);
-        acc = M::mma(af, kf[kt][ks], acc);
-      }
       const int key = key_t0 + col;
       float sum = 0.f;
       if (key_t0 + 31 >= a.k0) {  // tile holds frame keys: causal visibility per row
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const f32x4_t mv = *reinterpret_cast<const f32x4_t*>(&sm[ro + 8 * j + 4 * hh]);
-          const f32x4_t rv = *reinterpret_cast<const f32x4_t*>(&sr[ro + 8 * j + 4 * hh]);
           const int4 lv = *reinterpret_cast<const int4*>(&slim[ro + 8 * j + 4 * hh]);
           const int lvv[4] = {lv.x, lv.y, lv.z, lv.w};
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const float x = acc[4 * j + q];
-            const float p = fast_exp2(fmaf(x, a.c_lo, fmaf(x, a.c_hi, -mv[q]))) * rv[q];
+            const float x = acc[kt][4 * j + q];
+            const float p = fast_exp2(fmaf(x, a.c_lo, fmaf(x, a.c_hi, -mv[j][q]))) * rv[j][q];
             sum += key < lvv[q] ? p : 0.f;
           }
         }
       } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const f32x4_t mv = *reinterpret_cast<const f32x4_t*>(&sm[ro + 8 * j + 4 * hh]);
-          const f32x4_t rv = *reinterpret_cast<const f32x4_t*>(&sr[ro + 8 * j + 4 * hh]);
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const float x = acc[4 * j + q];
-            sum += fast_exp2(fmaf(x, a.c_lo, fmaf(x, a.c_hi, -mv[q]))) * rv[q];
+            const float x = acc[kt][4 * j + q];
+            sum += fast_exp2(fmaf(x, a.c_lo, fmaf(x, a.c_hi, -mv[j][q]))) * rv[j][q];
           }
-        }
       }
       cs[kt] += (double)sum;
     }
