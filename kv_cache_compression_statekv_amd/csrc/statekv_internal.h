@@ -123,6 +123,7 @@ constexpr int kSelEvict = 2;   // scores and Top-B
 // Rows handled by one pass-1 work-group / keys by one score work-group.
 int attn_rows_per_wg(Dt dt, int d);
 int score_keys_per_wg(Dt dt);
+int score_waves_per_wg(Dt dt);
 // Work-groups of the RoPE part of the RoPE kernel for T tokens.
 int rope_blocks(int T);
 

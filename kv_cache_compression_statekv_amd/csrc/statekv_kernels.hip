@@ -693,7 +693,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fwd_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Score pass.  Work-group = 4 waves; each wave keeps KT tiles of 32 keys in
+// Score pass.  Work-group = NW waves; each wave keeps KT tiles of 32 keys in
 // registers (the B operand of S = Q K^T) and all waves stream the same
 // 32-row Q tiles through double-buffered LDS (the next tile is loaded while
 // the current one is computed).  The row statistics of the work-group's rows
@@ -705,17 +705,18 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fwd_kernel(AttnArgs a) {
 // key's fixed-point total.  Every sum has a fixed order (or is an integer
 // sum), so the scores are deterministic.
 // ---------------------------------------------------------------------------
-template <class E, int D, int KT>
-__global__ __launch_bounds__(256, 1) void attn_score_kernel(ScoreArgs a) {
+template <class E, int D, int KT, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void attn_score_kernel(ScoreArgs a) {
   typedef typename E::T T;
   typedef Mma<E> M;
   constexpr int RT = 32;
   constexpr int EPV = 16 / (int)sizeof(T);
   constexpr int QSTR = D + EPV;
   constexpr int NKS = D / M::KS;
-  constexpr int BNK = 4 * 32 * KT;
+  constexpr int NT = 64 * NW;
+  constexpr int BNK = NW * 32 * KT;
   constexpr int CPR = D / EPV;                       // 16-byte chunks per Q row
-  constexpr int QCH = (RT * CPR + kAttnThreads - 1) / kAttnThreads;
+  constexpr int QCH = (RT * CPR + NT - 1) / NT;
   __shared__ __attribute__((aligned(16))) T Qs[2][RT * QSTR];
   __shared__ __attribute__((aligned(16))) float sm[kScoreMaxRows];
   __shared__ __attribute__((aligned(16))) float sr[kScoreMaxRows];
@@ -755,7 +756,7 @@ __global__ __launch_bounds__(256, 1) void attn_score_kernel(ScoreArgs a) {
   // Row statistics of the work-group's rows (padded to whole tiles), from the
   // key-split partials of pass 1: m = max_s m_s, l = sum_s 2^(m_s - m) l_s
   // (exact powers of two, fp64 sum).  Padding rows get 1/l = 0.
-  for (int i = tid; i < ntile * RT; i += kAttnThreads) {
+  for (int i = tid; i < ntile * RT; i += NT) {
     const int r = rstart + i;
     float m = 0.f, rinv = 0.f;
     int lim = 0;
@@ -777,7 +778,7 @@ __global__ __launch_bounds__(256, 1) void attn_score_kernel(ScoreArgs a) {
   auto load_tile = [&](int rt) {
 #pragma unroll
     for (int j = 0; j < QCH; ++j) {
-      const int t = tid + j * kAttnThreads;
+      const int t = tid + j * NT;
       const int rr = t / CPR, cc = t - rr * CPR;
       const int r = rt + rr;
       qr[j] = u32x4_t{0u, 0u, 0u, 0u};
@@ -787,7 +788,7 @@ __global__ __launch_bounds__(256, 1) void attn_score_kernel(ScoreArgs a) {
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int j = 0; j < QCH; ++j) {
-      const int t = tid + j * kAttnThreads;
+      const int t = tid + j * NT;
       const int rr = t / CPR, cc = t - rr * CPR;
       if (t < RT * CPR) *reinterpret_cast<u32x4_t*>(&Qs[buf][rr * QSTR + cc * EPV]) = qr[j];
     }
@@ -1277,7 +1278,19 @@ int attn_rows_per_wg(Dt dt, int) {
   if (dt != Dt::BF16) return 4 * 32;
   return attn_variant() == 4 ? 4 * 32 * 2 : 8 * 32;
 }
-int score_keys_per_wg(Dt dt) { return 4 * 32 * (dt == Dt::BF16 ? kKtBf16 : kKtF32); }
+// Score pass shape: 4 waves (256 keys per work-group); STATEKV_SCORE_WAVES=8
+// selects 8 waves (512 keys) for bf16, which halves the Q traffic but measured
+// slower on the larger shapes.
+static int score_waves(Dt dt) {
+  static int v = -1;
+  if (v < 0) {
+    const char* e = getenv("STATEKV_SCORE_WAVES");
+    v = (e && atoi(e) == 8) ? 8 : 4;
+  }
+  return dt == Dt::BF16 ? v : 4;
+}
+int score_keys_per_wg(Dt dt) { return score_waves(dt) * 32 * (dt == Dt::BF16 ? kKtBf16 : kKtF32); }
+int score_waves_per_wg(Dt dt) { return score_waves(dt); }
 
 hipError_t launch_rope_table(const RopeTableArgs& a, hipStream_t s) {
   const size_t total = (size_t)a.npos * a.half;
@@ -1318,13 +1331,18 @@ hipError_t launch_attn(Dt dt, int d, const AttnArgs& a, int row_tiles, int split
 }
 
 hipError_t launch_score(Dt dt, int d, const ScoreArgs& a, int key_blocks, int rsplits, hipStream_t s) {
-  const dim3 grid(key_blocks, a.Hkv, rsplits), block(kAttnThreads);
+  const dim3 grid(key_blocks, a.Hkv, rsplits);
   if (dt == Dt::BF16) {
-    if (d == 64) hipLaunchKernelGGL((attn_score_kernel<BF16, 64, kKtBf16>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((attn_score_kernel<BF16, 128, kKtBf16>), grid, block, 0, s, a);
+    if (score_waves(dt) == 8) {
+      if (d == 64) hipLaunchKernelGGL((attn_score_kernel<BF16, 64, kKtBf16, 8>), grid, dim3(512), 0, s, a);
+      else hipLaunchKernelGGL((attn_score_kernel<BF16, 128, kKtBf16, 8>), grid, dim3(512), 0, s, a);
+    } else {
+      if (d == 64) hipLaunchKernelGGL((attn_score_kernel<BF16, 64, kKtBf16, 4>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((attn_score_kernel<BF16, 128, kKtBf16, 4>), grid, dim3(256), 0, s, a);
+    }
   } else {
-    if (d == 64) hipLaunchKernelGGL((attn_score_kernel<F32, 64, kKtF32>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((attn_score_kernel<F32, 128, kKtF32>), grid, block, 0, s, a);
+    if (d == 64) hipLaunchKernelGGL((attn_score_kernel<F32, 64, kKtF32, 4>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((attn_score_kernel<F32, 128, kKtF32, 4>), grid, dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }

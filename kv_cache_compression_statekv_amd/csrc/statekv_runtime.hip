@@ -162,9 +162,9 @@ void scaled_inv_freq(int d, double base, double alpha, int orig_ctx, double* out
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 // Pass 1 runs best with one work-group (8 waves) per compute unit: about 256
-// work-groups; the score pass with about two (4 waves each).
+// work-groups; the score pass with about 8 waves per compute unit.
 constexpr int kAttnTargetWGs = 256;
-constexpr int kScoreTargetWGs = 512;
+constexpr int kScoreTargetWaves = 256 * 8;
 
 // Key splits of pass 1 for a pool of P keys: enough work-groups to fill the
 // chip, at least 4 blocks of 64 keys per split.
@@ -180,7 +180,8 @@ void attn_geometry(const statekv_state* s, int P, int* splits, int* kps) {
 void score_geometry(const statekv_state* s, int P, int* key_blocks, int* rsplits, int* rps) {
   const int kb = ceil_div(P, score_keys_per_wg(s->dt));
   const int base = kb * s->Hkv;
-  int rs = std::max(1, std::min(ceil_div(kScoreTargetWGs, base), ceil_div(s->R, 128)));
+  const int target = kScoreTargetWaves / score_waves_per_wg(s->dt);
+  int rs = std::max(1, std::min(ceil_div(target, base), ceil_div(s->R, 128)));
   rs = std::min(rs, s->score_rsplits_max);
   rs = std::max(rs, ceil_div(s->R, kScoreMaxRows));  // rows per work-group fit the LDS statistics
   const int r = ceil_div(ceil_div(s->R, rs), 32) * 32;
@@ -312,7 +313,7 @@ int statekv_create(const statekv_layer_cfg* cfg, int32_t budget_B, float alpha,
   s->attn_tiles = ceil_div(s->R, attn_rows_per_wg(s->dt, s->D));
   s->attn_splits_max = std::min(std::min(kMaxSplits, ceil_div(kAttnTargetWGs, s->attn_tiles * s->Hkv)),
                                 std::max(1, ceil_div(s->cap, 4 * kAttnBN)));
-  s->score_rsplits_max = std::max(ceil_div(s->R, kScoreMaxRows), ceil_div(s->R, 128));
+  s->score_rsplits_max = std::max(ceil_div(s->R, kScoreMaxRows), ceil_div(s->R, 32));
   // Tuning overrides (launch geometry only; the result does not depend on them).
   if (const char* e = getenv("STATEKV_ATTN_SPLITS")) {
     const int v = atoi(e);
