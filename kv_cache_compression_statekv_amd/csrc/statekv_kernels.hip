@@ -225,6 +225,17 @@ __device__ __forceinline__ void merge_split_stats(const float (&ms)[kMaxSplits],
     if (ms[sp] != -INFINITY) l += ldexp(ls[sp], (int)(ms[sp] - m));
 }
 
+// Work-groups are dispatched round-robin over the 8 XCDs, each with its own
+// L2.  Renumbering the linear work-group id this way makes consecutive
+// logical indices run on the same XCD, so work-groups that read the same data
+// share one L2.  A permutation of [0, n): results do not depend on it.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_remap(int id, int n) {
+  const int xcd = id % kXcds, local = id / kXcds;
+  const int q = n / kXcds, r = n % kXcds;   // XCDs below r receive q + 1 work-groups
+  return xcd * q + min(xcd, r) + local;
+}
+
 // One 16-byte chunk of a move: task t = (move i, KV head g, chunk c); K and V.
 // The move list holds slots below B and rows in [B, cap); clamping only
 // guards the copy against a malformed list.
@@ -534,9 +545,14 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fwd_kernel(AttnArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, hh = lane >> 5;
-  const int g = blockIdx.y, split = blockIdx.z;
-  // Heaviest row tiles first (later tokens see more keys).
-  const int row_wg = (gridDim.x - 1 - blockIdx.x) * BM;
+  // Logical (row tile, KV head, split); the row tiles of one (head, split)
+  // share its K/V blocks and run on one XCD.  Heaviest row tiles first (later
+  // tokens see more keys).
+  const int wl = xcd_remap(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z),
+                           gridDim.x * gridDim.y * gridDim.z);
+  const int tile = wl % gridDim.x, wrest = wl / gridDim.x;
+  const int g = wrest % gridDim.y, split = wrest / gridDim.y;
+  const int row_wg = (gridDim.x - 1 - tile) * BM;
   const int row_last = min(a.R, row_wg + BM) - 1;
   const int tok_min = row_wg / a.G;
   const int need_end = a.k0 + row_last / a.G + 1;  // keys beyond are masked for every row
@@ -725,8 +741,13 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_score_kernel(ScoreArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, hh = lane >> 5;
-  const int g = blockIdx.y, rsplit = blockIdx.z;
-  const int key_wg = blockIdx.x * BNK;
+  // Logical (key block, KV head, row split); the key blocks of one (head,
+  // row split) share its Q rows and run on one XCD.
+  const int wl = xcd_remap(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z),
+                           gridDim.x * gridDim.y * gridDim.z);
+  const int kblock = wl % gridDim.x, wrest = wl / gridDim.x;
+  const int g = wrest % gridDim.y, rsplit = wrest / gridDim.y;
+  const int key_wg = kblock * BNK;
   const int key_w = key_wg + wave * 32 * KT;
 
   const T* qbase = (const T*)a.qrot + (size_t)g * a.R * D;
