@@ -45,6 +45,9 @@ def parse_args():
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="bounded CPU work for the oracle baseline (0 disables it)")
     p.add_argument("--no-kernel-timing", action="store_true")
+    p.add_argument("--recent-window", action="store_true",
+                   help="keep the B most recent tokens (the compute-matched ReKV-style window) "
+                        "instead of the B best-scoring candidates")
     p.add_argument("--quadratic", action="store_true",
                    help="also run the quadratic comparison over the workload's full stream: "
                         "one-shot full causal attention over all N*T tokens, full attention "
@@ -238,6 +241,8 @@ def main():
     st = skv.StateKV(n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, tokens_per_frame=T,
                      max_frames=total, budget=B, alpha=wl.alpha, dtype=wl.dtype,
                      rope_base=wl.rope_base, rope_orig_ctx=wl.rope_orig_ctx)
+    if args.recent_window:
+        st.set_flags(skv.FLAG_RECENT_WINDOW)
     lib, h = st._lib, st._h
     ptrs = [tuple(t.data_ptr() for t in f) for f in frames]
     optr = out.data_ptr()
@@ -263,7 +268,7 @@ def main():
     kernels = {}
     lat = []
     if timing_pass:
-        st.set_flags(skv.FLAG_KERNEL_TIMING)
+        st.set_flags(skv.FLAG_KERNEL_TIMING | (skv.FLAG_RECENT_WINDOW if args.recent_window else 0))
         st.kernel_times(reset=True)
         stream = torch.cuda.current_stream()
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(timing_pass + 1)]
@@ -275,11 +280,12 @@ def main():
         lat = [evs[i].elapsed_time(evs[i + 1]) for i in range(timing_pass)]
         for name, (ms, cnt) in st.kernel_times().items():
             kernels[name] = {"avg_us": 1e3 * ms / cnt if cnt else None, "launches": cnt}
-        st.set_flags(0)
+        st.set_flags(skv.FLAG_RECENT_WINDOW if args.recent_window else 0)
 
     pairs = pair_count(T, B)
     attn_flops = 4.0 * Hq * d * pairs                 # QK^T + PV, causal-counted
-    executed_flops = 6.0 * Hq * d * pairs             # + QK^T recomputed by the score pass
+    # + QK^T recomputed by the score pass (skipped by the recency window)
+    executed_flops = (4.0 if args.recent_window else 6.0) * Hq * d * pairs
     roofline = None
     extra = {}
     if kernels.get("attn_fwd", {}).get("avg_us"):
@@ -355,7 +361,8 @@ def main():
         "config": {"workload": f"{wl.name}: 1 layer, Hq={Hq}, Hkv={Hkv}, d={d}, T={T}, B={B}, "
                                f"alpha={wl.alpha:g}, seeded Gaussian frames with {wl.n_sinks} "
                                f"drifting sink keys per frame",
-                   "tokens_per_frame": T, "budget": B, "layers": 1},
+                   "tokens_per_frame": T, "budget": B, "layers": 1,
+                   "policy": "recent window (ReKV-style)" if args.recent_window else "StateKV Top-B"},
         "tokens_per_s": round(fps * T, 1),
         "roofline": roofline,
         "cpu_baseline": cpu,

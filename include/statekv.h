@@ -161,6 +161,11 @@ int statekv_scores(const statekv_state* s, statekv_scores_view* out);
 
 #define STATEKV_FLAG_ALWAYS_SCORE  1u  /* score the pool even while it fits in B */
 #define STATEKV_FLAG_KERNEL_TIMING 2u  /* time each kernel with HIP events */
+/* Keep the B most recent tokens (a sliding window over the stream, the
+ * compute-matched ReKV baseline of 实验关键数据) instead of the B best-scoring
+ * candidates.  The score pass is skipped unless STATEKV_FLAG_ALWAYS_SCORE is
+ * also set (then the scores are computed and reported, but not used). */
+#define STATEKV_FLAG_RECENT_WINDOW 4u
 
 /* Set option flags (STATEKV_FLAG_*).  Takes effect from the next frame. */
 int statekv_set_flags(statekv_state* s, uint32_t flags);

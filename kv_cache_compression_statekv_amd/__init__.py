@@ -32,6 +32,7 @@ DTYPE_F32 = 2
 
 FLAG_ALWAYS_SCORE = 1
 FLAG_KERNEL_TIMING = 2
+FLAG_RECENT_WINDOW = 4
 
 KERNEL_NAMES = ["rope_append", "attn_fwd", "attn_score", "select_merge"]
 
@@ -273,4 +274,4 @@ class StateKV:
 
 __all__ = ["StateKV", "StateKVError", "load_library", "build_library", "library_path",
            "declared_functions", "error_string", "KERNEL_NAMES",
-           "FLAG_ALWAYS_SCORE", "FLAG_KERNEL_TIMING"]
+           "FLAG_ALWAYS_SCORE", "FLAG_KERNEL_TIMING", "FLAG_RECENT_WINDOW"]

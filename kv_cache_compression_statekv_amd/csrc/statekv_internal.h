@@ -107,6 +107,8 @@ struct SelectArgs {
   int32_t* move_src;           // [T] out: rows of the kept frame tokens at or beyond B, ascending
   int32_t* move_count;         // [1] out
   int32_t P, B, mode;          // mode: kSelMerge, kSelScores or kSelEvict
+  int32_t recent;              // 1: keep the B most recent candidates (positions), not the best scores
+  int32_t scored;              // 1: the score pass ran; write scores and keep flags
   int32_t k0, foff;            // pool index -> row
   double score_scale;          // 2^-kScoreFracBits / (Hq * T)
   const void* opart;

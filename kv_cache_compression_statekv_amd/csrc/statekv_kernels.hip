@@ -886,7 +886,9 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_score_kernel(ScoreArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Top-B selection (work-group 0 of select_kernel, 1024 threads).
+// Top-B selection (work-group 0 of select_kernel, 1024 threads).  With the
+// recency window the selection value is the position instead of the score, so
+// the same steps evict the oldest tokens.
 // Scores s_j = (fixed-point column sum) / (Hq*T), rounded to fp32.  The pool
 // keeps its B best under (score descending, position ascending), i.e. it
 // evicts the E = P - B smallest 64-bit keys
@@ -1035,13 +1037,18 @@ __device__ void select_top_b(const SelectArgs& a, SelectShared& sh) {
 #pragma unroll
     for (int j = 0; j < kChunk; ++j) {
       const int idx = (j0 + j) * kSelectThreads + tid;
-      fx[j] = idx < a.P ? a.colsum[idx] : 0ull;
+      fx[j] = 0ull;
+      if (idx < a.P)
+        fx[j] = a.recent ? (unsigned long long)a.pool_pos[pool_row(idx, a.k0, a.foff)] : a.colsum[idx];
     }
 #pragma unroll
     for (int j = 0; j < kChunk; ++j) {
       const int idx = (j0 + j) * kSelectThreads + tid;
       if (idx < a.P) {
-        const uint32_t fb = __float_as_uint((float)((double)fx[j] * a.score_scale));
+        // Selection value: the score's bits, or for the recency window the
+        // position (older tokens have smaller values and are evicted first).
+        const uint32_t fb = a.recent ? (uint32_t)fx[j]
+                                     : __float_as_uint((float)((double)fx[j] * a.score_scale));
         sh.val[idx] = fb;
         flo = min(flo, fb);
         fhi = max(fhi, fb);
@@ -1160,11 +1167,14 @@ __device__ void select_top_b(const SelectArgs& a, SelectShared& sh) {
 
   // Outputs (the positions of the scored pool are rebuilt on request from the
   // row positions and the positions the moves overwrite).
-  for (int idx = tid; idx < a.P; idx += kSelectThreads) {
-    const uint32_t v = sh.val[idx];
-    a.scores[idx] = __uint_as_float(v & 0x7fffffffu);
-    a.keep_flag[idx] = (int)(1u - (v >> 31));
-    a.colsum[idx] = 0ull;  // ready for the next frame's score pass
+  if (a.scored) {
+    for (int idx = tid; idx < a.P; idx += kSelectThreads) {
+      const uint32_t v = sh.val[idx];
+      a.scores[idx] = a.recent ? (float)((double)a.colsum[idx] * a.score_scale)
+                               : __uint_as_float(v & 0x7fffffffu);
+      a.keep_flag[idx] = (int)(1u - (v >> 31));
+      a.colsum[idx] = 0ull;  // ready for the next frame's score pass
+    }
   }
   if (holes | movers) {
     int bh = base & 0xffff, bm = base >> 16;

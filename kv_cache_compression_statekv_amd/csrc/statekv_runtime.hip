@@ -401,7 +401,8 @@ int statekv_set_stream(statekv_state* s, void* hip_stream) {
 
 int statekv_set_flags(statekv_state* s, uint32_t flags) {
   if (!s) return STATEKV_EINVAL;
-  if (flags & ~(STATEKV_FLAG_ALWAYS_SCORE | STATEKV_FLAG_KERNEL_TIMING)) return STATEKV_EINVAL;
+  if (flags & ~(STATEKV_FLAG_ALWAYS_SCORE | STATEKV_FLAG_KERNEL_TIMING | STATEKV_FLAG_RECENT_WINDOW))
+    return STATEKV_EINVAL;
   s->flags = flags;
   return STATEKV_OK;
 }
@@ -418,7 +419,8 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const 
   const int P = k0 + s->T;
   const hipStream_t st = s->stream;
   const bool evict = P > s->B;
-  const bool scored = evict || (s->flags & STATEKV_FLAG_ALWAYS_SCORE);
+  const bool recent = (s->flags & STATEKV_FLAG_RECENT_WINDOW) != 0;
+  const bool scored = (evict && !recent) || (s->flags & STATEKV_FLAG_ALWAYS_SCORE);
   if (scored && P > kMaxPool) return STATEKV_EINVAL;   // beyond the selection's pool limit
   // Rows of this frame: right after the state, or, while the previous
   // frame's moves are pending, the region its rows do not occupy.
@@ -519,6 +521,8 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const 
     a.k0 = k0;
     a.foff = foff;
     a.mode = evict ? kSelEvict : (scored ? kSelScores : kSelMerge);
+    a.recent = recent ? 1 : 0;
+    a.scored = scored ? 1 : 0;
     a.score_scale = 1.0 / ((double)(1ull << kScoreFracBits) * (double)s->Hq * (double)s->T);
     a.opart = s->opart;
     a.epart = s->epart;
@@ -544,6 +548,8 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const 
     s->score_k0 = k0;
     s->score_foff = foff;
     s->score_evicted = evict;
+  } else if (evict) {
+    s->score_frame = -1;   // the pool has changed: earlier scores no longer describe it
   }
   s->count = evict ? (int)s->B : P;
   s->frames_done = n + 1;

@@ -6,5 +6,5 @@ package.  It shares no code with the HIP library or its binding.
 from .statekv_oracle import (  # noqa: F401
     CompressedState, LayerConfig, OracleStream, StepResult, frame_step,
     round_f64_to_bf16, round_storage, rope_cos_sin, rope_inv_freq, rope_rotate,
-    select_top_b, yarn_inv_freq, yarn_logit_scale,
+    select_recent, select_top_b, yarn_inv_freq, yarn_logit_scale,
 )

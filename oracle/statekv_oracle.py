@@ -152,6 +152,10 @@ class LayerConfig:
     rope_base: float
     alpha: float = 1.0
     rope_orig_ctx: int = 32768
+    # "statekv": keep the B best-scoring candidates (关键设计 2).  "recent": keep
+    # the B most recent tokens, a sliding window over the stream (the ReKV
+    # baseline's compute-matched window, 实验关键数据).
+    policy: str = "statekv"
 
     @property
     def group(self) -> int:
@@ -203,6 +207,15 @@ def select_top_b(scores32: np.ndarray, pool_pos: np.ndarray, budget: int) -> np.
     return kept
 
 
+def select_recent(pool_pos: np.ndarray, budget: int) -> np.ndarray:
+    """The B most recent candidates (largest positions), returned in pool order."""
+    n = pool_pos.size
+    if n <= budget:
+        return np.arange(n, dtype=np.int64)
+    order = sorted(range(n), key=lambda j: -int(pool_pos[j]))
+    return np.array(sorted(order[:budget], key=lambda j: int(pool_pos[j])), dtype=np.int64)
+
+
 def frame_step(cfg: LayerConfig, state: CompressedState, Q, K, V, n: int) -> StepResult:
     """One layer's StateKV step for frame n (0-based) of the stream.
 
@@ -249,8 +262,12 @@ def frame_step(cfg: LayerConfig, state: CompressedState, Q, K, V, n: int) -> Ste
     scores = col_sum / float(Hq * T)
     scores32 = scores.astype(np.float32).astype(np.float64)
 
-    # 5. Top-B selection and the next compressed state, kept in position order.
-    keep = select_top_b(scores32, pool_pos, cfg.budget)
+    # 5. Top-B selection (or the recency window) and the next compressed
+    #    state, kept in position order.
+    if cfg.policy == "recent":
+        keep = select_recent(pool_pos, cfg.budget)
+    else:
+        keep = select_top_b(scores32, pool_pos, cfg.budget)
     new_state = CompressedState(K_pool[:, keep, :].copy(), V_pool[:, keep, :].copy(),
                                 pool_pos[keep].copy())
 

@@ -2,6 +2,8 @@
 same seeded frames and compare them to the stated bars."""
 from __future__ import annotations
 
+import dataclasses
+
 import numpy as np
 import torch
 
@@ -51,11 +53,12 @@ def output_error(o_gpu: np.ndarray, o_ref: np.ndarray) -> float:
     return float((num / den).max())
 
 
-def selection_violations(res, keep_pos_gpu: np.ndarray, budget: int):
-    """Candidates kept by one side only whose oracle score lies outside the band."""
+def selection_violations(res, keep_pos_gpu: np.ndarray, budget: int, policy: str = "statekv"):
+    """Candidates kept by one side only whose oracle score lies outside the band
+    (the recency window has no band: its set must be identical)."""
     kept_o = set(res.state.pos.tolist())
     kept_g = set(int(p) for p in keep_pos_gpu)
-    if res.pool_pos.size <= budget:
+    if res.pool_pos.size <= budget or policy == "recent":
         return sorted(kept_o ^ kept_g)
     s = res.scores32
     order = sorted(range(s.size), key=lambda j: (-s[j], res.pool_pos[j]))
@@ -71,6 +74,8 @@ class StepCheck:
     def __init__(self, wl: StreamConfig, layer: int = 0, flags: int = 0, max_frames=None):
         self.wl = wl
         self.cfg = oracle_cfg(wl)
+        if flags & skv.FLAG_RECENT_WINDOW:
+            self.cfg = dataclasses.replace(self.cfg, policy="recent")
         self.st = make_state(wl, max_frames)
         if flags:
             self.st.set_flags(flags)
@@ -99,7 +104,7 @@ class StepCheck:
         k_new, v_new, pos_new = self.st.compressed_view()
         pos_new = pos_new.cpu().numpy().astype(np.int64)
         rep["state_size"] = (int(pos_new.size), int(res.state.count))
-        rep["violations"] = selection_violations(res, pos_new, wl.budget)
+        rep["violations"] = selection_violations(res, pos_new, wl.budget, self.cfg.policy)
         # The state is a set of slots: positions are unique (slot order is free).
         rep["unique"] = bool(np.unique(pos_new).size == pos_new.size)
         # Every kept row equals the pool row at its position (bit-exact).

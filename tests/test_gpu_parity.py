@@ -90,6 +90,29 @@ def test_full_size_sampled_frames(name, layer, frames, check):
     print("worst", name, layer, worst, flush=True)
 
 
+@pytest.mark.parametrize("name,frames,check,extra", [
+    ("ragged_bf16_d64", 9, None, 0),
+    ("ragged_bf16_d128_yarn", 8, None, skv.FLAG_ALWAYS_SCORE),
+    ("f32_d128_mha", 5, None, 0),
+    ("ivl3_1b", 24, [15, 16, 17, 23], 0),
+], ids=["bf16_d64", "bf16_d128_scored", "f32", "ivl3_1b"])
+def test_recent_window_policy(name, frames, check, extra):
+    """Recency window (the ReKV-style baseline): the GPU keeps exactly the last B
+    tokens and its outputs match the oracle's recency policy."""
+    wl = (SMALL.get(name) or CONFIGS[name]).replace(n_frames=frames)
+    chk = StepCheck(wl, flags=skv.FLAG_RECENT_WINDOW | extra)
+    T, B = wl.tokens_per_frame, wl.budget
+    for n in range(frames):
+        rep = chk.step(check=check is None or n in check)
+        if rep is None:
+            continue
+        print(name, rep, flush=True)
+        assert_step_ok(rep, wl.dtype)
+        _, _, pos = chk.st.compressed_view()
+        lo = max(0, (n + 1) * T - B)
+        assert sorted(pos.cpu().numpy().tolist()) == list(range(lo, (n + 1) * T))
+
+
 def test_bursts_are_exercised():
     wl = CONFIGS["qwen3vl_2b"]
     fs = FrameStream(wl, 0)

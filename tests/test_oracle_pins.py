@@ -185,6 +185,45 @@ def test_no_eviction_stream_is_full_causal_attention(dtype):
     assert stream.state.count == N * T
 
 
+def _sdpa_masked(q_rot, k_rot, v, n_q, n_kv, visible):
+    """torch fp64 SDPA over [L][H][d] inputs with a boolean [L][L] visibility mask."""
+    G = n_q // n_kv
+    q = torch.from_numpy(q_rot).permute(1, 0, 2)
+    k = torch.from_numpy(k_rot).permute(1, 0, 2).repeat_interleave(G, dim=0)
+    vv = torch.from_numpy(v).permute(1, 0, 2).repeat_interleave(G, dim=0)
+    o = torch.nn.functional.scaled_dot_product_attention(q, k, vv, attn_mask=torch.from_numpy(visible))
+    return o.permute(1, 0, 2).numpy()
+
+
+def test_recent_window_stream_is_banded_causal_attention():
+    """Recency policy (the ReKV-style window): the state before frame n holds the
+    last min(B, nT) tokens, so a query at position p of frame n sees exactly the
+    keys p' with max(0, nT - B) <= p' <= p: one banded causal attention."""
+    T, N, B, Hq, Hkv, d = 7, 6, 16, 4, 2, 32
+    cfg = LayerConfig(n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, tokens_per_frame=T,
+                      budget=B, dtype="f32", rope_base=1e4, policy="recent")
+    rng = np.random.default_rng(14)
+    frames = [_rand_frame(rng, T, Hq, Hkv, d) for _ in range(N)]
+    stream = OracleStream(cfg)
+    outs = []
+    for n, f in enumerate(frames):
+        outs.append(stream.step(*f).O_exact)
+        lo = max(0, (n + 1) * T - B)
+        assert stream.state.pos.tolist() == list(range(lo, (n + 1) * T))
+    L = N * T
+    Q = np.concatenate([f[0] for f in frames])
+    K = np.concatenate([f[1] for f in frames])
+    V = np.concatenate([f[2] for f in frames])
+    theta = 10000.0 ** (-np.arange(d // 2) * 2.0 / d)
+    q_rot = _textbook_rope(Q, np.arange(L), theta).astype(np.float32).astype(np.float64)
+    k_rot = _textbook_rope(K, np.arange(L), theta).astype(np.float32).astype(np.float64)
+    p = np.arange(L)
+    lo = np.maximum(0, (p // T) * T - B)
+    visible = (p[None, :] <= p[:, None]) & (p[None, :] >= lo[:, None])
+    want = _sdpa_masked(q_rot, k_rot, V, Hq, Hkv, visible)
+    assert np.max(np.abs(np.concatenate(outs) - want)) < 1e-5
+
+
 def test_scores_are_a_distribution_over_the_pool():
     cfg = LayerConfig(n_q_heads=4, n_kv_heads=1, head_dim=64, tokens_per_frame=16,
                       budget=24, dtype="bf16", rope_base=1e6, alpha=4.0)
