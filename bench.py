@@ -48,6 +48,11 @@ def parse_args():
     p.add_argument("--recent-window", action="store_true",
                    help="keep the B most recent tokens (the compute-matched ReKV-style window) "
                         "instead of the B best-scoring candidates")
+    p.add_argument("--b-sweep", default="",
+                   help="comma-separated budgets: run the workload's shape over --sweep-frames "
+                        "frames at each B and compare with one-shot full causal attention over "
+                        "the same tokens")
+    p.add_argument("--sweep-frames", type=int, default=512)
     p.add_argument("--quadratic", action="store_true",
                    help="also run the quadratic comparison over the workload's full stream: "
                         "one-shot full causal attention over all N*T tokens, full attention "
@@ -190,6 +195,67 @@ def quadratic_comparison(skv, torch, np, wl):
     }
 
 
+def budget_sweep(skv, torch, np, wl, budgets, n_frames):
+    """Per-budget cost of a stream of n_frames frames (one layer), and one-shot
+    full causal attention over the same n_frames*T tokens."""
+    from kv_cache_compression_statekv_amd.workload import FrameStream
+
+    T, Hq, Hkv, d = wl.tokens_per_frame, wl.n_q_heads, wl.n_kv_heads, wl.head_dim
+    tdtype = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    fs = FrameStream(wl, 0)
+    distinct = 16   # frames reused cyclically (positions still advance)
+    frames = [tuple(torch.from_numpy(x).to(tdtype).cuda() for x in fs.frame(n)) for n in range(distinct)]
+    common = dict(n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, alpha=wl.alpha, dtype=wl.dtype,
+                  rope_base=wl.rope_base, rope_orig_ctx=wl.rope_orig_ctx)
+    stream = torch.cuda.current_stream()
+    L = n_frames * T
+    out = []
+    for B in budgets:
+        st = skv.StateKV(tokens_per_frame=T, max_frames=n_frames, budget=B, **common)
+        o = torch.empty((T, Hq, d), dtype=tdtype, device="cuda")
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_frames + 1)]
+        evs[0].record(stream)
+        for n in range(n_frames):
+            st.prefill_frame(*frames[n % distinct], n, out=o)
+            evs[n + 1].record(stream)
+        torch.cuda.synchronize()
+        lat = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(n_frames)]) * 1e3
+        st.close()
+        flops = 0.0
+        for n in range(n_frames):
+            k = min(B, n * T)
+            pairs = T * k + T * (T + 1) // 2
+            evicts = k + T > B
+            flops += (6.0 if evicts else 4.0) * Hq * d * pairs
+        steady = lat[min(n_frames - 1, -(-B // T)):]
+        out.append({"budget": B, "total_ms": round(float(lat.sum()) / 1e3, 3),
+                    "steady_frame_us_median": round(float(np.median(steady)), 2),
+                    "executed_tflop": round(flops / 1e12, 3)})
+    # One-shot full causal attention over the same L tokens (a state that never evicts).
+    Q = torch.cat([frames[n % distinct][0] for n in range(n_frames)])
+    K = torch.cat([frames[n % distinct][1] for n in range(n_frames)])
+    V = torch.cat([frames[n % distinct][2] for n in range(n_frames)])
+    o = torch.empty((L, Hq, d), dtype=tdtype, device="cuda")
+    ms = []
+    for i in range(3):
+        st = skv.StateKV(tokens_per_frame=L, max_frames=1, budget=L, **common)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        st.prefill_frame(Q, K, V, 0, out=o)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        st.close()
+        if i:
+            ms.append(e0.elapsed_time(e1))
+    full_ms = float(np.median(ms))
+    full_flops = 4.0 * Hq * d * L * (L + 1) / 2
+    for r in out:
+        r["time_vs_full_one_shot"] = round(r["total_ms"] / full_ms, 4)
+        r["flops_vs_full"] = round(r["executed_tflop"] * 1e12 / full_flops, 4)
+    return {"frames": n_frames, "tokens": L, "full_causal_one_shot_ms": round(full_ms, 3),
+            "full_causal_tflop": round(full_flops / 1e12, 3), "budgets": out}
+
+
 def main():
     args = parse_args()
     if args.summarize_pmc:
@@ -312,6 +378,10 @@ def main():
         }
 
     quadratic = quadratic_comparison(skv, torch, np, wl) if args.quadratic else None
+    b_sweep = None
+    if args.b_sweep:
+        b_sweep = budget_sweep(skv, torch, np, wl, [int(b) for b in args.b_sweep.split(",")],
+                               args.sweep_frames)
 
     # CPU baseline: the oracle, started from the GPU's state, on the next frames.
     cpu = None
@@ -369,6 +439,7 @@ def main():
         "kernels": kernels,
         **extra,
         **({"quadratic": quadratic} if quadratic else {}),
+        **({"b_sweep": b_sweep} if b_sweep else {}),
         "attn_fwd_algorithmic_gflop": round(attn_flops / 1e9, 4),
         "executed_gflop_attention_passes": round(executed_flops / 1e9, 4),
     }
