@@ -51,8 +51,9 @@ extern "C" {
 
 #define STATEKV_OK          0
 #define STATEKV_EINVAL     -1  /* a null pointer, bad size or unsupported shape */
-#define STATEKV_EORDER     -2  /* n is not the next frame of the stream */
-#define STATEKV_ECAPACITY  -3  /* the detailed cache is full (max_frames reached) */
+#define STATEKV_EORDER     -2  /* n is not the next frame of the stream, or a frame
+                                  after the text phase has begun */
+#define STATEKV_ECAPACITY  -3  /* the detailed cache is full (max_frames or max_text reached) */
 #define STATEKV_ENOMEM     -4  /* device allocation failed */
 #define STATEKV_EDEVICE    -5  /* the HIP runtime reported an error */
 #define STATEKV_ENONFINITE -6  /* an input frame held NaN or Inf */
@@ -70,6 +71,8 @@ typedef struct statekv_layer_cfg {
   int32_t dtype;            /* STATEKV_DTYPE_BF16 or STATEKV_DTYPE_F32 */
   double  rope_base;        /* RoPE base (> 1) */
   int32_t rope_orig_ctx;    /* original context of the YaRN ramp (>= 1) */
+  int32_t max_text;         /* text tokens the detailed cache holds after the
+                               frames (>= 0; 0 disables statekv_decode) */
 } statekv_layer_cfg;
 
 typedef struct statekv_state statekv_state;
@@ -101,9 +104,9 @@ typedef struct statekv_scores_view {
 
 /*
  * Create the per-layer state: compressed state of capacity B (empty), the
- * detailed cache for cfg->max_frames * T tokens, and all scratch buffers, on
- * the current HIP device.  Everything is allocated here; later calls do not
- * allocate.  alpha >= 1 is the global RoPE scaling factor (关键设计 3), fixed
+ * detailed cache for cfg->max_frames * T + cfg->max_text tokens, and all
+ * scratch buffers, on the current HIP device.  Everything is allocated here;
+ * later calls do not allocate.  alpha >= 1 is the global RoPE scaling factor (关键设计 3), fixed
  * for the life of the state.  Requires B >= 1 and B + T <= 32768, except
  * when B >= max_frames * T: such a state never evicts (full causal attention
  * over the stream, the quadratic baseline) and may hold any number of tokens.
@@ -145,9 +148,10 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K,
 int statekv_compressed_view(const statekv_state* s, statekv_view* out);
 
 /*
- * Detailed state D: k, v are [frames_done*T][Hkv][d] (token_stride = Hkv*d,
- * head_stride = d), row p holding the token at stream position p.  Synchronises
- * the state's stream.  Valid until destroy.  Returns ENONFINITE as above.
+ * Detailed state D: k, v are [count][Hkv][d] (token_stride = Hkv*d,
+ * head_stride = d), row p holding the token at stream position p:
+ * count = frames_done*T + the text tokens decoded so far.  Synchronises the
+ * state's stream.  Valid until destroy.  Returns ENONFINITE as above.
  */
 int statekv_detailed_view(const statekv_state* s, statekv_view* out);
 
@@ -158,6 +162,25 @@ int statekv_detailed_view(const statekv_state* s, statekv_view* out);
  * next prefill_frame or destroy.
  */
 int statekv_scores(const statekv_state* s, statekv_scores_view* out);
+
+/*
+ * Text phase (整体框架 and 关键设计 1: once the frames are done, generation
+ * uses the whole detailed cache D as its context; 关键设计 3: the same fixed
+ * alpha, positions continuing the virtual length).  Appends t text tokens
+ * (prompt chunk or generated tokens) at stream positions P0..P0+t-1, with
+ * P0 = frames_done*T + text tokens already decoded, and attends them causally
+ * over every row of D:
+ *   Q [t][Hq][d], K [t][Hkv][d], V [t][Hkv][d]: projected, pre-RoPE inputs
+ *     (device, caller-owned, read only);
+ *   O [t][Hq][d]: attention output (device, caller-owned, written).
+ * Query i sees D rows 0..P0+i (all frame tokens, earlier text, itself).  The
+ * compressed state is neither read nor changed.  1 <= t <= T (EINVAL
+ * otherwise); ECAPACITY when the text would exceed cfg->max_text.  After the
+ * first decode, statekv_prefill_frame returns EORDER.  Asynchronous like
+ * prefill_frame; non-finite inputs are reported by the next view.
+ */
+int statekv_decode(statekv_state* s, const void* Q, const void* K, const void* V,
+                   int32_t t, void* O);
 
 #define STATEKV_FLAG_ALWAYS_SCORE  1u  /* score the pool even while it fits in B */
 #define STATEKV_FLAG_KERNEL_TIMING 2u  /* time each kernel with HIP events */
@@ -177,7 +200,10 @@ int statekv_set_flags(statekv_state* s, uint32_t flags);
 #define STATEKV_K_ATTN     1  /* fused attention, pass 1 (split over keys) */
 #define STATEKV_K_SCORE    2  /* recompute pass: per-key column sums */
 #define STATEKV_K_SELECT   3  /* Top-B decision; merge of the key splits into O */
-#define STATEKV_K_COUNT    4
+#define STATEKV_K_DEC_ROPE  4 /* text phase: RoPE of the text tokens + append to D */
+#define STATEKV_K_DEC_ATTN  5 /* text phase: attention over D, split over keys */
+#define STATEKV_K_DEC_MERGE 6 /* text phase: merge of the key splits into O */
+#define STATEKV_K_COUNT    7
 
 /*
  * With STATEKV_FLAG_KERNEL_TIMING set, per-kernel device time (HIP events on

@@ -34,7 +34,8 @@ FLAG_ALWAYS_SCORE = 1
 FLAG_KERNEL_TIMING = 2
 FLAG_RECENT_WINDOW = 4
 
-KERNEL_NAMES = ["rope_append", "attn_fwd", "attn_score", "select_merge"]
+KERNEL_NAMES = ["rope_append", "attn_fwd", "attn_score", "select_merge",
+                "decode_rope", "decode_attn", "decode_merge"]
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
                       "include", "statekv.h")
@@ -50,6 +51,7 @@ class LayerCfg(ctypes.Structure):
         ("dtype", ctypes.c_int32),
         ("rope_base", ctypes.c_double),
         ("rope_orig_ctx", ctypes.c_int32),
+        ("max_text", ctypes.c_int32),
     ]
 
 
@@ -111,6 +113,7 @@ def load_library(build_if_missing: bool = True) -> ctypes.CDLL:
     lib.statekv_create.argtypes = [ctypes.POINTER(LayerCfg), I32, F32, ctypes.POINTER(P)]
     lib.statekv_set_stream.argtypes = [P, P]
     lib.statekv_prefill_frame.argtypes = [P, P, P, P, I32, P]
+    lib.statekv_decode.argtypes = [P, P, P, P, I32, P]
     lib.statekv_compressed_view.argtypes = [P, ctypes.POINTER(View)]
     lib.statekv_detailed_view.argtypes = [P, ctypes.POINTER(View)]
     lib.statekv_scores.argtypes = [P, ctypes.POINTER(ScoresView)]
@@ -120,7 +123,7 @@ def load_library(build_if_missing: bool = True) -> ctypes.CDLL:
     lib.statekv_destroy.restype = None
     lib.statekv_strerror.argtypes = [ctypes.c_int]
     lib.statekv_strerror.restype = ctypes.c_char_p
-    for name in ("statekv_create", "statekv_set_stream", "statekv_prefill_frame",
+    for name in ("statekv_create", "statekv_set_stream", "statekv_prefill_frame", "statekv_decode",
                  "statekv_compressed_view", "statekv_detailed_view", "statekv_scores",
                  "statekv_set_flags", "statekv_kernel_times"):
         getattr(lib, name).restype = ctypes.c_int
@@ -162,7 +165,7 @@ class StateKV:
     def __init__(self, *, n_q_heads: int, n_kv_heads: int, head_dim: int,
                  tokens_per_frame: int, max_frames: int, budget: int, alpha: float = 1.0,
                  dtype: str = "bf16", rope_base: float = 1e6, rope_orig_ctx: int = 32768,
-                 stream=None):
+                 max_text: int = 0, stream=None):
         self._lib = load_library()
         if dtype not in _ABI_DTYPE:
             raise ValueError(f"dtype must be 'bf16' or 'f32', not {dtype!r}")
@@ -171,9 +174,10 @@ class StateKV:
         self.Hq, self.Hkv, self.d = n_q_heads, n_kv_heads, head_dim
         self.T, self.max_frames, self.budget = tokens_per_frame, max_frames, budget
         self.alpha = alpha
+        self.max_text = max_text
         self.device = torch.device("cuda", torch.cuda.current_device())
         cfg = LayerCfg(n_q_heads, n_kv_heads, head_dim, tokens_per_frame, max_frames,
-                       _ABI_DTYPE[dtype], float(rope_base), rope_orig_ctx)
+                       _ABI_DTYPE[dtype], float(rope_base), rope_orig_ctx, max_text)
         handle = ctypes.c_void_p()
         rc = self._lib.statekv_create(ctypes.byref(cfg), budget, float(alpha), ctypes.byref(handle))
         if rc != STATEKV_OK:
@@ -207,8 +211,8 @@ class StateKV:
         self._check(self._lib.statekv_set_flags(self._h, flags), "statekv_set_flags")
 
     # -- the frame step -------------------------------------------------------
-    def _frame_tensor(self, x: torch.Tensor, heads: int, name: str):
-        want = (self.T, heads, self.d)
+    def _frame_tensor(self, x: torch.Tensor, heads: int, name: str, tokens=None):
+        want = (self.T if tokens is None else tokens, heads, self.d)
         if not isinstance(x, torch.Tensor) or x.device.type != "cuda":
             raise ValueError(f"{name} must be a CUDA/HIP tensor")
         if x.dtype != self.torch_dtype or tuple(x.shape) != want or not x.is_contiguous():
@@ -228,6 +232,24 @@ class StateKV:
                     "statekv_prefill_frame")
         return out
 
+    # -- the text phase ---------------------------------------------------------
+    def decode(self, Q, K, V, out=None) -> torch.Tensor:
+        """Append t text tokens (Q [t][Hq][d], K, V [t][Hkv][d]) after everything
+        processed so far and attend them over the whole detailed cache; returns
+        O [t][Hq][d] (asynchronous on the state's stream)."""
+        t = Q.shape[0] if isinstance(Q, torch.Tensor) and Q.dim() == 3 else -1
+        self._frame_tensor(Q, self.Hq, "Q", t)
+        self._frame_tensor(K, self.Hkv, "K", t)
+        self._frame_tensor(V, self.Hkv, "V", t)
+        if out is None:
+            out = torch.empty((t, self.Hq, self.d), dtype=self.torch_dtype, device=Q.device)
+        else:
+            self._frame_tensor(out, self.Hq, "out", t)
+        self._check(self._lib.statekv_decode(self._h, Q.data_ptr(), K.data_ptr(), V.data_ptr(),
+                                             t, out.data_ptr()),
+                    "statekv_decode")
+        return out
+
     # -- views (copied into new tensors) ------------------------------------------
     def compressed_view(self):
         """(Kbar [Hkv][count][d], Vbar [Hkv][count][d], pos [count] int32), copies in slot order."""
@@ -241,7 +263,7 @@ class StateKV:
         return k[:, : v.count].contiguous(), vv[:, : v.count].contiguous(), pos
 
     def detailed_view(self):
-        """(D_K [n*T][Hkv][d], D_V [n*T][Hkv][d]), copies."""
+        """(D_K [count][Hkv][d], D_V [count][Hkv][d]), copies; count = n*T + text tokens."""
         v = View()
         self._check(self._lib.statekv_detailed_view(self._h, ctypes.byref(v)),
                     "statekv_detailed_view")

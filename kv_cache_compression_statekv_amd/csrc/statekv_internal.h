@@ -16,6 +16,7 @@ constexpr int kSelectThreads = 1024;
 constexpr int kMaxPool = 32768;      // B + T limit of the single-work-group select
 constexpr int kSelectBins = 4096;
 constexpr int kSelCand = 1024;       // boundary candidates resolved by rank counting
+constexpr int kDecodeMaxSplits = 1024;  // key splits of the text-phase attention
 // Column sums are accumulated as unsigned 64-bit fixed point with this many
 // fractional bits: integer addition is associative, so the sum does not depend
 // on the order in which work-groups add their partials.  A sum is at most
@@ -44,22 +45,24 @@ struct MovesArgs {
   int32_t Hkv, cap, B, row_bytes, max_moves;
 };
 
-// Per-frame arguments of the RoPE + append kernel.  Work-groups at or beyond
-// rope_blocks apply the previous frame's moves (mv.max_moves > 0): they touch
-// state slots below B and the previous frame's rows, never this frame's.
+// Arguments of the RoPE + append kernel for T tokens at stream positions
+// pos0..pos0+T-1 (a frame, or a chunk of text tokens).  Work-groups at or
+// beyond rope_blocks apply the previous frame's moves (mv.max_moves > 0):
+// they touch state slots below B and the previous frame's rows, never this
+// frame's.  Text tokens go to D only (kpool, vpool and pool_pos null).
 struct RopeArgs {
   const void* q;          // [T][Hq][d]
   const void* k;          // [T][Hkv][d]
   const void* v;          // [T][Hkv][d]
-  const float2* table;    // [max_frames*T][d/2]
+  const float2* table;    // [positions][d/2]
   void* qrot;             // [Hkv][G*T][d], row r = token*G + head-in-group
   void* kpool;            // [Hkv][cap][d]: state rows; this frame's rows at frame_base
   void* vpool;            // [Hkv][cap][d]
   int32_t* pool_pos;      // [cap] position of every row
-  void* dk;               // [max_frames*T][Hkv][d]
-  void* dv;               // [max_frames*T][Hkv][d]
+  void* dk;               // [positions][Hkv][d]
+  void* dv;               // [positions][Hkv][d]
   int32_t* nonfinite;     // set to 1 when an input element is NaN or Inf
-  int32_t n, T, Hq, Hkv, G, cap, frame_base, rope_blocks;
+  int32_t pos0, T, Hq, Hkv, G, cap, frame_base, rope_blocks;
   MovesArgs mv;
 };
 
@@ -94,6 +97,31 @@ struct ScoreArgs {
   unsigned long long* colsum;  // [cap] column sums, fixed point (2^-kScoreFracBits units)
   float c_hi, c_lo;            // sigma * log2(e) = c_hi + c_lo
   int32_t R, G, cap, P, k0, foff, rps, Hkv, S, ss;
+};
+
+// Text-phase attention over the detailed cache D (token-major rows): one
+// work-group per (tile of 32 query rows, KV head, key split).  Its NW waves
+// take the 32-key sub-tiles of every block of 32*NW keys and are merged in
+// LDS at the end.  With one split the work-group writes O; otherwise it
+// leaves (m_s, l_s, O_s) for the merge kernel.
+struct DecodeArgs {
+  const void* qrot;       // [Hkv][R][d], row r = token*G + head-in-group
+  const void* dk;         // [positions][Hkv][d]
+  const void* dv;         // [positions][Hkv][d]
+  float* opart;           // [S][Hkv][R][d] unnormalised partial outputs (S > 1)
+  float* mpart;           // [S][Hkv][R] reference maxima (integers, log2 units)
+  double* lpart;          // [S][Hkv][R] row sums of 2^(x*c - m_s)
+  void* out;              // [t][Hq][d] (S == 1)
+  float c_hi;             // sigma * log2(e) rounded to fp32
+  int32_t R, G, Hq, Hkv, P, k0, kps, S;  // P = k0 + t keys; k0 keys precede the text
+};
+
+struct DecodeMergeArgs {
+  const float* opart;
+  const float* mpart;
+  const double* lpart;
+  void* out;              // [t][Hq][d]
+  int32_t R, G, Hq, Hkv, S;
 };
 
 // Work-group 0: scores and the Top-B decision; work-groups 1..: the merge of
@@ -135,6 +163,10 @@ hipError_t launch_attn(Dt dt, int d, const AttnArgs& a, int row_tiles, int split
 hipError_t launch_score(Dt dt, int d, const ScoreArgs& a, int key_blocks, int rsplits, hipStream_t s);
 hipError_t launch_select(Dt dt, int d, const SelectArgs& a, hipStream_t s);
 hipError_t launch_moves(const MovesArgs& a, hipStream_t s);
+// Keys per block of the text-phase attention kernel.
+int decode_block_keys(Dt dt);
+hipError_t launch_decode(Dt dt, int d, const DecodeArgs& a, int row_tiles, hipStream_t s);
+hipError_t launch_decode_merge(Dt dt, int d, const DecodeMergeArgs& a, hipStream_t s);
 // Positions of a scored pool of P candidates: the position of its row, or
 // for an evicted slot below B that a move has since filled, the saved one.
 hipError_t launch_score_positions(int32_t* score_pos, const int32_t* pool_pos,

@@ -282,7 +282,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeArgs a) {
     const int tok = tok0 + lt;
     if (tok >= a.T) continue;
     const int k = c * 8;
-    const int pos = a.n * a.T + tok;
+    const int pos = a.pos0 + tok;
     const T* src;
     T* dst0;
     T* dst1 = nullptr;
@@ -293,8 +293,8 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeArgs a) {
     } else {
       const int g = hd - a.Hq;
       src = (const T*)a.k + ((size_t)tok * a.Hkv + g) * D;
-      dst0 = (T*)a.kpool + ((size_t)g * a.cap + a.frame_base + tok) * D;
-      dst1 = (T*)a.dk + ((size_t)pos * a.Hkv + g) * D;
+      dst0 = (T*)a.dk + ((size_t)pos * a.Hkv + g) * D;
+      if (a.kpool) dst1 = (T*)a.kpool + ((size_t)g * a.cap + a.frame_base + tok) * D;
     }
     float x1[8], x2[8];
     Vec8<E>::load(src + k, x1);
@@ -339,10 +339,11 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) finite &= isfinite(__uint_as_float(v[j]));
     }
-    *reinterpret_cast<u32x4_t*>((T*)a.vpool + ((size_t)g * a.cap + a.frame_base + tok) * D + c * VEC) = v;
-    *reinterpret_cast<u32x4_t*>((T*)a.dv + ((size_t)(a.n * a.T + tok) * a.Hkv + g) * D + c * VEC) = v;
+    if (a.vpool)
+      *reinterpret_cast<u32x4_t*>((T*)a.vpool + ((size_t)g * a.cap + a.frame_base + tok) * D + c * VEC) = v;
+    *reinterpret_cast<u32x4_t*>((T*)a.dv + ((size_t)(a.pos0 + tok) * a.Hkv + g) * D + c * VEC) = v;
   }
-  if (tid < TPW && tok0 + tid < a.T) a.pool_pos[a.frame_base + tok0 + tid] = a.n * a.T + tok0 + tid;
+  if (a.pool_pos && tid < TPW && tok0 + tid < a.T) a.pool_pos[a.frame_base + tok0 + tid] = a.pos0 + tok0 + tid;
   if (!finite) atomicOr(a.nonfinite, 1);
 }
 
@@ -366,10 +367,10 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeArgs a) {
 // row sum l only needs the weights near the maximum, whose exponent error
 // c_lo*x is common to them, so it stays within about 1e-7 of the exact sum.
 // ---------------------------------------------------------------------------
-template <class E, int D, int NT>
+template <class E, int D, int NT, int BN_ = kAttnBN>
 struct AttnStage {
   typedef typename E::T T;
-  static constexpr int BN = kAttnBN;
+  static constexpr int BN = BN_;
   static constexpr int EPV = 16 / (int)sizeof(T);
   static constexpr int KSTR = D + EPV;
   static constexpr int VSTR = BN + EPV;
@@ -384,8 +385,10 @@ struct AttnStage {
   u32x4_t kr[KCH];
   u32x4_t vr[VCH];
 
+  // Key j of the block is row pool_row(j, k0, foff) of kbase / vbase; rows
+  // are rs elements apart.
   __device__ __forceinline__ void load(const T* kbase, const T* vbase, int kb, int kend, int k0,
-                                       int foff, int tid) {
+                                       int foff, size_t rs, int tid) {
     constexpr int CPR = D / EPV;
 #pragma unroll
     for (int j = 0; j < KCH; ++j) {
@@ -394,7 +397,7 @@ struct AttnStage {
       const int key = kb + rr;
       kr[j] = u32x4_t{0u, 0u, 0u, 0u};
       if (key < kend)
-        kr[j] = *reinterpret_cast<const u32x4_t*>(kbase + (size_t)pool_row(key, k0, foff) * D + cc * EPV);
+        kr[j] = *reinterpret_cast<const u32x4_t*>(kbase + (size_t)pool_row(key, k0, foff) * rs + cc * EPV);
     }
     if constexpr (sizeof(T) == 2) {
       constexpr int NKQ = BN / KG;
@@ -407,7 +410,7 @@ struct AttnStage {
           const int key = kb + kq * KG + j;
           vr[u * KG + j] = u32x4_t{0u, 0u, 0u, 0u};
           if (t < VTASKS && key < kend)
-            vr[u * KG + j] = *reinterpret_cast<const u32x4_t*>(vbase + (size_t)pool_row(key, k0, foff) * D + dc * 8);
+            vr[u * KG + j] = *reinterpret_cast<const u32x4_t*>(vbase + (size_t)pool_row(key, k0, foff) * rs + dc * 8);
         }
       }
     } else {
@@ -418,7 +421,7 @@ struct AttnStage {
         const int key = kb + rr;
         vr[j] = u32x4_t{0u, 0u, 0u, 0u};
         if (key < kend)
-          vr[j] = *reinterpret_cast<const u32x4_t*>(vbase + (size_t)pool_row(key, k0, foff) * D + cc * 4);
+          vr[j] = *reinterpret_cast<const u32x4_t*>(vbase + (size_t)pool_row(key, k0, foff) * rs + cc * 4);
       }
     }
   }
@@ -591,7 +594,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fwd_kernel(AttnArgs a) {
   Stage stage;
   const int nblk = kend > kbeg ? (kend - kbeg + BN - 1) / BN : 0;
   if (nblk > 0) {
-    stage.load(kbase, vbase, kbeg, kend, a.k0, a.foff, tid);
+    stage.load(kbase, vbase, kbeg, kend, a.k0, a.foff, D, tid);
     stage.store(Ks[0], Vt[0], tid);
   }
   __syncthreads();
@@ -599,7 +602,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fwd_kernel(AttnArgs a) {
   for (int b = 0; b < nblk; ++b) {
     const int kb = kbeg + b * BN;
     const int buf = b & 1;
-    if (b + 1 < nblk) stage.load(kbase, vbase, kb + BN, kend, a.k0, a.foff, tid);
+    if (b + 1 < nblk) stage.load(kbase, vbase, kb + BN, kend, a.k0, a.foff, D, tid);
     const T* ks_ = Ks[buf];
     const T* vt_ = Vt[buf];
 
@@ -705,6 +708,252 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fwd_kernel(AttnArgs a) {
                                                                 o[qt][dt][4 * j + 2], o[qt][dt][4 * j + 3], sc);
       }
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Text-phase attention over the detailed cache D.  Text queries are few (G*t
+// rows per KV head), so the work is a stream over D's rows: HBM-bound.  A
+// work-group owns one tile of 32 query rows and a contiguous key split; each
+// block of BN = 32*NW keys is loaded with 16-byte coalesced reads (D rows are
+// Hkv*d elements apart), staged in LDS as K and V^T (as in pass 1), and wave
+// w computes the block's w-th 32-key sub-tile: S^T = K Q^T, online softmax,
+// O^T += V^T P^T.  The next block's loads are in flight during the compute.
+// At the end the waves' (m, l, O) are merged with exact power-of-two factors.
+// Visibility: key j is seen by the query of text token i iff j < k0 + i + 1.
+// ---------------------------------------------------------------------------
+template <class E, int D, int NW>
+__global__ __launch_bounds__(64 * NW, 2) void decode_attn_kernel(DecodeArgs a) {
+  typedef typename E::T T;
+  typedef Mma<E> M;
+  constexpr int NT = 64 * NW;
+  constexpr int BN = 32 * NW;
+  typedef AttnStage<E, D, NT, BN> Stage;
+  constexpr int KSTR = Stage::KSTR;
+  constexpr int VSTR = Stage::VSTR;
+  constexpr int NKS = D / M::KS;
+  constexpr int NDT = D / 32;
+  constexpr int KBYTES = BN * KSTR * (int)sizeof(T);
+  constexpr int VBYTES = D * VSTR * (int)sizeof(T);
+  constexpr int OSTR = D + 4;                       // fp32 row stride of the wave merge
+  constexpr int RBYTES = NW * 32 * OSTR * 4;
+  constexpr int LBYTES = KBYTES + VBYTES > RBYTES ? KBYTES + VBYTES : RBYTES;
+  __shared__ __attribute__((aligned(16))) char lds[LBYTES];
+  __shared__ float wm[NW][32];
+  __shared__ double wsum[NW][32];
+  T* Ks = reinterpret_cast<T*>(lds);
+  T* Vt = reinterpret_cast<T*>(lds + KBYTES);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, hh = lane >> 5;
+  // Logical (row tile, KV head, split): the row tiles of one (head, split)
+  // read the same keys and run on one XCD.
+  const int wl = xcd_remap(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z),
+                           gridDim.x * gridDim.y * gridDim.z);
+  const int tile = wl % gridDim.x, wrest = wl / gridDim.x;
+  const int g = wrest % gridDim.y, split = wrest / gridDim.y;
+  const int row0 = tile * 32;
+  const int row_last = min(a.R, row0 + 32) - 1;
+  const int kbeg = split * a.kps;
+  const int kend = min(min(kbeg + a.kps, a.k0 + row_last / a.G + 1), a.P);
+  const int full_end = min(kend, a.k0 + row0 / a.G + 1);   // visible to every row of the tile
+  const size_t rs = (size_t)a.Hkv * D;
+  const T* qbase = (const T*)a.qrot + (size_t)g * a.R * D;
+  const T* kbase = (const T*)a.dk + (size_t)g * D;
+  const T* vbase = (const T*)a.dv + (size_t)g * D;
+
+  const int r = row0 + col;
+  int lim[1] = {min(kend, a.k0 + (r < a.R ? r / a.G : -1) + 1)};
+  typename M::Frag qf[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks)
+    qf[ks] = r < a.R ? M::ld(qbase + (size_t)r * D + ks * M::KS + hh * M::KL) : M::zero();
+
+  f32x16_t o[1][NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) o[0][dt] = f32x16_t{};
+  float m_run[1] = {-INFINITY};
+  double l_run[1] = {0.0};
+
+  Stage stage;
+  const int nblk = kend > kbeg ? (kend - kbeg + BN - 1) / BN : 0;
+  if (nblk > 0) stage.load(kbase, vbase, kbeg, kend, a.k0, 0, rs, tid);
+  for (int b = 0; b < nblk; ++b) {
+    const int kb = kbeg + b * BN;
+    if (b > 0) __syncthreads();   // every wave is done with the previous block
+    stage.store(Ks, Vt, tid);
+    __syncthreads();
+    if (b + 1 < nblk) stage.load(kbase, vbase, kb + BN, kend, a.k0, 0, rs, tid);
+    const int ksub = kb + wave * 32;
+    if (ksub < kend) {
+      f32x16_t sacc[1] = {f32x16_t{}};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const typename M::Frag af = M::ld(&Ks[(wave * 32 + col) * KSTR + ks * M::KS + hh * M::KL]);
+        sacc[0] = M::mma(af, qf[ks], sacc[0]);
+      }
+      float alpha[1];
+      if (ksub + 32 > full_end)
+        online_softmax<1, true>(sacc, m_run, l_run, alpha, lim, ksub, hh, a.c_hi);
+      else
+        online_softmax<1, false>(sacc, m_run, l_run, alpha, lim, ksub, hh, a.c_hi);
+      if (__ballot(alpha[0] != 1.f)) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[0][dt] *= alpha[0];
+      }
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm) {
+          bf16x8_t pf;
+#pragma unroll
+          for (int t = 0; t < 8; ++t) pf[t] = (__bf16)sacc[0][8 * mm + t];
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) {
+            const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(
+                &Vt[(dt * 32 + col) * VSTR + wave * 32 + mm * 16 + hh * 8]);
+            o[0][dt] = M::mma(af, pf, o[0][dt]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int t = 0; t < 16; ++t) {
+            const int kin = wave * 32 + 8 * (t >> 2) + 4 * hh + (t & 3);
+            o[0][dt] = M::mma(Vt[(dt * 32 + col) * VSTR + kin], sacc[0][t], o[0][dt]);
+          }
+      }
+    }
+  }
+
+  // Merge of the waves: m = max_w m_w; each wave's l and O scale by the exact
+  // factor 2^(m_w - m); the sums run in wave order.
+  const double lt = l_run[0] + __shfl_xor(l_run[0], 32);
+  __syncthreads();                  // the last block's LDS reads are done
+  if (hh == 0) {
+    wm[wave][col] = m_run[0];
+    wsum[wave][col] = lt;
+  }
+  __syncthreads();
+  float m = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) m = fmaxf(m, wm[w][col]);
+  const float fw = m_run[0] == -INFINITY ? 0.f : ldexpf(1.f, (int)(m_run[0] - m));
+  float* red = reinterpret_cast<float*>(lds);
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<f32x4_t*>(&red[(wave * 32 + col) * OSTR + dt * 32 + 8 * j + 4 * hh]) =
+          f32x4_t{o[0][dt][4 * j], o[0][dt][4 * j + 1], o[0][dt][4 * j + 2], o[0][dt][4 * j + 3]} * fw;
+  __syncthreads();
+  // Thread task: (row, 4 dims); rows of the tile in order.
+  constexpr int CPR = D / 4;
+  for (int e = tid; e < 32 * CPR; e += NT) {
+    const int rr = e / CPR, c = e - rr * CPR;
+    const int row = row0 + rr;
+    if (row >= a.R) continue;
+    float mr = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) mr = fmaxf(mr, wm[w][rr]);
+    double l = 0.0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+      if (wm[w][rr] != -INFINITY) l += ldexp(wsum[w][rr], (int)(wm[w][rr] - mr));
+    f32x4_t acc = *reinterpret_cast<const f32x4_t*>(&red[rr * OSTR + 4 * c]);
+#pragma unroll
+    for (int w = 1; w < NW; ++w) acc += *reinterpret_cast<const f32x4_t*>(&red[(w * 32 + rr) * OSTR + 4 * c]);
+    if (a.S == 1) {
+      const float inv = (float)(1.0 / l);
+      const int tok = row / a.G;
+      const int h = g * a.G + (row - tok * a.G);
+      T* out = (T*)a.out + ((size_t)tok * a.Hq + h) * D + c * 4;
+      if constexpr (sizeof(T) == 2) {
+        const u32x2_t v = {(uint32_t)f32_to_bf16(acc[0] * inv) | ((uint32_t)f32_to_bf16(acc[1] * inv) << 16),
+                           (uint32_t)f32_to_bf16(acc[2] * inv) | ((uint32_t)f32_to_bf16(acc[3] * inv) << 16)};
+        *reinterpret_cast<u32x2_t*>(out) = v;
+      } else {
+        *reinterpret_cast<f32x4_t*>(out) = acc * inv;
+      }
+    } else {
+      const size_t ri = ((size_t)split * a.Hkv + g) * a.R + row;
+      *reinterpret_cast<f32x4_t*>(a.opart + ri * D + c * 4) = acc;
+      if (c == 0) {
+        a.mpart[ri] = mr;
+        a.lpart[ri] = l;
+      }
+    }
+  }
+}
+
+// Merge of the text-phase key splits: one work-group per (KV head, row).
+// m = max_s m_s; weights 2^(m_s - m) are exact; l and O are summed in a fixed
+// order (per thread over its splits, then across threads in index order), so
+// the result does not depend on scheduling.
+constexpr int kDecodeMergeThreads = 256;
+
+template <class E, int D>
+__global__ __launch_bounds__(kDecodeMergeThreads) void decode_merge_kernel(DecodeMergeArgs a) {
+  typedef typename E::T T;
+  constexpr int NT = kDecodeMergeThreads;
+  constexpr int CPR = D / 4;
+  constexpr int SG = NT / CPR;                       // split groups
+  __shared__ float wts[kDecodeMaxSplits];
+  __shared__ float redm[NT];
+  __shared__ double redl[NT];
+  __shared__ __attribute__((aligned(16))) f32x4_t redo[SG][CPR];
+  const int tid = threadIdx.x;
+  const size_t nrows = (size_t)a.Hkv * a.R;
+  const size_t row = blockIdx.x;                     // = g*R + r
+  float mt = -INFINITY;
+  for (int s = tid; s < a.S; s += NT) mt = fmaxf(mt, a.mpart[s * nrows + row]);
+  redm[tid] = mt;
+  __syncthreads();
+  for (int w = NT / 2; w > 0; w >>= 1) {
+    if (tid < w) redm[tid] = fmaxf(redm[tid], redm[tid + w]);
+    __syncthreads();
+  }
+  const float m = redm[0];
+  double lt = 0.0;
+  for (int s = tid; s < a.S; s += NT) {
+    const float ms = a.mpart[s * nrows + row];
+    const float w = ms != -INFINITY ? ldexpf(1.f, (int)(ms - m)) : 0.f;
+    wts[s] = w;
+    if (w != 0.f) lt += (double)w * a.lpart[s * nrows + row];
+  }
+  redl[tid] = lt;
+  __syncthreads();
+  for (int w = NT / 2; w > 0; w >>= 1) {
+    if (tid < w) redl[tid] += redl[tid + w];
+    __syncthreads();
+  }
+  const double l = redl[0];
+  const int c = tid % CPR, sg = tid / CPR;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s = sg; s < a.S; s += SG) {
+    const float w = wts[s];
+    if (w != 0.f) {
+      const f32x4_t os = *reinterpret_cast<const f32x4_t*>(a.opart + (s * nrows + row) * D + c * 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = fmaf(w, os[e], acc[e]);
+    }
+  }
+  redo[sg][c] = acc;
+  __syncthreads();
+  if (sg != 0) return;
+  for (int j = 1; j < SG; ++j) acc += redo[j][c];
+  const float inv = (float)(1.0 / l);
+  const int g = (int)(row / a.R), r = (int)(row - (size_t)g * a.R);
+  const int tok = r / a.G;
+  const int h = g * a.G + (r - tok * a.G);
+  T* out = (T*)a.out + ((size_t)tok * a.Hq + h) * D + c * 4;
+  if constexpr (sizeof(T) == 2) {
+    const u32x2_t v = {(uint32_t)f32_to_bf16(acc[0] * inv) | ((uint32_t)f32_to_bf16(acc[1] * inv) << 16),
+                       (uint32_t)f32_to_bf16(acc[2] * inv) | ((uint32_t)f32_to_bf16(acc[3] * inv) << 16)};
+    *reinterpret_cast<u32x2_t*>(out) = v;
+  } else {
+    *reinterpret_cast<f32x4_t*>(out) = acc * inv;
   }
 }
 
@@ -1387,6 +1636,38 @@ hipError_t launch_select(Dt dt, int d, const SelectArgs& a, hipStream_t s) {
   } else {
     if (d == 64) hipLaunchKernelGGL((select_kernel<F32, 64>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((select_kernel<F32, 128>), grid, block, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+// Waves of the text-phase attention kernel: 4 (bf16) or 2 (fp32, whose
+// staged block would otherwise not leave room for two work-groups per CU).
+constexpr int kDecodeWavesBf16 = 4;
+constexpr int kDecodeWavesF32 = 2;
+int decode_block_keys(Dt dt) { return 32 * (dt == Dt::BF16 ? kDecodeWavesBf16 : kDecodeWavesF32); }
+
+hipError_t launch_decode(Dt dt, int d, const DecodeArgs& a, int row_tiles, hipStream_t s) {
+  const dim3 grid(row_tiles, a.Hkv, a.S);
+  if (dt == Dt::BF16) {
+    const dim3 block(64 * kDecodeWavesBf16);
+    if (d == 64) hipLaunchKernelGGL((decode_attn_kernel<BF16, 64, kDecodeWavesBf16>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((decode_attn_kernel<BF16, 128, kDecodeWavesBf16>), grid, block, 0, s, a);
+  } else {
+    const dim3 block(64 * kDecodeWavesF32);
+    if (d == 64) hipLaunchKernelGGL((decode_attn_kernel<F32, 64, kDecodeWavesF32>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((decode_attn_kernel<F32, 128, kDecodeWavesF32>), grid, block, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_merge(Dt dt, int d, const DecodeMergeArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)((size_t)a.Hkv * a.R)), block(kDecodeMergeThreads);
+  if (dt == Dt::BF16) {
+    if (d == 64) hipLaunchKernelGGL((decode_merge_kernel<BF16, 64>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((decode_merge_kernel<BF16, 128>), grid, block, 0, s, a);
+  } else {
+    if (d == 64) hipLaunchKernelGGL((decode_merge_kernel<F32, 64>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((decode_merge_kernel<F32, 128>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }

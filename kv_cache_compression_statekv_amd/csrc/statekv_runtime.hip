@@ -12,13 +12,16 @@
 //                     moves, as its own rows lie in the other region.  A view
 //                     of the state performs pending moves first.
 //   ppos              [cap] absolute stream positions of those rows.
-//   dk, dv            [max_frames*T][Hkv][d]: the detailed cache D.
+//   dk, dv            [max_frames*T + max_text][Hkv][d]: the detailed cache D
+//                     (row = stream position: the frames, then the text).
 //   qrot              [Hkv][G*T][d]: the frame's rotated queries, rows grouped
 //                     by KV head (row = token*G + head-in-group).
 //   opart/mpart/lpart split-over-keys partials of attention pass 1 (merged
 //                     into O by the select kernel's merge work-groups; the
 //                     score pass forms its row statistics from mpart/lpart).
-//   rope_tab          [max_frames*T][d/2] fp32 (cos, sin) of the scaled angles.
+//   rope_tab          [max_frames*T + max_text][d/2] fp32 (cos, sin) of the
+//                     scaled angles.
+//   dec_opart/mpart/lpart  split-over-keys partials of the text-phase attention.
 //   colsum            [cap] per-key column sums, 64-bit fixed point; the select
 //                     kernel reads and clears them.
 //   scores, keep_flag              scores of the last scored pool.
@@ -51,6 +54,7 @@ struct statekv_state {
   int attn_tiles, attn_splits_max;
   bool never_evicts;
   int score_rsplits_max;
+  int dec_target_wgs;
 
   void* kpool;
   void* vpool;
@@ -73,11 +77,15 @@ struct statekv_state {
   int32_t* evicted_pos;
   double* inv_freq;
   int32_t* nonfinite;
+  float* dec_opart;
+  float* dec_mpart;
+  double* dec_lpart;
 
   float c_hi, c_lo;  // softmax scale times log2(e), as a float pair
 
   int count;         // tokens in the compressed state
   int frames_done;
+  int text_done;     // text tokens appended to D by statekv_decode
 
   // rows of the last frame; moves of its selection not yet performed
   int frame_base;
@@ -120,7 +128,7 @@ void release(statekv_state* s) {
   void* bufs[] = {s->kpool, s->vpool, s->ppos, s->dk, s->dv, s->qrot, s->opart, s->epart, s->mpart,
                   s->lpart, s->rope_tab, s->colsum, s->scores, s->score_pos, s->keep_flag,
                   s->move_dst, s->move_src, s->move_count, s->evicted_pos, s->inv_freq,
-                  s->nonfinite};
+                  s->nonfinite, s->dec_opart, s->dec_mpart, s->dec_lpart};
   for (void* b : bufs)
     if (b) (void)hipFree(b);
   for (auto& ring : s->ev)
@@ -188,6 +196,22 @@ void score_geometry(const statekv_state* s, int P, int* key_blocks, int* rsplits
   *key_blocks = kb;
   *rsplits = ceil_div(s->R, r);
   *rps = r;
+}
+
+// Text phase: t tokens over P keys.  Row tiles of 32 rows per KV head; key
+// splits of whole blocks, enough work-groups for two per CU.
+constexpr int kDecodeTargetWGs = 512;
+
+void decode_geometry(const statekv_state* s, int t, int64_t P, int* tiles, int* splits, int* kps) {
+  const int bk = decode_block_keys(s->dt);
+  const int tl = ceil_div(s->G * t, 32);
+  const int64_t blocks = (P + bk - 1) / bk;
+  int sp = (int)std::max<int64_t>(1, std::min<int64_t>(ceil_div(s->dec_target_wgs, tl * s->Hkv), blocks));
+  sp = std::min(sp, kDecodeMaxSplits);
+  const int64_t k = ((P + sp - 1) / sp + bk - 1) / bk * bk;
+  *tiles = tl;
+  *splits = (int)((P + k - 1) / k);
+  *kps = (int)k;
 }
 
 struct KernelTimer {
@@ -273,8 +297,10 @@ int statekv_create(const statekv_layer_cfg* cfg, int32_t budget_B, float alpha,
   if (c.dtype != STATEKV_DTYPE_BF16 && c.dtype != STATEKV_DTYPE_F32) return STATEKV_EINVAL;
   if (!(c.rope_base > 1.0) || !isfinite(c.rope_base) || c.rope_orig_ctx < 1) return STATEKV_EINVAL;
   if (!(alpha >= 1.0f) || !isfinite(alpha)) return STATEKV_EINVAL;
-  const int64_t positions = (int64_t)c.max_frames * c.tokens_per_frame;
-  if (positions > INT32_MAX) return STATEKV_EINVAL;
+  if (c.max_text < 0) return STATEKV_EINVAL;
+  const int64_t positions = (int64_t)c.max_frames * c.tokens_per_frame;   // frame tokens
+  const int64_t all_positions = positions + c.max_text;                   // rows of D
+  if (all_positions > INT32_MAX) return STATEKV_EINVAL;
   // The selection runs in one work-group over at most kMaxPool candidates; a
   // budget that holds every token of the stream never selects (full
   // attention) and has no such limit.
@@ -303,6 +329,7 @@ int statekv_create(const statekv_layer_cfg* cfg, int32_t budget_B, float alpha,
   s->cap = s->never_evicts ? c.max_frames * c.tokens_per_frame : budget_B + 2 * s->T;
   s->stream = nullptr;
   s->score_frame = -1;
+  s->dec_target_wgs = kDecodeTargetWGs;
 
   int rc = check(hipGetDevice(&s->device));
   if (rc) {
@@ -319,6 +346,10 @@ int statekv_create(const statekv_layer_cfg* cfg, int32_t budget_B, float alpha,
     const int v = atoi(e);
     if (v >= 1) s->attn_splits_max = std::min(v, s->attn_splits_max);
   }
+  if (const char* e = getenv("STATEKV_DECODE_WGS")) {
+    const int v = atoi(e);
+    if (v >= 1) s->dec_target_wgs = v;
+  }
   if (const char* e = getenv("STATEKV_SCORE_RSPLITS")) {
     const int v = atoi(e);
     if (v >= 1)
@@ -327,7 +358,15 @@ int statekv_create(const statekv_layer_cfg* cfg, int32_t budget_B, float alpha,
 
   const size_t E = s->esize, D = s->D;
   const size_t pool_bytes = (size_t)s->Hkv * s->cap * D * E;
-  const size_t det_bytes = (size_t)positions * s->Hkv * D * E;
+  const size_t det_bytes = (size_t)all_positions * s->Hkv * D * E;
+  // Text-phase partials: the largest split count times rows over t = 1..T.
+  size_t dec_rows = 0;
+  if (c.max_text > 0)
+    for (int t = 1; t <= s->T; ++t) {
+      int tl, sp, kp;
+      decode_geometry(s, t, all_positions, &tl, &sp, &kp);
+      if (sp > 1) dec_rows = std::max(dec_rows, (size_t)sp * s->Hkv * s->G * t);
+    }
   const size_t rows_all = (size_t)s->Hkv * s->R;
   const size_t S = s->attn_splits_max;
   rc = alloc(&s->kpool, pool_bytes);
@@ -341,7 +380,7 @@ int statekv_create(const statekv_layer_cfg* cfg, int32_t budget_B, float alpha,
   const size_t stat_rows = (rows_all + 31) / 32 * 32;   // whole groups of 32 rows
   if (!rc) rc = alloc(&s->mpart, stat_rows * S * sizeof(float));
   if (!rc) rc = alloc(&s->lpart, stat_rows * S * sizeof(double));
-  if (!rc) rc = alloc(&s->rope_tab, (size_t)positions * (D / 2) * sizeof(float2));
+  if (!rc) rc = alloc(&s->rope_tab, (size_t)all_positions * (D / 2) * sizeof(float2));
   if (!rc) rc = alloc(&s->colsum, (size_t)s->cap * sizeof(unsigned long long));
   if (!rc) rc = alloc(&s->scores, (size_t)s->cap * sizeof(float));
   if (!rc) rc = alloc(&s->score_pos, (size_t)s->cap * sizeof(int32_t));
@@ -352,6 +391,9 @@ int statekv_create(const statekv_layer_cfg* cfg, int32_t budget_B, float alpha,
   if (!rc) rc = alloc(&s->evicted_pos, (size_t)s->B * sizeof(int32_t));
   if (!rc) rc = alloc(&s->inv_freq, D / 2 * sizeof(double));
   if (!rc) rc = alloc(&s->nonfinite, sizeof(int32_t));
+  if (!rc) rc = alloc(&s->dec_opart, dec_rows * D * sizeof(float));
+  if (!rc) rc = alloc(&s->dec_mpart, dec_rows * sizeof(float));
+  if (!rc) rc = alloc(&s->dec_lpart, dec_rows * sizeof(double));
   if (!rc) {
     double table[64];
     scaled_inv_freq(s->D, c.rope_base, (double)alpha, c.rope_orig_ctx, table);
@@ -361,7 +403,7 @@ int statekv_create(const statekv_layer_cfg* cfg, int32_t budget_B, float alpha,
     RopeTableArgs ta{};
     ta.inv_freq = s->inv_freq;
     ta.table = s->rope_tab;
-    ta.npos = (int32_t)positions;
+    ta.npos = (int32_t)all_positions;
     ta.half = s->D / 2;
     rc = check(launch_rope_table(ta, nullptr));
   }
@@ -410,7 +452,7 @@ int statekv_set_flags(statekv_state* s, uint32_t flags) {
 int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const void* V,
                           int32_t n, void* O) {
   if (!s || !Q || !K || !V || !O) return STATEKV_EINVAL;
-  if (n != s->frames_done) return STATEKV_EORDER;
+  if (n != s->frames_done || s->text_done > 0) return STATEKV_EORDER;
   if (n >= s->cfg.max_frames) return STATEKV_ECAPACITY;
   int rc = check(hipSetDevice(s->device));
   if (rc) return rc;
@@ -441,7 +483,7 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const 
     a.dk = s->dk;
     a.dv = s->dv;
     a.nonfinite = s->nonfinite;
-    a.n = n;
+    a.pos0 = n * s->T;
     a.T = s->T;
     a.Hq = s->Hq;
     a.Hkv = s->Hkv;
@@ -557,6 +599,85 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const 
   return STATEKV_OK;
 }
 
+int statekv_decode(statekv_state* s, const void* Q, const void* K, const void* V, int32_t t,
+                   void* O) {
+  if (!s || !Q || !K || !V || !O) return STATEKV_EINVAL;
+  if (t < 1 || t > s->T) return STATEKV_EINVAL;
+  if ((int64_t)s->text_done + t > s->cfg.max_text) return STATEKV_ECAPACITY;
+  int rc = check(hipSetDevice(s->device));
+  if (rc) return rc;
+  const hipStream_t st = s->stream;
+  const int P0 = s->frames_done * s->T + s->text_done;   // keys before the text chunk
+  const int P = P0 + t;
+  {
+    KernelTimer tm(s, STATEKV_K_DEC_ROPE);
+    RopeArgs a{};
+    a.q = Q;
+    a.k = K;
+    a.v = V;
+    a.table = s->rope_tab;
+    a.qrot = s->qrot;
+    a.dk = s->dk;
+    a.dv = s->dv;
+    a.nonfinite = s->nonfinite;
+    a.pos0 = P0;
+    a.T = t;
+    a.Hq = s->Hq;
+    a.Hkv = s->Hkv;
+    a.G = s->G;
+    a.cap = s->cap;
+    a.rope_blocks = rope_blocks(t);
+    a.mv = moves_args(s, 0);
+    rc = check(launch_rope(s->dt, s->D, a, st));
+    tm.done();
+    if (rc) return rc;
+  }
+  int tiles, splits, kps;
+  decode_geometry(s, t, P, &tiles, &splits, &kps);
+  {
+    KernelTimer tm(s, STATEKV_K_DEC_ATTN);
+    DecodeArgs a{};
+    a.qrot = s->qrot;
+    a.dk = s->dk;
+    a.dv = s->dv;
+    a.opart = s->dec_opart;
+    a.mpart = s->dec_mpart;
+    a.lpart = s->dec_lpart;
+    a.out = O;
+    a.c_hi = s->c_hi;
+    a.R = s->G * t;
+    a.G = s->G;
+    a.Hq = s->Hq;
+    a.Hkv = s->Hkv;
+    a.P = P;
+    a.k0 = P0;
+    a.kps = kps;
+    a.S = splits;
+    rc = check(launch_decode(s->dt, s->D, a, tiles, st));
+    tm.done();
+    if (rc) return rc;
+  }
+  if (splits > 1) {
+    KernelTimer tm(s, STATEKV_K_DEC_MERGE);
+    DecodeMergeArgs a{};
+    a.opart = s->dec_opart;
+    a.mpart = s->dec_mpart;
+    a.lpart = s->dec_lpart;
+    a.out = O;
+    a.R = s->G * t;
+    a.G = s->G;
+    a.Hq = s->Hq;
+    a.Hkv = s->Hkv;
+    a.S = splits;
+    rc = check(launch_decode_merge(s->dt, s->D, a, st));
+    tm.done();
+    if (rc) return rc;
+  }
+  s->text_done += t;
+  s->ev_slot = (s->ev_slot + 1) % statekv_state::kRing;
+  return STATEKV_OK;
+}
+
 int statekv_compressed_view(const statekv_state* s, statekv_view* out) {
   if (!s || !out) return STATEKV_EINVAL;
   int rc = check(hipSetDevice(s->device));
@@ -587,7 +708,7 @@ int statekv_detailed_view(const statekv_state* s, statekv_view* out) {
   out->k = s->dk;
   out->v = s->dv;
   out->pos = nullptr;
-  out->count = (int64_t)s->frames_done * s->T;
+  out->count = (int64_t)s->frames_done * s->T + s->text_done;
   out->head_stride = s->D;
   out->token_stride = (int64_t)s->Hkv * s->D;
   out->n_kv_heads = s->Hkv;

@@ -30,7 +30,7 @@ import numpy as np
 
 ROOT_SEED = 20261202
 
-TAG_Q, TAG_K, TAG_V, TAG_SINK, TAG_BURST = 0, 1, 2, 3, 4
+TAG_Q, TAG_K, TAG_V, TAG_SINK, TAG_BURST, TAG_TEXT = 0, 1, 2, 3, 4, 5
 
 
 @dataclasses.dataclass(frozen=True)
@@ -173,6 +173,20 @@ class FrameStream:
         if cfg.dtype == "bf16":
             q, k, v = round_to_bf16(q), round_to_bf16(k), round_to_bf16(v)
         return q, k, v
+
+
+def text_tokens(cfg: StreamConfig, first_pos: int, t: int, layer: int = 0):
+    """(Q, K, V) of t text tokens starting at stream position first_pos (the
+    text phase after the frames): N(0, 1) draws, [t][H][d] fp32 arrays holding
+    storage values, seeded by (config, layer, first_pos + 1, text tag)."""
+    Hq, Hkv, d = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    rng = _rng(cfg, layer, first_pos + 1, TAG_TEXT)
+    q = rng.standard_normal((t, Hq, d), dtype=np.float32)
+    k = rng.standard_normal((t, Hkv, d), dtype=np.float32)
+    v = rng.standard_normal((t, Hkv, d), dtype=np.float32)
+    if cfg.dtype == "bf16":
+        q, k, v = round_to_bf16(q), round_to_bf16(k), round_to_bf16(v)
+    return q, k, v
 
 
 def stream_tokens(cfg: StreamConfig, n_frames: int, layer: int = 0):

@@ -26,12 +26,16 @@ even, to the storage dtype ("bf16" or "f32").  Scores are fp64 sums, rounded
 to fp32 only for the Top-B decision (the precision the GPU takes it in).
 Matrix products use numpy's float64 matmul as a library primitive.
 
-Parity: RoPE (alpha = 1), attention, scores, selection and the state update
-are pinned by tests (textbook complex-form RoPE, relative-position invariance,
-reduction to causal scaled-dot-product attention, score sum = 1, brute force on
-tiny inputs, tie and subset invariants).  The YaRN frequency ramp and logit
-temperature used for alpha > 1 are not on the pages: parity unpinned beyond
-the invariance checks.
+The text phase (decode_step) attends text tokens over the whole detailed cache
+D, continuing the virtual positions.
+
+Parity: RoPE (alpha = 1), attention, scores, selection, the state update and
+the text phase are pinned by tests (textbook complex-form RoPE,
+relative-position invariance, reduction to causal scaled-dot-product attention
+for frames and for the text after an evicting stream, score sum = 1, brute
+force on tiny inputs, tie and subset invariants).  The YaRN frequency ramp and
+logit temperature used for alpha > 1 are not on the pages: parity unpinned
+beyond the invariance checks.
 """
 from __future__ import annotations
 
@@ -276,17 +280,76 @@ def frame_step(cfg: LayerConfig, state: CompressedState, Q, K, V, n: int) -> Ste
                       scores=scores, scores32=scores32, keep=keep, state=new_state)
 
 
+# --------------------------------------------------------------------------
+# The text phase over the detailed cache (整体框架, 关键设计 1 and 3)
+# --------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class DecodeResult:
+    Q_rot: np.ndarray        # [t][Hq][d] storage values
+    K_rot: np.ndarray        # [t][Hkv][d] storage values (appended to D)
+    V: np.ndarray            # [t][Hkv][d] (appended to D)
+    positions: np.ndarray    # [t] stream positions of the text tokens
+    O_exact: np.ndarray      # [t][Hq][d] float64 attention output
+    O: np.ndarray            # [t][Hq][d] rounded to the storage dtype
+
+
+def decode_step(cfg: LayerConfig, D_K, D_V, Q, K, V) -> DecodeResult:
+    """t text tokens attend over the whole detailed cache D and over themselves.
+
+    Once the frames are processed, generation mounts the full detailed state D
+    as its KV cache (整体框架; 关键设计 1).  The text continues the virtual
+    length: with P0 rows in D (every frame token, then earlier text), text
+    token i sits at position P0 + i and is rotated with the same fixed table
+    (关键设计 3).  It sees every D row and the text tokens up to itself.
+    D_K, D_V: [P0][Hkv][d] storage values in stream order (row = position);
+    Q: [t][Hq][d], K and V: [t][Hkv][d].
+    """
+    Hq, Hkv, d = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    G = cfg.group
+    D_K = np.asarray(D_K, dtype=np.float64).reshape(-1, Hkv, d)
+    D_V = np.asarray(D_V, dtype=np.float64).reshape(-1, Hkv, d)
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    t = Q.shape[0]
+    assert Q.shape == (t, Hq, d) and K.shape == (t, Hkv, d) and V.shape == (t, Hkv, d)
+    P0 = D_K.shape[0]
+    positions = P0 + np.arange(t, dtype=np.int64)
+    inv_freq = yarn_inv_freq(d, cfg.rope_base, cfg.alpha, cfg.rope_orig_ctx)
+    cos, sin = rope_cos_sin(positions, inv_freq)
+    Q_rot = rope_rotate(Q, cos, sin, cfg.dtype)
+    K_rot = rope_rotate(K, cos, sin, cfg.dtype)
+    keys = np.concatenate([D_K, K_rot], axis=0)          # [P0+t][Hkv][d], row = position
+    vals = np.concatenate([D_V, V], axis=0)
+    key_pos = np.arange(P0 + t, dtype=np.int64)
+    visible = key_pos[None, :] <= positions[:, None]      # [t][P0+t]
+    sigma = yarn_logit_scale(d, cfg.alpha)
+    O_exact = np.zeros((t, Hq, d), dtype=np.float64)
+    for h in range(Hq):
+        g = h // G
+        logits = sigma * (Q_rot[:, h, :] @ keys[:, g, :].T)
+        logits = np.where(visible, logits, -np.inf)
+        w = np.exp(logits - logits.max(axis=1, keepdims=True))
+        O_exact[:, h, :] = (w / w.sum(axis=1, keepdims=True)) @ vals[:, g, :]
+    return DecodeResult(Q_rot=Q_rot, K_rot=K_rot, V=V.copy(), positions=positions,
+                        O_exact=O_exact, O=round_storage(O_exact, cfg.dtype))
+
+
 class OracleStream:
-    """Runs the oracle over consecutive frames and keeps the detailed cache D."""
+    """Runs the oracle over consecutive frames, then text tokens, and keeps the
+    detailed cache D."""
 
     def __init__(self, cfg: LayerConfig):
         self.cfg = cfg
         self.state = CompressedState.empty(cfg)
         self.frames_done = 0
+        self.text_done = 0
         self.D_K = []
         self.D_V = []
 
     def step(self, Q, K, V) -> StepResult:
+        assert self.text_done == 0, "frames come before the text"
         res = frame_step(self.cfg, self.state, Q, K, V, self.frames_done)
         self.state = res.state
         self.D_K.append(res.K_rot)   # detailed state: every frame's rotated keys
@@ -294,6 +357,18 @@ class OracleStream:
         self.frames_done += 1
         return res
 
+    def decode(self, Q, K, V) -> DecodeResult:
+        """Text tokens after everything so far, attending over the whole of D."""
+        D_K, D_V = self.detailed()
+        res = decode_step(self.cfg, D_K, D_V, Q, K, V)
+        self.D_K.append(res.K_rot)
+        self.D_V.append(res.V)
+        self.text_done += res.positions.size
+        return res
+
     def detailed(self):
-        """D as ([n*T][Hkv][d], [n*T][Hkv][d])."""
+        """D as ([rows][Hkv][d], [rows][Hkv][d]), rows = n*T + text tokens."""
+        if not self.D_K:
+            z = np.zeros((0, self.cfg.n_kv_heads, self.cfg.head_dim), dtype=np.float64)
+            return z, z.copy()
         return np.concatenate(self.D_K, axis=0), np.concatenate(self.D_V, axis=0)

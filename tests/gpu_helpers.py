@@ -24,11 +24,12 @@ def oracle_cfg(wl: StreamConfig) -> LayerConfig:
                        rope_base=wl.rope_base, alpha=wl.alpha, rope_orig_ctx=wl.rope_orig_ctx)
 
 
-def make_state(wl: StreamConfig, max_frames: int | None = None) -> skv.StateKV:
+def make_state(wl: StreamConfig, max_frames: int | None = None, max_text: int = 0) -> skv.StateKV:
     return skv.StateKV(n_q_heads=wl.n_q_heads, n_kv_heads=wl.n_kv_heads, head_dim=wl.head_dim,
                        tokens_per_frame=wl.tokens_per_frame,
                        max_frames=max_frames or wl.n_frames, budget=wl.budget, alpha=wl.alpha,
-                       dtype=wl.dtype, rope_base=wl.rope_base, rope_orig_ctx=wl.rope_orig_ctx)
+                       dtype=wl.dtype, rope_base=wl.rope_base, rope_orig_ctx=wl.rope_orig_ctx,
+                       max_text=max_text)
 
 
 def to_device(x: np.ndarray, dtype: str) -> torch.Tensor:

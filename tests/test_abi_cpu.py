@@ -11,8 +11,8 @@ import kv_cache_compression_statekv_amd as skv
 def test_every_declared_function_is_exported():
     lib = skv.load_library()
     names = skv.declared_functions()
-    assert {"statekv_create", "statekv_prefill_frame", "statekv_compressed_view",
-            "statekv_detailed_view", "statekv_destroy"} <= set(names)
+    assert {"statekv_create", "statekv_prefill_frame", "statekv_decode",
+            "statekv_compressed_view", "statekv_detailed_view", "statekv_destroy"} <= set(names)
     for name in names:
         assert hasattr(lib, name), name
 
@@ -25,7 +25,7 @@ def test_error_strings():
 
 def _cfg(**kw):
     base = dict(n_q_heads=4, n_kv_heads=2, head_dim=64, tokens_per_frame=16, max_frames=4,
-                dtype=skv.DTYPE_BF16, rope_base=1e6, rope_orig_ctx=32768)
+                dtype=skv.DTYPE_BF16, rope_base=1e6, rope_orig_ctx=32768, max_text=0)
     base.update(kw)
     return skv.LayerCfg(**base)
 
@@ -34,6 +34,9 @@ def _cfg(**kw):
     dict(n_q_heads=0), dict(n_kv_heads=0), dict(n_q_heads=6, n_kv_heads=4),
     dict(head_dim=96), dict(head_dim=32), dict(tokens_per_frame=0), dict(max_frames=0),
     dict(dtype=7), dict(rope_base=1.0), dict(rope_base=math.inf), dict(rope_orig_ctx=0),
+    dict(max_text=-1),
+    # frame tokens fit 32-bit positions, frames plus text do not
+    dict(tokens_per_frame=1 << 16, max_frames=(1 << 15) - 1, max_text=1 << 16),
 ])
 def test_create_rejects_bad_config(bad):
     lib = skv.load_library()
@@ -67,6 +70,16 @@ def test_create_accepts_full_attention_budget_beyond_pool_limit():
         lib.statekv_destroy(h)
 
 
+def test_layer_cfg_matches_the_header():
+    """The ctypes mirror of statekv_layer_cfg has the header's fields, in order."""
+    import re
+    text = open(skv.HEADER).read()
+    body = re.search(r"typedef struct statekv_layer_cfg \{(.*?)\} statekv_layer_cfg;", text, re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    fields = re.findall(r"\b(\w+)\s*;", body)
+    assert fields == [f[0] for f in skv.LayerCfg._fields_]
+
+
 def test_null_arguments_are_rejected():
     lib = skv.load_library()
     h = ctypes.c_void_p()
@@ -74,6 +87,7 @@ def test_null_arguments_are_rejected():
     cfg = _cfg()
     assert lib.statekv_create(ctypes.byref(cfg), 64, 1.0, None) == skv.STATEKV_EINVAL
     assert lib.statekv_prefill_frame(None, None, None, None, 0, None) == skv.STATEKV_EINVAL
+    assert lib.statekv_decode(None, None, None, None, 1, None) == skv.STATEKV_EINVAL
     v = skv.View()
     assert lib.statekv_compressed_view(None, ctypes.byref(v)) == skv.STATEKV_EINVAL
     assert lib.statekv_detailed_view(None, ctypes.byref(v)) == skv.STATEKV_EINVAL

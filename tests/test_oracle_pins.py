@@ -10,7 +10,10 @@ Each pin is chosen so that a plausible slip in the oracle fails it:
   * a stream with B >= N*T vs full causal attention over all N*T tokens
     (virtual positions nT + i, frame indexing, state carry-over);
   * scores are a probability distribution over the pool (denominator Hq*T);
-  * selection with ties keeps the older token.
+  * selection with ties keeps the older token;
+  * the text phase after an evicting stream vs the last rows of one causal
+    attention over every frame token and the text (D keeps what C evicted;
+    positions continue at N*T; chunking does not matter).
 Brute-force comparisons on tiny inputs live in test_oracle_bruteforce.py.
 """
 from fractions import Fraction
@@ -21,7 +24,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import (CompressedState, LayerConfig, OracleStream, frame_step,
+from oracle import (CompressedState, LayerConfig, OracleStream, decode_step, frame_step,
                     round_f64_to_bf16, rope_cos_sin, rope_inv_freq, rope_rotate,
                     select_top_b, yarn_inv_freq, yarn_logit_scale)
 
@@ -222,6 +225,69 @@ def test_recent_window_stream_is_banded_causal_attention():
     visible = (p[None, :] <= p[:, None]) & (p[None, :] >= lo[:, None])
     want = _sdpa_masked(q_rot, k_rot, V, Hq, Hkv, visible)
     assert np.max(np.abs(np.concatenate(outs) - want)) < 1e-5
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_text_phase_is_the_tail_of_full_causal_attention(dtype):
+    """After N frames with eviction (B < N*T), text tokens decoded in chunks of
+    3, 1 and 2 equal the last 6 rows of one causal attention over all N*T frame
+    tokens followed by the 6 text tokens, at positions 0..N*T+5: the text sees
+    the detailed cache, not the compressed state."""
+    T, N, B, Hq, Hkv, d = 7, 5, 9, 6, 2, 32
+    cfg = LayerConfig(n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, tokens_per_frame=T,
+                      budget=B, dtype=dtype, rope_base=1e4)
+    rng = np.random.default_rng(21)
+    frames = [_rand_frame(rng, T, Hq, Hkv, d) for _ in range(N)]
+    text = _rand_frame(rng, 6, Hq, Hkv, d)
+    if dtype == "bf16":
+        frames = [tuple(round_f64_to_bf16(x) for x in f) for f in frames]
+        text = tuple(round_f64_to_bf16(x) for x in text)
+    stream = OracleStream(cfg)
+    for f in frames:
+        stream.step(*f)
+    assert stream.state.count == B                     # C evicted; D holds everything
+    outs = []
+    for lo, hi in [(0, 3), (3, 4), (4, 6)]:
+        res = stream.decode(*(x[lo:hi] for x in text))
+        assert res.positions.tolist() == list(range(N * T + lo, N * T + hi))
+        outs.append(res.O_exact)
+    L = N * T + 6
+    Q = np.concatenate([f[0] for f in frames] + [text[0]])
+    K = np.concatenate([f[1] for f in frames] + [text[1]])
+    V = np.concatenate([f[2] for f in frames] + [text[2]])
+    theta = 10000.0 ** (-np.arange(d // 2) * 2.0 / d)
+    q_rot = _textbook_rope(Q, np.arange(L), theta)
+    k_rot = _textbook_rope(K, np.arange(L), theta)
+    if dtype == "bf16":
+        q_rot, k_rot = round_f64_to_bf16(q_rot), round_f64_to_bf16(k_rot)
+    else:
+        q_rot = q_rot.astype(np.float32).astype(np.float64)
+        k_rot = k_rot.astype(np.float32).astype(np.float64)
+    want = _sdpa_causal(q_rot, k_rot, V, Hq, Hkv)[N * T:]
+    tol = 1e-5 if dtype == "f32" else 2e-2
+    assert np.max(np.abs(np.concatenate(outs) - want)) < tol
+    D_K, _ = stream.detailed()
+    assert D_K.shape[0] == L
+
+
+def test_text_phase_chunking_is_invisible():
+    """Decoding t tokens at once equals decoding them one by one (causal mask
+    inside the chunk, positions advancing by one)."""
+    cfg = LayerConfig(n_q_heads=4, n_kv_heads=1, head_dim=64, tokens_per_frame=5,
+                      budget=4, dtype="f32", rope_base=1e6, alpha=4.0)
+    rng = np.random.default_rng(22)
+    DK = rng.standard_normal((23, 1, 64)).astype(np.float32).astype(np.float64)
+    DV = rng.standard_normal((23, 1, 64)).astype(np.float32).astype(np.float64)
+    Q, K, V = _rand_frame(rng, 4, 4, 1, 64)
+    whole = decode_step(cfg, DK, DV, Q, K, V)
+    dk, dv, rows = DK, DV, []
+    for i in range(4):
+        r = decode_step(cfg, dk, dv, Q[i:i + 1], K[i:i + 1], V[i:i + 1])
+        dk = np.concatenate([dk, r.K_rot])
+        dv = np.concatenate([dv, r.V])
+        rows.append(r.O_exact)
+    assert np.array_equal(whole.K_rot, np.concatenate([dk[23:]]))
+    assert np.max(np.abs(np.concatenate(rows) - whole.O_exact)) < 1e-12
 
 
 def test_scores_are_a_distribution_over_the_pool():
