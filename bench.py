@@ -57,6 +57,14 @@ def parse_args():
                    help="also run the quadratic comparison over the workload's full stream: "
                         "one-shot full causal attention over all N*T tokens, full attention "
                         "streamed frame by frame (no eviction), and StateKV streamed")
+    p.add_argument("--decode-tokens", type=int, default=0,
+                   help="also time the text phase: after --decode-frames frames of the workload "
+                        "(default: its full stream), a --decode-prompt-token chunk and then this "
+                        "many single-token steps, each attending over the whole detailed cache")
+    p.add_argument("--decode-frames", type=int, default=0)
+    p.add_argument("--decode-prompt", type=int, default=64)
+    p.add_argument("--decode-only", action="store_true",
+                   help="skip the frame-step measurement (only with --decode-tokens)")
     p.add_argument("--copy-calibration-mb", type=int, default=0,
                    help="first run one device-to-device copy of this many MiB (a kernel of known "
                         "traffic that rocprofv3 counters are scaled by)")
@@ -256,6 +264,86 @@ def budget_sweep(skv, torch, np, wl, budgets, n_frames):
             "full_causal_tflop": round(full_flops / 1e12, 3), "budgets": out}
 
 
+def decode_bench(skv, torch, np, wl, n_frames, n_tokens, prompt, distinct=8):
+    """Text phase after a stream of n_frames frames (one layer): a prompt chunk
+    of `prompt` tokens, then n_tokens single-token steps, each attending over
+    every row of D.  Frames cycle through `distinct` seeded frames (positions,
+    so rotated keys, still advance)."""
+    from kv_cache_compression_statekv_amd.workload import FrameStream, text_tokens
+
+    T, Hq, Hkv, d, B = wl.tokens_per_frame, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.budget
+    tdtype = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    esize = 2 if wl.dtype == "bf16" else 4
+    prompt = max(1, min(prompt, T))
+    fs = FrameStream(wl, 0)
+    frames = [tuple(torch.from_numpy(x).to(tdtype).cuda() for x in fs.frame(n))
+              for n in range(min(distinct, n_frames))]
+    P0 = n_frames * T
+    n_text = prompt + 2 * n_tokens
+    text = [torch.from_numpy(x).to(tdtype).cuda() for x in text_tokens(wl, P0, n_text)]
+    st = skv.StateKV(n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, tokens_per_frame=T,
+                     max_frames=n_frames, budget=B, alpha=wl.alpha, dtype=wl.dtype,
+                     rope_base=wl.rope_base, rope_orig_ctx=wl.rope_orig_ctx, max_text=n_text)
+    o = torch.empty((T, Hq, d), dtype=tdtype, device="cuda")
+    for n in range(n_frames):
+        st.prefill_frame(*frames[n % len(frames)], n, out=o)
+    stream = torch.cuda.current_stream()
+    lib, h = st._lib, st._h
+    row = [(x.data_ptr(), x[0].numel() * x.element_size()) for x in text]
+    optr = o.data_ptr()
+
+    def dec(i, t):
+        ptr = [p + i * rb for p, rb in row]
+        rc = lib.statekv_decode(h, ptr[0], ptr[1], ptr[2], t, optr)
+        if rc:
+            raise skv.StateKVError(rc, "statekv_decode")
+
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    dec(0, prompt)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    prompt_us = e0.elapsed_time(e1) * 1e3
+
+    def token_pass(first):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_tokens + 1)]
+        evs[0].record(stream)
+        for i in range(n_tokens):
+            dec(first + i, 1)
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        return np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(n_tokens)]) * 1e3
+
+    lat = token_pass(prompt)
+    st.set_flags(skv.FLAG_KERNEL_TIMING)
+    st.kernel_times(reset=True)
+    token_pass(prompt + n_tokens)
+    kernels = {}
+    for name, (ms, cnt) in st.kernel_times().items():
+        if name.startswith("decode") and cnt:
+            kernels[name] = {"avg_us": round(1e3 * ms / cnt, 2), "launches": cnt}
+    st.close()
+    # Bytes the attention kernel must read per token: K and V of every visible
+    # key (the context, the prompt and the earlier generated tokens).
+    keys = P0 + prompt + n_tokens + (n_tokens - 1) / 2.0
+    kv_bytes = keys * Hkv * d * esize * 2
+    res = {"frames": n_frames, "frame_tokens": P0, "prompt_tokens": prompt,
+           "prompt_us": round(prompt_us, 2), "token_steps": n_tokens,
+           "token_us_median": round(float(np.median(lat)), 2),
+           "token_us_p99": round(float(np.quantile(lat, 0.99)), 2),
+           "tokens_per_s": round(1e6 / float(np.median(lat)), 1),
+           "kv_bytes_per_token": int(kv_bytes), "kernels": kernels}
+    t_attn = kernels.get("decode_attn", {}).get("avg_us")
+    if t_attn:
+        gbs = kv_bytes / (t_attn * 1e-6) / 1e9
+        res["roofline_decode_attn"] = {"bound": "hbm", "achieved": round(gbs, 1),
+                                       "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                       "frac": round(gbs / PEAK_HBM_GBS, 4)}
+        res["step_hbm_frac"] = round(kv_bytes / (float(np.median(lat)) * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
+    return res
+
+
 def main():
     args = parse_args()
     if args.summarize_pmc:
@@ -276,6 +364,16 @@ def main():
     from kv_cache_compression_statekv_amd.workload import CONFIGS, FrameStream
 
     wl = CONFIGS[args.workload]
+    if args.decode_only:
+        if args.decode_tokens <= 0:
+            print("--decode-only needs --decode-tokens", file=sys.stderr)
+            sys.exit(2)
+        torch.cuda.set_device(0)
+        rec = {"workload": wl.name, "decode": decode_bench(
+            skv, torch, np, wl, args.decode_frames or wl.n_frames, args.decode_tokens,
+            args.decode_prompt)}
+        print(json.dumps(rec))
+        return
     T, Hq, Hkv, d, B = wl.tokens_per_frame, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.budget
     fill = math.ceil(B / T)
     W = max(args.warmup, fill)
@@ -378,6 +476,10 @@ def main():
         }
 
     quadratic = quadratic_comparison(skv, torch, np, wl) if args.quadratic else None
+    decode = None
+    if args.decode_tokens > 0:
+        decode = decode_bench(skv, torch, np, wl, args.decode_frames or wl.n_frames,
+                              args.decode_tokens, args.decode_prompt)
     b_sweep = None
     if args.b_sweep:
         b_sweep = budget_sweep(skv, torch, np, wl, [int(b) for b in args.b_sweep.split(",")],
@@ -440,6 +542,7 @@ def main():
         **extra,
         **({"quadratic": quadratic} if quadratic else {}),
         **({"b_sweep": b_sweep} if b_sweep else {}),
+        **({"decode": decode} if decode else {}),
         "attn_fwd_algorithmic_gflop": round(attn_flops / 1e9, 4),
         "executed_gflop_attention_passes": round(executed_flops / 1e9, 4),
     }

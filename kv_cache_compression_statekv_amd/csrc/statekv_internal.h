@@ -86,6 +86,10 @@ struct AttnArgs {
   float c_hi;             // sigma * log2(e) rounded to fp32
   int32_t R, G, cap, P, k0, foff, kps, Hkv;
   int32_t ss;             // split stride of the statistics (maximum splits)
+  // Element strides of the key / value rows: between KV heads and between
+  // rows.  The pool is [Hkv][cap][d] (cap*d, d); the detailed cache, read by
+  // text chunks, is [positions][Hkv][d] (d, Hkv*d).
+  int64_t kv_hs, kv_rs;
 };
 
 // Score pass: one work-group per (key block, KV head, row split).
@@ -99,13 +103,20 @@ struct ScoreArgs {
   int32_t R, G, cap, P, k0, foff, rps, Hkv, S, ss;
 };
 
-// Text-phase attention over the detailed cache D (token-major rows): one
-// work-group per (tile of 32 query rows, KV head, key split).  Its NW waves
-// take the 32-key sub-tiles of every block of 32*NW keys and are merged in
-// LDS at the end.  With one split the work-group writes O; otherwise it
-// leaves (m_s, l_s, O_s) for the merge kernel.
+// Text-phase attention over the detailed cache D (token-major rows) for at
+// most 32 query rows per KV head: one work-group per (KV head, key split).
+// Its NW waves take the 32-key sub-tiles of every block of 32*NW keys and are
+// merged in LDS at the end.  With one split the work-group writes O;
+// otherwise it leaves (m_s, l_s, O_s) for the merge kernel.
 struct DecodeArgs {
-  const void* qrot;       // [Hkv][R][d], row r = token*G + head-in-group
+  // The text tokens' projected inputs: the kernel rotates queries and keys
+  // itself (R = G*t <= 32 rows per KV head, one row tile) and appends the
+  // rotated keys and the values to D.
+  const void* q;          // [t][Hq][d]
+  const void* k;          // [t][Hkv][d]
+  const void* v;          // [t][Hkv][d]
+  const float2* table;    // [positions][d/2]
+  int32_t* nonfinite;
   const void* dk;         // [positions][Hkv][d]
   const void* dv;         // [positions][Hkv][d]
   float* opart;           // [S][Hkv][R][d] unnormalised partial outputs (S > 1)
@@ -165,7 +176,7 @@ hipError_t launch_select(Dt dt, int d, const SelectArgs& a, hipStream_t s);
 hipError_t launch_moves(const MovesArgs& a, hipStream_t s);
 // Keys per block of the text-phase attention kernel.
 int decode_block_keys(Dt dt);
-hipError_t launch_decode(Dt dt, int d, const DecodeArgs& a, int row_tiles, hipStream_t s);
+hipError_t launch_decode(Dt dt, int d, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_merge(Dt dt, int d, const DecodeMergeArgs& a, hipStream_t s);
 // Positions of a scored pool of P candidates: the position of its row, or
 // for an evicted slot below B that a move has since filled, the saved one.

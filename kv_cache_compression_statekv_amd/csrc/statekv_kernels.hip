@@ -16,6 +16,11 @@
 //                       the attention output.
 //   moves_kernel        关键设计 2: build C_n from the kept candidates (kept
 //                       frame rows move into the evicted slots).
+//   decode_attn_kernel  整体框架 / 关键设计 1, 3: after the frames, text
+//   decode_merge_kernel tokens attend over the whole detailed cache D at the
+//                       continuing virtual positions (split over keys, then
+//                       merged).  Longer text chunks reuse the RoPE kernel,
+//                       attn_fwd_kernel (with D's strides) and the merge.
 //
 // Matrix-core tiles use v_mfma_f32_32x32x16_bf16 (bf16 storage) or
 // v_mfma_f32_32x32x2_f32 (fp32 storage).  Accumulator layout of a 32x32 tile:
@@ -56,6 +61,12 @@ template <> struct Mma<BF16> {
     u32x4_t z = {0u, 0u, 0u, 0u};
     return __builtin_bit_cast(bf16x8_t, z);
   }
+  static __device__ __forceinline__ Frag from(const uint16_t* y) {
+    u32x4_t v;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = (uint32_t)y[2 * j] | ((uint32_t)y[2 * j + 1] << 16);
+    return __builtin_bit_cast(bf16x8_t, v);
+  }
 };
 
 template <> struct Mma<F32> {
@@ -67,6 +78,7 @@ template <> struct Mma<F32> {
   }
   static __device__ __forceinline__ Frag ld(const float* p) { return *p; }
   static __device__ __forceinline__ Frag zero() { return 0.0f; }
+  static __device__ __forceinline__ Frag from(const float* y) { return y[0]; }
 };
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
@@ -153,6 +165,16 @@ template <> struct Vec8<F32> {
     *reinterpret_cast<f32x4_t*>(p + 4) = f32x4_t{y[4], y[5], y[6], y[7]};
   }
 };
+
+// One rotation pair: (u, v) by the fp32 (c, s) of its angle, in fp64 with one
+// fused multiply-add per output (the other product is exact in fp64), rounded
+// once to storage.
+template <class E>
+__device__ __forceinline__ void rope_pair(float u, float v, float2 cs, typename E::T& y1, typename E::T& y2) {
+  const double du = u, dv = v, c = cs.x, sn = cs.y;
+  y1 = Store<E>::from_f64(fma(du, c, -(dv * sn)));
+  y2 = Store<E>::from_f64(fma(dv, c, du * sn));
+}
 
 // cos / sin of (p * theta_k) for every stream position p and frequency k,
 // evaluated in fp64 and rounded to fp32; built once when the state is created.
@@ -307,10 +329,8 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeArgs a) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       finite &= isfinite(x1[j]) && isfinite(x2[j]);
-      const double cc = cs4[j >> 1][2 * (j & 1)], ss = cs4[j >> 1][2 * (j & 1) + 1];
-      const double u = x1[j], v = x2[j];
-      y1[j] = Store<E>::from_f64(fma(u, cc, -(v * ss)));
-      y2[j] = Store<E>::from_f64(fma(v, cc, u * ss));
+      rope_pair<E>(x1[j], x2[j], float2{cs4[j >> 1][2 * (j & 1)], cs4[j >> 1][2 * (j & 1) + 1]},
+                   y1[j], y2[j]);
     }
     Vec8<E>::store(dst0 + k, y1);
     Vec8<E>::store(dst0 + k + HALF, y2);
@@ -565,8 +585,9 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fwd_kernel(AttnArgs a) {
   const int full_end = min(kend, a.k0 + tok_min + 1);
 
   const T* qbase = (const T*)a.qrot + (size_t)g * a.R * D;
-  const T* kbase = (const T*)a.kpool + (size_t)g * a.cap * D;
-  const T* vbase = (const T*)a.vpool + (size_t)g * a.cap * D;
+  const T* kbase = (const T*)a.kpool + (size_t)g * a.kv_hs;
+  const T* vbase = (const T*)a.vpool + (size_t)g * a.kv_hs;
+  const size_t rs = (size_t)a.kv_rs;
 
   typename M::Frag qf[QT][NKS];
   int qrow[QT], lim[QT];
@@ -594,7 +615,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fwd_kernel(AttnArgs a) {
   Stage stage;
   const int nblk = kend > kbeg ? (kend - kbeg + BN - 1) / BN : 0;
   if (nblk > 0) {
-    stage.load(kbase, vbase, kbeg, kend, a.k0, a.foff, D, tid);
+    stage.load(kbase, vbase, kbeg, kend, a.k0, a.foff, rs, tid);
     stage.store(Ks[0], Vt[0], tid);
   }
   __syncthreads();
@@ -602,7 +623,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fwd_kernel(AttnArgs a) {
   for (int b = 0; b < nblk; ++b) {
     const int kb = kbeg + b * BN;
     const int buf = b & 1;
-    if (b + 1 < nblk) stage.load(kbase, vbase, kb + BN, kend, a.k0, a.foff, D, tid);
+    if (b + 1 < nblk) stage.load(kbase, vbase, kb + BN, kend, a.k0, a.foff, rs, tid);
     const T* ks_ = Ks[buf];
     const T* vt_ = Vt[buf];
 
@@ -712,13 +733,18 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fwd_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Text-phase attention over the detailed cache D.  Text queries are few (G*t
-// rows per KV head), so the work is a stream over D's rows: HBM-bound.  A
-// work-group owns one tile of 32 query rows and a contiguous key split; each
-// block of BN = 32*NW keys is loaded with 16-byte coalesced reads (D rows are
-// Hkv*d elements apart), staged in LDS as K and V^T (as in pass 1), and wave
-// w computes the block's w-th 32-key sub-tile: S^T = K Q^T, online softmax,
-// O^T += V^T P^T.  The next block's loads are in flight during the compute.
+// Text-phase attention over the detailed cache D for t text tokens with
+// G*t <= 32 query rows per KV head (single-token decode and short chunks).
+// Few queries make this a stream over D's rows: HBM-bound.  A work-group owns
+// one KV head and a contiguous key split; each block of BN = 32*NW keys is
+// loaded with 16-byte coalesced reads (D rows are Hkv*d elements apart),
+// staged in LDS as K and V^T (as in pass 1), and wave w computes the block's
+// w-th 32-key sub-tile: S^T = K Q^T, online softmax, O^T += V^T P^T.  The next
+// block's loads are in flight during the compute.
+// The text tokens themselves are not yet in D: the work-group rotates its
+// query rows from the projected input (the RoPE kernel's arithmetic), stages
+// the text keys of its split in a separate LDS tile (rotated K, V) that is
+// attended after the block loop, and appends those rows to D for later calls.
 // At the end the waves' (m, l, O) are merged with exact power-of-two factors.
 // Visibility: key j is seen by the query of text token i iff j < k0 + i + 1.
 // ---------------------------------------------------------------------------
@@ -738,7 +764,10 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_attn_kernel(DecodeArgs a) {
   constexpr int OSTR = D + 4;                       // fp32 row stride of the wave merge
   constexpr int RBYTES = NW * 32 * OSTR * 4;
   constexpr int LBYTES = KBYTES + VBYTES > RBYTES ? KBYTES + VBYTES : RBYTES;
+  constexpr int VSTR_T = 32 + 16 / (int)sizeof(T);  // V^T row stride of the text tile
   __shared__ __attribute__((aligned(16))) char lds[LBYTES];
+  __shared__ __attribute__((aligned(16))) T Kt[32 * KSTR];
+  __shared__ __attribute__((aligned(16))) T Vtt[D * VSTR_T];
   __shared__ float wm[NW][32];
   __shared__ double wsum[NW][32];
   T* Ks = reinterpret_cast<T*>(lds);
@@ -747,28 +776,89 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_attn_kernel(DecodeArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, hh = lane >> 5;
-  // Logical (row tile, KV head, split): the row tiles of one (head, split)
-  // read the same keys and run on one XCD.
-  const int wl = xcd_remap(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z),
-                           gridDim.x * gridDim.y * gridDim.z);
-  const int tile = wl % gridDim.x, wrest = wl / gridDim.x;
-  const int g = wrest % gridDim.y, split = wrest / gridDim.y;
-  const int row0 = tile * 32;
-  const int row_last = min(a.R, row0 + 32) - 1;
+  const int g = blockIdx.x, split = blockIdx.y;
+  const int row0 = 0;
+  const int row_last = a.R - 1;
   const int kbeg = split * a.kps;
   const int kend = min(min(kbeg + a.kps, a.k0 + row_last / a.G + 1), a.P);
   const int full_end = min(kend, a.k0 + row0 / a.G + 1);   // visible to every row of the tile
   const size_t rs = (size_t)a.Hkv * D;
-  const T* qbase = (const T*)a.qrot + (size_t)g * a.R * D;
   const T* kbase = (const T*)a.dk + (size_t)g * D;
   const T* vbase = (const T*)a.dv + (size_t)g * D;
 
   const int r = row0 + col;
+  // The block loop streams D's keys below k0; the split's text keys
+  // [tbeg, kend) (at most 32) are staged from the projected inputs into their
+  // own LDS tile up front (K rotated here), attended last, and appended to D
+  // for later calls.
+  const int dend = min(kend, a.k0);                         // keys read from D
+  const int tbeg = max(kbeg, a.k0);
+  const int ntext = max(0, kend - tbeg);
   int lim[1] = {min(kend, a.k0 + (r < a.R ? r / a.G : -1) + 1)};
+  int lim_d[1] = {min(lim[0], dend)};
+  Stage stage;
+  const int nblk = dend > kbeg ? (dend - kbeg + BN - 1) / BN : 0;
+  bool finite = true;
+  if (nblk > 0) stage.load(kbase, vbase, kbeg, dend, a.k0, 0, rs, tid);
+
   typename M::Frag qf[NKS];
+  {
+    constexpr int HALF = D / 2;
+    constexpr int QSTR = D + 16 / (int)sizeof(T);
+    const T zero = Store<E>::from_f32(0.f);
+    // Query rows, rotated at positions k0 + token (the RoPE kernel's
+    // arithmetic), through LDS that the first block has not yet claimed.
+    T* Qs = reinterpret_cast<T*>(lds);
+    for (int task = tid; task < 32 * HALF; task += NT) {
+      const int rr = task / HALF, i = task - rr * HALF;
+      const int row = row0 + rr;
+      T y1 = zero, y2 = zero;
+      if (row < a.R) {
+        const int tok = row / a.G;
+        const int h = g * a.G + (row - tok * a.G);
+        const T* qs = (const T*)a.q + ((size_t)tok * a.Hq + h) * D;
+        const float u = Store<E>::load(qs + i), v = Store<E>::load(qs + i + HALF);
+        finite &= isfinite(u) && isfinite(v);
+        rope_pair<E>(u, v, a.table[(size_t)(a.k0 + tok) * HALF + i], y1, y2);
+      }
+      Qs[rr * QSTR + i] = y1;
+      Qs[rr * QSTR + i + HALF] = y2;
+    }
+    // Text tile: 32 key rows of K and the matching V^T columns (zeros beyond
+    // the text keys), with the block layout of the stage.
+    for (int task = tid; task < 32 * HALF; task += NT) {
+      const int kk = task / HALF, i = task - kk * HALF;
+      T y1 = zero, y2 = zero;
+      if (kk < ntext) {
+        const int key = tbeg + kk;
+        const T* row = (const T*)a.k + ((size_t)(key - a.k0) * a.Hkv + g) * D;
+        const float u = Store<E>::load(row + i), v = Store<E>::load(row + i + HALF);
+        finite &= isfinite(u) && isfinite(v);
+        rope_pair<E>(u, v, a.table[(size_t)key * HALF + i], y1, y2);
+        T* drow = (T*)a.dk + ((size_t)key * a.Hkv + g) * D;   // append to D
+        drow[i] = y1;
+        drow[i + HALF] = y2;
+      }
+      Kt[kk * KSTR + i] = y1;
+      Kt[kk * KSTR + i + HALF] = y2;
+    }
+    for (int task = tid; task < 32 * D; task += NT) {
+      const int e = task / 32, kk = task - e * 32;
+      T x = zero;
+      if (kk < ntext) {
+        const int key = tbeg + kk;
+        x = ((const T*)a.v)[((size_t)(key - a.k0) * a.Hkv + g) * D + e];
+        finite &= isfinite(Store<E>::load(&x));
+        ((T*)a.dv)[((size_t)key * a.Hkv + g) * D + e] = x;     // append to D
+      }
+      const int slot = sizeof(T) == 2 ? (kk & ~12) | ((kk & 4) << 1) | ((kk & 8) >> 1) : kk;
+      Vtt[e * VSTR_T + slot] = x;
+    }
+    __syncthreads();
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks)
-    qf[ks] = r < a.R ? M::ld(qbase + (size_t)r * D + ks * M::KS + hh * M::KL) : M::zero();
+    for (int ks = 0; ks < NKS; ++ks) qf[ks] = M::ld(&Qs[col * QSTR + ks * M::KS + hh * M::KL]);
+    __syncthreads();   // the first block's store reuses the query rows' LDS
+  }
 
   f32x16_t o[1][NDT];
 #pragma unroll
@@ -776,57 +866,60 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_attn_kernel(DecodeArgs a) {
   float m_run[1] = {-INFINITY};
   double l_run[1] = {0.0};
 
-  Stage stage;
-  const int nblk = kend > kbeg ? (kend - kbeg + BN - 1) / BN : 0;
-  if (nblk > 0) stage.load(kbase, vbase, kbeg, kend, a.k0, 0, rs, tid);
+  // One 32-key sub-tile: keys kb + 0..31 are rows koff.. of Kb and columns
+  // koff.. of Vb.  S^T = K Q^T, online softmax, O^T += V^T P^T.
+  auto subtile = [&](int kb, const T* Kb, const T* Vb, int vstr, int koff, const int (&lm)[1], int fend) {
+    f32x16_t sacc[1] = {f32x16_t{}};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const typename M::Frag af = M::ld(&Kb[(koff + col) * KSTR + ks * M::KS + hh * M::KL]);
+      sacc[0] = M::mma(af, qf[ks], sacc[0]);
+    }
+    float alpha[1];
+    if (kb + 32 > fend)
+      online_softmax<1, true>(sacc, m_run, l_run, alpha, lm, kb, hh, a.c_hi);
+    else
+      online_softmax<1, false>(sacc, m_run, l_run, alpha, lm, kb, hh, a.c_hi);
+    if (__ballot(alpha[0] != 1.f)) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) o[0][dt] *= alpha[0];
+    }
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm) {
+        bf16x8_t pf;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) pf[t] = (__bf16)sacc[0][8 * mm + t];
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(
+              &Vb[(dt * 32 + col) * vstr + koff + mm * 16 + hh * 8]);
+          o[0][dt] = M::mma(af, pf, o[0][dt]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          const int kin = koff + 8 * (t >> 2) + 4 * hh + (t & 3);
+          o[0][dt] = M::mma(Vb[(dt * 32 + col) * vstr + kin], sacc[0][t], o[0][dt]);
+        }
+    }
+  };
+
+  const int full_end_d = min(full_end, dend);
   for (int b = 0; b < nblk; ++b) {
     const int kb = kbeg + b * BN;
     if (b > 0) __syncthreads();   // every wave is done with the previous block
     stage.store(Ks, Vt, tid);
     __syncthreads();
-    if (b + 1 < nblk) stage.load(kbase, vbase, kb + BN, kend, a.k0, 0, rs, tid);
-    const int ksub = kb + wave * 32;
-    if (ksub < kend) {
-      f32x16_t sacc[1] = {f32x16_t{}};
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const typename M::Frag af = M::ld(&Ks[(wave * 32 + col) * KSTR + ks * M::KS + hh * M::KL]);
-        sacc[0] = M::mma(af, qf[ks], sacc[0]);
-      }
-      float alpha[1];
-      if (ksub + 32 > full_end)
-        online_softmax<1, true>(sacc, m_run, l_run, alpha, lim, ksub, hh, a.c_hi);
-      else
-        online_softmax<1, false>(sacc, m_run, l_run, alpha, lim, ksub, hh, a.c_hi);
-      if (__ballot(alpha[0] != 1.f)) {
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) o[0][dt] *= alpha[0];
-      }
-      if constexpr (sizeof(T) == 2) {
-#pragma unroll
-        for (int mm = 0; mm < 2; ++mm) {
-          bf16x8_t pf;
-#pragma unroll
-          for (int t = 0; t < 8; ++t) pf[t] = (__bf16)sacc[0][8 * mm + t];
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) {
-            const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(
-                &Vt[(dt * 32 + col) * VSTR + wave * 32 + mm * 16 + hh * 8]);
-            o[0][dt] = M::mma(af, pf, o[0][dt]);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-          for (int t = 0; t < 16; ++t) {
-            const int kin = wave * 32 + 8 * (t >> 2) + 4 * hh + (t & 3);
-            o[0][dt] = M::mma(Vt[(dt * 32 + col) * VSTR + kin], sacc[0][t], o[0][dt]);
-          }
-      }
-    }
+    if (b + 1 < nblk) stage.load(kbase, vbase, kb + BN, dend, a.k0, 0, rs, tid);
+    if (kb + wave * 32 < dend) subtile(kb + wave * 32, Ks, Vt, VSTR, wave * 32, lim_d, full_end_d);
   }
+  if (ntext > 0 && wave == 0) subtile(tbeg, Kt, Vtt, VSTR_T, 0, lim, full_end);
 
+  if (!finite) atomicOr(a.nonfinite, 1);
   // Merge of the waves: m = max_w m_w; each wave's l and O scale by the exact
   // factor 2^(m_w - m); the sums run in wave order.
   const double lt = l_run[0] + __shfl_xor(l_run[0], 32);
@@ -887,62 +980,82 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_attn_kernel(DecodeArgs a) {
   }
 }
 
-// Merge of the text-phase key splits: one work-group per (KV head, row).
-// m = max_s m_s; weights 2^(m_s - m) are exact; l and O are summed in a fixed
-// order (per thread over its splits, then across threads in index order), so
-// the result does not depend on scheduling.
-constexpr int kDecodeMergeThreads = 256;
+// Merge of the text-phase key splits: one work-group per (KV head, row), one
+// thread per split for the statistics.  m = max_s m_s; the weights
+// 2^(m_s - m) are exact; l and O are summed in a fixed order (a fixed
+// butterfly inside each wave, then waves in order; per thread over its
+// splits, then thread groups in order), so the result does not depend on
+// scheduling.  Splits that saw no key hold zeros and weigh 0.
+constexpr int kDecodeMergeThreads = 1024;
+static_assert(kDecodeMaxSplits <= kDecodeMergeThreads, "one split per merge thread");
 
 template <class E, int D>
 __global__ __launch_bounds__(kDecodeMergeThreads) void decode_merge_kernel(DecodeMergeArgs a) {
   typedef typename E::T T;
   constexpr int NT = kDecodeMergeThreads;
+  constexpr int NWV = NT / 64;
   constexpr int CPR = D / 4;
-  constexpr int SG = NT / CPR;                       // split groups
+  constexpr int SG = NT / CPR;                       // split groups of the accumulation
   __shared__ float wts[kDecodeMaxSplits];
-  __shared__ float redm[NT];
-  __shared__ double redl[NT];
+  __shared__ float wmax[NWV];
+  __shared__ double wl[NWV];
   __shared__ __attribute__((aligned(16))) f32x4_t redo[SG][CPR];
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const size_t nrows = (size_t)a.Hkv * a.R;
   const size_t row = blockIdx.x;                     // = g*R + r
-  float mt = -INFINITY;
-  for (int s = tid; s < a.S; s += NT) mt = fmaxf(mt, a.mpart[s * nrows + row]);
-  redm[tid] = mt;
-  __syncthreads();
-  for (int w = NT / 2; w > 0; w >>= 1) {
-    if (tid < w) redm[tid] = fmaxf(redm[tid], redm[tid + w]);
-    __syncthreads();
-  }
-  const float m = redm[0];
-  double lt = 0.0;
-  for (int s = tid; s < a.S; s += NT) {
-    const float ms = a.mpart[s * nrows + row];
-    const float w = ms != -INFINITY ? ldexpf(1.f, (int)(ms - m)) : 0.f;
-    wts[s] = w;
-    if (w != 0.f) lt += (double)w * a.lpart[s * nrows + row];
-  }
-  redl[tid] = lt;
-  __syncthreads();
-  for (int w = NT / 2; w > 0; w >>= 1) {
-    if (tid < w) redl[tid] += redl[tid + w];
-    __syncthreads();
-  }
-  const double l = redl[0];
   const int c = tid % CPR, sg = tid / CPR;
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s = sg; s < a.S; s += SG) {
-    const float w = wts[s];
-    if (w != 0.f) {
-      const f32x4_t os = *reinterpret_cast<const f32x4_t*>(a.opart + (s * nrows + row) * D + c * 4);
+  // Every load is issued before the first reduction: the statistics of this
+  // thread's split and the first PF partial outputs of its split group.
+  constexpr int PF = 8;
+  f32x4_t os[PF];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = fmaf(w, os[e], acc[e]);
-    }
+  for (int j = 0; j < PF; ++j) {
+    const int s = sg + j * SG;
+    os[j] = s < a.S ? *reinterpret_cast<const f32x4_t*>(a.opart + (s * nrows + row) * D + c * 4)
+                    : f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  const float ms = tid < a.S ? a.mpart[tid * nrows + row] : -INFINITY;
+  const double ls = tid < a.S ? a.lpart[tid * nrows + row] : 0.0;
+  float mx = ms;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  if (lane == 0) wmax[wave] = mx;
+  __syncthreads();
+  float m = wmax[0];
+#pragma unroll
+  for (int w = 1; w < NWV; ++w) m = fmaxf(m, wmax[w]);
+  const float wt = ms != -INFINITY ? ldexpf(1.f, (int)(ms - m)) : 0.f;
+  if (tid < a.S) wts[tid] = wt;
+  double lw = wt != 0.f ? (double)wt * ls : 0.0;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) lw += __shfl_xor(lw, o);
+  if (lane == 0) wl[wave] = lw;
+  __syncthreads();
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < PF; ++j) {
+    const int s = sg + j * SG;
+    const float w = s < a.S ? wts[s] : 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = fmaf(w, os[j][e], acc[e]);
+  }
+#pragma unroll 1
+  for (int s = sg + PF * SG; s < a.S; s += SG) {
+    const float w = wts[s];
+    const f32x4_t os = *reinterpret_cast<const f32x4_t*>(a.opart + (s * nrows + row) * D + c * 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = fmaf(w, os[e], acc[e]);
   }
   redo[sg][c] = acc;
   __syncthreads();
-  if (sg != 0) return;
+  if (tid >= CPR) return;
+  acc = redo[0][c];
+#pragma unroll 8
   for (int j = 1; j < SG; ++j) acc += redo[j][c];
+  double l = wl[0];
+#pragma unroll
+  for (int w = 1; w < NWV; ++w) l += wl[w];
   const float inv = (float)(1.0 / l);
   const int g = (int)(row / a.R), r = (int)(row - (size_t)g * a.R);
   const int tok = r / a.G;
@@ -1646,8 +1759,8 @@ constexpr int kDecodeWavesBf16 = 4;
 constexpr int kDecodeWavesF32 = 2;
 int decode_block_keys(Dt dt) { return 32 * (dt == Dt::BF16 ? kDecodeWavesBf16 : kDecodeWavesF32); }
 
-hipError_t launch_decode(Dt dt, int d, const DecodeArgs& a, int row_tiles, hipStream_t s) {
-  const dim3 grid(row_tiles, a.Hkv, a.S);
+hipError_t launch_decode(Dt dt, int d, const DecodeArgs& a, hipStream_t s) {
+  const dim3 grid(a.Hkv, a.S);
   if (dt == Dt::BF16) {
     const dim3 block(64 * kDecodeWavesBf16);
     if (d == 64) hipLaunchKernelGGL((decode_attn_kernel<BF16, 64, kDecodeWavesBf16>), grid, block, 0, s, a);

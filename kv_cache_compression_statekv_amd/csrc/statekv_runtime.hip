@@ -52,6 +52,7 @@ struct statekv_state {
 
   // launch geometry
   int attn_tiles, attn_splits_max;
+  int stat_ss;           // split stride of the pass-1 partials (kMaxSplits with a text phase)
   bool never_evicts;
   int score_rsplits_max;
   int dec_target_wgs;
@@ -199,16 +200,28 @@ void score_geometry(const statekv_state* s, int P, int* key_blocks, int* rsplits
 }
 
 // Text phase: t tokens over P keys.  Row tiles of 32 rows per KV head; key
-// splits of whole blocks, enough work-groups for two per CU.
-constexpr int kDecodeTargetWGs = 512;
+// splits of whole blocks, about one work-group per CU (measured best for
+// long contexts).
+constexpr int kDecodeTargetWGs = 256;
 
-void decode_geometry(const statekv_state* s, int t, int64_t P, int* tiles, int* splits, int* kps) {
+void decode_geometry(const statekv_state* s, int64_t P, int* splits, int* kps) {
   const int bk = decode_block_keys(s->dt);
-  const int tl = ceil_div(s->G * t, 32);
   const int64_t blocks = (P + bk - 1) / bk;
-  int sp = (int)std::max<int64_t>(1, std::min<int64_t>(ceil_div(s->dec_target_wgs, tl * s->Hkv), blocks));
+  int sp = (int)std::max<int64_t>(1, std::min<int64_t>(ceil_div(s->dec_target_wgs, s->Hkv), blocks));
   sp = std::min(sp, kDecodeMaxSplits);
   const int64_t k = ((P + sp - 1) / sp + bk - 1) / bk * bk;
+  *splits = (int)((P + k - 1) / k);
+  *kps = (int)k;
+}
+
+// Text chunks with more than 32 query rows per KV head: pass 1 over D, row
+// tiles of the pass-1 kernel, key splits up to kMaxSplits.
+void chunk_geometry(const statekv_state* s, int t, int64_t P, int* tiles, int* splits, int* kps) {
+  const int tl = ceil_div(s->G * t, attn_rows_per_wg(s->dt, s->D));
+  int sp = (int)std::max<int64_t>(1, std::min<int64_t>(ceil_div(kAttnTargetWGs, tl * s->Hkv),
+                                                       (P + 4 * kAttnBN - 1) / (4 * kAttnBN)));
+  sp = std::min(sp, s->stat_ss);
+  const int64_t k = ((P + sp - 1) / sp + kAttnBN - 1) / kAttnBN * kAttnBN;
   *tiles = tl;
   *splits = (int)((P + k - 1) / k);
   *kps = (int)k;
@@ -359,16 +372,19 @@ int statekv_create(const statekv_layer_cfg* cfg, int32_t budget_B, float alpha,
   const size_t E = s->esize, D = s->D;
   const size_t pool_bytes = (size_t)s->Hkv * s->cap * D * E;
   const size_t det_bytes = (size_t)all_positions * s->Hkv * D * E;
-  // Text-phase partials: the largest split count times rows over t = 1..T.
+  // Text-phase partials of the single-tile kernel: splits times rows, for
+  // the largest chunk it takes (G*t <= 32).
   size_t dec_rows = 0;
-  if (c.max_text > 0)
-    for (int t = 1; t <= s->T; ++t) {
-      int tl, sp, kp;
-      decode_geometry(s, t, all_positions, &tl, &sp, &kp);
-      if (sp > 1) dec_rows = std::max(dec_rows, (size_t)sp * s->Hkv * s->G * t);
-    }
+  if (c.max_text > 0 && s->G <= 32) {
+    int sp, kp;
+    decode_geometry(s, all_positions, &sp, &kp);
+    if (sp > 1) dec_rows = (size_t)sp * s->Hkv * 32;
+  }
   const size_t rows_all = (size_t)s->Hkv * s->R;
-  const size_t S = s->attn_splits_max;
+  // Text chunks of more than 32 query rows per KV head run through pass 1
+  // over D and may use up to kMaxSplits key splits.
+  s->stat_ss = c.max_text > 0 ? kMaxSplits : s->attn_splits_max;
+  const size_t S = s->stat_ss;
   rc = alloc(&s->kpool, pool_bytes);
   if (!rc) rc = alloc(&s->vpool, pool_bytes);
   if (!rc) rc = alloc(&s->ppos, (size_t)s->cap * sizeof(int32_t));
@@ -516,8 +532,10 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const 
     a.k0 = k0;
     a.foff = foff;
     a.kps = kps;
-    a.ss = s->attn_splits_max;
+    a.ss = s->stat_ss;
     a.Hkv = s->Hkv;
+    a.kv_hs = (int64_t)s->cap * s->D;
+    a.kv_rs = s->D;
     rc = check(launch_attn(s->dt, s->D, a, s->attn_tiles, splits, st));
     tm.done();
     if (rc) return rc;
@@ -532,7 +550,7 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const 
     a.mpart = s->mpart;
     a.lpart = s->lpart;
     a.S = splits;
-    a.ss = s->attn_splits_max;
+    a.ss = s->stat_ss;
     a.colsum = s->colsum;
     a.c_hi = s->c_hi;
     a.c_lo = s->c_lo;
@@ -576,7 +594,7 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const 
     a.G = s->G;
     a.Hq = s->Hq;
     a.S = splits;
-    a.ss = s->attn_splits_max;
+    a.ss = s->stat_ss;
     rc = check(launch_select(s->dt, s->D, a, st));
     tm.done();
     if (rc) return rc;
@@ -609,69 +627,128 @@ int statekv_decode(statekv_state* s, const void* Q, const void* K, const void* V
   const hipStream_t st = s->stream;
   const int P0 = s->frames_done * s->T + s->text_done;   // keys before the text chunk
   const int P = P0 + t;
-  {
-    KernelTimer tm(s, STATEKV_K_DEC_ROPE);
-    RopeArgs a{};
-    a.q = Q;
-    a.k = K;
-    a.v = V;
-    a.table = s->rope_tab;
-    a.qrot = s->qrot;
-    a.dk = s->dk;
-    a.dv = s->dv;
-    a.nonfinite = s->nonfinite;
-    a.pos0 = P0;
-    a.T = t;
-    a.Hq = s->Hq;
-    a.Hkv = s->Hkv;
-    a.G = s->G;
-    a.cap = s->cap;
-    a.rope_blocks = rope_blocks(t);
-    a.mv = moves_args(s, 0);
-    rc = check(launch_rope(s->dt, s->D, a, st));
-    tm.done();
-    if (rc) return rc;
-  }
-  int tiles, splits, kps;
-  decode_geometry(s, t, P, &tiles, &splits, &kps);
-  {
-    KernelTimer tm(s, STATEKV_K_DEC_ATTN);
-    DecodeArgs a{};
-    a.qrot = s->qrot;
-    a.dk = s->dk;
-    a.dv = s->dv;
-    a.opart = s->dec_opart;
-    a.mpart = s->dec_mpart;
-    a.lpart = s->dec_lpart;
-    a.out = O;
-    a.c_hi = s->c_hi;
-    a.R = s->G * t;
-    a.G = s->G;
-    a.Hq = s->Hq;
-    a.Hkv = s->Hkv;
-    a.P = P;
-    a.k0 = P0;
-    a.kps = kps;
-    a.S = splits;
-    rc = check(launch_decode(s->dt, s->D, a, tiles, st));
-    tm.done();
-    if (rc) return rc;
-  }
-  if (splits > 1) {
-    KernelTimer tm(s, STATEKV_K_DEC_MERGE);
-    DecodeMergeArgs a{};
-    a.opart = s->dec_opart;
-    a.mpart = s->dec_mpart;
-    a.lpart = s->dec_lpart;
-    a.out = O;
-    a.R = s->G * t;
-    a.G = s->G;
-    a.Hq = s->Hq;
-    a.Hkv = s->Hkv;
-    a.S = splits;
-    rc = check(launch_decode_merge(s->dt, s->D, a, st));
-    tm.done();
-    if (rc) return rc;
+  const int R = s->G * t;
+  if (R <= 32) {
+    // Few query rows: one kernel streams D (rotating the text tokens and
+    // appending them to D itself), then the merge of its key splits.
+    int splits, kps;
+    decode_geometry(s, P, &splits, &kps);
+    {
+      KernelTimer tm(s, STATEKV_K_DEC_ATTN);
+      DecodeArgs a{};
+      a.q = Q;
+      a.k = K;
+      a.v = V;
+      a.table = s->rope_tab;
+      a.nonfinite = s->nonfinite;
+      a.dk = s->dk;
+      a.dv = s->dv;
+      a.opart = s->dec_opart;
+      a.mpart = s->dec_mpart;
+      a.lpart = s->dec_lpart;
+      a.out = O;
+      a.c_hi = s->c_hi;
+      a.R = R;
+      a.G = s->G;
+      a.Hq = s->Hq;
+      a.Hkv = s->Hkv;
+      a.P = P;
+      a.k0 = P0;
+      a.kps = kps;
+      a.S = splits;
+      rc = check(launch_decode(s->dt, s->D, a, st));
+      tm.done();
+      if (rc) return rc;
+    }
+    if (splits > 1) {
+      KernelTimer tm(s, STATEKV_K_DEC_MERGE);
+      DecodeMergeArgs a{};
+      a.opart = s->dec_opart;
+      a.mpart = s->dec_mpart;
+      a.lpart = s->dec_lpart;
+      a.out = O;
+      a.R = R;
+      a.G = s->G;
+      a.Hq = s->Hq;
+      a.Hkv = s->Hkv;
+      a.S = splits;
+      rc = check(launch_decode_merge(s->dt, s->D, a, st));
+      tm.done();
+      if (rc) return rc;
+    }
+  } else {
+    // A longer chunk (a prompt): the frame step's kernels over D.  RoPE and
+    // append, attention pass 1 with D's strides, the merge of the splits.
+    {
+      KernelTimer tm(s, STATEKV_K_DEC_ROPE);
+      RopeArgs a{};
+      a.q = Q;
+      a.k = K;
+      a.v = V;
+      a.table = s->rope_tab;
+      a.qrot = s->qrot;
+      a.dk = s->dk;
+      a.dv = s->dv;
+      a.nonfinite = s->nonfinite;
+      a.pos0 = P0;
+      a.T = t;
+      a.Hq = s->Hq;
+      a.Hkv = s->Hkv;
+      a.G = s->G;
+      a.cap = s->cap;
+      a.rope_blocks = rope_blocks(t);
+      a.mv = moves_args(s, 0);
+      rc = check(launch_rope(s->dt, s->D, a, st));
+      tm.done();
+      if (rc) return rc;
+    }
+    int tiles, splits, kps;
+    chunk_geometry(s, t, P, &tiles, &splits, &kps);
+    {
+      KernelTimer tm(s, STATEKV_K_DEC_ATTN);
+      AttnArgs a{};
+      a.qrot = s->qrot;
+      a.kpool = s->dk;
+      a.vpool = s->dv;
+      a.opart = s->opart;
+      a.epart = s->epart;
+      a.mpart = s->mpart;
+      a.lpart = s->lpart;
+      a.c_hi = s->c_hi;
+      a.R = R;
+      a.G = s->G;
+      a.cap = s->cap;
+      a.P = P;
+      a.k0 = P0;
+      a.foff = 0;
+      a.kps = kps;
+      a.ss = s->stat_ss;
+      a.Hkv = s->Hkv;
+      a.kv_hs = s->D;
+      a.kv_rs = (int64_t)s->Hkv * s->D;
+      rc = check(launch_attn(s->dt, s->D, a, tiles, splits, st));
+      tm.done();
+      if (rc) return rc;
+    }
+    {
+      KernelTimer tm(s, STATEKV_K_DEC_MERGE);
+      SelectArgs a{};
+      a.mode = kSelMerge;
+      a.opart = s->opart;
+      a.epart = s->epart;
+      a.mpart = s->mpart;
+      a.lpart = s->lpart;
+      a.out = O;
+      a.Hkv = s->Hkv;
+      a.R = R;
+      a.G = s->G;
+      a.Hq = s->Hq;
+      a.S = splits;
+      a.ss = s->stat_ss;
+      rc = check(launch_select(s->dt, s->D, a, st));
+      tm.done();
+      if (rc) return rc;
+    }
   }
   s->text_done += t;
   s->ev_slot = (s->ev_slot + 1) % statekv_state::kRing;

@@ -167,3 +167,18 @@ def test_chunk_longer_than_a_frame_is_rejected():
     with pytest.raises(skv.StateKVError) as e:
         st.decode(q, k, v)
     assert e.value.code == skv.STATEKV_EINVAL
+
+
+@pytest.mark.parametrize("t,field", [(1, "k"), (1, "q"), (50, "v")], ids=["fused_k", "fused_q", "rope_v"])
+def test_nonfinite_text_is_reported(t, field):
+    """A NaN in the text inputs is reported by the next view, whether the
+    attention kernel rotates the tokens itself (one row tile) or not."""
+    wl = SMALL["ragged_bf16_d64"]
+    st = make_state(wl, max_frames=1, max_text=64)
+    st.prefill_frame(*[to_device(x, wl.dtype) for x in FrameStream(wl).frame(0)], n=0)
+    q, k, v = (x.copy() for x in text_tokens(wl, 200, t))
+    {"q": q, "k": k, "v": v}[field][t - 1, 0, 3] = np.nan
+    st.decode(*[to_device(x, wl.dtype) for x in (q, k, v)])
+    with pytest.raises(skv.StateKVError) as e:
+        st.detailed_view()
+    assert e.value.code == skv.STATEKV_ENONFINITE
