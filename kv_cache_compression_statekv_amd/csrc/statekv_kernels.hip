@@ -550,7 +550,7 @@ __device__ __forceinline__ void online_softmax(f32x16_t (&sacc)[QT], float (&m_r
   }
 }
 
-template <class E, int D, int QT, int NW>
+template <class E, int D, int QT, int NW, int NPF = 1>
 __global__ __launch_bounds__(64 * NW, 1) void attn_fwd_kernel(AttnArgs a) {
   typedef typename E::T T;
   typedef Mma<E> M;
@@ -612,18 +612,18 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fwd_kernel(AttnArgs a) {
     l_run[qt] = 0.0;
   }
 
-  Stage stage;
+  // NPF register stages: block b's loads are issued NPF blocks ahead of its
+  // compute, so short splits (a few blocks per work-group) have all their
+  // loads in flight at once.  Blocks pass through two LDS buffers.
+  Stage st[NPF];
   const int nblk = kend > kbeg ? (kend - kbeg + BN - 1) / BN : 0;
-  if (nblk > 0) {
-    stage.load(kbase, vbase, kbeg, kend, a.k0, a.foff, rs, tid);
-    stage.store(Ks[0], Vt[0], tid);
-  }
+#pragma unroll
+  for (int i = 0; i < NPF; ++i)
+    if (i < nblk) st[i].load(kbase, vbase, kbeg + i * BN, kend, a.k0, a.foff, rs, tid);
+  if (nblk > 0) st[0].store(Ks[0], Vt[0], tid);
   __syncthreads();
 
-  for (int b = 0; b < nblk; ++b) {
-    const int kb = kbeg + b * BN;
-    const int buf = b & 1;
-    if (b + 1 < nblk) stage.load(kbase, vbase, kb + BN, kend, a.k0, a.foff, rs, tid);
+  auto compute = [&](int kb, int buf) {
     const T* ks_ = Ks[buf];
     const T* vt_ = Vt[buf];
 
@@ -688,8 +688,21 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fwd_kernel(AttnArgs a) {
       }
     }
 
-    if (b + 1 < nblk) stage.store(Ks[buf ^ 1], Vt[buf ^ 1], tid);
-    __syncthreads();
+  };
+
+  for (int b0 = 0; b0 < nblk; b0 += NPF) {
+#pragma unroll
+    for (int i = 0; i < NPF; ++i) {
+      const int b = b0 + i;
+      if (b < nblk) {
+        const int kb = kbeg + b * BN;
+        const int buf = b & 1;
+        if (b + NPF < nblk) st[i].load(kbase, vbase, kb + NPF * BN, kend, a.k0, a.foff, rs, tid);
+        compute(kb, buf);
+        if (b + 1 < nblk) st[(i + 1) % NPF].store(Ks[buf ^ 1], Vt[buf ^ 1], tid);
+        __syncthreads();
+      }
+    }
   }
 
   // Partial results of this key split.
@@ -1565,12 +1578,30 @@ __device__ void merge_splits(const SelectArgs& a, int wg, float* lds) {
   static_assert(GPW >= 1 && GPW * 32 * CPR == kSelectThreads, "merge work-group shape");
   float* wts = lds;                                   // [GPW*32][kMaxSplits]
   float* rinv = lds + GPW * 32 * kMaxSplits;          // [GPW*32]
+  typedef typename PartialOut<E>::V PV;
   const int tid = threadIdx.x;
   const size_t nrows = (size_t)a.Hkv * a.R;
   const int gsub = (tid >> 5) / CPR;
   const int c = (tid >> 5) - gsub * CPR;
   const int lrow = gsub * 32 + (tid & 31);
   const size_t base = ((size_t)wg * GPW + gsub) * 32 + (tid & 31);   // = g*R + r
+  // The partial outputs do not depend on the weights: the first MCH splits'
+  // loads are issued before the statistics, so they are all in flight at once.
+  constexpr int MCH = sizeof(T) == 2 ? 8 : 4;
+  PV os[MCH];
+  int8_t ep[MCH];
+  auto load_chunk = [&](int s0) {
+#pragma unroll
+    for (int j = 0; j < MCH; ++j) {
+      const int sp = s0 + j;
+      if (sp < a.S && base < nrows) {
+        const size_t ri = sp * nrows + base;
+        os[j] = reinterpret_cast<const PV*>(a.opart)[opart_group(ri, D) + (size_t)c * 32 + (ri & 31)];
+        ep[j] = sizeof(T) == 2 ? a.epart[ri] : (int8_t)0;
+      }
+    }
+  };
+  load_chunk(0);
   if (c == 0) {
     float w[kMaxSplits];
     float inv = 0.f;
@@ -1594,16 +1625,19 @@ __device__ void merge_splits(const SelectArgs& a, int wg, float* lds) {
   __syncthreads();
   if (base >= nrows) return;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < a.S; ++s) {
-    const float w = wts[lrow * kMaxSplits + s];
-    if (w != 0.f) {
-      const size_t ri = s * nrows + base;
-      typedef typename PartialOut<E>::V PV;
-      const f32x4_t os = PartialOut<E>::unpack(
-          reinterpret_cast<const PV*>(a.opart)[opart_group(ri, D) + (size_t)c * 32 + (ri & 31)]);
-      const float wo = sizeof(T) == 2 ? ldexpf(w, (int)a.epart[ri]) : w;
+  for (int s0 = 0; s0 < a.S; s0 += MCH) {
+    if (s0 > 0) load_chunk(s0);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = fmaf(wo, os[e], acc[e]);
+    for (int j = 0; j < MCH; ++j) {
+      const int sp = s0 + j;
+      // Splits that saw no key of the row have weight 0 and unwritten partials.
+      const float w = sp < a.S ? wts[lrow * kMaxSplits + sp] : 0.f;
+      if (w != 0.f) {
+        const f32x4_t o4 = PartialOut<E>::unpack(os[j]);
+        const float wo = sizeof(T) == 2 ? ldexpf(w, (int)ep[j]) : w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = fmaf(wo, o4[e], acc[e]);
+      }
     }
   }
   const float inv = rinv[lrow];
@@ -1667,6 +1701,19 @@ static int attn_variant() {
   return v;
 }
 
+// Register stages of pass 1's block prefetch: 2 for d = 128 (measured a few
+// percent faster on the long-pool shapes), 1 for d = 64 (no gain);
+// STATEKV_ATTN_PF = 1, 2 or 4 overrides.
+static int attn_prefetch(int d) {
+  static int v = -1;
+  if (v < 0) {
+    const char* e = getenv("STATEKV_ATTN_PF");
+    const int x = e ? atoi(e) : 0;
+    v = (x == 1 || x == 2 || x == 4) ? x : 0;
+  }
+  return v ? v : (d == 128 ? 2 : 1);
+}
+
 int attn_rows_per_wg(Dt dt, int) {
   if (dt != Dt::BF16) return 4 * 32;
   return attn_variant() == 4 ? 4 * 32 * 2 : 8 * 32;
@@ -1713,8 +1760,16 @@ hipError_t launch_attn(Dt dt, int d, const AttnArgs& a, int row_tiles, int split
       if (d == 64) hipLaunchKernelGGL((attn_fwd_kernel<BF16, 64, 2, 4>), grid, dim3(256), 0, s, a);
       else hipLaunchKernelGGL((attn_fwd_kernel<BF16, 128, 2, 4>), grid, dim3(256), 0, s, a);
     } else {
-      if (d == 64) hipLaunchKernelGGL((attn_fwd_kernel<BF16, 64, 1, 8>), grid, dim3(512), 0, s, a);
-      else hipLaunchKernelGGL((attn_fwd_kernel<BF16, 128, 1, 8>), grid, dim3(512), 0, s, a);
+      const int pf = attn_prefetch(d);
+      if (d == 64) {
+        if (pf == 4) hipLaunchKernelGGL((attn_fwd_kernel<BF16, 64, 1, 8, 4>), grid, dim3(512), 0, s, a);
+        else if (pf == 2) hipLaunchKernelGGL((attn_fwd_kernel<BF16, 64, 1, 8, 2>), grid, dim3(512), 0, s, a);
+        else hipLaunchKernelGGL((attn_fwd_kernel<BF16, 64, 1, 8, 1>), grid, dim3(512), 0, s, a);
+      } else {
+        if (pf == 4) hipLaunchKernelGGL((attn_fwd_kernel<BF16, 128, 1, 8, 4>), grid, dim3(512), 0, s, a);
+        else if (pf == 2) hipLaunchKernelGGL((attn_fwd_kernel<BF16, 128, 1, 8, 2>), grid, dim3(512), 0, s, a);
+        else hipLaunchKernelGGL((attn_fwd_kernel<BF16, 128, 1, 8, 1>), grid, dim3(512), 0, s, a);
+      }
     }
   } else {
     if (d == 64) hipLaunchKernelGGL((attn_fwd_kernel<F32, 64, 1, 4>), grid, dim3(256), 0, s, a);
