@@ -206,8 +206,10 @@ int statekv_set_flags(statekv_state* s, uint32_t flags);
 #define STATEKV_K_COUNT    7
 
 /*
- * With STATEKV_FLAG_KERNEL_TIMING set, per-kernel device time (HIP events on
- * the state's stream) is summed over frames.  Copies up to n_kernels sums in
+ * With STATEKV_FLAG_KERNEL_TIMING set, per-kernel device time is summed over
+ * frames: each timed kernel is dispatched with a start and a stop HIP event
+ * that the dispatch itself records (hipExtLaunchKernel), so the time is the
+ * kernel's execution, without the gaps between launches.  Copies up to n_kernels sums in
  * milliseconds into ms[] and launch counts into launches[] (either may be
  * NULL), synchronising the stream; reset != 0 clears the sums afterwards.
  */

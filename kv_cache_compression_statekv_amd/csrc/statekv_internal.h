@@ -161,6 +161,14 @@ constexpr int kSelMerge = 0;   // merge only (the pool fits in B and is not scor
 constexpr int kSelScores = 1;  // scores, everything kept
 constexpr int kSelEvict = 2;   // scores and Top-B
 
+// Start / stop events that the dispatch itself records (kernel timing): the
+// elapsed time between them is the kernel's execution, without the launch
+// gaps that separately recorded events would include.  Null: not timed.
+struct LaunchTiming {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
 // Rows handled by one pass-1 work-group / keys by one score work-group.
 int attn_rows_per_wg(Dt dt, int d);
 int score_keys_per_wg(Dt dt);
@@ -169,15 +177,18 @@ int score_waves_per_wg(Dt dt);
 int rope_blocks(int T);
 
 hipError_t launch_rope_table(const RopeTableArgs& a, hipStream_t s);
-hipError_t launch_rope(Dt dt, int d, const RopeArgs& a, hipStream_t s);
-hipError_t launch_attn(Dt dt, int d, const AttnArgs& a, int row_tiles, int splits, hipStream_t s);
-hipError_t launch_score(Dt dt, int d, const ScoreArgs& a, int key_blocks, int rsplits, hipStream_t s);
-hipError_t launch_select(Dt dt, int d, const SelectArgs& a, hipStream_t s);
+hipError_t launch_rope(Dt dt, int d, const RopeArgs& a, hipStream_t s, const LaunchTiming& tm = {});
+hipError_t launch_attn(Dt dt, int d, const AttnArgs& a, int row_tiles, int splits, hipStream_t s,
+                       const LaunchTiming& tm = {});
+hipError_t launch_score(Dt dt, int d, const ScoreArgs& a, int key_blocks, int rsplits, hipStream_t s,
+                        const LaunchTiming& tm = {});
+hipError_t launch_select(Dt dt, int d, const SelectArgs& a, hipStream_t s, const LaunchTiming& tm = {});
 hipError_t launch_moves(const MovesArgs& a, hipStream_t s);
 // Keys per block of the text-phase attention kernel.
 int decode_block_keys(Dt dt);
-hipError_t launch_decode(Dt dt, int d, const DecodeArgs& a, hipStream_t s);
-hipError_t launch_decode_merge(Dt dt, int d, const DecodeMergeArgs& a, hipStream_t s);
+hipError_t launch_decode(Dt dt, int d, const DecodeArgs& a, hipStream_t s, const LaunchTiming& tm = {});
+hipError_t launch_decode_merge(Dt dt, int d, const DecodeMergeArgs& a, hipStream_t s,
+                               const LaunchTiming& tm = {});
 // Positions of a scored pool of P candidates: the position of its row, or
 // for an evicted slot below B that a move has since filled, the saved one.
 hipError_t launch_score_positions(int32_t* score_pos, const int32_t* pool_pos,

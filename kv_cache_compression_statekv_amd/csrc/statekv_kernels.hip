@@ -29,6 +29,8 @@
 // slice [KL*(l/32), KL*(l/32) + KL) of the instruction's KS-deep reduction.
 #include "statekv_internal.h"
 
+#include <hip/hip_ext.h>
+
 #include <math.h>
 #include <stdlib.h>
 
@@ -1740,70 +1742,72 @@ hipError_t launch_rope_table(const RopeTableArgs& a, hipStream_t s) {
 
 int rope_blocks(int T) { return (T + kRopeTokensPerWG - 1) / kRopeTokensPerWG; }
 
-hipError_t launch_rope(Dt dt, int d, const RopeArgs& a, hipStream_t s) {
+hipError_t launch_rope(Dt dt, int d, const RopeArgs& a, hipStream_t s, const LaunchTiming& tm) {
   const size_t move_tasks = a.mv.max_moves > 0 ? (size_t)a.mv.max_moves * a.Hkv * (a.mv.row_bytes / 16) : 0;
   const int blocks = a.rope_blocks + (int)((move_tasks + 255) / 256);
   if (dt == Dt::BF16) {
-    if (d == 64) hipLaunchKernelGGL((rope_append_kernel<BF16, 64>), dim3(blocks), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((rope_append_kernel<BF16, 128>), dim3(blocks), dim3(256), 0, s, a);
+    if (d == 64) hipExtLaunchKernelGGL((rope_append_kernel<BF16, 64>), dim3(blocks), dim3(256), 0, s, tm.start, tm.stop, 0, a);
+    else hipExtLaunchKernelGGL((rope_append_kernel<BF16, 128>), dim3(blocks), dim3(256), 0, s, tm.start, tm.stop, 0, a);
   } else {
-    if (d == 64) hipLaunchKernelGGL((rope_append_kernel<F32, 64>), dim3(blocks), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((rope_append_kernel<F32, 128>), dim3(blocks), dim3(256), 0, s, a);
+    if (d == 64) hipExtLaunchKernelGGL((rope_append_kernel<F32, 64>), dim3(blocks), dim3(256), 0, s, tm.start, tm.stop, 0, a);
+    else hipExtLaunchKernelGGL((rope_append_kernel<F32, 128>), dim3(blocks), dim3(256), 0, s, tm.start, tm.stop, 0, a);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_attn(Dt dt, int d, const AttnArgs& a, int row_tiles, int splits, hipStream_t s) {
+hipError_t launch_attn(Dt dt, int d, const AttnArgs& a, int row_tiles, int splits, hipStream_t s,
+                       const LaunchTiming& tm) {
   const dim3 grid(row_tiles, a.Hkv, splits);
   if (dt == Dt::BF16) {
     if (attn_variant() == 4) {
-      if (d == 64) hipLaunchKernelGGL((attn_fwd_kernel<BF16, 64, 2, 4>), grid, dim3(256), 0, s, a);
-      else hipLaunchKernelGGL((attn_fwd_kernel<BF16, 128, 2, 4>), grid, dim3(256), 0, s, a);
+      if (d == 64) hipExtLaunchKernelGGL((attn_fwd_kernel<BF16, 64, 2, 4>), grid, dim3(256), 0, s, tm.start, tm.stop, 0, a);
+      else hipExtLaunchKernelGGL((attn_fwd_kernel<BF16, 128, 2, 4>), grid, dim3(256), 0, s, tm.start, tm.stop, 0, a);
     } else {
       const int pf = attn_prefetch(d);
       if (d == 64) {
-        if (pf == 4) hipLaunchKernelGGL((attn_fwd_kernel<BF16, 64, 1, 8, 4>), grid, dim3(512), 0, s, a);
-        else if (pf == 2) hipLaunchKernelGGL((attn_fwd_kernel<BF16, 64, 1, 8, 2>), grid, dim3(512), 0, s, a);
-        else hipLaunchKernelGGL((attn_fwd_kernel<BF16, 64, 1, 8, 1>), grid, dim3(512), 0, s, a);
+        if (pf == 4) hipExtLaunchKernelGGL((attn_fwd_kernel<BF16, 64, 1, 8, 4>), grid, dim3(512), 0, s, tm.start, tm.stop, 0, a);
+        else if (pf == 2) hipExtLaunchKernelGGL((attn_fwd_kernel<BF16, 64, 1, 8, 2>), grid, dim3(512), 0, s, tm.start, tm.stop, 0, a);
+        else hipExtLaunchKernelGGL((attn_fwd_kernel<BF16, 64, 1, 8, 1>), grid, dim3(512), 0, s, tm.start, tm.stop, 0, a);
       } else {
-        if (pf == 4) hipLaunchKernelGGL((attn_fwd_kernel<BF16, 128, 1, 8, 4>), grid, dim3(512), 0, s, a);
-        else if (pf == 2) hipLaunchKernelGGL((attn_fwd_kernel<BF16, 128, 1, 8, 2>), grid, dim3(512), 0, s, a);
-        else hipLaunchKernelGGL((attn_fwd_kernel<BF16, 128, 1, 8, 1>), grid, dim3(512), 0, s, a);
+        if (pf == 4) hipExtLaunchKernelGGL((attn_fwd_kernel<BF16, 128, 1, 8, 4>), grid, dim3(512), 0, s, tm.start, tm.stop, 0, a);
+        else if (pf == 2) hipExtLaunchKernelGGL((attn_fwd_kernel<BF16, 128, 1, 8, 2>), grid, dim3(512), 0, s, tm.start, tm.stop, 0, a);
+        else hipExtLaunchKernelGGL((attn_fwd_kernel<BF16, 128, 1, 8, 1>), grid, dim3(512), 0, s, tm.start, tm.stop, 0, a);
       }
     }
   } else {
-    if (d == 64) hipLaunchKernelGGL((attn_fwd_kernel<F32, 64, 1, 4>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((attn_fwd_kernel<F32, 128, 1, 4>), grid, dim3(256), 0, s, a);
+    if (d == 64) hipExtLaunchKernelGGL((attn_fwd_kernel<F32, 64, 1, 4>), grid, dim3(256), 0, s, tm.start, tm.stop, 0, a);
+    else hipExtLaunchKernelGGL((attn_fwd_kernel<F32, 128, 1, 4>), grid, dim3(256), 0, s, tm.start, tm.stop, 0, a);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_score(Dt dt, int d, const ScoreArgs& a, int key_blocks, int rsplits, hipStream_t s) {
+hipError_t launch_score(Dt dt, int d, const ScoreArgs& a, int key_blocks, int rsplits, hipStream_t s,
+                        const LaunchTiming& tm) {
   const dim3 grid(key_blocks, a.Hkv, rsplits);
   if (dt == Dt::BF16) {
     if (score_waves(dt) == 8) {
-      if (d == 64) hipLaunchKernelGGL((attn_score_kernel<BF16, 64, kKtBf16, 8>), grid, dim3(512), 0, s, a);
-      else hipLaunchKernelGGL((attn_score_kernel<BF16, 128, kKtBf16, 8>), grid, dim3(512), 0, s, a);
+      if (d == 64) hipExtLaunchKernelGGL((attn_score_kernel<BF16, 64, kKtBf16, 8>), grid, dim3(512), 0, s, tm.start, tm.stop, 0, a);
+      else hipExtLaunchKernelGGL((attn_score_kernel<BF16, 128, kKtBf16, 8>), grid, dim3(512), 0, s, tm.start, tm.stop, 0, a);
     } else {
-      if (d == 64) hipLaunchKernelGGL((attn_score_kernel<BF16, 64, kKtBf16, 4>), grid, dim3(256), 0, s, a);
-      else hipLaunchKernelGGL((attn_score_kernel<BF16, 128, kKtBf16, 4>), grid, dim3(256), 0, s, a);
+      if (d == 64) hipExtLaunchKernelGGL((attn_score_kernel<BF16, 64, kKtBf16, 4>), grid, dim3(256), 0, s, tm.start, tm.stop, 0, a);
+      else hipExtLaunchKernelGGL((attn_score_kernel<BF16, 128, kKtBf16, 4>), grid, dim3(256), 0, s, tm.start, tm.stop, 0, a);
     }
   } else {
-    if (d == 64) hipLaunchKernelGGL((attn_score_kernel<F32, 64, kKtF32, 4>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((attn_score_kernel<F32, 128, kKtF32, 4>), grid, dim3(256), 0, s, a);
+    if (d == 64) hipExtLaunchKernelGGL((attn_score_kernel<F32, 64, kKtF32, 4>), grid, dim3(256), 0, s, tm.start, tm.stop, 0, a);
+    else hipExtLaunchKernelGGL((attn_score_kernel<F32, 128, kKtF32, 4>), grid, dim3(256), 0, s, tm.start, tm.stop, 0, a);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_select(Dt dt, int d, const SelectArgs& a, hipStream_t s) {
+hipError_t launch_select(Dt dt, int d, const SelectArgs& a, hipStream_t s, const LaunchTiming& tm) {
   const size_t mthreads = ((size_t)a.Hkv * a.R + 31) / 32 * 32 * (d / 4);   // whole 32-row groups
   const dim3 grid((unsigned)(1 + (mthreads + kSelectThreads - 1) / kSelectThreads)), block(kSelectThreads);
   if (dt == Dt::BF16) {
-    if (d == 64) hipLaunchKernelGGL((select_kernel<BF16, 64>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((select_kernel<BF16, 128>), grid, block, 0, s, a);
+    if (d == 64) hipExtLaunchKernelGGL((select_kernel<BF16, 64>), grid, block, 0, s, tm.start, tm.stop, 0, a);
+    else hipExtLaunchKernelGGL((select_kernel<BF16, 128>), grid, block, 0, s, tm.start, tm.stop, 0, a);
   } else {
-    if (d == 64) hipLaunchKernelGGL((select_kernel<F32, 64>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((select_kernel<F32, 128>), grid, block, 0, s, a);
+    if (d == 64) hipExtLaunchKernelGGL((select_kernel<F32, 64>), grid, block, 0, s, tm.start, tm.stop, 0, a);
+    else hipExtLaunchKernelGGL((select_kernel<F32, 128>), grid, block, 0, s, tm.start, tm.stop, 0, a);
   }
   return hipGetLastError();
 }
@@ -1814,28 +1818,29 @@ constexpr int kDecodeWavesBf16 = 4;
 constexpr int kDecodeWavesF32 = 2;
 int decode_block_keys(Dt dt) { return 32 * (dt == Dt::BF16 ? kDecodeWavesBf16 : kDecodeWavesF32); }
 
-hipError_t launch_decode(Dt dt, int d, const DecodeArgs& a, hipStream_t s) {
+hipError_t launch_decode(Dt dt, int d, const DecodeArgs& a, hipStream_t s, const LaunchTiming& tm) {
   const dim3 grid(a.Hkv, a.S);
   if (dt == Dt::BF16) {
     const dim3 block(64 * kDecodeWavesBf16);
-    if (d == 64) hipLaunchKernelGGL((decode_attn_kernel<BF16, 64, kDecodeWavesBf16>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((decode_attn_kernel<BF16, 128, kDecodeWavesBf16>), grid, block, 0, s, a);
+    if (d == 64) hipExtLaunchKernelGGL((decode_attn_kernel<BF16, 64, kDecodeWavesBf16>), grid, block, 0, s, tm.start, tm.stop, 0, a);
+    else hipExtLaunchKernelGGL((decode_attn_kernel<BF16, 128, kDecodeWavesBf16>), grid, block, 0, s, tm.start, tm.stop, 0, a);
   } else {
     const dim3 block(64 * kDecodeWavesF32);
-    if (d == 64) hipLaunchKernelGGL((decode_attn_kernel<F32, 64, kDecodeWavesF32>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((decode_attn_kernel<F32, 128, kDecodeWavesF32>), grid, block, 0, s, a);
+    if (d == 64) hipExtLaunchKernelGGL((decode_attn_kernel<F32, 64, kDecodeWavesF32>), grid, block, 0, s, tm.start, tm.stop, 0, a);
+    else hipExtLaunchKernelGGL((decode_attn_kernel<F32, 128, kDecodeWavesF32>), grid, block, 0, s, tm.start, tm.stop, 0, a);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_decode_merge(Dt dt, int d, const DecodeMergeArgs& a, hipStream_t s) {
+hipError_t launch_decode_merge(Dt dt, int d, const DecodeMergeArgs& a, hipStream_t s,
+                               const LaunchTiming& tm) {
   const dim3 grid((unsigned)((size_t)a.Hkv * a.R)), block(kDecodeMergeThreads);
   if (dt == Dt::BF16) {
-    if (d == 64) hipLaunchKernelGGL((decode_merge_kernel<BF16, 64>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((decode_merge_kernel<BF16, 128>), grid, block, 0, s, a);
+    if (d == 64) hipExtLaunchKernelGGL((decode_merge_kernel<BF16, 64>), grid, block, 0, s, tm.start, tm.stop, 0, a);
+    else hipExtLaunchKernelGGL((decode_merge_kernel<BF16, 128>), grid, block, 0, s, tm.start, tm.stop, 0, a);
   } else {
-    if (d == 64) hipLaunchKernelGGL((decode_merge_kernel<F32, 64>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((decode_merge_kernel<F32, 128>), grid, block, 0, s, a);
+    if (d == 64) hipExtLaunchKernelGGL((decode_merge_kernel<F32, 64>), grid, block, 0, s, tm.start, tm.stop, 0, a);
+    else hipExtLaunchKernelGGL((decode_merge_kernel<F32, 128>), grid, block, 0, s, tm.start, tm.stop, 0, a);
   }
   return hipGetLastError();
 }

@@ -231,16 +231,16 @@ struct KernelTimer {
   statekv_state* s;
   int k;
   bool on;
+  LaunchTiming lt;   // events the timed dispatch records itself
   KernelTimer(statekv_state* st, int kernel)
       : s(st), k(kernel), on((st->flags & STATEKV_FLAG_KERNEL_TIMING) && st->ev_ok) {
     if (!on) return;
     drain_slot(s, s->ev_slot, k);  // the pair recorded kRing frames ago
-    (void)hipEventRecord(s->ev[s->ev_slot][k][0], s->stream);
+    lt.start = s->ev[s->ev_slot][k][0];
+    lt.stop = s->ev[s->ev_slot][k][1];
   }
   void done() {
-    if (!on) return;
-    (void)hipEventRecord(s->ev[s->ev_slot][k][1], s->stream);
-    s->ev_pending[s->ev_slot][k] = true;
+    if (on) s->ev_pending[s->ev_slot][k] = true;
   }
 };
 
@@ -508,7 +508,7 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const 
     a.frame_base = F;
     a.rope_blocks = rope_blocks(s->T);
     a.mv = moves_args(s, s->moves_pending ? s->pending_max_moves : 0);
-    rc = check(launch_rope(s->dt, s->D, a, st));
+    rc = check(launch_rope(s->dt, s->D, a, st, tm.lt));
     tm.done();
     if (rc) return rc;
   }
@@ -536,7 +536,7 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const 
     a.Hkv = s->Hkv;
     a.kv_hs = (int64_t)s->cap * s->D;
     a.kv_rs = s->D;
-    rc = check(launch_attn(s->dt, s->D, a, s->attn_tiles, splits, st));
+    rc = check(launch_attn(s->dt, s->D, a, s->attn_tiles, splits, st, tm.lt));
     tm.done();
     if (rc) return rc;
   }
@@ -562,7 +562,7 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const 
     a.foff = foff;
     a.rps = rps;
     a.Hkv = s->Hkv;
-    rc = check(launch_score(s->dt, s->D, a, key_blocks, rsplits, st));
+    rc = check(launch_score(s->dt, s->D, a, key_blocks, rsplits, st, tm.lt));
     tm.done();
     if (rc) return rc;
   }
@@ -595,7 +595,7 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const 
     a.Hq = s->Hq;
     a.S = splits;
     a.ss = s->stat_ss;
-    rc = check(launch_select(s->dt, s->D, a, st));
+    rc = check(launch_select(s->dt, s->D, a, st, tm.lt));
     tm.done();
     if (rc) return rc;
   }
@@ -656,7 +656,7 @@ int statekv_decode(statekv_state* s, const void* Q, const void* K, const void* V
       a.k0 = P0;
       a.kps = kps;
       a.S = splits;
-      rc = check(launch_decode(s->dt, s->D, a, st));
+      rc = check(launch_decode(s->dt, s->D, a, st, tm.lt));
       tm.done();
       if (rc) return rc;
     }
@@ -672,7 +672,7 @@ int statekv_decode(statekv_state* s, const void* Q, const void* K, const void* V
       a.Hq = s->Hq;
       a.Hkv = s->Hkv;
       a.S = splits;
-      rc = check(launch_decode_merge(s->dt, s->D, a, st));
+      rc = check(launch_decode_merge(s->dt, s->D, a, st, tm.lt));
       tm.done();
       if (rc) return rc;
     }
@@ -698,7 +698,7 @@ int statekv_decode(statekv_state* s, const void* Q, const void* K, const void* V
       a.cap = s->cap;
       a.rope_blocks = rope_blocks(t);
       a.mv = moves_args(s, 0);
-      rc = check(launch_rope(s->dt, s->D, a, st));
+      rc = check(launch_rope(s->dt, s->D, a, st, tm.lt));
       tm.done();
       if (rc) return rc;
     }
@@ -726,7 +726,7 @@ int statekv_decode(statekv_state* s, const void* Q, const void* K, const void* V
       a.Hkv = s->Hkv;
       a.kv_hs = s->D;
       a.kv_rs = (int64_t)s->Hkv * s->D;
-      rc = check(launch_attn(s->dt, s->D, a, tiles, splits, st));
+      rc = check(launch_attn(s->dt, s->D, a, tiles, splits, st, tm.lt));
       tm.done();
       if (rc) return rc;
     }
@@ -745,7 +745,7 @@ int statekv_decode(statekv_state* s, const void* Q, const void* K, const void* V
       a.Hq = s->Hq;
       a.S = splits;
       a.ss = s->stat_ss;
-      rc = check(launch_select(s->dt, s->D, a, st));
+      rc = check(launch_select(s->dt, s->D, a, st, tm.lt));
       tm.done();
       if (rc) return rc;
     }

@@ -72,12 +72,13 @@ class StepCheck:
     """Runs one stream on the GPU; frames in `check` are compared with the oracle
     started from the GPU's own state before that frame (teacher forcing)."""
 
-    def __init__(self, wl: StreamConfig, layer: int = 0, flags: int = 0, max_frames=None):
+    def __init__(self, wl: StreamConfig, layer: int = 0, flags: int = 0, max_frames=None,
+                 max_text: int = 0):
         self.wl = wl
         self.cfg = oracle_cfg(wl)
         if flags & skv.FLAG_RECENT_WINDOW:
             self.cfg = dataclasses.replace(self.cfg, policy="recent")
-        self.st = make_state(wl, max_frames)
+        self.st = make_state(wl, max_frames, max_text)
         if flags:
             self.st.set_flags(flags)
         self.frames = FrameStream(wl, layer)

@@ -19,7 +19,8 @@ import torch
 
 import kv_cache_compression_statekv_amd as skv
 from kv_cache_compression_statekv_amd.workload import CONFIGS, FrameStream, text_tokens
-from gpu_helpers import make_state, oracle_cfg, output_error, to_device, to_f64, OUT_TOL
+from gpu_helpers import (OUT_TOL, StepCheck, assert_step_ok, make_state, oracle_cfg, output_error,
+                         to_device, to_f64)
 from oracle import decode_step, rope_cos_sin, rope_rotate, yarn_inv_freq
 from test_gpu_parity import SMALL
 
@@ -132,6 +133,27 @@ def test_full_size_text_phase(name, frames, chunks, cycle):
     T = wl.tokens_per_frame
     check = sorted({0, frames // 2, frames - 1})
     _run(wl, frames, chunks, check_frames=check, frame_cycle=cycle)
+
+
+@pytest.mark.parametrize("name,frames,check", [("ragged_bf16_d128_yarn", 7, None),
+                                               ("ivl3_1b", 20, [15, 16, 19])],
+                         ids=["small", "ivl3_1b"])
+def test_frames_with_text_capacity(name, frames, check):
+    """A state with text capacity lays out the frame step's split partials with
+    a wider stride: the frames must still match the oracle, and the text
+    that follows must too."""
+    wl = (SMALL.get(name) or CONFIGS[name]).replace(n_frames=frames)
+    chk = StepCheck(wl, flags=skv.FLAG_ALWAYS_SCORE, max_text=8)
+    for n in range(frames):
+        rep = chk.step(check=check is None or n in check)
+        if rep is not None:
+            print(name, rep, flush=True)
+            assert_step_ok(rep, wl.dtype)
+    dk, dv = chk.st.detailed_view()
+    Q, K, V = text_tokens(wl, frames * wl.tokens_per_frame, 8)
+    O = chk.st.decode(to_device(Q, wl.dtype), to_device(K, wl.dtype), to_device(V, wl.dtype))
+    res = decode_step(oracle_cfg(wl), to_f64(dk), to_f64(dv), Q, K, V)
+    assert output_error(to_f64(O), res.O_exact) <= OUT_TOL[wl.dtype]
 
 
 def test_order_and_capacity_errors():
