@@ -10,9 +10,11 @@ are asked for.  All frames are resident in HBM before timing starts; W
 warm-up frames (the first B/T = 16 fill the state) precede K timed steps, so
 every timed step evicts T tokens (constant work per frame).
 
-Printed: one JSON line with frames/s (value), the roofline of the dominant
-kernel (attention pass 1) from HIP events on the library's stream, per-kernel
-times, per-step latency statistics, and the CPU oracle timed on the host
+Printed: one JSON line with frames/s (value, wall clock over the K timed
+steps), per-step latency statistics from events between steps in a second
+pass of K steps (flatness), per-kernel execution times from start / stop
+events recorded by each dispatch in a third pass, the roofline of the
+dominant kernel (attention pass 1), and the CPU oracle timed on the host
 cores on a bounded sample.
 """
 from __future__ import annotations
@@ -379,7 +381,8 @@ def main():
     W = max(args.warmup, fill)
     K = args.steps
     timing_pass = 0 if args.no_kernel_timing else K
-    total = W + K + timing_pass
+    latency_pass = K            # per-step events, no kernel timing: flatness
+    total = W + K + latency_pass + timing_pass
     tdtype = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
@@ -428,22 +431,29 @@ def main():
     elapsed = t1 - t0
     fps = K / elapsed
 
-    # Second pass: per-kernel HIP events (library stream) and per-step events.
+    # Second pass: per-step events on the stream (GPU time of each step, for
+    # flatness).  Third pass: per-kernel execution times from start / stop
+    # events that each dispatch records.
+    stream = torch.cuda.current_stream()
+    n0 = W + K
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(latency_pass + 1)]
+    evs[0].record(stream)
+    for i in range(latency_pass):
+        step(n0 + i)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    lat = [evs[i].elapsed_time(evs[i + 1]) for i in range(latency_pass)]
+    n0 += latency_pass
     kernels = {}
-    lat = []
     if timing_pass:
         st.set_flags(skv.FLAG_KERNEL_TIMING | (skv.FLAG_RECENT_WINDOW if args.recent_window else 0))
         st.kernel_times(reset=True)
-        stream = torch.cuda.current_stream()
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(timing_pass + 1)]
-        evs[0].record(stream)
-        for i, n in enumerate(range(W + K, W + K + timing_pass)):
+        for n in range(n0, n0 + timing_pass):
             step(n)
-            evs[i + 1].record(stream)
         torch.cuda.synchronize()
-        lat = [evs[i].elapsed_time(evs[i + 1]) for i in range(timing_pass)]
         for name, (ms, cnt) in st.kernel_times().items():
-            kernels[name] = {"avg_us": 1e3 * ms / cnt if cnt else None, "launches": cnt}
+            if cnt:
+                kernels[name] = {"avg_us": 1e3 * ms / cnt, "launches": cnt}
         st.set_flags(skv.FLAG_RECENT_WINDOW if args.recent_window else 0)
 
     pairs = pair_count(T, B)
@@ -458,10 +468,9 @@ def main():
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                     "traffic": load_traffic("attn_fwd", args.workload)}
-        t_passes = sum(kernels[k]["avg_us"] for k in ("attn_fwd", "attn_score")
-                       if kernels[k]["avg_us"]) * 1e-6
+        t_passes = sum(kernels[k]["avg_us"] for k in ("attn_fwd", "attn_score") if k in kernels) * 1e-6
         extra["attention_passes_mfma_frac"] = round(executed_flops / t_passes / 1e12 / PEAK_BF16_TFLOPS, 4)
-        t_step_kernels = sum(v["avg_us"] for v in kernels.values() if v["avg_us"]) * 1e-6
+        t_step_kernels = sum(v["avg_us"] for v in kernels.values()) * 1e-6
         extra["kernel_sum_us_per_step"] = round(t_step_kernels * 1e6, 2)
     if lat:
         lat_a = np.array(lat)
