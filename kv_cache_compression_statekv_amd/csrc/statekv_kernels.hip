@@ -126,6 +126,25 @@ template <> struct Store<F32> {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Lane l combined with lane l ^ 32: v_permlane32_swap exchanges the wave's
+// two halves in one VALU instruction (no LDS round trip).  Of its two
+// results, one holds lane l's own value and the other its partner's, in
+// either order; max and sum are symmetric, so both lanes of a pair get the
+// same bits.
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ double halves_sum(double x) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = (uint32_t)b, hi = (uint32_t)(b >> 32);
+  const auto rl = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+  const auto rh = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+  const double a = __builtin_bit_cast(double, (uint64_t)rl[0] | ((uint64_t)rh[0] << 32));
+  const double c = __builtin_bit_cast(double, (uint64_t)rl[1] | ((uint64_t)rh[1] << 32));
+  return a + c;
+}
+
 // ---------------------------------------------------------------------------
 // RoPE at virtual positions + append to the detailed cache.
 // Every (token, head, 8 rotation pairs) has its own thread: x1 = x[k..k+8),
@@ -524,7 +543,7 @@ __device__ __forceinline__ void online_softmax(f32x16_t (&sacc)[QT], float (&m_r
       }
       mx = fmaxf(mx, sacc[qt][i]);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * c_hi;
+    mx = halves_max(mx) * c_hi;
     alpha[qt] = 1.f;
     if (__ballot(mx > m_run[qt] + kLazyRescale)) {   // rare after the first sub-tile
       if (mx > m_run[qt] + kLazyRescale) {
@@ -710,7 +729,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fwd_kernel(AttnArgs a) {
   // Partial results of this key split.
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    const double lt = l_run[qt] + __shfl_xor(l_run[qt], 32);
+    const double lt = halves_sum(l_run[qt]);
     const int r = qrow[qt];
     if (r < a.R) {
       const size_t ri = ((size_t)split * a.Hkv + g) * a.R + r;
@@ -727,7 +746,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fwd_kernel(AttnArgs a) {
           for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
             for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(o[qt][dt][i]));
-          amax = fmaxf(amax, __shfl_xor(amax, 32));
+          amax = halves_max(amax);
           (void)frexpf(amax, &e);   // amax < 2^e
           if (hh == 0) a.epart[ri] = (int8_t)max(-127, min(127, e));
         }
@@ -937,7 +956,7 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_attn_kernel(DecodeArgs a) {
   if (!finite) atomicOr(a.nonfinite, 1);
   // Merge of the waves: m = max_w m_w; each wave's l and O scale by the exact
   // factor 2^(m_w - m); the sums run in wave order.
-  const double lt = l_run[0] + __shfl_xor(l_run[0], 32);
+  const double lt = halves_sum(l_run[0]);
   __syncthreads();                  // the last block's LDS reads are done
   if (hh == 0) {
     wm[wave][col] = m_run[0];
@@ -1252,7 +1271,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_score_kernel(ScoreArgs a) {
   }
 #pragma unroll
   for (int kt = 0; kt < KT; ++kt) {
-    const double tot = cs[kt] + __shfl_xor(cs[kt], 32);
+    const double tot = halves_sum(cs[kt]);
     const int key = key_w + kt * 32 + col;
     if (hh == 0 && key < a.P && tot > 0.0) {
       const unsigned long long fx =
