@@ -63,6 +63,7 @@ struct RopeArgs {
   void* dv;               // [positions][Hkv][d]
   int32_t* nonfinite;     // set to 1 when an input element is NaN or Inf
   int32_t pos0, T, Hq, Hkv, G, cap, frame_base, rope_blocks;
+  int32_t tpw;            // tokens per work-group of the RoPE part
   MovesArgs mv;
 };
 
@@ -174,7 +175,8 @@ int attn_rows_per_wg(Dt dt, int d);
 int score_keys_per_wg(Dt dt);
 int score_waves_per_wg(Dt dt);
 // Work-groups of the RoPE part of the RoPE kernel for T tokens.
-int rope_blocks(int T);
+int rope_tokens_per_wg(int Hq, int Hkv, int d);
+int rope_blocks(int T, int tpw);
 
 hipError_t launch_rope_table(const RopeTableArgs& a, hipStream_t s);
 hipError_t launch_rope(Dt dt, int d, const RopeArgs& a, hipStream_t s, const LaunchTiming& tm = {});

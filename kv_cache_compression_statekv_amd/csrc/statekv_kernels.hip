@@ -34,6 +34,8 @@
 #include <math.h>
 #include <stdlib.h>
 
+#include <algorithm>
+
 namespace statekv {
 namespace {
 
@@ -300,13 +302,12 @@ __device__ __forceinline__ void apply_move_chunk(const MovesArgs& a, size_t t) {
   }
 }
 
-constexpr int kRopeTokensPerWG = 4;
 
 template <class E, int D>
 __global__ __launch_bounds__(256) void rope_append_kernel(RopeArgs a) {
   typedef typename E::T T;
   constexpr int HALF = D / 2;
-  constexpr int TPW = kRopeTokensPerWG;
+  const int TPW = a.tpw;
   constexpr int CH = HALF / 8;  // 8-pair chunks per head
   const int tid = threadIdx.x;
   if ((int)blockIdx.x >= a.rope_blocks) {   // the previous frame's moves
@@ -1769,7 +1770,13 @@ hipError_t launch_rope_table(const RopeTableArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-int rope_blocks(int T) { return (T + kRopeTokensPerWG - 1) / kRopeTokensPerWG; }
+// Tokens per RoPE work-group: about one (token, head, 8 pairs) task per
+// thread, so that each thread's loads are in flight at once.
+int rope_tokens_per_wg(int Hq, int Hkv, int d) {
+  const int per_token = (Hq + Hkv) * (d / 16);
+  return std::max(1, std::min(64, 256 / per_token));
+}
+int rope_blocks(int T, int tpw) { return (T + tpw - 1) / tpw; }
 
 hipError_t launch_rope(Dt dt, int d, const RopeArgs& a, hipStream_t s, const LaunchTiming& tm) {
   const size_t move_tasks = a.mv.max_moves > 0 ? (size_t)a.mv.max_moves * a.Hkv * (a.mv.row_bytes / 16) : 0;

@@ -506,7 +506,8 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const 
     a.G = s->G;
     a.cap = s->cap;
     a.frame_base = F;
-    a.rope_blocks = rope_blocks(s->T);
+    a.tpw = rope_tokens_per_wg(s->Hq, s->Hkv, s->D);
+    a.rope_blocks = rope_blocks(s->T, a.tpw);
     a.mv = moves_args(s, s->moves_pending ? s->pending_max_moves : 0);
     rc = check(launch_rope(s->dt, s->D, a, st, tm.lt));
     tm.done();
@@ -696,7 +697,8 @@ int statekv_decode(statekv_state* s, const void* Q, const void* K, const void* V
       a.Hkv = s->Hkv;
       a.G = s->G;
       a.cap = s->cap;
-      a.rope_blocks = rope_blocks(t);
+      a.tpw = rope_tokens_per_wg(s->Hq, s->Hkv, s->D);
+      a.rope_blocks = rope_blocks(t, a.tpw);
       a.mv = moves_args(s, 0);
       rc = check(launch_rope(s->dt, s->D, a, st, tm.lt));
       tm.done();
