@@ -174,6 +174,8 @@ struct LaunchTiming {
 int attn_rows_per_wg(Dt dt, int d);
 int score_keys_per_wg(Dt dt);
 int score_waves_per_wg(Dt dt);
+// Score work-groups resident per CU (occupancy of the instantiation in use).
+int score_wgs_per_cu(Dt dt, int d);
 // Work-groups of the RoPE part of the RoPE kernel for T tokens.
 int rope_tokens_per_wg(int Hq, int Hkv, int d);
 int rope_blocks(int T, int tpw);

@@ -1128,7 +1128,7 @@ __global__ __launch_bounds__(kDecodeMergeThreads) void decode_merge_kernel(Decod
 // key's fixed-point total.  Every sum has a fixed order (or is an integer
 // sum), so the scores are deterministic.
 // ---------------------------------------------------------------------------
-template <class E, int D, int KT, int NW>
+template <class E, int D, int KT, int NW, int NPF = 1>
 __global__ __launch_bounds__(64 * NW, 1) void attn_score_kernel(ScoreArgs a) {
   typedef typename E::T T;
   typedef Mma<E> M;
@@ -1202,35 +1202,41 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_score_kernel(ScoreArgs a) {
     slim[i] = lim;
   }
 
-  u32x4_t qr[QCH];
-  auto load_tile = [&](int rt) {
+  // NPF register stages of Q tiles: tile it's loads are issued NPF tiles
+  // ahead of its compute; tiles pass through two LDS buffers.
+  u32x4_t qr[NPF][QCH];
+  auto load_tile = [&](u32x4_t (&q)[QCH], int rt) {
 #pragma unroll
     for (int j = 0; j < QCH; ++j) {
       const int t = tid + j * NT;
       const int rr = t / CPR, cc = t - rr * CPR;
       const int r = rt + rr;
-      qr[j] = u32x4_t{0u, 0u, 0u, 0u};
-      if (t < RT * CPR && r < r1) qr[j] = *reinterpret_cast<const u32x4_t*>(qbase + (size_t)r * D + cc * EPV);
+      q[j] = u32x4_t{0u, 0u, 0u, 0u};
+      if (t < RT * CPR && r < r1) q[j] = *reinterpret_cast<const u32x4_t*>(qbase + (size_t)r * D + cc * EPV);
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](const u32x4_t (&q)[QCH], int buf) {
 #pragma unroll
     for (int j = 0; j < QCH; ++j) {
       const int t = tid + j * NT;
       const int rr = t / CPR, cc = t - rr * CPR;
-      if (t < RT * CPR) *reinterpret_cast<u32x4_t*>(&Qs[buf][rr * QSTR + cc * EPV]) = qr[j];
+      if (t < RT * CPR) *reinterpret_cast<u32x4_t*>(&Qs[buf][rr * QSTR + cc * EPV]) = q[j];
     }
   };
 
-  if (ntile > 0) {
-    load_tile(rstart);
-    store_tile(0);
-  }
+#pragma unroll
+  for (int i = 0; i < NPF; ++i)
+    if (i < ntile) load_tile(qr[i], rstart + i * RT);
+  if (ntile > 0) store_tile(qr[0], 0);
   __syncthreads();
-  for (int it = 0; it < ntile; ++it) {
+  for (int it0 = 0; it0 < ntile; it0 += NPF)
+#pragma unroll
+  for (int ip = 0; ip < NPF; ++ip) {
+    const int it = it0 + ip;
+    if (it >= ntile) break;
     const int buf = it & 1;
     const int ro = it * RT;   // tile offset inside the statistics arrays
-    if (it + 1 < ntile) load_tile(rstart + (it + 1) * RT);
+    if (it + NPF < ntile) load_tile(qr[ip], rstart + (it + NPF) * RT);
     // S = Q K^T for the KT key tiles: Q fragments read once per k-slice and
     // fed to KT independent accumulation chains.
     f32x16_t acc[KT];
@@ -1277,7 +1283,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_score_kernel(ScoreArgs a) {
       }
       cs[kt] += (double)sum;
     }
-    if (it + 1 < ntile) store_tile(buf ^ 1);
+    if (it + 1 < ntile) store_tile(qr[(ip + 1) % NPF], buf ^ 1);
     __syncthreads();
   }
 #pragma unroll
@@ -1761,6 +1767,34 @@ static int score_waves(Dt dt) {
   }
   return dt == Dt::BF16 ? v : 4;
 }
+// Register stages of the score pass's Q-tile prefetch: 4 (5-7 % faster on
+// the long-pool shapes); STATEKV_SCORE_PF = 1, 2 or 4 overrides.
+static int score_prefetch() {
+  static int v = -1;
+  if (v < 0) {
+    const char* e = getenv("STATEKV_SCORE_PF");
+    const int x = e ? atoi(e) : 4;
+    v = (x == 1 || x == 2) ? x : 4;
+  }
+  return v;
+}
+
+// Work-groups of the score kernel that fit on one CU at once (0 if unknown).
+int score_wgs_per_cu(Dt dt, int d) {
+  int n = 0;
+  hipError_t e = hipSuccess;
+  if (dt == Dt::BF16 && score_waves(dt) == 4) {
+    const int pf = score_prefetch();
+#define STATEKV_OCC(DD, PF) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_score_kernel<BF16, DD, kKtBf16, 4, PF>, 256, 0)
+    if (d == 64) {
+      if (pf == 4) STATEKV_OCC(64, 4); else if (pf == 2) STATEKV_OCC(64, 2); else STATEKV_OCC(64, 1);
+    } else {
+      if (pf == 4) STATEKV_OCC(128, 4); else if (pf == 2) STATEKV_OCC(128, 2); else STATEKV_OCC(128, 1);
+    }
+#undef STATEKV_OCC
+  }
+  return e == hipSuccess ? n : 0;
+}
 int score_keys_per_wg(Dt dt) { return score_waves(dt) * 32 * (dt == Dt::BF16 ? kKtBf16 : kKtF32); }
 int score_waves_per_wg(Dt dt) { return score_waves(dt); }
 
@@ -1825,8 +1859,14 @@ hipError_t launch_score(Dt dt, int d, const ScoreArgs& a, int key_blocks, int rs
       if (d == 64) hipExtLaunchKernelGGL((attn_score_kernel<BF16, 64, kKtBf16, 8>), grid, dim3(512), 0, s, tm.start, tm.stop, 0, a);
       else hipExtLaunchKernelGGL((attn_score_kernel<BF16, 128, kKtBf16, 8>), grid, dim3(512), 0, s, tm.start, tm.stop, 0, a);
     } else {
-      if (d == 64) hipExtLaunchKernelGGL((attn_score_kernel<BF16, 64, kKtBf16, 4>), grid, dim3(256), 0, s, tm.start, tm.stop, 0, a);
-      else hipExtLaunchKernelGGL((attn_score_kernel<BF16, 128, kKtBf16, 4>), grid, dim3(256), 0, s, tm.start, tm.stop, 0, a);
+      const int pf = score_prefetch();
+#define STATEKV_SCORE(DD, PF) hipExtLaunchKernelGGL((attn_score_kernel<BF16, DD, kKtBf16, 4, PF>), grid, dim3(256), 0, s, tm.start, tm.stop, 0, a)
+      if (d == 64) {
+        if (pf == 4) STATEKV_SCORE(64, 4); else if (pf == 2) STATEKV_SCORE(64, 2); else STATEKV_SCORE(64, 1);
+      } else {
+        if (pf == 4) STATEKV_SCORE(128, 4); else if (pf == 2) STATEKV_SCORE(128, 2); else STATEKV_SCORE(128, 1);
+      }
+#undef STATEKV_SCORE
     }
   } else {
     if (d == 64) hipExtLaunchKernelGGL((attn_score_kernel<F32, 64, kKtF32, 4>), grid, dim3(256), 0, s, tm.start, tm.stop, 0, a);

@@ -55,6 +55,7 @@ struct statekv_state {
   int stat_ss;           // split stride of the pass-1 partials (kMaxSplits with a text phase)
   bool never_evicts;
   int score_rsplits_max;
+  int score_slots;       // score work-groups resident on the device at once (0: unknown)
   int dec_target_wgs;
 
   void* kpool;
@@ -186,13 +187,37 @@ void attn_geometry(const statekv_state* s, int P, int* splits, int* kps) {
   *kps = k;
 }
 
+// Row splits of the score pass.  Every work-group holds its key block and
+// walks its rows; with the resident work-group count known, the split
+// minimises (dispatch rounds) x (rows per work-group + a fixed cost of about
+// kScoreWGRows rows), so that a last, nearly empty round of work-groups is
+// avoided.  Otherwise: about 8 waves per CU.
+constexpr int kScoreWGRows = 48;
+
 void score_geometry(const statekv_state* s, int P, int* key_blocks, int* rsplits, int* rps) {
   const int kb = ceil_div(P, score_keys_per_wg(s->dt));
   const int base = kb * s->Hkv;
-  const int target = kScoreTargetWaves / score_waves_per_wg(s->dt);
-  int rs = std::max(1, std::min(ceil_div(target, base), ceil_div(s->R, 128)));
-  rs = std::min(rs, s->score_rsplits_max);
-  rs = std::max(rs, ceil_div(s->R, kScoreMaxRows));  // rows per work-group fit the LDS statistics
+  const int rs_lo = ceil_div(s->R, kScoreMaxRows);   // rows per work-group fit the LDS statistics
+  int rs;
+  if (s->score_slots > 0) {
+    const int rs_hi = std::max(rs_lo, std::min(s->score_rsplits_max, ceil_div(s->R, 32)));
+    long best = -1;
+    rs = rs_lo;
+    for (int x = rs_lo; x <= rs_hi; ++x) {
+      const int r = ceil_div(ceil_div(s->R, x), 32) * 32;
+      const long wgs = (long)base * ceil_div(s->R, r);
+      const long cost = (wgs + s->score_slots - 1) / s->score_slots * (long)(r + kScoreWGRows);
+      if (best < 0 || cost < best) {
+        best = cost;
+        rs = x;
+      }
+    }
+  } else {
+    const int target = kScoreTargetWaves / score_waves_per_wg(s->dt);
+    rs = std::max(1, std::min(ceil_div(target, base), ceil_div(s->R, 128)));
+    rs = std::min(rs, s->score_rsplits_max);
+    rs = std::max(rs, rs_lo);
+  }
   const int r = ceil_div(ceil_div(s->R, rs), 32) * 32;
   *key_blocks = kb;
   *rsplits = ceil_div(s->R, r);
@@ -354,6 +379,12 @@ int statekv_create(const statekv_layer_cfg* cfg, int32_t budget_B, float alpha,
   s->attn_splits_max = std::min(std::min(kMaxSplits, ceil_div(kAttnTargetWGs, s->attn_tiles * s->Hkv)),
                                 std::max(1, ceil_div(s->cap, 4 * kAttnBN)));
   s->score_rsplits_max = std::max(ceil_div(s->R, kScoreMaxRows), ceil_div(s->R, 32));
+  {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, s->device) != hipSuccess) cus = 0;
+    s->score_slots = cus * score_wgs_per_cu(s->dt, s->D);
+    if (const char* e = getenv("STATEKV_SCORE_SLOTS")) s->score_slots = atoi(e);
+  }
   // Tuning overrides (launch geometry only; the result does not depend on them).
   if (const char* e = getenv("STATEKV_ATTN_SPLITS")) {
     const int v = atoi(e);
