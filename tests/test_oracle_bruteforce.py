@@ -89,3 +89,41 @@ def test_gqa_bf16_frames_match_brute_force():
         assert np.max(np.abs(res.O_exact - out)) < 1e-12
         assert np.max(np.abs(res.scores - np.array(score))) < 1e-14
         assert res.keep.tolist() == keep
+
+
+def _brute_text(cfg, d_k, d_v, q_rot, k_rot, v):
+    """Text tokens after the rows of D: scalar loops over every visible key."""
+    t, Hq, d = q_rot.shape
+    G = Hq // cfg.n_kv_heads
+    P0 = d_k.shape[0]
+    keys = list(d_k) + list(k_rot)
+    vals = list(d_v) + list(v)
+    sigma = 1.0 / math.sqrt(d)
+    out = np.zeros((t, Hq, d))
+    for h in range(Hq):
+        g = h // G
+        for i in range(t):
+            vis = range(P0 + i + 1)          # every row of D, the text up to itself
+            logit = [sigma * sum(float(a) * float(b) for a, b in zip(q_rot[i, h], keys[j][g])) for j in vis]
+            mx = max(logit)
+            w = [math.exp(x - mx) for x in logit]
+            tot = sum(w)
+            for j, wj in zip(vis, w):
+                out[i, h] += (wj / tot) * vals[j][g]
+    return out
+
+
+def test_text_phase_matches_brute_force():
+    """Two frames (the second evicting), then text chunks of 2 and 1 tokens."""
+    cfg = LayerConfig(n_q_heads=4, n_kv_heads=2, head_dim=16, tokens_per_frame=4,
+                      budget=5, dtype="f32", rope_base=1e4)
+    rng = np.random.default_rng(12)
+    f = lambda *s: rng.standard_normal(s).astype(np.float32).astype(np.float64)
+    orc = OracleStream(cfg)
+    for _ in range(2):
+        orc.step(f(4, 4, 16), f(4, 2, 16), f(4, 2, 16))
+    for t in (2, 1):
+        d_k, d_v = orc.detailed()
+        res = orc.decode(f(t, 4, 16), f(t, 2, 16), f(t, 2, 16))
+        want = _brute_text(cfg, d_k, d_v, res.Q_rot, res.K_rot, res.V)
+        assert np.max(np.abs(res.O_exact - want)) < 1e-12
