@@ -519,11 +519,29 @@ def main():
             ostate = frame_step(cfg, ostate, q, k, v, n0 + done).state
             tc += time.perf_counter() - c0
             done += 1
+        # The same oracle on one thread (its matrix products' BLAS limited to
+        # one thread), on a third of the time budget.
+        one = None
+        try:
+            from threadpoolctl import threadpool_limits
+            with threadpool_limits(limits=1, user_api="blas"):
+                d1, t1 = 0, 0.0
+                while t1 < args.cpu_seconds / 3 and d1 < 512:
+                    q, k, v = fs.frame(n0 + done + d1)
+                    c0 = time.perf_counter()
+                    ostate = frame_step(cfg, ostate, q, k, v, n0 + done + d1).state
+                    t1 += time.perf_counter() - c0
+                    d1 += 1
+            one = round(d1 / t1, 4)
+        except ImportError:
+            pass
         cpu = {"value": round(done / tc, 4), "unit": "frames/s", "cores": blas_threads,
+               "value_1_thread": one,
                "kind": "oracle",
                "sample": f"{done} steady-state frames of the same stream (n={n0}..{n0 + done - 1}), "
                          f"float64 numpy oracle, {tc:.1f} s; cores = BLAS threads of its matrix "
-                         "products (element-wise steps run on one thread)"}
+                         "products (element-wise steps run on one thread); value_1_thread: the "
+                         "following frames with BLAS limited to one thread, a third of the time"}
 
     st.close()
     rec = {
