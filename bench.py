@@ -10,6 +10,10 @@ are asked for.  All frames are resident in HBM before timing starts; W
 warm-up frames (the first B/T = 16 fill the state) precede K timed steps, so
 every timed step evicts T tokens (constant work per frame).
 
+--layers L steps a stack of L independent layers of the workload's shape
+(each with its own seeded stream) through one launch per kernel; value is
+then layer-frames/s, L times the stack's steps/s.
+
 Printed: one JSON line with frames/s (value, wall clock over the K timed
 steps), per-step latency statistics from events between steps in a second
 pass of K steps (flatness), per-kernel execution times from start / stop
@@ -42,8 +46,13 @@ def parse_args():
     p.add_argument("--steps", type=int, default=512, help="timed frame steps (K)")
     p.add_argument("--warmup", type=int, default=16, help="untimed frames before timing (W)")
     p.add_argument("--workload", default="ivl3_1b")
-    p.add_argument("--distinct-frames", type=int, default=128,
-                   help="frames drawn from the generator; later steps reuse them cyclically")
+    p.add_argument("--distinct-frames", type=int, default=0,
+                   help="frames drawn from the generator; later steps reuse them cyclically "
+                        "(default: 128 for one layer, 4 for a stack)")
+    p.add_argument("--layers", type=int, default=1,
+                   help="run a stack of L independent layers of the workload's shape, every "
+                        "kernel of the step covering all L layers in one launch; value is then "
+                        "layer-frames/s (L x stack steps/s)")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="bounded CPU work for the oracle baseline (0 disables it)")
     p.add_argument("--no-kernel-timing", action="store_true")
@@ -377,6 +386,7 @@ def main():
         print(json.dumps(rec))
         return
     T, Hq, Hkv, d, B = wl.tokens_per_frame, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.budget
+    L = args.layers
     fill = math.ceil(B / T)
     W = max(args.warmup, fill)
     K = args.steps
@@ -395,19 +405,25 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # Inputs resident in HBM before timing.
-    fs = FrameStream(wl, 0)
-    distinct = min(total, args.distinct_frames)
+    # Inputs resident in HBM before timing (layer l of a stack: the seeded
+    # stream of layer l).
+    streams = [FrameStream(wl, l) for l in range(L)]
+    fs = streams[0]
+    distinct = min(total, args.distinct_frames or (128 if L == 1 else 4))
     frames = []
     for n in range(distinct):
-        q, k, v = fs.frame(n)
-        frames.append(tuple(torch.from_numpy(x).to(tdtype).to(dev).contiguous() for x in (q, k, v)))
-    out = torch.empty((T, Hq, d), dtype=tdtype, device=dev)
+        per_layer = [f.frame(n) for f in streams]
+        frames.append(tuple(
+            torch.from_numpy(per_layer[0][i] if L == 1 else np.stack([x[i] for x in per_layer]))
+            .to(tdtype).to(dev).contiguous() for i in range(3)))
+        if L > 1:
+            print(f"bench: frame {n + 1}/{distinct} of {L} layers uploaded", file=sys.stderr, flush=True)
+    out = torch.empty((T, Hq, d) if L == 1 else (L, T, Hq, d), dtype=tdtype, device=dev)
     torch.cuda.synchronize()
 
     st = skv.StateKV(n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, tokens_per_frame=T,
                      max_frames=total, budget=B, alpha=wl.alpha, dtype=wl.dtype,
-                     rope_base=wl.rope_base, rope_orig_ctx=wl.rope_orig_ctx)
+                     rope_base=wl.rope_base, rope_orig_ctx=wl.rope_orig_ctx, n_layers=L)
     if args.recent_window:
         st.set_flags(skv.FLAG_RECENT_WINDOW)
     lib, h = st._lib, st._h
@@ -429,7 +445,7 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     elapsed = t1 - t0
-    fps = K / elapsed
+    fps = L * K / elapsed      # layer-frames per second
 
     # Second pass: per-step events on the stream (GPU time of each step, for
     # flatness).  Third pass: per-kernel execution times from start / stop
@@ -457,9 +473,9 @@ def main():
         st.set_flags(skv.FLAG_RECENT_WINDOW if args.recent_window else 0)
 
     pairs = pair_count(T, B)
-    attn_flops = 4.0 * Hq * d * pairs                 # QK^T + PV, causal-counted
+    attn_flops = 4.0 * Hq * d * pairs * L             # QK^T + PV, causal-counted, all layers
     # + QK^T recomputed by the score pass (skipped by the recency window)
-    executed_flops = (4.0 if args.recent_window else 6.0) * Hq * d * pairs
+    executed_flops = (4.0 if args.recent_window else 6.0) * Hq * d * pairs * L
     roofline = None
     extra = {}
     if kernels.get("attn_fwd", {}).get("avg_us"):
@@ -467,7 +483,7 @@ def main():
         achieved = attn_flops / t_attn / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                    "traffic": load_traffic("attn_fwd", args.workload)}
+                    "traffic": load_traffic("attn_fwd", args.workload) if L == 1 else None}
         t_passes = sum(kernels[k]["avg_us"] for k in ("attn_fwd", "attn_score") if k in kernels) * 1e-6
         extra["attention_passes_mfma_frac"] = round(executed_flops / t_passes / 1e12 / PEAK_BF16_TFLOPS, 4)
         t_step_kernels = sum(v["avg_us"] for v in kernels.values()) * 1e-6
@@ -507,7 +523,7 @@ def main():
         cfg = LayerConfig(n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, tokens_per_frame=T,
                           budget=B, dtype=wl.dtype, rope_base=wl.rope_base, alpha=wl.alpha,
                           rope_orig_ctx=wl.rope_orig_ctx)
-        kk, vv, pp = st.compressed_view()
+        kk, vv, pp = st.compressed_view(0)
         ostate = CompressedState(kk.float().cpu().numpy().astype(np.float64),
                                  vv.float().cpu().numpy().astype(np.float64),
                                  pp.cpu().numpy().astype(np.int64))
@@ -552,15 +568,18 @@ def main():
         "steps": K,
         "warmup": W,
         "ms_per_step": round(1e3 * elapsed / K, 5),
+        "stack_steps_per_s": round(K / elapsed, 2),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic",
-        "config": {"workload": f"{wl.name}: 1 layer, Hq={Hq}, Hkv={Hkv}, d={d}, T={T}, B={B}, "
+        "config": {"workload": f"{wl.name}: {L} layer{'s' if L > 1 else ''}"
+                               f"{' stepped together (one launch per kernel)' if L > 1 else ''}, "
+                               f"Hq={Hq}, Hkv={Hkv}, d={d}, T={T}, B={B}, "
                                f"alpha={wl.alpha:g}, seeded Gaussian frames with {wl.n_sinks} "
                                f"drifting sink keys per frame",
-                   "tokens_per_frame": T, "budget": B, "layers": 1,
+                   "tokens_per_frame": T, "budget": B, "layers": L,
                    "policy": "recent window (ReKV-style)" if args.recent_window else "StateKV Top-B"},
         "tokens_per_s": round(fps * T, 1),
         "roofline": roofline,

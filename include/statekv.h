@@ -61,7 +61,11 @@ extern "C" {
 #define STATEKV_DTYPE_BF16  1
 #define STATEKV_DTYPE_F32   2
 
-/* Shape and RoPE parameters of one layer. */
+/* Shape and RoPE parameters of one layer; n_layers > 1 makes the state a
+ * stack of L such layers, each with its own compressed state and detailed
+ * cache, that advance frame by frame together (the layers of one stream
+ * position in a frame x layer wavefront, or independent streams of one
+ * shape).  Every frame-step kernel then covers all L layers in one launch. */
 typedef struct statekv_layer_cfg {
   int32_t n_q_heads;        /* Hq >= 1 */
   int32_t n_kv_heads;       /* Hkv >= 1, Hq % Hkv == 0; query head h uses KV head h / (Hq/Hkv) */
@@ -73,6 +77,8 @@ typedef struct statekv_layer_cfg {
   int32_t rope_orig_ctx;    /* original context of the YaRN ramp (>= 1) */
   int32_t max_text;         /* text tokens the detailed cache holds after the
                                frames (>= 0; 0 disables statekv_decode) */
+  int32_t n_layers;         /* L: independent layers held by one state and
+                               stepped together (0 or 1: a single layer) */
 } statekv_layer_cfg;
 
 typedef struct statekv_state statekv_state;
@@ -90,6 +96,9 @@ typedef struct statekv_view {
   int32_t        head_dim;
   int32_t        dtype;
   int32_t        frames_done;  /* frames processed so far */
+  int32_t        n_layers;     /* L */
+  int64_t        layer_stride; /* elements of k / v between consecutive layers */
+  int64_t        pos_layer_stride; /* elements of pos between consecutive layers */
 } statekv_view;
 
 /* Scores and selection of the most recent frame that computed them. */
@@ -100,12 +109,15 @@ typedef struct statekv_scores_view {
   int32_t        pool;      /* candidates: min(B, n*T) + T */
   int32_t        kept;      /* min(B, pool) */
   int32_t        frame;     /* frame index, or -1 if no frame has computed scores */
+  int32_t        n_layers;  /* L */
+  int64_t        layer_stride; /* elements of scores / pool_pos / keep_flag between layers */
 } statekv_scores_view;
 
 /*
- * Create the per-layer state: compressed state of capacity B (empty), the
- * detailed cache for cfg->max_frames * T + cfg->max_text tokens, and all
- * scratch buffers, on the current HIP device.  Everything is allocated here;
+ * Create the per-layer state (per layer of a stack of cfg->n_layers):
+ * compressed state of capacity B (empty), the detailed cache for
+ * cfg->max_frames * T + cfg->max_text tokens, and all scratch buffers, on
+ * the current HIP device.  1 <= n_layers <= 256.  Everything is allocated here;
  * later calls do not allocate.  alpha >= 1 is the global RoPE scaling factor (关键设计 3), fixed
  * for the life of the state.  Requires B >= 1 and B + T <= 32768, except
  * when B >= max_frames * T: such a state never evicts (full causal attention
@@ -120,10 +132,11 @@ int statekv_create(const statekv_layer_cfg* cfg, int32_t budget_B, float alpha,
 int statekv_set_stream(statekv_state* s, void* hip_stream);
 
 /*
- * One StateKV step of frame n (0-based; page frame n+1) for this layer.
- *   Q [T][Hq][d], K [T][Hkv][d], V [T][Hkv][d]: projected, pre-RoPE inputs
- *     (device, caller-owned, read only);
- *   O [T][Hq][d]: attention output (device, caller-owned, written).
+ * One StateKV step of frame n (0-based; page frame n+1) for this layer (for
+ * every layer of a stack: each layer is stepped exactly as a state of its own).
+ *   Q [L][T][Hq][d], K [L][T][Hkv][d], V [L][T][Hkv][d]: projected, pre-RoPE
+ *     inputs (device, caller-owned, read only; L = 1: [T][H][d]);
+ *   O [L][T][Hq][d]: attention output (device, caller-owned, written).
  * Rotates Q and K at positions nT..nT+T-1, attends over [compressed state;
  * frame], appends the rotated K and V to the detailed cache, scores the pool
  * and keeps min(B, pool) candidates as the next compressed state.
@@ -142,6 +155,8 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K,
  * head_stride (elements between KV heads: the row capacity times d) and
  * token_stride = d; pos[count] gives each slot's
  * stream position (slot order; sort by position for a sequence view).
+ * Layer l of a stack starts at k + l*layer_stride (v likewise) and
+ * pos + l*pos_layer_stride; every layer holds count tokens.
  * Synchronises the state's stream.  Valid until the next prefill_frame or
  * destroy.  Returns ENONFINITE if an input frame held NaN or Inf.
  */
@@ -150,7 +165,8 @@ int statekv_compressed_view(const statekv_state* s, statekv_view* out);
 /*
  * Detailed state D: k, v are [count][Hkv][d] (token_stride = Hkv*d,
  * head_stride = d), row p holding the token at stream position p:
- * count = frames_done*T + the text tokens decoded so far.  Synchronises the
+ * count = frames_done*T + the text tokens decoded so far; layer l of a stack
+ * starts at k + l*layer_stride.  Synchronises the
  * state's stream.  Valid until destroy.  Returns ENONFINITE as above.
  */
 int statekv_detailed_view(const statekv_state* s, statekv_view* out);
@@ -158,7 +174,8 @@ int statekv_detailed_view(const statekv_state* s, statekv_view* out);
 /*
  * Scores, pool positions and kept indices of the last frame that computed
  * them (frames whose pool does not exceed B skip scoring unless
- * STATEKV_FLAG_ALWAYS_SCORE is set).  Synchronises the stream; valid until the
+ * STATEKV_FLAG_ALWAYS_SCORE is set); layer l's arrays start layer_stride*l
+ * elements further.  Synchronises the stream; valid until the
  * next prefill_frame or destroy.
  */
 int statekv_scores(const statekv_state* s, statekv_scores_view* out);
@@ -170,9 +187,9 @@ int statekv_scores(const statekv_state* s, statekv_scores_view* out);
  * (prompt chunk or generated tokens) at stream positions P0..P0+t-1, with
  * P0 = frames_done*T + text tokens already decoded, and attends them causally
  * over every row of D:
- *   Q [t][Hq][d], K [t][Hkv][d], V [t][Hkv][d]: projected, pre-RoPE inputs
- *     (device, caller-owned, read only);
- *   O [t][Hq][d]: attention output (device, caller-owned, written).
+ *   Q [L][t][Hq][d], K [L][t][Hkv][d], V [L][t][Hkv][d]: projected, pre-RoPE
+ *     inputs (device, caller-owned, read only; L = 1: [t][H][d]);
+ *   O [L][t][Hq][d]: attention output (device, caller-owned, written).
  * Query i sees D rows 0..P0+i (all frame tokens, earlier text, itself).  The
  * compressed state is neither read nor changed.  1 <= t <= T (EINVAL
  * otherwise); ECAPACITY when the text would exceed cfg->max_text.  After the

@@ -52,6 +52,7 @@ class LayerCfg(ctypes.Structure):
         ("rope_base", ctypes.c_double),
         ("rope_orig_ctx", ctypes.c_int32),
         ("max_text", ctypes.c_int32),
+        ("n_layers", ctypes.c_int32),
     ]
 
 
@@ -67,6 +68,9 @@ class View(ctypes.Structure):
         ("head_dim", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
         ("frames_done", ctypes.c_int32),
+        ("n_layers", ctypes.c_int32),
+        ("layer_stride", ctypes.c_int64),
+        ("pos_layer_stride", ctypes.c_int64),
     ]
 
 
@@ -78,6 +82,8 @@ class ScoresView(ctypes.Structure):
         ("pool", ctypes.c_int32),
         ("kept", ctypes.c_int32),
         ("frame", ctypes.c_int32),
+        ("n_layers", ctypes.c_int32),
+        ("layer_stride", ctypes.c_int64),
     ]
 
 
@@ -160,12 +166,14 @@ _ABI_DTYPE = {"bf16": DTYPE_BF16, "f32": DTYPE_F32}
 
 
 class StateKV:
-    """One layer's StateKV state on the current GPU (compressed state C and detailed cache D)."""
+    """One layer's StateKV state on the current GPU (compressed state C and detailed cache D),
+    or with n_layers > 1 a stack of independent layers stepped together: frame tensors then
+    carry a leading layer dimension ([L][T][H][d]) and views take a layer index."""
 
     def __init__(self, *, n_q_heads: int, n_kv_heads: int, head_dim: int,
                  tokens_per_frame: int, max_frames: int, budget: int, alpha: float = 1.0,
                  dtype: str = "bf16", rope_base: float = 1e6, rope_orig_ctx: int = 32768,
-                 max_text: int = 0, stream=None):
+                 max_text: int = 0, n_layers: int = 1, stream=None):
         self._lib = load_library()
         if dtype not in _ABI_DTYPE:
             raise ValueError(f"dtype must be 'bf16' or 'f32', not {dtype!r}")
@@ -175,9 +183,10 @@ class StateKV:
         self.T, self.max_frames, self.budget = tokens_per_frame, max_frames, budget
         self.alpha = alpha
         self.max_text = max_text
+        self.L = n_layers
         self.device = torch.device("cuda", torch.cuda.current_device())
         cfg = LayerCfg(n_q_heads, n_kv_heads, head_dim, tokens_per_frame, max_frames,
-                       _ABI_DTYPE[dtype], float(rope_base), rope_orig_ctx, max_text)
+                       _ABI_DTYPE[dtype], float(rope_base), rope_orig_ctx, max_text, n_layers)
         handle = ctypes.c_void_p()
         rc = self._lib.statekv_create(ctypes.byref(cfg), budget, float(alpha), ctypes.byref(handle))
         if rc != STATEKV_OK:
@@ -211,20 +220,25 @@ class StateKV:
         self._check(self._lib.statekv_set_flags(self._h, flags), "statekv_set_flags")
 
     # -- the frame step -------------------------------------------------------
+    def _shape(self, tokens: int, heads: int):
+        one = (tokens, heads, self.d)
+        return one if self.L == 1 else (self.L,) + one
+
     def _frame_tensor(self, x: torch.Tensor, heads: int, name: str, tokens=None):
-        want = (self.T if tokens is None else tokens, heads, self.d)
+        want = self._shape(self.T if tokens is None else tokens, heads)
         if not isinstance(x, torch.Tensor) or x.device.type != "cuda":
             raise ValueError(f"{name} must be a CUDA/HIP tensor")
         if x.dtype != self.torch_dtype or tuple(x.shape) != want or not x.is_contiguous():
             raise ValueError(f"{name} must be a contiguous {self.torch_dtype} tensor of shape {want}")
 
     def prefill_frame(self, Q, K, V, n: int, out=None) -> torch.Tensor:
-        """Run frame n; returns O [T][Hq][d] (written asynchronously on the state's stream)."""
+        """Run frame n; returns O [T][Hq][d] ([L][T][Hq][d] for a stack), written
+        asynchronously on the state's stream."""
         self._frame_tensor(Q, self.Hq, "Q")
         self._frame_tensor(K, self.Hkv, "K")
         self._frame_tensor(V, self.Hkv, "V")
         if out is None:
-            out = torch.empty((self.T, self.Hq, self.d), dtype=self.torch_dtype, device=Q.device)
+            out = torch.empty(self._shape(self.T, self.Hq), dtype=self.torch_dtype, device=Q.device)
         else:
             self._frame_tensor(out, self.Hq, "out")
         self._check(self._lib.statekv_prefill_frame(self._h, Q.data_ptr(), K.data_ptr(),
@@ -236,13 +250,15 @@ class StateKV:
     def decode(self, Q, K, V, out=None) -> torch.Tensor:
         """Append t text tokens (Q [t][Hq][d], K, V [t][Hkv][d]) after everything
         processed so far and attend them over the whole detailed cache; returns
-        O [t][Hq][d] (asynchronous on the state's stream)."""
-        t = Q.shape[0] if isinstance(Q, torch.Tensor) and Q.dim() == 3 else -1
+        O [t][Hq][d] (asynchronous on the state's stream).  A stack takes and returns
+        [L][t][H][d]."""
+        rank = 3 if self.L == 1 else 4
+        t = Q.shape[rank - 3] if isinstance(Q, torch.Tensor) and Q.dim() == rank else -1
         self._frame_tensor(Q, self.Hq, "Q", t)
         self._frame_tensor(K, self.Hkv, "K", t)
         self._frame_tensor(V, self.Hkv, "V", t)
         if out is None:
-            out = torch.empty((t, self.Hq, self.d), dtype=self.torch_dtype, device=Q.device)
+            out = torch.empty(self._shape(t, self.Hq), dtype=self.torch_dtype, device=Q.device)
         else:
             self._frame_tensor(out, self.Hq, "out", t)
         self._check(self._lib.statekv_decode(self._h, Q.data_ptr(), K.data_ptr(), V.data_ptr(),
@@ -251,37 +267,53 @@ class StateKV:
         return out
 
     # -- views (copied into new tensors) ------------------------------------------
-    def compressed_view(self):
-        """(Kbar [Hkv][count][d], Vbar [Hkv][count][d], pos [count] int32), copies in slot order."""
+    def _layer(self, layer: int) -> int:
+        if not 0 <= layer < self.L:
+            raise ValueError(f"layer {layer} out of range for a stack of {self.L}")
+        return layer
+
+    def compressed_view(self, layer: int = 0):
+        """(Kbar [Hkv][count][d], Vbar [Hkv][count][d], pos [count] int32) of one layer,
+        copies in slot order."""
+        self._layer(layer)
         v = View()
         self._check(self._lib.statekv_compressed_view(self._h, ctypes.byref(v)),
                     "statekv_compressed_view")
         cap = v.head_stride // v.head_dim
-        k = _copy_to_tensor(v.k, (v.n_kv_heads, cap, v.head_dim), self.torch_dtype, self.device)
-        vv = _copy_to_tensor(v.v, (v.n_kv_heads, cap, v.head_dim), self.torch_dtype, self.device)
-        pos = _copy_to_tensor(v.pos, (v.count,), torch.int32, self.device)
+        esz = 2 if self.dtype == "bf16" else 4
+        ko = layer * v.layer_stride * esz
+        k = _copy_to_tensor(v.k + ko, (v.n_kv_heads, cap, v.head_dim), self.torch_dtype, self.device)
+        vv = _copy_to_tensor(v.v + ko, (v.n_kv_heads, cap, v.head_dim), self.torch_dtype, self.device)
+        pos = _copy_to_tensor(v.pos + layer * v.pos_layer_stride * 4, (v.count,), torch.int32,
+                              self.device)
         return k[:, : v.count].contiguous(), vv[:, : v.count].contiguous(), pos
 
-    def detailed_view(self):
-        """(D_K [count][Hkv][d], D_V [count][Hkv][d]), copies; count = n*T + text tokens."""
+    def detailed_view(self, layer: int = 0):
+        """(D_K [count][Hkv][d], D_V [count][Hkv][d]) of one layer, copies;
+        count = n*T + text tokens."""
+        self._layer(layer)
         v = View()
         self._check(self._lib.statekv_detailed_view(self._h, ctypes.byref(v)),
                     "statekv_detailed_view")
         shape = (v.count, v.n_kv_heads, v.head_dim)
-        return (_copy_to_tensor(v.k, shape, self.torch_dtype, self.device),
-                _copy_to_tensor(v.v, shape, self.torch_dtype, self.device))
+        ko = layer * v.layer_stride * (2 if self.dtype == "bf16" else 4)
+        return (_copy_to_tensor(v.k + ko, shape, self.torch_dtype, self.device),
+                _copy_to_tensor(v.v + ko, shape, self.torch_dtype, self.device))
 
-    def scores(self):
-        """dict(frame, scores [pool] f32, pool_pos [pool] i32, keep_flag [pool] i32) or None."""
+    def scores(self, layer: int = 0):
+        """dict(frame, scores [pool] f32, pool_pos [pool] i32, keep_flag [pool] i32) of one
+        layer, or None."""
+        self._layer(layer)
         sv = ScoresView()
         self._check(self._lib.statekv_scores(self._h, ctypes.byref(sv)), "statekv_scores")
         if sv.frame < 0:
             return None
+        o = layer * sv.layer_stride * 4
         return {
             "frame": sv.frame,
-            "scores": _copy_to_tensor(sv.scores, (sv.pool,), torch.float32, self.device),
-            "pool_pos": _copy_to_tensor(sv.pool_pos, (sv.pool,), torch.int32, self.device),
-            "keep_flag": _copy_to_tensor(sv.keep_flag, (sv.pool,), torch.int32, self.device),
+            "scores": _copy_to_tensor(sv.scores + o, (sv.pool,), torch.float32, self.device),
+            "pool_pos": _copy_to_tensor(sv.pool_pos + o, (sv.pool,), torch.int32, self.device),
+            "keep_flag": _copy_to_tensor(sv.keep_flag + o, (sv.pool,), torch.int32, self.device),
         }
 
     def kernel_times(self, reset: bool = False):

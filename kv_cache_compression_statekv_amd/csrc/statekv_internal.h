@@ -23,6 +23,7 @@ constexpr int kDecodeMaxSplits = 1024;  // key splits of the text-phase attentio
 // Hq*T (every weight 1), which stays below 2^63 for Hq*T <= 2^22.
 constexpr int kScoreFracBits = 40;
 constexpr int64_t kMaxRowsTimesHeads = 1 << 22;
+constexpr int kMaxLayers = 256;      // layers of one state (a stack stepped together)
 
 // Cos / sin table of the scaled RoPE angles, built once per state.
 struct RopeTableArgs {
@@ -33,7 +34,9 @@ struct RopeTableArgs {
 
 // Moves of a selection: row move_src[i] (a frame row at or beyond B) ->
 // slot move_dst[i] (< B) of every KV head, with its position; the position
-// the slot held is saved in evicted_pos[slot].
+// the slot held is saved in evicted_pos[slot].  Pointers address layer 0 of
+// a stack; layer l's arrays follow at fixed strides: Hkv*cap rows (pools),
+// cap (pool_pos), B (evicted_pos), list_stride (move lists), 1 (move_count).
 struct MovesArgs {
   void* kpool;
   void* vpool;
@@ -42,7 +45,7 @@ struct MovesArgs {
   const int32_t* move_dst;
   const int32_t* move_src;
   const int32_t* move_count;
-  int32_t Hkv, cap, B, row_bytes, max_moves;
+  int32_t Hkv, cap, B, row_bytes, max_moves, list_stride;
 };
 
 // Arguments of the RoPE + append kernel for T tokens at stream positions
@@ -50,6 +53,8 @@ struct MovesArgs {
 // beyond rope_blocks apply the previous frame's moves (mv.max_moves > 0):
 // they touch state slots below B and the previous frame's rows, never this
 // frame's.  Text tokens go to D only (kpool, vpool and pool_pos null).
+// Layer l of a stack (grid y) finds its inputs and qrot T*H*d elements per
+// layer further, its pool Hkv*cap*d, pool_pos cap and D det_ls.
 struct RopeArgs {
   const void* q;          // [T][Hq][d]
   const void* k;          // [T][Hkv][d]
@@ -64,6 +69,7 @@ struct RopeArgs {
   int32_t* nonfinite;     // set to 1 when an input element is NaN or Inf
   int32_t pos0, T, Hq, Hkv, G, cap, frame_base, rope_blocks;
   int32_t tpw;            // tokens per work-group of the RoPE part
+  int64_t det_ls;         // elements between layers of dk / dv
   MovesArgs mv;
 };
 
@@ -73,7 +79,10 @@ __host__ __device__ inline int pool_row(int j, int k0, int foff) { return j < k0
 
 // Attention pass 1: one work-group per (row tile, KV head, key split).
 // Per split and row it leaves (m_s, l_s, O_s) with m_s an integer (log2 units)
-// so that merging splits scales by exact powers of two.
+// so that merging splits scales by exact powers of two.  The KV heads of a
+// stack's layers are numbered layer-major (head = layer*lh + head in layer):
+// qrot and the partials are head-major over all of them; keys and values of
+// head (l, h) start at l*kv_ls + h*kv_hs.
 struct AttnArgs {
   const void* qrot;       // [Hkv][R][d]
   const void* kpool;      // [Hkv][cap][d]
@@ -85,27 +94,35 @@ struct AttnArgs {
   double* lpart;          // sums of 2^(x*c - m_s), per (row, split): split-major inside
                           // groups of 32 rows
   float c_hi;             // sigma * log2(e) rounded to fp32
-  int32_t R, G, cap, P, k0, foff, kps, Hkv;
+  int32_t R, G, cap, P, k0, foff, kps, Hkv;   // Hkv: KV heads of all layers
   int32_t ss;             // split stride of the statistics (maximum splits)
+  int32_t lh;             // KV heads per layer
   // Element strides of the key / value rows: between KV heads and between
   // rows.  The pool is [Hkv][cap][d] (cap*d, d); the detailed cache, read by
   // text chunks, is [positions][Hkv][d] (d, Hkv*d).
   int64_t kv_hs, kv_rs;
+  int64_t kv_ls;          // elements between layers of the key / value arrays
 };
 
-// Score pass: one work-group per (key block, KV head, row split).
+// Score pass: one work-group per (key block, KV head, row split); KV heads
+// of all layers of a stack, layer-major as in pass 1.
 struct ScoreArgs {
   const void* qrot;
   const void* kpool;
   const float* mpart;
   const double* lpart;
-  unsigned long long* colsum;  // [cap] column sums, fixed point (2^-kScoreFracBits units)
+  unsigned long long* colsum;  // [L][cap] column sums, fixed point (2^-kScoreFracBits units)
   float c_hi, c_lo;            // sigma * log2(e) = c_hi + c_lo
   int32_t R, G, cap, P, k0, foff, rps, Hkv, S, ss;
+  int32_t lh;                  // KV heads per layer
 };
 
 // Text-phase attention over the detailed cache D (token-major rows) for at
-// most 32 query rows per KV head: one work-group per (KV head, key split).
+// most 32 query rows per KV head: one work-group per (KV head, key split),
+// over the KV heads of all L layers of a stack (grid x = L*Hkv, layer-major).
+// Pointers address layer 0: layer l's inputs and output follow t*H*d
+// elements per layer further, its D rows det_ls further; the partials are
+// head-major over all L*Hkv heads.
 // Its NW waves take the 32-key sub-tiles of every block of 32*NW keys and are
 // merged in LDS at the end.  With one split the work-group writes O;
 // otherwise it leaves (m_s, l_s, O_s) for the merge kernel.
@@ -126,18 +143,23 @@ struct DecodeArgs {
   void* out;              // [t][Hq][d] (S == 1)
   float c_hi;             // sigma * log2(e) rounded to fp32
   int32_t R, G, Hq, Hkv, P, k0, kps, S;  // P = k0 + t keys; k0 keys precede the text
+  int32_t L;              // layers
+  int64_t det_ls;         // elements between layers of dk / dv
 };
 
 struct DecodeMergeArgs {
   const float* opart;
   const float* mpart;
   const double* lpart;
-  void* out;              // [t][Hq][d]
-  int32_t R, G, Hq, Hkv, S;
+  void* out;              // [L][t][Hq][d]
+  int32_t R, G, Hq, Hkv, S, L;   // Hkv per layer
 };
 
-// Work-group 0: scores and the Top-B decision; work-groups 1..: the merge of
-// the key splits of pass 1 into O (independent of the selection).
+// Work-groups 0..L-1: scores and the Top-B decision of layer l (none in
+// kSelMerge mode); the others: the merge of the key splits of pass 1 into O
+// (independent of the selection).  Selection pointers address layer 0; layer
+// l's arrays follow cap (colsum, pool_pos, scores, keep_flag), list_stride
+// (move lists) and 1 (move_count) elements further.
 struct SelectArgs {
   unsigned long long* colsum;  // [cap] fixed-point column sums; cleared after reading
   const int32_t* pool_pos;     // [cap] positions of the pool rows (by row)
@@ -155,8 +177,10 @@ struct SelectArgs {
   const int8_t* epart;
   const float* mpart;
   const double* lpart;
-  void* out;                   // [T][Hq][d]
-  int32_t Hkv, R, G, Hq, S, ss;
+  void* out;                   // [L][T][Hq][d]
+  int32_t Hkv, R, G, Hq, S, ss;   // Hkv: KV heads of all layers (layer-major)
+  int32_t L, lh, cap, list_stride;
+  int64_t out_ls;              // elements of out between layers
 };
 constexpr int kSelMerge = 0;   // merge only (the pool fits in B and is not scored)
 constexpr int kSelScores = 1;  // scores, everything kept
@@ -181,13 +205,14 @@ int rope_tokens_per_wg(int Hq, int Hkv, int d);
 int rope_blocks(int T, int tpw);
 
 hipError_t launch_rope_table(const RopeTableArgs& a, hipStream_t s);
-hipError_t launch_rope(Dt dt, int d, const RopeArgs& a, hipStream_t s, const LaunchTiming& tm = {});
+hipError_t launch_rope(Dt dt, int d, const RopeArgs& a, int layers, hipStream_t s,
+                       const LaunchTiming& tm = {});
 hipError_t launch_attn(Dt dt, int d, const AttnArgs& a, int row_tiles, int splits, hipStream_t s,
                        const LaunchTiming& tm = {});
 hipError_t launch_score(Dt dt, int d, const ScoreArgs& a, int key_blocks, int rsplits, hipStream_t s,
                         const LaunchTiming& tm = {});
 hipError_t launch_select(Dt dt, int d, const SelectArgs& a, hipStream_t s, const LaunchTiming& tm = {});
-hipError_t launch_moves(const MovesArgs& a, hipStream_t s);
+hipError_t launch_moves(const MovesArgs& a, int layers, hipStream_t s);
 // Keys per block of the text-phase attention kernel.
 int decode_block_keys(Dt dt);
 hipError_t launch_decode(Dt dt, int d, const DecodeArgs& a, hipStream_t s, const LaunchTiming& tm = {});
@@ -195,8 +220,11 @@ hipError_t launch_decode_merge(Dt dt, int d, const DecodeMergeArgs& a, hipStream
                                const LaunchTiming& tm = {});
 // Positions of a scored pool of P candidates: the position of its row, or
 // for an evicted slot below B that a move has since filled, the saved one.
+// Layer l's arrays follow cap (score_pos, pool_pos, keep_flag) and B
+// (evicted_pos) elements further.
 hipError_t launch_score_positions(int32_t* score_pos, const int32_t* pool_pos,
                                   const int32_t* evicted_pos, const int32_t* keep_flag, int P,
-                                  int B, int k0, int foff, bool moved, hipStream_t s);
+                                  int B, int k0, int foff, bool moved, int cap, int layers,
+                                  hipStream_t s);
 
 }  // namespace statekv

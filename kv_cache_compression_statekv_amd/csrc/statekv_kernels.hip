@@ -281,6 +281,19 @@ __device__ __forceinline__ int xcd_remap(int id, int n) {
   return xcd * q + min(xcd, r) + local;
 }
 
+// Layer l's slice of a stack's move arguments.
+__device__ __forceinline__ MovesArgs moves_layer(MovesArgs a, int l) {
+  const size_t pool_bytes = (size_t)a.Hkv * a.cap * a.row_bytes;
+  a.kpool = (char*)a.kpool + l * pool_bytes;
+  a.vpool = (char*)a.vpool + l * pool_bytes;
+  a.pool_pos += (size_t)l * a.cap;
+  a.evicted_pos += (size_t)l * a.B;
+  a.move_dst += (size_t)l * a.list_stride;
+  a.move_src += (size_t)l * a.list_stride;
+  a.move_count += l;
+  return a;
+}
+
 // One 16-byte chunk of a move: task t = (move i, KV head g, chunk c); K and V.
 // The move list holds slots below B and rows in [B, cap); clamping only
 // guards the copy against a malformed list.
@@ -304,15 +317,33 @@ __device__ __forceinline__ void apply_move_chunk(const MovesArgs& a, size_t t) {
 
 
 template <class E, int D>
-__global__ __launch_bounds__(256) void rope_append_kernel(RopeArgs a) {
+__global__ __launch_bounds__(256) void rope_append_kernel(RopeArgs a0) {
   typedef typename E::T T;
   constexpr int HALF = D / 2;
-  const int TPW = a.tpw;
+  const int TPW = a0.tpw;
   constexpr int CH = HALF / 8;  // 8-pair chunks per head
   const int tid = threadIdx.x;
-  if ((int)blockIdx.x >= a.rope_blocks) {   // the previous frame's moves
-    apply_move_chunk(a.mv, (size_t)(blockIdx.x - a.rope_blocks) * 256 + tid);
+  // Layer blockIdx.y of a stack: its slice of every array.
+  const size_t layer = blockIdx.y;
+  if ((int)blockIdx.x >= a0.rope_blocks) {   // the previous frame's moves
+    apply_move_chunk(moves_layer(a0.mv, (int)layer), (size_t)(blockIdx.x - a0.rope_blocks) * 256 + tid);
     return;
+  }
+  RopeArgs a = a0;
+  {
+    const size_t q_ls = (size_t)a.T * a.Hq * D, kv_ls = (size_t)a.T * a.Hkv * D;
+    const size_t pool_ls = (size_t)a.Hkv * a.cap * D;
+    a.q = (const T*)a.q + layer * q_ls;
+    a.k = (const T*)a.k + layer * kv_ls;
+    a.v = (const T*)a.v + layer * kv_ls;
+    a.qrot = (T*)a.qrot + layer * q_ls;
+    if (a.kpool) {
+      a.kpool = (T*)a.kpool + layer * pool_ls;
+      a.vpool = (T*)a.vpool + layer * pool_ls;
+      a.pool_pos += layer * a.cap;
+    }
+    a.dk = (T*)a.dk + layer * a.det_ls;
+    a.dv = (T*)a.dv + layer * a.det_ls;
   }
   const int tok0 = blockIdx.x * TPW;
   bool finite = true;
@@ -607,8 +638,10 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fwd_kernel(AttnArgs a) {
   const int full_end = min(kend, a.k0 + tok_min + 1);
 
   const T* qbase = (const T*)a.qrot + (size_t)g * a.R * D;
-  const T* kbase = (const T*)a.kpool + (size_t)g * a.kv_hs;
-  const T* vbase = (const T*)a.vpool + (size_t)g * a.kv_hs;
+  const int layer = g / a.lh, gl = g - layer * a.lh;
+  const size_t kvo = (size_t)layer * a.kv_ls + (size_t)gl * a.kv_hs;
+  const T* kbase = (const T*)a.kpool + kvo;
+  const T* vbase = (const T*)a.vpool + kvo;
   const size_t rs = (size_t)a.kv_rs;
 
   typename M::Frag qf[QT][NKS];
@@ -784,7 +817,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fwd_kernel(AttnArgs a) {
 // Visibility: key j is seen by the query of text token i iff j < k0 + i + 1.
 // ---------------------------------------------------------------------------
 template <class E, int D, int NW, int NPF = 1>
-__global__ __launch_bounds__(64 * NW, NPF > 1 ? 1 : 2) void decode_attn_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * NW, NPF > 1 ? 1 : 2) void decode_attn_kernel(DecodeArgs a0) {
   typedef typename E::T T;
   typedef Mma<E> M;
   constexpr int NT = 64 * NW;
@@ -811,7 +844,18 @@ __global__ __launch_bounds__(64 * NW, NPF > 1 ? 1 : 2) void decode_attn_kernel(D
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, hh = lane >> 5;
-  const int g = blockIdx.x, split = blockIdx.y;
+  const int gf = blockIdx.x, split = blockIdx.y;   // KV head over all layers
+  const int layer = gf / a0.Hkv, g = gf - layer * a0.Hkv;
+  DecodeArgs a = a0;   // layer's slice of inputs, D and output
+  {
+    const size_t t_ = (size_t)(a.R / a.G);
+    a.q = (const T*)a.q + layer * t_ * a.Hq * D;
+    a.out = (T*)a.out + layer * t_ * a.Hq * D;
+    a.k = (const T*)a.k + layer * t_ * a.Hkv * D;
+    a.v = (const T*)a.v + layer * t_ * a.Hkv * D;
+    a.dk = (const T*)a.dk + (size_t)layer * a.det_ls;
+    a.dv = (const T*)a.dv + (size_t)layer * a.det_ls;
+  }
   const int row0 = 0;
   const int row_last = a.R - 1;
   const int kbeg = split * a.kps;
@@ -1015,7 +1059,7 @@ __global__ __launch_bounds__(64 * NW, NPF > 1 ? 1 : 2) void decode_attn_kernel(D
         *reinterpret_cast<f32x4_t*>(out) = acc * inv;
       }
     } else {
-      const size_t ri = ((size_t)split * a.Hkv + g) * a.R + row;
+      const size_t ri = ((size_t)split * a.L * a.Hkv + gf) * a.R + row;
       *reinterpret_cast<f32x4_t*>(a.opart + ri * D + c * 4) = acc;
       if (c == 0) {
         a.mpart[ri] = mr;
@@ -1047,8 +1091,8 @@ __global__ __launch_bounds__(kDecodeMergeThreads) void decode_merge_kernel(Decod
   __shared__ __attribute__((aligned(16))) f32x4_t redo[SG][CPR];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const size_t nrows = (size_t)a.Hkv * a.R;
-  const size_t row = blockIdx.x;                     // = g*R + r
+  const size_t nrows = (size_t)a.L * a.Hkv * a.R;
+  const size_t row = blockIdx.x;                     // = (layer*Hkv + g)*R + r
   const int c = tid % CPR, sg = tid / CPR;
   // Every load is issued before the first reduction: the statistics of this
   // thread's split and the first PF partial outputs of its split group.
@@ -1102,10 +1146,11 @@ __global__ __launch_bounds__(kDecodeMergeThreads) void decode_merge_kernel(Decod
 #pragma unroll
   for (int w = 1; w < NWV; ++w) l += wl[w];
   const float inv = (float)(1.0 / l);
-  const int g = (int)(row / a.R), r = (int)(row - (size_t)g * a.R);
+  const int gf = (int)(row / a.R), r = (int)(row - (size_t)gf * a.R);
+  const int layer = gf / a.Hkv, g = gf - layer * a.Hkv;
   const int tok = r / a.G;
   const int h = g * a.G + (r - tok * a.G);
-  T* out = (T*)a.out + ((size_t)tok * a.Hq + h) * D + c * 4;
+  T* out = (T*)a.out + (size_t)layer * (a.R / a.G) * a.Hq * D + ((size_t)tok * a.Hq + h) * D + c * 4;
   if constexpr (sizeof(T) == 2) {
     const u32x2_t v = {(uint32_t)f32_to_bf16(acc[0] * inv) | ((uint32_t)f32_to_bf16(acc[1] * inv) << 16),
                        (uint32_t)f32_to_bf16(acc[2] * inv) | ((uint32_t)f32_to_bf16(acc[3] * inv) << 16)};
@@ -1293,7 +1338,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_score_kernel(ScoreArgs a) {
     if (hh == 0 && key < a.P && tot > 0.0) {
       const unsigned long long fx =
           (unsigned long long)(tot * (double)(1ull << kScoreFracBits) + 0.5);
-      atomicAdd(&a.colsum[key], fx);
+      atomicAdd(&a.colsum[(size_t)(g / a.lh) * a.cap + key], fx);
     }
   }
 }
@@ -1680,9 +1725,10 @@ __device__ void merge_splits(const SelectArgs& a, int wg, float* lds) {
   }
   const float inv = rinv[lrow];
   const int g = (int)(base / a.R), r = (int)(base - (size_t)g * a.R);
+  const int layer = g / a.lh;
   const int tok = r / a.G;
-  const int h = g * a.G + (r - tok * a.G);
-  T* out = (T*)a.out + ((size_t)tok * a.Hq + h) * D + c * 4;
+  const int h = (g - layer * a.lh) * a.G + (r - tok * a.G);
+  T* out = (T*)a.out + (size_t)layer * a.out_ls + ((size_t)tok * a.Hq + h) * D + c * 4;
   if constexpr (sizeof(T) == 2) {
     const u32x2_t v = {(uint32_t)f32_to_bf16(acc[0] * inv) | ((uint32_t)f32_to_bf16(acc[1] * inv) << 16),
                        (uint32_t)f32_to_bf16(acc[2] * inv) | ((uint32_t)f32_to_bf16(acc[3] * inv) << 16)};
@@ -1695,17 +1741,27 @@ __device__ void merge_splits(const SelectArgs& a, int wg, float* lds) {
 template <class E, int D>
 __global__ __launch_bounds__(kSelectThreads, 1) void select_kernel(SelectArgs a) {
   __shared__ SelectShared sh;   // the selection's state, or the merge's statistics
-  if (blockIdx.x > 0) {
-    merge_splits<E, D>(a, blockIdx.x - 1, reinterpret_cast<float*>(sh.val));
+  const int nsel = a.mode != kSelMerge ? a.L : 0;   // one selection work-group per layer
+  if ((int)blockIdx.x >= nsel) {
+    merge_splits<E, D>(a, blockIdx.x - nsel, reinterpret_cast<float*>(sh.val));
     return;
   }
-  if (a.mode != kSelMerge) select_top_b(a, sh);
+  SelectArgs b = a;
+  const size_t l = blockIdx.x;
+  b.colsum += l * a.cap;
+  b.pool_pos += l * a.cap;
+  b.scores += l * a.cap;
+  b.keep_flag += l * a.cap;
+  b.move_dst += l * a.list_stride;
+  b.move_src += l * a.list_stride;
+  b.move_count += l;
+  select_top_b(b, sh);
 }
 
 // Moves of a selection outside a frame step (before a view), 16 bytes per
 // thread: K and V of every KV head.
 __global__ __launch_bounds__(256) void moves_kernel(MovesArgs a) {
-  apply_move_chunk(a, (size_t)blockIdx.x * blockDim.x + threadIdx.x);
+  apply_move_chunk(moves_layer(a, blockIdx.y), (size_t)blockIdx.x * blockDim.x + threadIdx.x);
 }
 
 // Positions of the scored pool: row position, or the saved position of an
@@ -1713,9 +1769,14 @@ __global__ __launch_bounds__(256) void moves_kernel(MovesArgs a) {
 __global__ __launch_bounds__(256) void score_positions_kernel(int32_t* score_pos, const int32_t* pool_pos,
                                                               const int32_t* evicted_pos,
                                                               const int32_t* keep_flag, int P, int B,
-                                                              int k0, int foff, int moved) {
+                                                              int k0, int foff, int moved, int cap) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= P) return;
+  const size_t lc = (size_t)blockIdx.y * cap;   // layer blockIdx.y
+  score_pos += lc;
+  pool_pos += lc;
+  keep_flag += lc;
+  evicted_pos += (size_t)blockIdx.y * B;
   score_pos[i] = (moved && i < B && keep_flag[i] == 0) ? evicted_pos[i] : pool_pos[pool_row(i, k0, foff)];
 }
 
@@ -1812,9 +1873,9 @@ int rope_tokens_per_wg(int Hq, int Hkv, int d) {
 }
 int rope_blocks(int T, int tpw) { return (T + tpw - 1) / tpw; }
 
-hipError_t launch_rope(Dt dt, int d, const RopeArgs& a, hipStream_t s, const LaunchTiming& tm) {
+hipError_t launch_rope(Dt dt, int d, const RopeArgs& a, int layers, hipStream_t s, const LaunchTiming& tm) {
   const size_t move_tasks = a.mv.max_moves > 0 ? (size_t)a.mv.max_moves * a.Hkv * (a.mv.row_bytes / 16) : 0;
-  const int blocks = a.rope_blocks + (int)((move_tasks + 255) / 256);
+  const dim3 blocks(a.rope_blocks + (int)((move_tasks + 255) / 256), layers);
   if (dt == Dt::BF16) {
     if (d == 64) hipExtLaunchKernelGGL((rope_append_kernel<BF16, 64>), dim3(blocks), dim3(256), 0, s, tm.start, tm.stop, 0, a);
     else hipExtLaunchKernelGGL((rope_append_kernel<BF16, 128>), dim3(blocks), dim3(256), 0, s, tm.start, tm.stop, 0, a);
@@ -1877,7 +1938,8 @@ hipError_t launch_score(Dt dt, int d, const ScoreArgs& a, int key_blocks, int rs
 
 hipError_t launch_select(Dt dt, int d, const SelectArgs& a, hipStream_t s, const LaunchTiming& tm) {
   const size_t mthreads = ((size_t)a.Hkv * a.R + 31) / 32 * 32 * (d / 4);   // whole 32-row groups
-  const dim3 grid((unsigned)(1 + (mthreads + kSelectThreads - 1) / kSelectThreads)), block(kSelectThreads);
+  const int nsel = a.mode != kSelMerge ? a.L : 0;
+  const dim3 grid((unsigned)(nsel + (mthreads + kSelectThreads - 1) / kSelectThreads)), block(kSelectThreads);
   if (dt == Dt::BF16) {
     if (d == 64) hipExtLaunchKernelGGL((select_kernel<BF16, 64>), grid, block, 0, s, tm.start, tm.stop, 0, a);
     else hipExtLaunchKernelGGL((select_kernel<BF16, 128>), grid, block, 0, s, tm.start, tm.stop, 0, a);
@@ -1908,7 +1970,7 @@ static int decode_prefetch(int d) {
 }
 
 hipError_t launch_decode(Dt dt, int d, const DecodeArgs& a, hipStream_t s, const LaunchTiming& tm) {
-  const dim3 grid(a.Hkv, a.S);
+  const dim3 grid(a.L * a.Hkv, a.S);
   if (dt == Dt::BF16) {
     const dim3 block(64 * kDecodeWavesBf16);
     const int pf = decode_prefetch(d);
@@ -1929,7 +1991,7 @@ hipError_t launch_decode(Dt dt, int d, const DecodeArgs& a, hipStream_t s, const
 
 hipError_t launch_decode_merge(Dt dt, int d, const DecodeMergeArgs& a, hipStream_t s,
                                const LaunchTiming& tm) {
-  const dim3 grid((unsigned)((size_t)a.Hkv * a.R)), block(kDecodeMergeThreads);
+  const dim3 grid((unsigned)((size_t)a.L * a.Hkv * a.R)), block(kDecodeMergeThreads);
   if (dt == Dt::BF16) {
     if (d == 64) hipExtLaunchKernelGGL((decode_merge_kernel<BF16, 64>), grid, block, 0, s, tm.start, tm.stop, 0, a);
     else hipExtLaunchKernelGGL((decode_merge_kernel<BF16, 128>), grid, block, 0, s, tm.start, tm.stop, 0, a);
@@ -1940,17 +2002,18 @@ hipError_t launch_decode_merge(Dt dt, int d, const DecodeMergeArgs& a, hipStream
   return hipGetLastError();
 }
 
-hipError_t launch_moves(const MovesArgs& a, hipStream_t s) {
+hipError_t launch_moves(const MovesArgs& a, int layers, hipStream_t s) {
   const size_t total = (size_t)a.max_moves * a.Hkv * (a.row_bytes / 16);
-  hipLaunchKernelGGL(moves_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(moves_kernel, dim3((unsigned)((total + 255) / 256), layers), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_score_positions(int32_t* score_pos, const int32_t* pool_pos,
                                   const int32_t* evicted_pos, const int32_t* keep_flag, int P,
-                                  int B, int k0, int foff, bool moved, hipStream_t s) {
-  hipLaunchKernelGGL(score_positions_kernel, dim3((unsigned)((P + 255) / 256)), dim3(256), 0, s, score_pos,
-                     pool_pos, evicted_pos, keep_flag, P, B, k0, foff, moved ? 1 : 0);
+                                  int B, int k0, int foff, bool moved, int cap, int layers,
+                                  hipStream_t s) {
+  hipLaunchKernelGGL(score_positions_kernel, dim3((unsigned)((P + 255) / 256), layers), dim3(256), 0, s,
+                     score_pos, pool_pos, evicted_pos, keep_flag, P, B, k0, foff, moved ? 1 : 0, cap);
   return hipGetLastError();
 }
 

@@ -1,6 +1,8 @@
 // Host runtime and C ABI of the StateKV frame step (see include/statekv.h).
 //
-// State layout in HBM (one layer):
+// State layout in HBM (one layer; a stack of L layers holds L copies of every
+// per-layer array back to back, layer-major, so that its KV heads number
+// layer*Hkv + head in the head-major arrays):
 //   kpool, vpool      [Hkv][cap][d], cap = B + 2T.  Rows [0, count) hold the
 //                     compressed state (one slot per token, in slot order).
 //                     While the state fills, frame n is written right after
@@ -47,6 +49,9 @@ struct statekv_state {
   float alpha;
   Dt dt;
   int esize, Hq, Hkv, D, T, G, R, cap;
+  int L;                 // layers of the stack
+  int HkvAll;            // L * Hkv: KV heads over all layers
+  int64_t det_ls;        // elements of dk / dv per layer
   int device;
   hipStream_t stream;
 
@@ -179,7 +184,7 @@ constexpr int kScoreTargetWaves = 256 * 8;
 // Key splits of pass 1 for a pool of P keys: enough work-groups to fill the
 // chip, at least 4 blocks of 64 keys per split.
 void attn_geometry(const statekv_state* s, int P, int* splits, int* kps) {
-  const int base = s->attn_tiles * s->Hkv;
+  const int base = s->attn_tiles * s->HkvAll;
   int sp = std::max(1, std::min(ceil_div(kAttnTargetWGs, base), ceil_div(P, 4 * kAttnBN)));
   sp = std::min(sp, s->attn_splits_max);
   int k = ceil_div(ceil_div(P, sp), kAttnBN) * kAttnBN;
@@ -196,7 +201,7 @@ constexpr int kScoreWGRows = 48;
 
 void score_geometry(const statekv_state* s, int P, int* key_blocks, int* rsplits, int* rps) {
   const int kb = ceil_div(P, score_keys_per_wg(s->dt));
-  const int base = kb * s->Hkv;
+  const int base = kb * s->HkvAll;
   const int rs_lo = ceil_div(s->R, kScoreMaxRows);   // rows per work-group fit the LDS statistics
   int rs;
   if (s->score_slots > 0) {
@@ -232,7 +237,7 @@ constexpr int kDecodeTargetWGs = 256;
 void decode_geometry(const statekv_state* s, int64_t P, int* splits, int* kps) {
   const int bk = decode_block_keys(s->dt);
   const int64_t blocks = (P + bk - 1) / bk;
-  int sp = (int)std::max<int64_t>(1, std::min<int64_t>(ceil_div(s->dec_target_wgs, s->Hkv), blocks));
+  int sp = (int)std::max<int64_t>(1, std::min<int64_t>(ceil_div(s->dec_target_wgs, s->HkvAll), blocks));
   sp = std::min(sp, kDecodeMaxSplits);
   const int64_t k = ((P + sp - 1) / sp + bk - 1) / bk * bk;
   *splits = (int)((P + k - 1) / k);
@@ -243,7 +248,7 @@ void decode_geometry(const statekv_state* s, int64_t P, int* splits, int* kps) {
 // tiles of the pass-1 kernel, key splits up to kMaxSplits.
 void chunk_geometry(const statekv_state* s, int t, int64_t P, int* tiles, int* splits, int* kps) {
   const int tl = ceil_div(s->G * t, attn_rows_per_wg(s->dt, s->D));
-  int sp = (int)std::max<int64_t>(1, std::min<int64_t>(ceil_div(kAttnTargetWGs, tl * s->Hkv),
+  int sp = (int)std::max<int64_t>(1, std::min<int64_t>(ceil_div(kAttnTargetWGs, tl * s->HkvAll),
                                                        (P + 4 * kAttnBN - 1) / (4 * kAttnBN)));
   sp = std::min(sp, s->stat_ss);
   const int64_t k = ((P + sp - 1) / sp + kAttnBN - 1) / kAttnBN * kAttnBN;
@@ -283,13 +288,14 @@ MovesArgs moves_args(const statekv_state* s, int max_moves) {
   a.B = s->B;
   a.row_bytes = s->D * s->esize;
   a.max_moves = max_moves;
+  a.list_stride = s->T;
   return a;
 }
 
 // Performs the moves of the last selection if no frame step has yet.
 int apply_pending_moves(const statekv_state* s) {
   if (!s->moves_pending) return STATEKV_OK;
-  const int rc = check(launch_moves(moves_args(s, s->pending_max_moves), s->stream));
+  const int rc = check(launch_moves(moves_args(s, s->pending_max_moves), s->L, s->stream));
   if (!rc) s->moves_pending = false;
   return rc;
 }
@@ -336,6 +342,8 @@ int statekv_create(const statekv_layer_cfg* cfg, int32_t budget_B, float alpha,
   if (!(c.rope_base > 1.0) || !isfinite(c.rope_base) || c.rope_orig_ctx < 1) return STATEKV_EINVAL;
   if (!(alpha >= 1.0f) || !isfinite(alpha)) return STATEKV_EINVAL;
   if (c.max_text < 0) return STATEKV_EINVAL;
+  const int layers = c.n_layers == 0 ? 1 : c.n_layers;
+  if (layers < 1 || layers > kMaxLayers) return STATEKV_EINVAL;
   const int64_t positions = (int64_t)c.max_frames * c.tokens_per_frame;   // frame tokens
   const int64_t all_positions = positions + c.max_text;                   // rows of D
   if (all_positions > INT32_MAX) return STATEKV_EINVAL;
@@ -361,6 +369,8 @@ int statekv_create(const statekv_layer_cfg* cfg, int32_t budget_B, float alpha,
   s->T = c.tokens_per_frame;
   s->G = s->Hq / s->Hkv;
   s->R = s->G * s->T;
+  s->L = layers;
+  s->HkvAll = layers * s->Hkv;
   // Rows: the state, then two frame regions (frames alternate once they
   // evict); a stream that never evicts needs one row per token.
   s->never_evicts = budget_B >= (int64_t)c.max_frames * c.tokens_per_frame;
@@ -376,7 +386,7 @@ int statekv_create(const statekv_layer_cfg* cfg, int32_t budget_B, float alpha,
   }
 
   s->attn_tiles = ceil_div(s->R, attn_rows_per_wg(s->dt, s->D));
-  s->attn_splits_max = std::min(std::min(kMaxSplits, ceil_div(kAttnTargetWGs, s->attn_tiles * s->Hkv)),
+  s->attn_splits_max = std::min(std::min(kMaxSplits, ceil_div(kAttnTargetWGs, s->attn_tiles * s->HkvAll)),
                                 std::max(1, ceil_div(s->cap, 4 * kAttnBN)));
   s->score_rsplits_max = std::max(ceil_div(s->R, kScoreMaxRows), ceil_div(s->R, 32));
   {
@@ -400,25 +410,26 @@ int statekv_create(const statekv_layer_cfg* cfg, int32_t budget_B, float alpha,
       s->score_rsplits_max = std::max(ceil_div(s->R, kScoreMaxRows), std::min(v, s->score_rsplits_max));
   }
 
-  const size_t E = s->esize, D = s->D;
-  const size_t pool_bytes = (size_t)s->Hkv * s->cap * D * E;
-  const size_t det_bytes = (size_t)all_positions * s->Hkv * D * E;
+  const size_t E = s->esize, D = s->D, Ls = s->L;
+  const size_t pool_bytes = Ls * s->Hkv * s->cap * D * E;
+  s->det_ls = all_positions * s->Hkv * (int64_t)D;
+  const size_t det_bytes = Ls * (size_t)s->det_ls * E;
   // Text-phase partials of the single-tile kernel: splits times rows, for
   // the largest chunk it takes (G*t <= 32).
   size_t dec_rows = 0;
   if (c.max_text > 0 && s->G <= 32) {
     int sp, kp;
     decode_geometry(s, all_positions, &sp, &kp);
-    if (sp > 1) dec_rows = (size_t)sp * s->Hkv * 32;
+    if (sp > 1) dec_rows = (size_t)sp * s->HkvAll * 32;
   }
-  const size_t rows_all = (size_t)s->Hkv * s->R;
+  const size_t rows_all = (size_t)s->HkvAll * s->R;
   // Text chunks of more than 32 query rows per KV head run through pass 1
   // over D and may use up to kMaxSplits key splits.
   s->stat_ss = c.max_text > 0 ? kMaxSplits : s->attn_splits_max;
   const size_t S = s->stat_ss;
   rc = alloc(&s->kpool, pool_bytes);
   if (!rc) rc = alloc(&s->vpool, pool_bytes);
-  if (!rc) rc = alloc(&s->ppos, (size_t)s->cap * sizeof(int32_t));
+  if (!rc) rc = alloc(&s->ppos, Ls * s->cap * sizeof(int32_t));
   if (!rc) rc = alloc(&s->dk, det_bytes);
   if (!rc) rc = alloc(&s->dv, det_bytes);
   if (!rc) rc = alloc(&s->qrot, rows_all * D * E);
@@ -428,14 +439,14 @@ int statekv_create(const statekv_layer_cfg* cfg, int32_t budget_B, float alpha,
   if (!rc) rc = alloc(&s->mpart, stat_rows * S * sizeof(float));
   if (!rc) rc = alloc(&s->lpart, stat_rows * S * sizeof(double));
   if (!rc) rc = alloc(&s->rope_tab, (size_t)all_positions * (D / 2) * sizeof(float2));
-  if (!rc) rc = alloc(&s->colsum, (size_t)s->cap * sizeof(unsigned long long));
-  if (!rc) rc = alloc(&s->scores, (size_t)s->cap * sizeof(float));
-  if (!rc) rc = alloc(&s->score_pos, (size_t)s->cap * sizeof(int32_t));
-  if (!rc) rc = alloc(&s->keep_flag, (size_t)s->cap * sizeof(int32_t));
-  if (!rc) rc = alloc(&s->move_dst, (size_t)s->T * sizeof(int32_t));
-  if (!rc) rc = alloc(&s->move_src, (size_t)s->T * sizeof(int32_t));
-  if (!rc) rc = alloc(&s->move_count, sizeof(int32_t));
-  if (!rc) rc = alloc(&s->evicted_pos, (size_t)s->B * sizeof(int32_t));
+  if (!rc) rc = alloc(&s->colsum, Ls * s->cap * sizeof(unsigned long long));
+  if (!rc) rc = alloc(&s->scores, Ls * s->cap * sizeof(float));
+  if (!rc) rc = alloc(&s->score_pos, Ls * s->cap * sizeof(int32_t));
+  if (!rc) rc = alloc(&s->keep_flag, Ls * s->cap * sizeof(int32_t));
+  if (!rc) rc = alloc(&s->move_dst, Ls * s->T * sizeof(int32_t));
+  if (!rc) rc = alloc(&s->move_src, Ls * s->T * sizeof(int32_t));
+  if (!rc) rc = alloc(&s->move_count, Ls * sizeof(int32_t));
+  if (!rc) rc = alloc(&s->evicted_pos, Ls * s->B * sizeof(int32_t));
   if (!rc) rc = alloc(&s->inv_freq, D / 2 * sizeof(double));
   if (!rc) rc = alloc(&s->nonfinite, sizeof(int32_t));
   if (!rc) rc = alloc(&s->dec_opart, dec_rows * D * sizeof(float));
@@ -455,9 +466,9 @@ int statekv_create(const statekv_layer_cfg* cfg, int32_t budget_B, float alpha,
     rc = check(launch_rope_table(ta, nullptr));
   }
   if (!rc) rc = check(hipMemset(s->nonfinite, 0, sizeof(int32_t)));
-  if (!rc) rc = check(hipMemset(s->colsum, 0, (size_t)s->cap * sizeof(unsigned long long)));
-  if (!rc) rc = check(hipMemset(s->ppos, 0, (size_t)s->cap * sizeof(int32_t)));
-  if (!rc) rc = check(hipMemset(s->move_count, 0, sizeof(int32_t)));
+  if (!rc) rc = check(hipMemset(s->colsum, 0, Ls * s->cap * sizeof(unsigned long long)));
+  if (!rc) rc = check(hipMemset(s->ppos, 0, Ls * s->cap * sizeof(int32_t)));
+  if (!rc) rc = check(hipMemset(s->move_count, 0, Ls * sizeof(int32_t)));
   if (!rc) rc = check(hipDeviceSynchronize());
   if (!rc) {
     s->ev_ok = true;
@@ -539,8 +550,9 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const 
     a.frame_base = F;
     a.tpw = rope_tokens_per_wg(s->Hq, s->Hkv, s->D);
     a.rope_blocks = rope_blocks(s->T, a.tpw);
+    a.det_ls = s->det_ls;
     a.mv = moves_args(s, s->moves_pending ? s->pending_max_moves : 0);
-    rc = check(launch_rope(s->dt, s->D, a, st, tm.lt));
+    rc = check(launch_rope(s->dt, s->D, a, s->L, st, tm.lt));
     tm.done();
     if (rc) return rc;
   }
@@ -565,9 +577,11 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const 
     a.foff = foff;
     a.kps = kps;
     a.ss = s->stat_ss;
-    a.Hkv = s->Hkv;
+    a.Hkv = s->HkvAll;
+    a.lh = s->Hkv;
     a.kv_hs = (int64_t)s->cap * s->D;
     a.kv_rs = s->D;
+    a.kv_ls = (int64_t)s->Hkv * s->cap * s->D;
     rc = check(launch_attn(s->dt, s->D, a, s->attn_tiles, splits, st, tm.lt));
     tm.done();
     if (rc) return rc;
@@ -593,7 +607,8 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const 
     a.k0 = k0;
     a.foff = foff;
     a.rps = rps;
-    a.Hkv = s->Hkv;
+    a.Hkv = s->HkvAll;
+    a.lh = s->Hkv;
     rc = check(launch_score(s->dt, s->D, a, key_blocks, rsplits, st, tm.lt));
     tm.done();
     if (rc) return rc;
@@ -621,12 +636,17 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const 
     a.mpart = s->mpart;
     a.lpart = s->lpart;
     a.out = O;
-    a.Hkv = s->Hkv;
+    a.Hkv = s->HkvAll;
     a.R = s->R;
     a.G = s->G;
     a.Hq = s->Hq;
     a.S = splits;
     a.ss = s->stat_ss;
+    a.L = s->L;
+    a.lh = s->Hkv;
+    a.cap = s->cap;
+    a.list_stride = s->T;
+    a.out_ls = (int64_t)s->T * s->Hq * s->D;
     rc = check(launch_select(s->dt, s->D, a, st, tm.lt));
     tm.done();
     if (rc) return rc;
@@ -688,6 +708,8 @@ int statekv_decode(statekv_state* s, const void* Q, const void* K, const void* V
       a.k0 = P0;
       a.kps = kps;
       a.S = splits;
+      a.L = s->L;
+      a.det_ls = s->det_ls;
       rc = check(launch_decode(s->dt, s->D, a, st, tm.lt));
       tm.done();
       if (rc) return rc;
@@ -704,6 +726,7 @@ int statekv_decode(statekv_state* s, const void* Q, const void* K, const void* V
       a.Hq = s->Hq;
       a.Hkv = s->Hkv;
       a.S = splits;
+      a.L = s->L;
       rc = check(launch_decode_merge(s->dt, s->D, a, st, tm.lt));
       tm.done();
       if (rc) return rc;
@@ -730,8 +753,9 @@ int statekv_decode(statekv_state* s, const void* Q, const void* K, const void* V
       a.cap = s->cap;
       a.tpw = rope_tokens_per_wg(s->Hq, s->Hkv, s->D);
       a.rope_blocks = rope_blocks(t, a.tpw);
+      a.det_ls = s->det_ls;
       a.mv = moves_args(s, 0);
-      rc = check(launch_rope(s->dt, s->D, a, st, tm.lt));
+      rc = check(launch_rope(s->dt, s->D, a, s->L, st, tm.lt));
       tm.done();
       if (rc) return rc;
     }
@@ -756,9 +780,11 @@ int statekv_decode(statekv_state* s, const void* Q, const void* K, const void* V
       a.foff = 0;
       a.kps = kps;
       a.ss = s->stat_ss;
-      a.Hkv = s->Hkv;
+      a.Hkv = s->HkvAll;
+      a.lh = s->Hkv;
       a.kv_hs = s->D;
       a.kv_rs = (int64_t)s->Hkv * s->D;
+      a.kv_ls = s->det_ls;
       rc = check(launch_attn(s->dt, s->D, a, tiles, splits, st, tm.lt));
       tm.done();
       if (rc) return rc;
@@ -772,12 +798,15 @@ int statekv_decode(statekv_state* s, const void* Q, const void* K, const void* V
       a.mpart = s->mpart;
       a.lpart = s->lpart;
       a.out = O;
-      a.Hkv = s->Hkv;
+      a.Hkv = s->HkvAll;
       a.R = R;
       a.G = s->G;
       a.Hq = s->Hq;
       a.S = splits;
       a.ss = s->stat_ss;
+      a.L = s->L;
+      a.lh = s->Hkv;
+      a.out_ls = (int64_t)t * s->Hq * s->D;
       rc = check(launch_select(s->dt, s->D, a, st, tm.lt));
       tm.done();
       if (rc) return rc;
@@ -806,6 +835,9 @@ int statekv_compressed_view(const statekv_state* s, statekv_view* out) {
   out->head_dim = s->D;
   out->dtype = s->cfg.dtype;
   out->frames_done = s->frames_done;
+  out->n_layers = s->L;
+  out->layer_stride = (int64_t)s->Hkv * s->cap * s->D;
+  out->pos_layer_stride = s->cap;
   return STATEKV_OK;
 }
 
@@ -825,6 +857,9 @@ int statekv_detailed_view(const statekv_state* s, statekv_view* out) {
   out->head_dim = s->D;
   out->dtype = s->cfg.dtype;
   out->frames_done = s->frames_done;
+  out->n_layers = s->L;
+  out->layer_stride = s->det_ls;
+  out->pos_layer_stride = 0;
   return STATEKV_OK;
 }
 
@@ -842,7 +877,7 @@ int statekv_scores(const statekv_state* s, statekv_scores_view* out) {
   if (!rc)
     rc = check(launch_score_positions(s->score_pos, s->ppos, s->evicted_pos, s->keep_flag,
                                       s->score_pool, s->B, s->score_k0, s->score_foff,
-                                      s->score_evicted, s->stream));
+                                      s->score_evicted, s->cap, s->L, s->stream));
   if (!rc) rc = check(hipStreamSynchronize(s->stream));
   if (rc) return rc;
   out->scores = s->scores;
@@ -850,6 +885,8 @@ int statekv_scores(const statekv_state* s, statekv_scores_view* out) {
   out->keep_flag = s->keep_flag;
   out->pool = s->score_pool;
   out->kept = std::min(s->score_pool, (int)s->B);
+  out->n_layers = s->L;
+  out->layer_stride = s->cap;
   return STATEKV_OK;
 }
 

@@ -24,12 +24,13 @@ def oracle_cfg(wl: StreamConfig) -> LayerConfig:
                        rope_base=wl.rope_base, alpha=wl.alpha, rope_orig_ctx=wl.rope_orig_ctx)
 
 
-def make_state(wl: StreamConfig, max_frames: int | None = None, max_text: int = 0) -> skv.StateKV:
+def make_state(wl: StreamConfig, max_frames: int | None = None, max_text: int = 0,
+               layers: int = 1) -> skv.StateKV:
     return skv.StateKV(n_q_heads=wl.n_q_heads, n_kv_heads=wl.n_kv_heads, head_dim=wl.head_dim,
                        tokens_per_frame=wl.tokens_per_frame,
                        max_frames=max_frames or wl.n_frames, budget=wl.budget, alpha=wl.alpha,
                        dtype=wl.dtype, rope_base=wl.rope_base, rope_orig_ctx=wl.rope_orig_ctx,
-                       max_text=max_text)
+                       max_text=max_text, n_layers=layers)
 
 
 def to_device(x: np.ndarray, dtype: str) -> torch.Tensor:
@@ -43,8 +44,8 @@ def to_f64(t: torch.Tensor) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def gpu_state_as_oracle(st: skv.StateKV) -> CompressedState:
-    k, v, pos = st.compressed_view()
+def gpu_state_as_oracle(st: skv.StateKV, layer: int = 0) -> CompressedState:
+    k, v, pos = st.compressed_view(layer)
     return CompressedState(to_f64(k), to_f64(v), pos.cpu().numpy().astype(np.int64))
 
 
@@ -70,40 +71,61 @@ def selection_violations(res, keep_pos_gpu: np.ndarray, budget: int, policy: str
 
 class StepCheck:
     """Runs one stream on the GPU; frames in `check` are compared with the oracle
-    started from the GPU's own state before that frame (teacher forcing)."""
+    started from the GPU's own state before that frame (teacher forcing).
+
+    layers > 1 runs a stack: layer l of the stack takes the seeded stream of
+    layer `layer + l`, and the layers in check_layers (default: all) are each
+    compared with the oracle; step() then returns a list of reports."""
 
     def __init__(self, wl: StreamConfig, layer: int = 0, flags: int = 0, max_frames=None,
-                 max_text: int = 0):
+                 max_text: int = 0, layers: int = 1, check_layers=None):
         self.wl = wl
         self.cfg = oracle_cfg(wl)
         if flags & skv.FLAG_RECENT_WINDOW:
             self.cfg = dataclasses.replace(self.cfg, policy="recent")
-        self.st = make_state(wl, max_frames, max_text)
+        self.L = layers
+        self.check_layers = list(range(layers)) if check_layers is None else list(check_layers)
+        self.st = make_state(wl, max_frames, max_text, layers)
         if flags:
             self.st.set_flags(flags)
-        self.frames = FrameStream(wl, layer)
+        self.streams = [FrameStream(wl, layer + l) for l in range(layers)]
+        self.frames = self.streams[0]
         self.n = 0
         self.report = []
 
+    def _inputs(self, frames):
+        dt = self.wl.dtype
+        if self.L == 1:
+            return [to_device(x, dt) for x in frames[0]]
+        return [to_device(np.stack([f[i] for f in frames]), dt) for i in range(3)]
+
     def step(self, check: bool):
         wl, n = self.wl, self.n
-        Q, K, V = self.frames.frame(n)
-        before = gpu_state_as_oracle(self.st) if check else None
-        O = self.st.prefill_frame(to_device(Q, wl.dtype), to_device(K, wl.dtype),
-                                  to_device(V, wl.dtype), n)
+        frames = [fs.frame(n) for fs in self.streams]
+        befores = {l: gpu_state_as_oracle(self.st, l) for l in self.check_layers} if check else None
+        O = self.st.prefill_frame(*self._inputs(frames), n)
         self.n += 1
         if not check:
             return None
         torch.cuda.synchronize()
+        reps = []
+        for l in self.check_layers:
+            o = O if self.L == 1 else O[l]
+            reps.append(self._compare(l, befores[l], frames[l], o, n))
+        return reps[0] if self.L == 1 else reps
+
+    def _compare(self, layer, before, frame, O, n):
+        wl = self.wl
+        Q, K, V = frame
         res = frame_step(self.cfg, before, Q, K, V, n)
-        rep = {"frame": n, "out_err": output_error(to_f64(O), res.O_exact)}
+        rep = {"frame": n, "layer": layer, "out_err": output_error(to_f64(O), res.O_exact)}
         # Detailed cache rows of this frame: bit-exact rotated K and V.
-        dk, dv = self.st.detailed_view()
+        dk, dv = self.st.detailed_view(layer)
         T = wl.tokens_per_frame
         rep["d_k_exact"] = bool(np.array_equal(to_f64(dk[n * T:(n + 1) * T]), res.K_rot))
         rep["d_v_exact"] = bool(np.array_equal(to_f64(dv[n * T:(n + 1) * T]), res.V))
         # New compressed state: positions and rows.
-        k_new, v_new, pos_new = self.st.compressed_view()
+        k_new, v_new, pos_new = self.st.compressed_view(layer)
         pos_new = pos_new.cpu().numpy().astype(np.int64)
         rep["state_size"] = (int(pos_new.size), int(res.state.count))
         rep["violations"] = selection_violations(res, pos_new, wl.budget, self.cfg.policy)
@@ -123,7 +145,7 @@ class StepCheck:
         pos_t = torch.from_numpy(pos_new).to(dk.device)
         rep["state_matches_D"] = (bool(torch.equal(k_new, dk[pos_t].transpose(0, 1)))
                                   and bool(torch.equal(v_new, dv[pos_t].transpose(0, 1))))
-        sc = self.st.scores()
+        sc = self.st.scores(layer)
         if sc is not None and sc["frame"] == n:
             s_gpu = sc["scores"].cpu().numpy().astype(np.float64)
             rel = np.abs(s_gpu - res.scores) / np.maximum(res.scores, 1e-300)

@@ -70,14 +70,25 @@ def test_create_accepts_full_attention_budget_beyond_pool_limit():
         lib.statekv_destroy(h)
 
 
-def test_layer_cfg_matches_the_header():
-    """The ctypes mirror of statekv_layer_cfg has the header's fields, in order."""
+@pytest.mark.parametrize("name,mirror", [("statekv_layer_cfg", "LayerCfg"),
+                                         ("statekv_view", "View"),
+                                         ("statekv_scores_view", "ScoresView")])
+def test_struct_mirrors_match_the_header(name, mirror):
+    """The ctypes mirrors of the ABI structs have the header's fields, in order."""
     import re
     text = open(skv.HEADER).read()
-    body = re.search(r"typedef struct statekv_layer_cfg \{(.*?)\} statekv_layer_cfg;", text, re.S).group(1)
+    body = re.search(r"typedef struct %s \{(.*?)\} %s;" % (name, name), text, re.S).group(1)
     body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
     fields = re.findall(r"\b(\w+)\s*;", body)
-    assert fields == [f[0] for f in skv.LayerCfg._fields_]
+    assert fields == [f[0] for f in getattr(skv, mirror)._fields_]
+
+
+@pytest.mark.parametrize("layers", [-1, 257])
+def test_create_rejects_bad_layer_counts(layers):
+    lib = skv.load_library()
+    h = ctypes.c_void_p()
+    cfg = _cfg(n_layers=layers)
+    assert lib.statekv_create(ctypes.byref(cfg), 64, 1.0, ctypes.byref(h)) == skv.STATEKV_EINVAL
 
 
 def test_null_arguments_are_rejected():
