@@ -196,6 +196,8 @@ struct LaunchTiming {
 
 // Rows handled by one pass-1 work-group / keys by one score work-group.
 int attn_rows_per_wg(Dt dt, int d);
+// Keys per LDS block of pass 1 (key splits are whole blocks).
+int attn_block_keys(Dt dt, int d);
 int score_keys_per_wg(Dt dt);
 int score_waves_per_wg(Dt dt);
 // Score work-groups resident per CU (occupancy of the instantiation in use).

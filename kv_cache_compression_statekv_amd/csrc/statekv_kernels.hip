@@ -459,18 +459,44 @@ struct AttnStage {
   u32x4_t vr[VCH];
 
   // Key j of the block is row pool_row(j, k0, foff) of kbase / vbase; rows
-  // are rs elements apart.
+  // are rs elements apart (rs < 2^24).  Row kb + r of the block sits at
+  // (kb + r) * rs, plus foff * rs from key k0 on: the block's part is uniform
+  // (scalar arithmetic) and a thread's r * rs (r < BN) is a 24-bit product
+  // that does not change from block to block.  Keys at or beyond kend (the
+  // last block of a range) read the row of key kend - 1 instead: the softmax
+  // masks them, so these finite rows only fill the tile, and no load needs a
+  // branch.
   __device__ __forceinline__ void load(const T* kbase, const T* vbase, int kb, int kend, int k0,
                                        int foff, size_t rs, int tid) {
     constexpr int CPR = D / EPV;
+    const int64_t blk = (int64_t)kb * (int64_t)rs;
+    const int64_t fo = (int64_t)foff * (int64_t)rs;
+    const uint32_t rs32 = (uint32_t)rs;
+    const int rlast = kend - 1 - kb;   // last valid row of the block (>= 0)
+    // Whole block on one side of k0 (nearly every block): one uniform base.
+    if (kb + BN <= kend && (kb + BN <= k0 || kb >= k0)) {
+      const int64_t ub = blk + (kb >= k0 ? fo : 0);
+      load_rows(kbase + ub, vbase + ub, [&](int rr) -> int64_t { return (int64_t)__umul24((uint32_t)rr, rs32); },
+                tid);
+    } else {
+      load_rows(kbase + blk, vbase + blk, [&](int rr) -> int64_t {
+        const int rc = min(rr, rlast);
+        return (int64_t)__umul24((uint32_t)rc, rs32) + (kb + rc >= k0 ? fo : 0);
+      }, tid);
+    }
+  }
+
+  // Row r of the block is at kb_ + row_off(r) (keys) and vb_ + row_off(r).
+  template <class RowOff>
+  __device__ __forceinline__ void load_rows(const T* kb_, const T* vb_, RowOff row_off, int tid) {
+    constexpr int CPR = D / EPV;
+    const T* kbase = kb_;
+    const T* vbase = vb_;
 #pragma unroll
     for (int j = 0; j < KCH; ++j) {
       const int t = tid + j * NT;
       const int rr = t / CPR, cc = t - rr * CPR;
-      const int key = kb + rr;
-      kr[j] = u32x4_t{0u, 0u, 0u, 0u};
-      if (key < kend)
-        kr[j] = *reinterpret_cast<const u32x4_t*>(kbase + (size_t)pool_row(key, k0, foff) * rs + cc * EPV);
+      kr[j] = *reinterpret_cast<const u32x4_t*>(kbase + row_off(rr) + cc * EPV);
     }
     if constexpr (sizeof(T) == 2) {
       constexpr int NKQ = BN / KG;
@@ -480,10 +506,9 @@ struct AttnStage {
         const int kq = t % NKQ, dc = t / NKQ;
 #pragma unroll
         for (int j = 0; j < KG; ++j) {
-          const int key = kb + kq * KG + j;
           vr[u * KG + j] = u32x4_t{0u, 0u, 0u, 0u};
-          if (t < VTASKS && key < kend)
-            vr[u * KG + j] = *reinterpret_cast<const u32x4_t*>(vbase + (size_t)pool_row(key, k0, foff) * rs + dc * 8);
+          if (VTASKS % NT == 0 || t < VTASKS)
+            vr[u * KG + j] = *reinterpret_cast<const u32x4_t*>(vbase + row_off(kq * KG + j) + dc * 8);
         }
       }
     } else {
@@ -491,10 +516,7 @@ struct AttnStage {
       for (int j = 0; j < VCH; ++j) {
         const int t = tid + j * NT;
         const int rr = t % BN, cc = t / BN;
-        const int key = kb + rr;
-        vr[j] = u32x4_t{0u, 0u, 0u, 0u};
-        if (key < kend)
-          vr[j] = *reinterpret_cast<const u32x4_t*>(vbase + (size_t)pool_row(key, k0, foff) * rs + cc * 4);
+        vr[j] = *reinterpret_cast<const u32x4_t*>(vbase + row_off(rr) + cc * 4);
       }
     }
   }
@@ -559,11 +581,13 @@ struct AttnStage {
 // merge factor 2^(m_old - m_new) is an exact power of two.
 constexpr float kLazyRescale = 8.f;
 
+// First half: masking, the sub-tile's row maximum and the reference update
+// (alpha, and l rescaled).  Second half (softmax_exp): the weights and their
+// row sum.  online_softmax is the two in sequence.
 template <int QT, bool MASK>
-__device__ __forceinline__ void online_softmax(f32x16_t (&sacc)[QT], float (&m_run)[QT],
-                                               double (&l_run)[QT], float (&alpha)[QT],
-                                               const int (&lim)[QT], int kb, int hh,
-                                               float c_hi) {
+__device__ __forceinline__ void softmax_max(f32x16_t (&sacc)[QT], float (&m_run)[QT],
+                                            double (&l_run)[QT], float (&alpha)[QT],
+                                            const int (&lim)[QT], int kb, int hh, float c_hi) {
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     float mx = -INFINITY;
@@ -591,25 +615,66 @@ __device__ __forceinline__ void online_softmax(f32x16_t (&sacc)[QT], float (&m_r
         m_run[qt] = m_new;
       }
     }
+  }
+}
+
+template <int QT>
+__device__ __forceinline__ void softmax_exp(f32x16_t (&sacc)[QT], const float (&m_run)[QT],
+                                            double (&l_run)[QT], float c_hi) {
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
     const float m_use = m_run[qt] == -INFINITY ? 0.f : m_run[qt];
-    float rs = 0.f;
+    // Row sum in a fixed order: four interleaved partial sums, then pairwise.
+    float r4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const float p = fast_exp2(fmaf(sacc[qt][i], c_hi, -m_use));
       sacc[qt][i] = p;
-      rs += p;
+      r4[i & 3] += p;
     }
-    l_run[qt] += (double)rs;
+    l_run[qt] += (double)((r4[0] + r4[1]) + (r4[2] + r4[3]));
   }
 }
 
-template <class E, int D, int QT, int NW, int NPF = 1>
-__global__ __launch_bounds__(64 * NW, 1) void attn_fwd_kernel(AttnArgs a) {
+template <int QT, bool MASK>
+__device__ __forceinline__ void online_softmax(f32x16_t (&sacc)[QT], float (&m_run)[QT],
+                                               double (&l_run)[QT], float (&alpha)[QT],
+                                               const int (&lim)[QT], int kb, int hh,
+                                               float c_hi) {
+  softmax_max<QT, MASK>(sacc, m_run, l_run, alpha, lim, kb, hh, c_hi);
+  softmax_exp<QT>(sacc, m_run, l_run, c_hi);
+}
+
+// Scheduling groups of a straight-line region: R0 LDS reads (the first
+// matrix operands), V0 VALU instructions while they are in flight, then N
+// times (one MFMA, RI further LDS reads, V VALU instructions), so that each
+// matrix instruction runs beside the wave's vector work and later operands
+// are read meanwhile.
+template <int R0, int V0, int N, int RI, int V>
+__device__ __forceinline__ void interleave_mfma_valu() {
+  __builtin_amdgcn_sched_group_barrier(0x100, R0, 0);   // LDS reads
+  __builtin_amdgcn_sched_group_barrier(0x002, V0, 0);   // VALU
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+    if (RI > 0) __builtin_amdgcn_sched_group_barrier(0x100, RI, 0);   // LDS reads
+    __builtin_amdgcn_sched_group_barrier(0x002, V, 0);   // VALU
+  }
+}
+
+// WPE: waves per SIMD the registers are sized for.  With d = 64 two 8-wave
+// work-groups fit on a CU when registers are capped at 128 per lane (WPE =
+// 4): worth it when the grid has more work-groups than CUs; otherwise the
+// uncapped build (WPE = 1) runs faster.
+template <class E, int D, int QT, int NW, int NPF = 1, int BN_ = kAttnBN, int WPE = 1>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE)))
+void attn_fwd_kernel(AttnArgs a) {
   typedef typename E::T T;
   typedef Mma<E> M;
   constexpr int NT = 64 * NW;
-  typedef AttnStage<E, D, NT> Stage;
-  constexpr int BN = kAttnBN;
+  constexpr int BN = BN_;
+  typedef AttnStage<E, D, NT, BN> Stage;
+  constexpr int NSUB = BN / 32;   // 32-key sub-tiles per block
   constexpr int KSTR = Stage::KSTR;
   constexpr int VSTR = Stage::VSTR;
   constexpr int NKS = D / M::KS;
@@ -682,9 +747,84 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fwd_kernel(AttnArgs a) {
     const T* ks_ = Ks[buf];
     const T* vt_ = Vt[buf];
 
-    // Two sub-tiles of 32 keys: S^T = K Q^T, softmax, O^T += V^T P^T.  Both
-    // sub-tiles' QK^T are issued first, so that the softmax of one overlaps
-    // the matrix work of the other (the MFMA pipe runs beside the VALU).
+    if constexpr (sizeof(T) == 2) {
+      // NSUB sub-tiles of 32 keys, software-pipelined inside the wave:
+      //   QK(0); max(0);
+      //   for s: [PV(s-1), QK(s+1)] beside [exp(s), pack(s)]; rescale(s); max(s+1)
+      //   PV(NSUB-1)
+      // so the matrix pipe works while the VALU computes the weights.  Per
+      // row the arithmetic and its order are those of online_softmax: max(s)
+      // fixes the reference of sub-tile s and rescales l; O is rescaled for
+      // it after PV(s-1) and before PV(s).
+      auto qk = [&](int sub, f32x16_t (&acc)[QT]) {
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) acc[qt] = f32x16_t{};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          const typename M::Frag af = M::ld(&ks_[(sub * 32 + col) * KSTR + ks * M::KS + hh * M::KL]);
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt) acc[qt] = M::mma(af, qf[qt][ks], acc[qt]);
+        }
+      };
+      auto pack = [&](const f32x16_t (&acc)[QT], bf16x8_t (&pf)[2][QT]) {
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+            for (int t = 0; t < 8; ++t) pf[mm][qt][t] = (__bf16)acc[qt][8 * mm + t];
+      };
+      auto pv = [&](int sub, const bf16x8_t (&pf)[2][QT]) {
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) {
+            const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(
+                &vt_[(dt * 32 + col) * VSTR + sub * 32 + mm * 16 + hh * 8]);
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt) o[qt][dt] = M::mma(af, pf[mm][qt], o[qt][dt]);
+          }
+      };
+      auto rescale = [&](const float (&alpha)[QT]) {
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+          if (__ballot(alpha[qt] != 1.f)) {
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) o[qt][dt] *= alpha[qt];
+          }
+      };
+      auto smax = [&](int sub, f32x16_t (&acc)[QT], float (&alpha)[QT]) {
+        const int ksub = kb + 32 * sub;
+        if (ksub + 32 > full_end)
+          softmax_max<QT, true>(acc, m_run, l_run, alpha, lim, ksub, hh, a.c_hi);
+        else
+          softmax_max<QT, false>(acc, m_run, l_run, alpha, lim, ksub, hh, a.c_hi);
+      };
+      f32x16_t sb[2][QT];          // S of sub-tiles s and s+1
+      bf16x8_t pb[2][2][QT];       // P of sub-tiles s-1 and s
+      float alpha[QT];
+      qk(0, sb[0]);
+      smax(0, sb[0], alpha);
+#pragma unroll
+      for (int sub = 0; sub < NSUB; ++sub) {
+        const int c = sub & 1;
+        if (sub >= 1) pv(sub - 1, pb[c ^ 1]);
+        if (sub + 1 < NSUB) qk(sub + 1, sb[c ^ 1]);
+        softmax_exp<QT>(sb[c], m_run, l_run, a.c_hi);
+        pack(sb[c], pb[c]);
+        if (sub >= 1 && sub + 1 < NSUB)
+          interleave_mfma_valu<4, 12, (NKS + 2 * NDT) * QT, 1, 3>();
+        else if (sub + 1 < NSUB)
+          interleave_mfma_valu<NKS, 12, NKS * QT, 0, 6>();
+        else
+          interleave_mfma_valu<2 * NDT, 12, 2 * NDT * QT, 0, 6>();
+        rescale(alpha);                                   // O for sub-tile s's reference
+        if (sub + 1 < NSUB) smax(sub + 1, sb[c ^ 1], alpha);
+      }
+      pv(NSUB - 1, pb[(NSUB - 1) & 1]);
+      return;
+    }
+
     f32x16_t sacc[2][QT];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
@@ -752,9 +892,18 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fwd_kernel(AttnArgs a) {
       if (b < nblk) {
         const int kb = kbeg + b * BN;
         const int buf = b & 1;
-        if (b + NPF < nblk) st[i].load(kbase, vbase, kb + NPF * BN, kend, a.k0, a.foff, rs, tid);
-        compute(kb, buf);
-        if (b + 1 < nblk) st[(i + 1) % NPF].store(Ks[buf ^ 1], Vt[buf ^ 1], tid);
+        if constexpr (NPF >= 2) {
+          // Stage b+1 (loaded NPF-1 blocks ago) goes to the other buffer first,
+          // beside this block's compute: that buffer was last read before the
+          // previous barrier, and the barrier below publishes it.
+          if (b + 1 < nblk) st[(i + 1) % NPF].store(Ks[buf ^ 1], Vt[buf ^ 1], tid);
+          if (b + NPF < nblk) st[i].load(kbase, vbase, kb + NPF * BN, kend, a.k0, a.foff, rs, tid);
+          compute(kb, buf);
+        } else {
+          if (b + NPF < nblk) st[i].load(kbase, vbase, kb + NPF * BN, kend, a.k0, a.foff, rs, tid);
+          compute(kb, buf);
+          if (b + 1 < nblk) st[(i + 1) % NPF].store(Ks[buf ^ 1], Vt[buf ^ 1], tid);
+        }
         __syncthreads();
       }
     }
@@ -1813,6 +1962,23 @@ static int attn_prefetch(int d) {
   return v ? v : (d == 128 ? 2 : 1);
 }
 
+// Compute units of the current device (0 if unknown).
+static int device_cus() {
+  static int cus = -1;
+  if (cus < 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      n = 0;
+    cus = n;
+  }
+  return cus;
+}
+
+// Keys per pass-1 block (128-key blocks measured slower: fewer resident
+// stages per LDS byte).
+int attn_block_keys(Dt, int) { return kAttnBN; }
+
 int attn_rows_per_wg(Dt dt, int) {
   if (dt != Dt::BF16) return 4 * 32;
   return attn_variant() == 4 ? 4 * 32 * 2 : 8 * 32;
@@ -1895,7 +2061,9 @@ hipError_t launch_attn(Dt dt, int d, const AttnArgs& a, int row_tiles, int split
       else hipExtLaunchKernelGGL((attn_fwd_kernel<BF16, 128, 2, 4>), grid, dim3(256), 0, s, tm.start, tm.stop, 0, a);
     } else {
       const int pf = attn_prefetch(d);
-      if (d == 64) {
+      if (d == 64 && (long)row_tiles * a.Hkv * splits > device_cus()) {
+        hipExtLaunchKernelGGL((attn_fwd_kernel<BF16, 64, 1, 8, 1, kAttnBN, 4>), grid, dim3(512), 0, s, tm.start, tm.stop, 0, a);
+      } else if (d == 64) {
         if (pf == 4) hipExtLaunchKernelGGL((attn_fwd_kernel<BF16, 64, 1, 8, 4>), grid, dim3(512), 0, s, tm.start, tm.stop, 0, a);
         else if (pf == 2) hipExtLaunchKernelGGL((attn_fwd_kernel<BF16, 64, 1, 8, 2>), grid, dim3(512), 0, s, tm.start, tm.stop, 0, a);
         else hipExtLaunchKernelGGL((attn_fwd_kernel<BF16, 64, 1, 8, 1>), grid, dim3(512), 0, s, tm.start, tm.stop, 0, a);

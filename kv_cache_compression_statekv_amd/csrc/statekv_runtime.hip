@@ -185,9 +185,10 @@ constexpr int kScoreTargetWaves = 256 * 8;
 // chip, at least 4 blocks of 64 keys per split.
 void attn_geometry(const statekv_state* s, int P, int* splits, int* kps) {
   const int base = s->attn_tiles * s->HkvAll;
-  int sp = std::max(1, std::min(ceil_div(kAttnTargetWGs, base), ceil_div(P, 4 * kAttnBN)));
+  const int bn = attn_block_keys(s->dt, s->D);
+  int sp = std::max(1, std::min(ceil_div(kAttnTargetWGs, base), ceil_div(P, 4 * bn)));
   sp = std::min(sp, s->attn_splits_max);
-  int k = ceil_div(ceil_div(P, sp), kAttnBN) * kAttnBN;
+  int k = ceil_div(ceil_div(P, sp), bn) * bn;
   *splits = ceil_div(P, k);
   *kps = k;
 }
@@ -248,10 +249,11 @@ void decode_geometry(const statekv_state* s, int64_t P, int* splits, int* kps) {
 // tiles of the pass-1 kernel, key splits up to kMaxSplits.
 void chunk_geometry(const statekv_state* s, int t, int64_t P, int* tiles, int* splits, int* kps) {
   const int tl = ceil_div(s->G * t, attn_rows_per_wg(s->dt, s->D));
+  const int bn = attn_block_keys(s->dt, s->D);
   int sp = (int)std::max<int64_t>(1, std::min<int64_t>(ceil_div(kAttnTargetWGs, tl * s->HkvAll),
-                                                       (P + 4 * kAttnBN - 1) / (4 * kAttnBN)));
+                                                       (P + 4 * bn - 1) / (4 * bn)));
   sp = std::min(sp, s->stat_ss);
-  const int64_t k = ((P + sp - 1) / sp + kAttnBN - 1) / kAttnBN * kAttnBN;
+  const int64_t k = ((P + sp - 1) / sp + bn - 1) / bn * bn;
   *tiles = tl;
   *splits = (int)((P + k - 1) / k);
   *kps = (int)k;
@@ -337,6 +339,9 @@ int statekv_create(const statekv_layer_cfg* cfg, int32_t budget_B, float alpha,
   const statekv_layer_cfg c = *cfg;
   if (c.n_q_heads < 1 || c.n_kv_heads < 1 || c.n_q_heads % c.n_kv_heads != 0) return STATEKV_EINVAL;
   if (c.head_dim != 64 && c.head_dim != 128) return STATEKV_EINVAL;
+  // Rows of the detailed cache are Hkv*d elements apart; the kernels form
+  // in-block row offsets as 24-bit products.
+  if ((int64_t)c.n_kv_heads * c.head_dim >= (1 << 24)) return STATEKV_EINVAL;
   if (c.tokens_per_frame < 1 || c.max_frames < 1) return STATEKV_EINVAL;
   if (c.dtype != STATEKV_DTYPE_BF16 && c.dtype != STATEKV_DTYPE_F32) return STATEKV_EINVAL;
   if (!(c.rope_base > 1.0) || !isfinite(c.rope_base) || c.rope_orig_ctx < 1) return STATEKV_EINVAL;
@@ -387,7 +392,7 @@ int statekv_create(const statekv_layer_cfg* cfg, int32_t budget_B, float alpha,
 
   s->attn_tiles = ceil_div(s->R, attn_rows_per_wg(s->dt, s->D));
   s->attn_splits_max = std::min(std::min(kMaxSplits, ceil_div(kAttnTargetWGs, s->attn_tiles * s->HkvAll)),
-                                std::max(1, ceil_div(s->cap, 4 * kAttnBN)));
+                                std::max(1, ceil_div(s->cap, 4 * attn_block_keys(s->dt, s->D))));
   s->score_rsplits_max = std::max(ceil_div(s->R, kScoreMaxRows), ceil_div(s->R, 32));
   {
     int cus = 0;
