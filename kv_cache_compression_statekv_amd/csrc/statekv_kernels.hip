@@ -1375,29 +1375,10 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_score_kernel(ScoreArgs a) {
   const int nrow = r1 - rstart;
   const int ntile = nrow > 0 ? (nrow + RT - 1) / RT : 0;
 
-  // Row statistics of the work-group's rows (padded to whole tiles), from the
-  // key-split partials of pass 1: m = max_s m_s, l = sum_s 2^(m_s - m) l_s
-  // (exact powers of two, fp64 sum).  Padding rows get 1/l = 0.
-  for (int i = tid; i < ntile * RT; i += NT) {
-    const int r = rstart + i;
-    float m = 0.f, rinv = 0.f;
-    int lim = 0;
-    if (r < r1) {
-      float ms[kMaxSplits];
-      double ls[kMaxSplits];
-      load_split_stats(a.mpart, a.lpart, (size_t)g * a.R + r, a.S, a.ss, ms, ls);
-      double l;
-      merge_split_stats(ms, ls, m, l);
-      rinv = (float)(1.0 / l);
-      lim = a.k0 + r / a.G + 1;   // keys below this are visible to row r
-    }
-    sm[i] = m;
-    sr[i] = rinv;
-    slim[i] = lim;
-  }
-
   // NPF register stages of Q tiles: tile it's loads are issued NPF tiles
-  // ahead of its compute; tiles pass through two LDS buffers.
+  // ahead of its compute; tiles pass through two LDS buffers.  The first
+  // NPF tiles' loads are issued before the row statistics are merged, so the
+  // two latencies overlap.
   u32x4_t qr[NPF][QCH];
   auto load_tile = [&](u32x4_t (&q)[QCH], int rt) {
 #pragma unroll
@@ -1421,6 +1402,27 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_score_kernel(ScoreArgs a) {
 #pragma unroll
   for (int i = 0; i < NPF; ++i)
     if (i < ntile) load_tile(qr[i], rstart + i * RT);
+  // Row statistics of the work-group's rows (padded to whole tiles), from the
+  // key-split partials of pass 1: m = max_s m_s, l = sum_s 2^(m_s - m) l_s
+  // (exact powers of two, fp64 sum).  Padding rows get 1/l = 0.
+  for (int i = tid; i < ntile * RT; i += NT) {
+    const int r = rstart + i;
+    float m = 0.f, rinv = 0.f;
+    int lim = 0;
+    if (r < r1) {
+      float ms[kMaxSplits];
+      double ls[kMaxSplits];
+      load_split_stats(a.mpart, a.lpart, (size_t)g * a.R + r, a.S, a.ss, ms, ls);
+      double l;
+      merge_split_stats(ms, ls, m, l);
+      rinv = (float)(1.0 / l);
+      lim = a.k0 + r / a.G + 1;   // keys below this are visible to row r
+    }
+    sm[i] = m;
+    sr[i] = rinv;
+    slim[i] = lim;
+  }
+
   if (ntile > 0) store_tile(qr[0], 0);
   __syncthreads();
   for (int it0 = 0; it0 < ntile; it0 += NPF)
