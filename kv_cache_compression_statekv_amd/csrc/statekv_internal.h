@@ -161,16 +161,17 @@ struct DecodeMergeArgs {
 // l's arrays follow cap (colsum, pool_pos, scores, keep_flag), list_stride
 // (move lists) and 1 (move_count) elements further.
 struct SelectArgs {
-  unsigned long long* colsum;  // [cap] fixed-point column sums; cleared after reading
+  const unsigned long long* colsum;  // [cap] fixed-point column sums of this frame
+  // The other column-sum buffer, cleared by the merge work-groups for the
+  // next scored frame (null: nothing to clear); clear_n elements.
+  unsigned long long* colsum_clear;
+  int64_t clear_n;
   const int32_t* pool_pos;     // [cap] positions of the pool rows (by row)
-  float* scores;               // [P] out: fp32 scores
-  int32_t* keep_flag;          // [P] out: 1 if the candidate stays in the state
   int32_t* move_dst;           // [T] out: evicted state slots (< B), ascending
   int32_t* move_src;           // [T] out: rows of the kept frame tokens at or beyond B, ascending
   int32_t* move_count;         // [1] out
   int32_t P, B, mode;          // mode: kSelMerge, kSelScores or kSelEvict
   int32_t recent;              // 1: keep the B most recent candidates (positions), not the best scores
-  int32_t scored;              // 1: the score pass ran; write scores and keep flags
   int32_t k0, foff;            // pool index -> row
   double score_scale;          // 2^-kScoreFracBits / (Hq * T)
   const void* opart;
@@ -222,11 +223,26 @@ hipError_t launch_decode_merge(Dt dt, int d, const DecodeMergeArgs& a, hipStream
                                const LaunchTiming& tm = {});
 // Positions of a scored pool of P candidates: the position of its row, or
 // for an evicted slot below B that a move has since filled, the saved one.
-// Layer l's arrays follow cap (score_pos, pool_pos, keep_flag) and B
-// (evicted_pos) elements further.
-hipError_t launch_score_positions(int32_t* score_pos, const int32_t* pool_pos,
-                                  const int32_t* evicted_pos, const int32_t* keep_flag, int P,
-                                  int B, int k0, int foff, bool moved, int cap, int layers,
-                                  hipStream_t s);
+// The scores view of the last scored pool of P candidates, rebuilt on
+// request: scores from the column sums, keep flags from the move lists of
+// the selection (a slot below B stays unless it is a move destination; a row
+// at or beyond B stays only if it is a move source) and positions (the row's,
+// or for a slot below B that a move has since filled, the saved one).  Layer
+// l's arrays follow cap (colsum, scores, keep_flag, score_pos, pool_pos), B
+// (evicted_pos), list_stride (move lists) and 1 (move_count) elements further.
+struct ScoreViewArgs {
+  const unsigned long long* colsum;
+  const int32_t* pool_pos;
+  const int32_t* evicted_pos;
+  const int32_t* move_dst;
+  const int32_t* move_src;
+  const int32_t* move_count;
+  float* scores;
+  int32_t* keep_flag;
+  int32_t* score_pos;
+  double score_scale;          // 2^-kScoreFracBits / (Hq * T)
+  int32_t P, B, k0, foff, moved, cap, list_stride;
+};
+hipError_t launch_score_view(const ScoreViewArgs& a, int layers, hipStream_t s);
 
 }  // namespace statekv

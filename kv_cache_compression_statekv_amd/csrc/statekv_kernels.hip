@@ -1774,17 +1774,9 @@ __device__ void select_top_b(const SelectArgs& a, SelectShared& sh) {
   int total;
   const int base = block_excl_scan(holes | (movers << 16), sh.scan, &total);
 
-  // Outputs (the positions of the scored pool are rebuilt on request from the
-  // row positions and the positions the moves overwrite).
-  if (a.scored) {
-    for (int idx = tid; idx < a.P; idx += kSelectThreads) {
-      const uint32_t v = sh.val[idx];
-      a.scores[idx] = a.recent ? (float)((double)a.colsum[idx] * a.score_scale)
-                               : __uint_as_float(v & 0x7fffffffu);
-      a.keep_flag[idx] = (int)(1u - (v >> 31));
-      a.colsum[idx] = 0ull;  // ready for the next frame's score pass
-    }
-  }
+  // Outputs: the move list only.  Scores, keep flags and positions of the
+  // scored pool are rebuilt on request from the column sums and the move
+  // list, and the merge work-groups clear the other column-sum buffer.
   if (holes | movers) {
     int bh = base & 0xffff, bm = base >> 16;
     for (int idx = i0; idx < i1; ++idx) {
@@ -1894,15 +1886,19 @@ __global__ __launch_bounds__(kSelectThreads, 1) void select_kernel(SelectArgs a)
   __shared__ SelectShared sh;   // the selection's state, or the merge's statistics
   const int nsel = a.mode != kSelMerge ? a.L : 0;   // one selection work-group per layer
   if ((int)blockIdx.x >= nsel) {
-    merge_splits<E, D>(a, blockIdx.x - nsel, reinterpret_cast<float*>(sh.val));
+    const int wg = blockIdx.x - nsel;
+    if (a.colsum_clear) {   // the next scored frame's column sums start at zero
+      const size_t stride = (size_t)(gridDim.x - nsel) * kSelectThreads;
+      for (size_t i = (size_t)wg * kSelectThreads + threadIdx.x; i < (size_t)a.clear_n; i += stride)
+        a.colsum_clear[i] = 0ull;
+    }
+    merge_splits<E, D>(a, wg, reinterpret_cast<float*>(sh.val));
     return;
   }
   SelectArgs b = a;
   const size_t l = blockIdx.x;
   b.colsum += l * a.cap;
   b.pool_pos += l * a.cap;
-  b.scores += l * a.cap;
-  b.keep_flag += l * a.cap;
   b.move_dst += l * a.list_stride;
   b.move_src += l * a.list_stride;
   b.move_count += l;
@@ -1915,20 +1911,28 @@ __global__ __launch_bounds__(256) void moves_kernel(MovesArgs a) {
   apply_move_chunk(moves_layer(a, blockIdx.y), (size_t)blockIdx.x * blockDim.x + threadIdx.x);
 }
 
-// Positions of the scored pool: row position, or the saved position of an
-// evicted slot below B that a move has filled since.
-__global__ __launch_bounds__(256) void score_positions_kernel(int32_t* score_pos, const int32_t* pool_pos,
-                                                              const int32_t* evicted_pos,
-                                                              const int32_t* keep_flag, int P, int B,
-                                                              int k0, int foff, int moved, int cap) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= P) return;
-  const size_t lc = (size_t)blockIdx.y * cap;   // layer blockIdx.y
-  score_pos += lc;
-  pool_pos += lc;
-  keep_flag += lc;
-  evicted_pos += (size_t)blockIdx.y * B;
-  score_pos[i] = (moved && i < B && keep_flag[i] == 0) ? evicted_pos[i] : pool_pos[pool_row(i, k0, foff)];
+// The scores view of the last scored pool (one thread per candidate, layer
+// blockIdx.y): the fp32 score of the column sum (the value the selection
+// ranked), the keep flag from the move list, and the candidate's position.
+__global__ __launch_bounds__(256) void score_view_kernel(ScoreViewArgs a) {
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= a.P) return;
+  const size_t l = blockIdx.y, lc = l * a.cap;
+  const int row = pool_row(j, a.k0, a.foff);
+  const int32_t* mdst = a.move_dst + l * a.list_stride;
+  const int32_t* msrc = a.move_src + l * a.list_stride;
+  const int cnt = min(a.move_count[l], a.list_stride);
+  int keep;
+  if (j < a.B) {
+    keep = 1;
+    for (int i = 0; i < cnt; ++i) keep &= mdst[i] != j;
+  } else {
+    keep = 0;
+    for (int i = 0; i < cnt; ++i) keep |= msrc[i] == row;
+  }
+  a.scores[lc + j] = (float)((double)a.colsum[lc + j] * a.score_scale);
+  a.keep_flag[lc + j] = keep;
+  a.score_pos[lc + j] = (a.moved && j < a.B && !keep) ? a.evicted_pos[l * a.B + j] : a.pool_pos[lc + row];
 }
 
 }  // namespace
@@ -2178,12 +2182,8 @@ hipError_t launch_moves(const MovesArgs& a, int layers, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_score_positions(int32_t* score_pos, const int32_t* pool_pos,
-                                  const int32_t* evicted_pos, const int32_t* keep_flag, int P,
-                                  int B, int k0, int foff, bool moved, int cap, int layers,
-                                  hipStream_t s) {
-  hipLaunchKernelGGL(score_positions_kernel, dim3((unsigned)((P + 255) / 256), layers), dim3(256), 0, s,
-                     score_pos, pool_pos, evicted_pos, keep_flag, P, B, k0, foff, moved ? 1 : 0, cap);
+hipError_t launch_score_view(const ScoreViewArgs& a, int layers, hipStream_t s) {
+  hipLaunchKernelGGL(score_view_kernel, dim3((unsigned)((a.P + 255) / 256), layers), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

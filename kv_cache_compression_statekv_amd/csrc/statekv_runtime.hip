@@ -24,9 +24,11 @@
 //   rope_tab          [max_frames*T + max_text][d/2] fp32 (cos, sin) of the
 //                     scaled angles.
 //   dec_opart/mpart/lpart  split-over-keys partials of the text-phase attention.
-//   colsum            [cap] per-key column sums, 64-bit fixed point; the select
-//                     kernel reads and clears them.
-//   scores, keep_flag              scores of the last scored pool.
+//   colsum            [2][cap] per-key column sums, 64-bit fixed point, two
+//                     buffers used by alternate scored frames: the select
+//                     launch reads one and its merge work-groups clear the other.
+//   scores, keep_flag              scores of the last scored pool, rebuilt on
+//                                  request by statekv_scores.
 //   move_dst, move_src, move_count the moves of the last selection.
 //   evicted_pos                    [B] positions the last moves overwrote, by slot.
 //   score_pos                      positions of the last scored pool, rebuilt
@@ -101,6 +103,8 @@ struct statekv_state {
 
   // scores of the last frame that computed them
   int score_frame, score_pool, score_k0, score_foff;
+  int colsum_next;       // column-sum buffer of the next scored frame (0 or 1)
+  int colsum_last;       // buffer of the last scored frame
   bool score_evicted;
 
   uint32_t flags;
@@ -444,7 +448,7 @@ int statekv_create(const statekv_layer_cfg* cfg, int32_t budget_B, float alpha,
   if (!rc) rc = alloc(&s->mpart, stat_rows * S * sizeof(float));
   if (!rc) rc = alloc(&s->lpart, stat_rows * S * sizeof(double));
   if (!rc) rc = alloc(&s->rope_tab, (size_t)all_positions * (D / 2) * sizeof(float2));
-  if (!rc) rc = alloc(&s->colsum, Ls * s->cap * sizeof(unsigned long long));
+  if (!rc) rc = alloc(&s->colsum, 2 * Ls * s->cap * sizeof(unsigned long long));
   if (!rc) rc = alloc(&s->scores, Ls * s->cap * sizeof(float));
   if (!rc) rc = alloc(&s->score_pos, Ls * s->cap * sizeof(int32_t));
   if (!rc) rc = alloc(&s->keep_flag, Ls * s->cap * sizeof(int32_t));
@@ -471,7 +475,7 @@ int statekv_create(const statekv_layer_cfg* cfg, int32_t budget_B, float alpha,
     rc = check(launch_rope_table(ta, nullptr));
   }
   if (!rc) rc = check(hipMemset(s->nonfinite, 0, sizeof(int32_t)));
-  if (!rc) rc = check(hipMemset(s->colsum, 0, Ls * s->cap * sizeof(unsigned long long)));
+  if (!rc) rc = check(hipMemset(s->colsum, 0, 2 * Ls * s->cap * sizeof(unsigned long long)));
   if (!rc) rc = check(hipMemset(s->ppos, 0, Ls * s->cap * sizeof(int32_t)));
   if (!rc) rc = check(hipMemset(s->move_count, 0, Ls * sizeof(int32_t)));
   if (!rc) rc = check(hipDeviceSynchronize());
@@ -602,7 +606,7 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const 
     a.lpart = s->lpart;
     a.S = splits;
     a.ss = s->stat_ss;
-    a.colsum = s->colsum;
+    a.colsum = s->colsum + (size_t)s->colsum_next * s->L * s->cap;
     a.c_hi = s->c_hi;
     a.c_lo = s->c_lo;
     a.R = s->R;
@@ -621,10 +625,13 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const 
   {
     KernelTimer tm(s, STATEKV_K_SELECT);
     SelectArgs a{};
-    a.colsum = s->colsum;
+    const size_t cs_n = (size_t)s->L * s->cap;
+    a.colsum = s->colsum + (size_t)s->colsum_next * cs_n;
+    if (scored) {
+      a.colsum_clear = s->colsum + (size_t)(s->colsum_next ^ 1) * cs_n;
+      a.clear_n = (int64_t)cs_n;
+    }
     a.pool_pos = s->ppos;
-    a.scores = s->scores;
-    a.keep_flag = s->keep_flag;
     a.move_dst = s->move_dst;
     a.move_src = s->move_src;
     a.move_count = s->move_count;
@@ -634,7 +641,6 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const 
     a.foff = foff;
     a.mode = evict ? kSelEvict : (scored ? kSelScores : kSelMerge);
     a.recent = recent ? 1 : 0;
-    a.scored = scored ? 1 : 0;
     a.score_scale = 1.0 / ((double)(1ull << kScoreFracBits) * (double)s->Hq * (double)s->T);
     a.opart = s->opart;
     a.epart = s->epart;
@@ -660,6 +666,8 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const 
   s->pending_max_moves = evict ? std::min(P - (int)s->B, (int)s->B) : 0;
   s->frame_base = F;
   if (scored) {
+    s->colsum_last = s->colsum_next;
+    s->colsum_next ^= 1;
     s->score_frame = n;
     s->score_pool = P;
     s->score_k0 = k0;
@@ -876,13 +884,31 @@ int statekv_scores(const statekv_state* s, statekv_scores_view* out) {
   memset(out, 0, sizeof(*out));
   out->frame = s->score_frame;
   if (s->score_frame < 0) return STATEKV_OK;
-  // Positions at scoring time: those of the pool rows, except in the slots
+  // Scores from the frame's column sums, keep flags from its move list, and
+  // positions at scoring time: those of the pool rows, except in the slots
   // that the selection's moves have filled since.
   rc = apply_pending_moves(s);
-  if (!rc)
-    rc = check(launch_score_positions(s->score_pos, s->ppos, s->evicted_pos, s->keep_flag,
-                                      s->score_pool, s->B, s->score_k0, s->score_foff,
-                                      s->score_evicted, s->cap, s->L, s->stream));
+  if (!rc) {
+    ScoreViewArgs a{};
+    a.colsum = s->colsum + (size_t)s->colsum_last * s->L * s->cap;
+    a.pool_pos = s->ppos;
+    a.evicted_pos = s->evicted_pos;
+    a.move_dst = s->move_dst;
+    a.move_src = s->move_src;
+    a.move_count = s->move_count;
+    a.scores = s->scores;
+    a.keep_flag = s->keep_flag;
+    a.score_pos = s->score_pos;
+    a.score_scale = 1.0 / ((double)(1ull << kScoreFracBits) * (double)s->Hq * (double)s->T);
+    a.P = s->score_pool;
+    a.B = s->B;
+    a.k0 = s->score_k0;
+    a.foff = s->score_foff;
+    a.moved = s->score_evicted ? 1 : 0;
+    a.cap = s->cap;
+    a.list_stride = s->T;
+    rc = check(launch_score_view(a, s->L, s->stream));
+  }
   if (!rc) rc = check(hipStreamSynchronize(s->stream));
   if (rc) return rc;
   out->scores = s->scores;
