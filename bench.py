@@ -488,6 +488,18 @@ def main():
         extra["attention_passes_mfma_frac"] = round(executed_flops / t_passes / 1e12 / PEAK_BF16_TFLOPS, 4)
         t_step_kernels = sum(v["avg_us"] for v in kernels.values()) * 1e-6
         extra["kernel_sum_us_per_step"] = round(t_step_kernels * 1e6, 2)
+    if kernels.get("rope_append", {}).get("avg_us"):
+        # RoPE + append (copy-like, HBM roofline): reads Q, K, V of the frame and
+        # its rows of the cos/sin table; writes the rotated queries, the frame's
+        # pool rows and its D rows (K and V).  The previous frame's moves (at
+        # most T rows per KV head, K and V, read and written) are not counted.
+        esz = 2 if wl.dtype == "bf16" else 4
+        rope_bytes = L * ((Hq + 2 * Hkv) * T * d * esz + T * d * 4 + (Hq + 4 * Hkv) * T * d * esz)
+        gbs = rope_bytes / (kernels["rope_append"]["avg_us"] * 1e-6) / 1e9
+        extra["hbm_rope_append"] = {"bytes": rope_bytes, "achieved_gbs": round(gbs, 1),
+                                    "peak_gbs": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4),
+                                    "note": "algorithmic bytes of the frame's RoPE and appends; "
+                                            "latency-bound at these sizes"}
     if lat:
         lat_a = np.array(lat)
         idx = np.arange(lat_a.size)

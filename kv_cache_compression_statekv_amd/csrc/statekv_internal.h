@@ -10,7 +10,8 @@ enum class Dt : int { BF16 = 1, F32 = 2 };
 
 constexpr int kAttnThreads = 256;
 constexpr int kAttnBN = 64;          // keys per LDS block in attention pass 1
-constexpr int kMaxSplits = 24;       // key splits of pass 1 (merges unroll over them)
+constexpr int kMaxSplits = 24;       // key splits of a frame's pass 1 (merges unroll over them)
+constexpr int kMaxMergeSplits = 512; // key splits of a text chunk's pass 1 (merged in a loop)
 constexpr int kScoreMaxRows = 512;   // rows of one score work-group (row statistics in LDS)
 constexpr int kSelectThreads = 1024;
 constexpr int kMaxPool = 32768;      // B + T limit of the single-work-group select

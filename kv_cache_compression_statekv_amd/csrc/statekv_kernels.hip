@@ -1795,15 +1795,20 @@ __device__ void select_top_b(const SelectArgs& a, SelectShared& sh) {
 // of the partials; one thread per row merges the row's split statistics into
 // LDS (weights 2^(m_s - m), exact powers of two, and 1/l), which the row's
 // other threads read.  Partials of splits that saw no key of a row were never
-// written, so they are selected out, not multiplied.
+// written, so they are selected out, not multiplied.  Up to kMaxSplits splits
+// (a frame) the statistics sit in registers; more (a text chunk over a long
+// cache, up to kMaxMergeSplits) are merged in two loops over the splits with
+// the same arithmetic in the same order.
 template <class E, int D>
 __device__ void merge_splits(const SelectArgs& a, int wg, float* lds) {
   typedef typename E::T T;
   constexpr int CPR = D / 4;
   constexpr int GPW = kSelectThreads / (32 * CPR);   // row groups per work-group
   static_assert(GPW >= 1 && GPW * 32 * CPR == kSelectThreads, "merge work-group shape");
-  float* wts = lds;                                   // [GPW*32][kMaxSplits]
-  float* rinv = lds + GPW * 32 * kMaxSplits;          // [GPW*32]
+  static_assert(GPW * 32 * (kMaxMergeSplits + 1) * sizeof(float) <= sizeof(SelectShared), "merge weights in LDS");
+  const int wstr = a.S <= kMaxSplits ? kMaxSplits : a.S;   // weights per row
+  float* wts = lds;                                   // [GPW*32][wstr]
+  float* rinv = lds + GPW * 32 * wstr;                // [GPW*32]
   typedef typename PartialOut<E>::V PV;
   const int tid = threadIdx.x;
   const size_t nrows = (size_t)a.Hkv * a.R;
@@ -1828,7 +1833,27 @@ __device__ void merge_splits(const SelectArgs& a, int wg, float* lds) {
     }
   };
   load_chunk(0);
-  if (c == 0) {
+  if (c == 0 && a.S > kMaxSplits) {
+    float inv = 0.f;
+    if (base < nrows) {
+      float m = -INFINITY;
+      for (int sp = 0; sp < a.S; ++sp) m = fmaxf(m, a.mpart[stat_index(base, sp, a.ss)]);
+      double l = 0.0;
+      for (int sp = 0; sp < a.S; ++sp) {
+        const float ms = a.mpart[stat_index(base, sp, a.ss)];
+        float w = 0.f;
+        if (ms != -INFINITY) {
+          w = ldexpf(1.f, (int)(ms - m));
+          l += ldexp(a.lpart[stat_index(base, sp, a.ss)], (int)(ms - m));
+        }
+        wts[lrow * wstr + sp] = w;
+      }
+      inv = (float)(1.0 / l);
+    } else {
+      for (int sp = 0; sp < a.S; ++sp) wts[lrow * wstr + sp] = 0.f;
+    }
+    rinv[lrow] = inv;
+  } else if (c == 0) {
     float w[kMaxSplits];
     float inv = 0.f;
 #pragma unroll
@@ -1857,7 +1882,7 @@ __device__ void merge_splits(const SelectArgs& a, int wg, float* lds) {
     for (int j = 0; j < MCH; ++j) {
       const int sp = s0 + j;
       // Splits that saw no key of the row have weight 0 and unwritten partials.
-      const float w = sp < a.S ? wts[lrow * kMaxSplits + sp] : 0.f;
+      const float w = sp < a.S ? wts[lrow * wstr + sp] : 0.f;
       if (w != 0.f) {
         const f32x4_t o4 = PartialOut<E>::unpack(os[j]);
         const float wo = sizeof(T) == 2 ? ldexpf(w, (int)ep[j]) : w;

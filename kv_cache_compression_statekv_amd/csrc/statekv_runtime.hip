@@ -250,13 +250,30 @@ void decode_geometry(const statekv_state* s, int64_t P, int* splits, int* kps) {
 }
 
 // Text chunks with more than 32 query rows per KV head: pass 1 over D, row
-// tiles of the pass-1 kernel, key splits up to kMaxSplits.
+// tiles of the pass-1 kernel.  The split partials are sized for a frame's
+// rows and stat_ss splits; a chunk of t tokens has fewer rows, so it may use
+// proportionally more splits (up to kMaxMergeSplits): short prompts over a
+// long cache then still fill the chip.
+int chunk_split_cap(const statekv_state* s, int t) {
+  const int64_t rows_all = (int64_t)s->HkvAll * s->R;
+  const int64_t rows = (int64_t)s->HkvAll * s->G * t;
+  const int64_t by_partials = (int64_t)s->stat_ss * rows_all / rows;
+  const int64_t by_stats = (int64_t)s->stat_ss * ((rows_all + 31) / 32) / ((rows + 31) / 32);
+  return (int)std::max<int64_t>(1, std::min<int64_t>(kMaxMergeSplits, std::min(by_partials, by_stats)));
+}
+
+// At least kChunkSplitBlocks blocks per split: shorter splits cost more in
+// per-work-group overhead and merge traffic than they gain (measured on a
+// 16k-key cache).
+constexpr int kChunkSplitBlocks = 12;
+
 void chunk_geometry(const statekv_state* s, int t, int64_t P, int* tiles, int* splits, int* kps) {
   const int tl = ceil_div(s->G * t, attn_rows_per_wg(s->dt, s->D));
   const int bn = attn_block_keys(s->dt, s->D);
+  const int64_t min_keys = (int64_t)kChunkSplitBlocks * bn;
   int sp = (int)std::max<int64_t>(1, std::min<int64_t>(ceil_div(kAttnTargetWGs, tl * s->HkvAll),
-                                                       (P + 4 * bn - 1) / (4 * bn)));
-  sp = std::min(sp, s->stat_ss);
+                                                       (P + min_keys - 1) / min_keys));
+  sp = std::min(sp, chunk_split_cap(s, t));
   const int64_t k = ((P + sp - 1) / sp + bn - 1) / bn * bn;
   *tiles = tl;
   *splits = (int)((P + k - 1) / k);
@@ -792,7 +809,7 @@ int statekv_decode(statekv_state* s, const void* Q, const void* K, const void* V
       a.k0 = P0;
       a.foff = 0;
       a.kps = kps;
-      a.ss = s->stat_ss;
+      a.ss = splits;   // the chunk's statistics stride (chunk_split_cap sized it)
       a.Hkv = s->HkvAll;
       a.lh = s->Hkv;
       a.kv_hs = s->D;
@@ -816,7 +833,7 @@ int statekv_decode(statekv_state* s, const void* Q, const void* K, const void* V
       a.G = s->G;
       a.Hq = s->Hq;
       a.S = splits;
-      a.ss = s->stat_ss;
+      a.ss = splits;
       a.L = s->L;
       a.lh = s->Hkv;
       a.out_ls = (int64_t)t * s->Hq * s->D;
