@@ -13,10 +13,10 @@ constexpr int kAttnBN = 64;          // keys per LDS block in attention pass 1
 constexpr int kMaxSplits = 24;       // key splits of a frame's pass 1 (merges unroll over them)
 constexpr int kMaxMergeSplits = 512; // key splits of a text chunk's pass 1 (merged in a loop)
 constexpr int kScoreMaxRows = 512;   // rows of one score work-group (row statistics in LDS)
-constexpr int kSelectThreads = 1024;
+constexpr int kSelectThreads = 1024;  // select launch: selection and merge work-groups
 constexpr int kMaxPool = 32768;      // B + T limit of the single-work-group select
 constexpr int kSelectBins = 4096;
-constexpr int kSelCand = 1024;       // boundary candidates resolved by rank counting
+constexpr int kSelCand = kSelectThreads;  // boundary candidates resolved by rank counting (one per thread)
 constexpr int kDecodeMaxSplits = 1024;  // key splits of the text-phase attention
 // Column sums are accumulated as unsigned 64-bit fixed point with this many
 // fractional bits: integer addition is associative, so the sum does not depend

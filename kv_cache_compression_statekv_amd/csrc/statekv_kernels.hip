@@ -1581,7 +1581,13 @@ struct SelectShared {
 // One refinement of the boundary: histogram of the values get(idx) in
 // [lo, hi] (get returns false for rows outside the set), then the bucket
 // holding the need-th smallest becomes the new [lo, hi].  Returns that
-// bucket's count.
+// bucket's count.  The histogram is all zero on entry and on return: each
+// thread clears the bins it scanned, and the next round's counts come after
+// its first barrier.  sh.bucket/below/cnt are written by the one thread whose
+// bins hold the need-th value; the next round writes them only after its
+// first barrier, when every thread has read them.
+constexpr int kBinsPerThread = kSelectBins / kSelectThreads;
+static_assert(kBinsPerThread * kSelectThreads == kSelectBins, "histogram scan shape");
 template <class Get>
 __device__ int refine_boundary(SelectShared& sh, int P, uint32_t& lo, uint32_t& hi, int& need, Get get) {
   const int tid = threadIdx.x;
@@ -1589,37 +1595,31 @@ __device__ int refine_boundary(SelectShared& sh, int P, uint32_t& lo, uint32_t& 
   const int bits = span ? 32 - __clz((int)span) : 0;
   const int shift = bits > 12 ? bits - 12 : 0;
   const int nb = (int)(span >> shift) + 1;
-  for (int x = tid; x < nb; x += kSelectThreads) sh.hist[x] = 0;
-  if (tid == 0) {
-    sh.bucket = 0;
-    sh.below = 0;
-    sh.cnt = 0;
-  }
-  __syncthreads();
   for (int idx = tid; idx < P; idx += kSelectThreads) {
     uint32_t v;
     if (get(idx, v) && v >= lo && v <= hi) atomicAdd(&sh.hist[(int)((v - lo) >> shift)], 1);
   }
   __syncthreads();
-  int c4[4];
-  int s4 = 0;
+  int cb[kBinsPerThread];
+  int sb = 0;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int q = tid * 4 + u;
-    c4[u] = q < nb ? sh.hist[q] : 0;
-    s4 += c4[u];
+  for (int u = 0; u < kBinsPerThread; ++u) {
+    const int q = tid * kBinsPerThread + u;
+    cb[u] = q < nb ? sh.hist[q] : 0;
+    sb += cb[u];
   }
   int total;
-  int run = block_excl_scan(s4, sh.scan, &total);
+  int run = block_excl_scan(sb, sh.scan, &total);
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int q = tid * 4 + u;
-    if (q < nb && run < need && need <= run + c4[u]) {
+  for (int u = 0; u < kBinsPerThread; ++u) {
+    const int q = tid * kBinsPerThread + u;
+    if (q < nb && run < need && need <= run + cb[u]) {
       sh.bucket = q;
       sh.below = run;
-      sh.cnt = c4[u];
+      sh.cnt = cb[u];
     }
-    run += c4[u];
+    run += cb[u];
+    sh.hist[q] = 0;
   }
   __syncthreads();
   need -= sh.below;
@@ -1627,9 +1627,7 @@ __device__ int refine_boundary(SelectShared& sh, int P, uint32_t& lo, uint32_t& 
   const uint32_t width_m1 = (uint32_t)((1ull << shift) - 1ull);
   hi = (hi - blo > width_m1) ? blo + width_m1 : hi;
   lo = blo;
-  const int cnt = sh.cnt;
-  __syncthreads();
-  return cnt;
+  return sh.cnt;
 }
 
 __device__ void select_top_b(const SelectArgs& a, SelectShared& sh) {
@@ -1640,6 +1638,14 @@ __device__ void select_top_b(const SelectArgs& a, SelectShared& sh) {
   // are written after the last one.
   const int C = (a.P + kSelectThreads - 1) / kSelectThreads;
   constexpr int kChunk = 8;
+  // Zero state of the refinement and the candidate count; the barrier after
+  // the loads publishes it.
+#pragma unroll
+  for (int u = 0; u < kBinsPerThread; ++u) sh.hist[tid * kBinsPerThread + u] = 0;
+  if (tid == 0) {
+    sh.ncand = 0;
+    sh.any_tie = 0;
+  }
   uint32_t flo = ~0u, fhi = 0u;
   for (int j0 = 0; j0 < C; j0 += kChunk) {
     unsigned long long fx[kChunk];
@@ -1706,11 +1712,6 @@ __device__ void select_top_b(const SelectArgs& a, SelectShared& sh) {
 
     // Rows below the boundary are evicted (bit 31 of their entry); the
     // candidates are collected.
-    if (tid == 0) {
-      sh.ncand = 0;
-      sh.any_tie = 0;
-    }
-    __syncthreads();
     for (int idx = tid; idx < a.P; idx += kSelectThreads) {
       const uint32_t v = sh.val[idx];
       bool ev = v < lo;
@@ -1722,15 +1723,17 @@ __device__ void select_top_b(const SelectArgs& a, SelectShared& sh) {
       }
       if (cand) {
         const int slot = atomicAdd(&sh.ncand, 1);
-        sh.cand_v[slot] = v;
-        sh.cand_idx[slot] = idx;
+        if (slot < kSelCand) {   // always true when positions are unique
+          sh.cand_v[slot] = v;
+          sh.cand_idx[slot] = idx;
+        }
       }
       if (ev) sh.val[idx] = v | 0x80000000u;
     }
     __syncthreads();
     // Rank of each candidate among the candidates: by score bits, and by ~pos
     // among equal score bits (read only when such ties exist).
-    const int nc = sh.ncand;
+    const int nc = min(sh.ncand, kSelCand);
     int rank = 0, eq = 0;
     uint32_t mine = 0u;
     if (tid < nc) {
@@ -1760,6 +1763,8 @@ __device__ void select_top_b(const SelectArgs& a, SelectShared& sh) {
     }
   }
 
+  // Without the eviction steps, the barrier that publishes the loaded rows.
+  if (a.mode != kSelEvict) __syncthreads();
   // Move list from the flags: every thread scans a contiguous range of rows so
   // that holes (evicted slots below B) and movers (kept rows at or beyond B)
   // come out ascending.
@@ -1777,15 +1782,18 @@ __device__ void select_top_b(const SelectArgs& a, SelectShared& sh) {
   // Outputs: the move list only.  Scores, keep flags and positions of the
   // scored pool are rebuilt on request from the column sums and the move
   // list, and the merge work-groups clear the other column-sum buffer.
+  // With unique positions exactly P - B rows are evicted, so at most
+  // min(T, B) moves exist; the writes are still bounded by the lists'
+  // capacity, so inconsistent inputs cannot write past them.
   if (holes | movers) {
     int bh = base & 0xffff, bm = base >> 16;
     for (int idx = i0; idx < i1; ++idx) {
       const uint32_t ev = sh.val[idx] >> 31;
-      if (idx < a.B && ev) a.move_dst[bh++] = idx;
-      if (idx >= a.B && !ev) a.move_src[bm++] = pool_row(idx, a.k0, a.foff);
+      if (idx < a.B && ev && bh < a.list_stride) a.move_dst[bh++] = idx;
+      if (idx >= a.B && !ev && bm < a.list_stride) a.move_src[bm++] = pool_row(idx, a.k0, a.foff);
     }
   }
-  if (tid == 0) *a.move_count = total & 0xffff;
+  if (tid == 0) *a.move_count = min(min(total & 0xffff, total >> 16), a.list_stride);
 }
 
 // Merge of the key splits of pass 1:
