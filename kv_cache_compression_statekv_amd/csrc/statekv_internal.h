@@ -69,7 +69,6 @@ struct RopeArgs {
   void* dv;               // [positions][Hkv][d]
   int32_t* nonfinite;     // set to 1 when an input element is NaN or Inf
   int32_t pos0, T, Hq, Hkv, G, cap, frame_base, rope_blocks;
-  int32_t tpw;            // tokens per work-group of the RoPE part
   int64_t det_ls;         // elements between layers of dk / dv
   MovesArgs mv;
 };
@@ -205,8 +204,7 @@ int score_waves_per_wg(Dt dt);
 // Score work-groups resident per CU (occupancy of the instantiation in use).
 int score_wgs_per_cu(Dt dt, int d);
 // Work-groups of the RoPE part of the RoPE kernel for T tokens.
-int rope_tokens_per_wg(int Hq, int Hkv, int d);
-int rope_blocks(int T, int tpw);
+int rope_blocks(int T, int Hq, int Hkv, int d, int esize);
 
 hipError_t launch_rope_table(const RopeTableArgs& a, hipStream_t s);
 hipError_t launch_rope(Dt dt, int d, const RopeArgs& a, int layers, hipStream_t s,

@@ -316,12 +316,53 @@ __device__ __forceinline__ void apply_move_chunk(const MovesArgs& a, size_t t) {
 }
 
 
+// Four rotation pairs of one (token, head): x1 = x[k..k+4), x2 = x[k+d/2..).
+template <class E> struct Vec4;
+template <> struct Vec4<BF16> {
+  static __device__ __forceinline__ void load(const uint16_t* p, float* x) {
+    const u32x2_t v = *reinterpret_cast<const u32x2_t*>(p);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      x[2 * j] = __uint_as_float(v[j] << 16);
+      x[2 * j + 1] = __uint_as_float(v[j] & 0xffff0000u);
+    }
+  }
+  static __device__ __forceinline__ void store(uint16_t* p, const uint16_t* y) {
+    *reinterpret_cast<u32x2_t*>(p) = u32x2_t{(uint32_t)y[0] | ((uint32_t)y[1] << 16),
+                                             (uint32_t)y[2] | ((uint32_t)y[3] << 16)};
+  }
+};
+template <> struct Vec4<F32> {
+  static __device__ __forceinline__ void load(const float* p, float* x) {
+    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(p);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[j] = v[j];
+  }
+  static __device__ __forceinline__ void store(float* p, const float* y) {
+    *reinterpret_cast<f32x4_t*>(p) = f32x4_t{y[0], y[1], y[2], y[3]};
+  }
+};
+
+// Threads of the RoPE launch: one task each, (token, head, 4 rotation pairs)
+// for the query and key heads, then (token, KV head, 16 bytes) for the
+// values.  Short per-thread work keeps the launch's latency chain (load,
+// fp64 rotation, store) short; the value loads are issued by their own
+// threads, beside the rotations.
+constexpr int kRopePairsPerTask = 4;
+__host__ __device__ inline int64_t rope_qk_tasks(int T, int Hq, int Hkv, int d) {
+  return (int64_t)T * (Hq + Hkv) * (d / 2 / kRopePairsPerTask);
+}
+__host__ __device__ inline int64_t rope_v_tasks(int T, int Hkv, int d, int esize) {
+  return (int64_t)T * Hkv * (d * esize / 16);
+}
+
 template <class E, int D>
 __global__ __launch_bounds__(256) void rope_append_kernel(RopeArgs a0) {
   typedef typename E::T T;
   constexpr int HALF = D / 2;
-  const int TPW = a0.tpw;
-  constexpr int CH = HALF / 8;  // 8-pair chunks per head
+  constexpr int CH = HALF / kRopePairsPerTask;   // tasks per head
+  constexpr int VEC = 16 / (int)sizeof(T);
+  constexpr int VCH = D / VEC;                   // value chunks per head
   const int tid = threadIdx.x;
   // Layer blockIdx.y of a stack: its slice of every array.
   const size_t layer = blockIdx.y;
@@ -345,18 +386,17 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeArgs a0) {
     a.dk = (T*)a.dk + layer * a.det_ls;
     a.dv = (T*)a.dv + layer * a.det_ls;
   }
-  const int tok0 = blockIdx.x * TPW;
-  bool finite = true;
   const int nh = a.Hq + a.Hkv;
-  const size_t rows_per_group = (size_t)a.G * a.T;
-  for (int t = tid; t < TPW * nh * CH; t += 256) {
-    const int c = t % CH;
-    const int rest = t / CH;
-    const int hd = rest % nh;
-    const int lt = rest / nh;
-    const int tok = tok0 + lt;
-    if (tok >= a.T) continue;
-    const int k = c * 8;
+  const int64_t nqk = rope_qk_tasks(a.T, a.Hq, a.Hkv, D);
+  const int64_t nv = rope_v_tasks(a.T, a.Hkv, D, (int)sizeof(T));
+  const int64_t t = (int64_t)blockIdx.x * 256 + tid;
+  bool finite = true;
+  if (t < nqk) {
+    const int c = (int)(t % CH);
+    const int64_t rest = t / CH;
+    const int hd = (int)(rest % nh);
+    const int tok = (int)(rest / nh);
+    const int k = c * kRopePairsPerTask;
     const int pos = a.pos0 + tok;
     const T* src;
     T* dst0;
@@ -364,44 +404,38 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeArgs a0) {
     if (hd < a.Hq) {
       const int g = hd / a.G, hl = hd - g * a.G;
       src = (const T*)a.q + ((size_t)tok * a.Hq + hd) * D;
-      dst0 = (T*)a.qrot + ((size_t)g * rows_per_group + (size_t)tok * a.G + hl) * D;
+      dst0 = (T*)a.qrot + ((size_t)g * a.G * a.T + (size_t)tok * a.G + hl) * D;
     } else {
       const int g = hd - a.Hq;
       src = (const T*)a.k + ((size_t)tok * a.Hkv + g) * D;
       dst0 = (T*)a.dk + ((size_t)pos * a.Hkv + g) * D;
       if (a.kpool) dst1 = (T*)a.kpool + ((size_t)g * a.cap + a.frame_base + tok) * D;
+      if (a.pool_pos && g == 0 && c == 0) a.pool_pos[a.frame_base + tok] = pos;
     }
-    float x1[8], x2[8];
-    Vec8<E>::load(src + k, x1);
-    Vec8<E>::load(src + k + HALF, x2);
+    float x1[kRopePairsPerTask], x2[kRopePairsPerTask];
+    Vec4<E>::load(src + k, x1);
+    Vec4<E>::load(src + k + HALF, x2);
     const f32x4_t* tb = reinterpret_cast<const f32x4_t*>(a.table + (size_t)pos * HALF + k);
-    f32x4_t cs4[4];
+    const f32x4_t cs4[2] = {tb[0], tb[1]};   // (cos, sin) of pairs k, k+1 and k+2, k+3
+    T y1[kRopePairsPerTask], y2[kRopePairsPerTask];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) cs4[j] = tb[j];   // (cos, sin) of pairs k+2j, k+2j+1
-    T y1[8], y2[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < kRopePairsPerTask; ++j) {
       finite &= isfinite(x1[j]) && isfinite(x2[j]);
-      rope_pair<E>(x1[j], x2[j], float2{cs4[j >> 1][2 * (j & 1)], cs4[j >> 1][2 * (j & 1) + 1]},
-                   y1[j], y2[j]);
+      rope_pair<E>(x1[j], x2[j], float2{cs4[j >> 1][2 * (j & 1)], cs4[j >> 1][2 * (j & 1) + 1]}, y1[j], y2[j]);
     }
-    Vec8<E>::store(dst0 + k, y1);
-    Vec8<E>::store(dst0 + k + HALF, y2);
+    Vec4<E>::store(dst0 + k, y1);
+    Vec4<E>::store(dst0 + k + HALF, y2);
     if (dst1) {
-      Vec8<E>::store(dst1 + k, y1);
-      Vec8<E>::store(dst1 + k + HALF, y2);
+      Vec4<E>::store(dst1 + k, y1);
+      Vec4<E>::store(dst1 + k + HALF, y2);
     }
-  }
-  // Values: copied unrotated to the pool and to D, 16 bytes per task.
-  constexpr int VEC = 16 / (int)sizeof(T);
-  constexpr int VCH = D / VEC;
-  for (int t = tid; t < TPW * a.Hkv * VCH; t += 256) {
-    const int c = t % VCH;
-    const int rest = t / VCH;
-    const int g = rest % a.Hkv;
-    const int lt = rest / a.Hkv;
-    const int tok = tok0 + lt;
-    if (tok >= a.T) continue;
+  } else if (t < nqk + nv) {
+    // Values: copied unrotated to the pool and to D, 16 bytes per task.
+    const int64_t tv = t - nqk;
+    const int c = (int)(tv % VCH);
+    const int64_t rest = tv / VCH;
+    const int g = (int)(rest % a.Hkv);
+    const int tok = (int)(rest / a.Hkv);
     const u32x4_t v = *reinterpret_cast<const u32x4_t*>((const T*)a.v + ((size_t)tok * a.Hkv + g) * D + c * VEC);
     if constexpr (sizeof(T) == 2) {
       float x[8];
@@ -416,7 +450,6 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeArgs a0) {
       *reinterpret_cast<u32x4_t*>((T*)a.vpool + ((size_t)g * a.cap + a.frame_base + tok) * D + c * VEC) = v;
     *reinterpret_cast<u32x4_t*>((T*)a.dv + ((size_t)(a.pos0 + tok) * a.Hkv + g) * D + c * VEC) = v;
   }
-  if (a.pool_pos && tid < TPW && tok0 + tid < a.T) a.pool_pos[a.frame_base + tok0 + tid] = a.pos0 + tok0 + tid;
   if (!finite) atomicOr(a.nonfinite, 1);
 }
 
@@ -2070,13 +2103,11 @@ hipError_t launch_rope_table(const RopeTableArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Tokens per RoPE work-group: about one (token, head, 8 pairs) task per
-// thread, so that each thread's loads are in flight at once.
-int rope_tokens_per_wg(int Hq, int Hkv, int d) {
-  const int per_token = (Hq + Hkv) * (d / 16);
-  return std::max(1, std::min(64, 256 / per_token));
+// Work-groups of the RoPE part of a launch for T tokens (before the move
+// work-groups).
+int rope_blocks(int T, int Hq, int Hkv, int d, int esize) {
+  return (int)((rope_qk_tasks(T, Hq, Hkv, d) + rope_v_tasks(T, Hkv, d, esize) + 255) / 256);
 }
-int rope_blocks(int T, int tpw) { return (T + tpw - 1) / tpw; }
 
 hipError_t launch_rope(Dt dt, int d, const RopeArgs& a, int layers, hipStream_t s, const LaunchTiming& tm) {
   const size_t move_tasks = a.mv.max_moves > 0 ? (size_t)a.mv.max_moves * a.Hkv * (a.mv.row_bytes / 16) : 0;

@@ -574,8 +574,7 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const 
     a.G = s->G;
     a.cap = s->cap;
     a.frame_base = F;
-    a.tpw = rope_tokens_per_wg(s->Hq, s->Hkv, s->D);
-    a.rope_blocks = rope_blocks(s->T, a.tpw);
+    a.rope_blocks = rope_blocks(s->T, s->Hq, s->Hkv, s->D, s->esize);
     a.det_ls = s->det_ls;
     a.mv = moves_args(s, s->moves_pending ? s->pending_max_moves : 0);
     rc = check(launch_rope(s->dt, s->D, a, s->L, st, tm.lt));
@@ -781,8 +780,7 @@ int statekv_decode(statekv_state* s, const void* Q, const void* K, const void* V
       a.Hkv = s->Hkv;
       a.G = s->G;
       a.cap = s->cap;
-      a.tpw = rope_tokens_per_wg(s->Hq, s->Hkv, s->D);
-      a.rope_blocks = rope_blocks(t, a.tpw);
+      a.rope_blocks = rope_blocks(t, s->Hq, s->Hkv, s->D, s->esize);
       a.det_ls = s->det_ls;
       a.mv = moves_args(s, 0);
       rc = check(launch_rope(s->dt, s->D, a, s->L, st, tm.lt));
