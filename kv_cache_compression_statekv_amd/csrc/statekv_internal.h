@@ -199,8 +199,8 @@ struct LaunchTiming {
 int attn_rows_per_wg(Dt dt, int d);
 // Keys per LDS block of pass 1 (key splits are whole blocks).
 int attn_block_keys(Dt dt, int d);
-int score_keys_per_wg(Dt dt);
-int score_waves_per_wg(Dt dt);
+int score_keys_per_wg(Dt dt, int waves);
+int score_waves_forced(Dt dt);
 // Score work-groups resident per CU (occupancy of the instantiation in use).
 int score_wgs_per_cu(Dt dt, int d);
 // Work-groups of the RoPE part of the RoPE kernel for T tokens.
@@ -211,8 +211,8 @@ hipError_t launch_rope(Dt dt, int d, const RopeArgs& a, int layers, hipStream_t 
                        const LaunchTiming& tm = {});
 hipError_t launch_attn(Dt dt, int d, const AttnArgs& a, int row_tiles, int splits, hipStream_t s,
                        const LaunchTiming& tm = {});
-hipError_t launch_score(Dt dt, int d, const ScoreArgs& a, int key_blocks, int rsplits, hipStream_t s,
-                        const LaunchTiming& tm = {});
+hipError_t launch_score(Dt dt, int d, const ScoreArgs& a, int key_blocks, int rsplits, int waves,
+                        hipStream_t s, const LaunchTiming& tm);
 hipError_t launch_select(Dt dt, int d, const SelectArgs& a, hipStream_t s, const LaunchTiming& tm = {});
 hipError_t launch_moves(const MovesArgs& a, int layers, hipStream_t s);
 // Keys per block of the text-phase attention kernel.

@@ -2055,14 +2055,18 @@ int attn_rows_per_wg(Dt dt, int) {
   if (dt != Dt::BF16) return 4 * 32;
   return attn_variant() == 4 ? 4 * 32 * 2 : 8 * 32;
 }
-// Score pass shape: 4 waves (256 keys per work-group); STATEKV_SCORE_WAVES=8
-// selects 8 waves (512 keys) for bf16, which halves the Q traffic but measured
-// slower on the larger shapes.
-static int score_waves(Dt dt) {
+// Score pass shape: 4 waves (256 keys per work-group), or for bf16 8 waves
+// (512 keys), which halves the Q traffic: faster when the whole grid is
+// resident at once (a single layer at B = 4096: 9.9 -> 9.4 us), slower on the
+// long-pool shapes and stacks, whose grids take several rounds (stress shape
+// 69 -> 78 us).  The runtime picks per frame; STATEKV_SCORE_WAVES = 4 or 8
+// forces one.  Returns 0 when not forced.
+int score_waves_forced(Dt dt) {
   static int v = -1;
   if (v < 0) {
     const char* e = getenv("STATEKV_SCORE_WAVES");
-    v = (e && atoi(e) == 8) ? 8 : 4;
+    const int x = e ? atoi(e) : 0;
+    v = (x == 4 || x == 8) ? x : 0;
   }
   return dt == Dt::BF16 ? v : 4;
 }
@@ -2082,7 +2086,7 @@ static int score_prefetch() {
 int score_wgs_per_cu(Dt dt, int d) {
   int n = 0;
   hipError_t e = hipSuccess;
-  if (dt == Dt::BF16 && score_waves(dt) == 4) {
+  if (dt == Dt::BF16) {
     const int pf = score_prefetch();
 #define STATEKV_OCC(DD, PF) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_score_kernel<BF16, DD, kKtBf16, 4, PF>, 256, 0)
     if (d == 64) {
@@ -2094,8 +2098,7 @@ int score_wgs_per_cu(Dt dt, int d) {
   }
   return e == hipSuccess ? n : 0;
 }
-int score_keys_per_wg(Dt dt) { return score_waves(dt) * 32 * (dt == Dt::BF16 ? kKtBf16 : kKtF32); }
-int score_waves_per_wg(Dt dt) { return score_waves(dt); }
+int score_keys_per_wg(Dt dt, int waves) { return waves * 32 * (dt == Dt::BF16 ? kKtBf16 : kKtF32); }
 
 hipError_t launch_rope_table(const RopeTableArgs& a, hipStream_t s) {
   const size_t total = (size_t)a.npos * a.half;
@@ -2150,11 +2153,11 @@ hipError_t launch_attn(Dt dt, int d, const AttnArgs& a, int row_tiles, int split
   return hipGetLastError();
 }
 
-hipError_t launch_score(Dt dt, int d, const ScoreArgs& a, int key_blocks, int rsplits, hipStream_t s,
-                        const LaunchTiming& tm) {
+hipError_t launch_score(Dt dt, int d, const ScoreArgs& a, int key_blocks, int rsplits, int waves,
+                        hipStream_t s, const LaunchTiming& tm) {
   const dim3 grid(key_blocks, a.Hkv, rsplits);
   if (dt == Dt::BF16) {
-    if (score_waves(dt) == 8) {
+    if (waves == 8) {
       if (d == 64) hipExtLaunchKernelGGL((attn_score_kernel<BF16, 64, kKtBf16, 8>), grid, dim3(512), 0, s, tm.start, tm.stop, 0, a);
       else hipExtLaunchKernelGGL((attn_score_kernel<BF16, 128, kKtBf16, 8>), grid, dim3(512), 0, s, tm.start, tm.stop, 0, a);
     } else {

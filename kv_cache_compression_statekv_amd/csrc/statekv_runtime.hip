@@ -201,11 +201,16 @@ void attn_geometry(const statekv_state* s, int P, int* splits, int* kps) {
 // walks its rows; with the resident work-group count known, the split
 // minimises (dispatch rounds) x (rows per work-group + a fixed cost of about
 // kScoreWGRows rows), so that a last, nearly empty round of work-groups is
-// avoided.  Otherwise: about 8 waves per CU.
+// avoided.  Otherwise: about 8 waves per CU.  The model is that of the
+// 4-wave kernel; when its grid is resident all at once (one round), bf16
+// frames use the 8-wave kernel with the same rows per work-group instead
+// (half the work-groups, each over twice the keys).
 constexpr int kScoreWGRows = 48;
 
-void score_geometry(const statekv_state* s, int P, int* key_blocks, int* rsplits, int* rps) {
-  const int kb = ceil_div(P, score_keys_per_wg(s->dt));
+void score_geometry(const statekv_state* s, int P, int* key_blocks, int* rsplits, int* rps, int* waves) {
+  const int forced = score_waves_forced(s->dt);
+  const int w0 = forced ? forced : 4;
+  const int kb = ceil_div(P, score_keys_per_wg(s->dt, w0));
   const int base = kb * s->HkvAll;
   const int rs_lo = ceil_div(s->R, kScoreMaxRows);   // rows per work-group fit the LDS statistics
   int rs;
@@ -223,15 +228,20 @@ void score_geometry(const statekv_state* s, int P, int* key_blocks, int* rsplits
       }
     }
   } else {
-    const int target = kScoreTargetWaves / score_waves_per_wg(s->dt);
+    const int target = kScoreTargetWaves / w0;
     rs = std::max(1, std::min(ceil_div(target, base), ceil_div(s->R, 128)));
     rs = std::min(rs, s->score_rsplits_max);
     rs = std::max(rs, rs_lo);
   }
   const int r = ceil_div(ceil_div(s->R, rs), 32) * 32;
-  *key_blocks = kb;
+  int w = w0;
+  if (!forced && s->dt == Dt::BF16 && s->score_slots > 0 &&
+      (long)base * ceil_div(s->R, r) <= s->score_slots)
+    w = 8;
+  *key_blocks = w == w0 ? kb : ceil_div(P, score_keys_per_wg(s->dt, w));
   *rsplits = ceil_div(s->R, r);
   *rps = r;
+  *waves = w;
 }
 
 // Text phase: t tokens over P keys.  Row tiles of 32 rows per KV head; key
@@ -612,8 +622,8 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const 
     if (rc) return rc;
   }
   if (scored) {
-    int key_blocks, rsplits, rps;
-    score_geometry(s, P, &key_blocks, &rsplits, &rps);
+    int key_blocks, rsplits, rps, waves;
+    score_geometry(s, P, &key_blocks, &rsplits, &rps, &waves);
     KernelTimer tm(s, STATEKV_K_SCORE);
     ScoreArgs a{};
     a.qrot = s->qrot;
@@ -634,7 +644,7 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const 
     a.rps = rps;
     a.Hkv = s->HkvAll;
     a.lh = s->Hkv;
-    rc = check(launch_score(s->dt, s->D, a, key_blocks, rsplits, st, tm.lt));
+    rc = check(launch_score(s->dt, s->D, a, key_blocks, rsplits, waves, st, tm.lt));
     tm.done();
     if (rc) return rc;
   }
