@@ -90,6 +90,23 @@ def test_full_size_sampled_frames(name, layer, frames, check):
     print("worst", name, layer, worst, flush=True)
 
 
+# The largest pool the single-work-group selection takes: B + T = 32768
+# candidates (32 rows per selection thread), teacher-forced at the fill
+# boundary and on the first evicting frames.
+LARGEST_POOL = _small("largest_pool", 108, n_q_heads=2, n_kv_heads=1, tokens_per_frame=256,
+                      budget=32768 - 256, n_frames=130, n_sinks=4)
+
+
+def test_largest_selection_pool():
+    wl = LARGEST_POOL
+    chk = StepCheck(wl)
+    for n in range(wl.n_frames):
+        rep = chk.step(check=n >= 126)
+        if rep is not None:
+            print(n, rep, flush=True)
+            assert_step_ok(rep, wl.dtype)
+
+
 @pytest.mark.parametrize("name,frames,check,extra", [
     ("ragged_bf16_d64", 9, None, 0),
     ("ragged_bf16_d128_yarn", 8, None, skv.FLAG_ALWAYS_SCORE),
