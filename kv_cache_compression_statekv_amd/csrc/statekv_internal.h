@@ -203,6 +203,7 @@ int score_keys_per_wg(Dt dt, int waves);
 int score_waves_forced(Dt dt);
 // Score work-groups resident per CU (occupancy of the instantiation in use).
 int score_wgs_per_cu(Dt dt, int d);
+int score8_wgs_per_cu(int d);
 // Work-groups of the RoPE part of the RoPE kernel for T tokens.
 int rope_blocks(int T, int Hq, int Hkv, int d, int esize);
 

@@ -2070,16 +2070,18 @@ int score_waves_forced(Dt dt) {
   }
   return dt == Dt::BF16 ? v : 4;
 }
-// Register stages of the score pass's Q-tile prefetch: 4 (5-7 % faster on
-// the long-pool shapes); STATEKV_SCORE_PF = 1, 2 or 4 overrides.
-static int score_prefetch() {
+// Register stages of the score pass's Q-tile prefetch (4-wave kernel): 4 for
+// d = 128 (5-7 % faster on the long-pool shapes), 2 for d = 64, where it
+// leaves room for three waves per SIMD (16 % faster on the 28-layer ivl3_1b
+// stack); STATEKV_SCORE_PF = 1, 2 or 4 overrides.
+static int score_prefetch(int d) {
   static int v = -1;
   if (v < 0) {
     const char* e = getenv("STATEKV_SCORE_PF");
-    const int x = e ? atoi(e) : 4;
-    v = (x == 1 || x == 2) ? x : 4;
+    const int x = e ? atoi(e) : 0;
+    v = (x == 1 || x == 2 || x == 4) ? x : 0;
   }
-  return v;
+  return v ? v : (d == 64 ? 2 : 4);
 }
 
 // Work-groups of the score kernel that fit on one CU at once (0 if unknown).
@@ -2087,7 +2089,7 @@ int score_wgs_per_cu(Dt dt, int d) {
   int n = 0;
   hipError_t e = hipSuccess;
   if (dt == Dt::BF16) {
-    const int pf = score_prefetch();
+    const int pf = score_prefetch(d);
 #define STATEKV_OCC(DD, PF) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_score_kernel<BF16, DD, kKtBf16, 4, PF>, 256, 0)
     if (d == 64) {
       if (pf == 4) STATEKV_OCC(64, 4); else if (pf == 2) STATEKV_OCC(64, 2); else STATEKV_OCC(64, 1);
@@ -2096,6 +2098,14 @@ int score_wgs_per_cu(Dt dt, int d) {
     }
 #undef STATEKV_OCC
   }
+  return e == hipSuccess ? n : 0;
+}
+// Work-groups of the 8-wave score kernel (bf16) that fit on one CU at once.
+int score8_wgs_per_cu(int d) {
+  int n = 0;
+  const hipError_t e = d == 64
+      ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_score_kernel<BF16, 64, kKtBf16, 8>, 512, 0)
+      : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_score_kernel<BF16, 128, kKtBf16, 8>, 512, 0);
   return e == hipSuccess ? n : 0;
 }
 int score_keys_per_wg(Dt dt, int waves) { return waves * 32 * (dt == Dt::BF16 ? kKtBf16 : kKtF32); }
@@ -2161,7 +2171,7 @@ hipError_t launch_score(Dt dt, int d, const ScoreArgs& a, int key_blocks, int rs
       if (d == 64) hipExtLaunchKernelGGL((attn_score_kernel<BF16, 64, kKtBf16, 8>), grid, dim3(512), 0, s, tm.start, tm.stop, 0, a);
       else hipExtLaunchKernelGGL((attn_score_kernel<BF16, 128, kKtBf16, 8>), grid, dim3(512), 0, s, tm.start, tm.stop, 0, a);
     } else {
-      const int pf = score_prefetch();
+      const int pf = score_prefetch(d);
 #define STATEKV_SCORE(DD, PF) hipExtLaunchKernelGGL((attn_score_kernel<BF16, DD, kKtBf16, 4, PF>), grid, dim3(256), 0, s, tm.start, tm.stop, 0, a)
       if (d == 64) {
         if (pf == 4) STATEKV_SCORE(64, 4); else if (pf == 2) STATEKV_SCORE(64, 2); else STATEKV_SCORE(64, 1);

@@ -63,6 +63,7 @@ struct statekv_state {
   bool never_evicts;
   int score_rsplits_max;
   int score_slots;       // score work-groups resident on the device at once (0: unknown)
+  int score_slots8;      // the same for the 8-wave score kernel (bf16)
   int dec_target_wgs;
 
   void* kpool;
@@ -201,10 +202,12 @@ void attn_geometry(const statekv_state* s, int P, int* splits, int* kps) {
 // walks its rows; with the resident work-group count known, the split
 // minimises (dispatch rounds) x (rows per work-group + a fixed cost of about
 // kScoreWGRows rows), so that a last, nearly empty round of work-groups is
-// avoided.  Otherwise: about 8 waves per CU.  The model is that of the
-// 4-wave kernel; when its grid is resident all at once (one round), bf16
-// frames use the 8-wave kernel with the same rows per work-group instead
-// (half the work-groups, each over twice the keys).
+// avoided.  Otherwise: about 8 waves per CU.  That model is the 4-wave
+// kernel's.  When the 8-wave kernel (bf16: twice the keys per work-group,
+// half the Q traffic) fits the whole pool in one round of resident
+// work-groups, it runs instead, with the most rows per work-group that one
+// round allows (a single layer at B = 4096; long pools and stacks take
+// several rounds and keep 4 waves, which measured faster there).
 constexpr int kScoreWGRows = 48;
 
 void score_geometry(const statekv_state* s, int P, int* key_blocks, int* rsplits, int* rps, int* waves) {
@@ -233,12 +236,18 @@ void score_geometry(const statekv_state* s, int P, int* key_blocks, int* rsplits
     rs = std::min(rs, s->score_rsplits_max);
     rs = std::max(rs, rs_lo);
   }
-  const int r = ceil_div(ceil_div(s->R, rs), 32) * 32;
-  int w = w0;
-  if (!forced && s->dt == Dt::BF16 && s->score_slots > 0 &&
-      (long)base * ceil_div(s->R, r) <= s->score_slots)
-    w = 8;
-  *key_blocks = w == w0 ? kb : ceil_div(P, score_keys_per_wg(s->dt, w));
+  int r = ceil_div(ceil_div(s->R, rs), 32) * 32;
+  int w = w0, kbw = kb;
+  if (!forced && s->dt == Dt::BF16 && s->score_slots8 > 0) {
+    const int kb8 = ceil_div(P, score_keys_per_wg(s->dt, 8));
+    const int rs8 = std::min(s->score_slots8 / (kb8 * s->HkvAll), std::min(s->score_rsplits_max, ceil_div(s->R, 32)));
+    if (rs8 >= rs_lo) {
+      w = 8;
+      kbw = kb8;
+      r = ceil_div(ceil_div(s->R, rs8), 32) * 32;
+    }
+  }
+  *key_blocks = kbw;
   *rsplits = ceil_div(s->R, r);
   *rps = r;
   *waves = w;
@@ -429,6 +438,7 @@ int statekv_create(const statekv_layer_cfg* cfg, int32_t budget_B, float alpha,
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, s->device) != hipSuccess) cus = 0;
     s->score_slots = cus * score_wgs_per_cu(s->dt, s->D);
+    s->score_slots8 = s->dt == Dt::BF16 ? cus * score8_wgs_per_cu(s->D) : 0;
     if (const char* e = getenv("STATEKV_SCORE_SLOTS")) s->score_slots = atoi(e);
   }
   // Tuning overrides (launch geometry only; the result does not depend on them).
