@@ -194,6 +194,30 @@ def test_two_runs_are_bitwise_identical():
         assert torch.equal(x, y)
 
 
+def test_side_stream_run_matches_default_stream():
+    """The state takes torch's current stream at creation: a stream run on a
+    side stream (inputs uploaded and outputs read on it) gives the same bits
+    as on the default stream."""
+    wl = SMALL["ragged_bf16_d64"]
+    outs = []
+    for side in (False, True):
+        stream = torch.cuda.Stream() if side else torch.cuda.current_stream()
+        with torch.cuda.stream(stream):
+            st = make_state(wl)
+            fs = FrameStream(wl)
+            os_ = [st.prefill_frame(*[to_device(x, wl.dtype) for x in fs.frame(n)], n=n).cpu()
+                   for n in range(wl.n_frames)]
+            k, v, pos = st.compressed_view()
+            dk, dv = st.detailed_view()
+            outs.append((os_, k.cpu(), v.cpu(), pos.cpu(), dk.cpu(), dv.cpu()))
+            st.close()
+    a, b = outs
+    for x, y in zip(a[0], b[0]):
+        assert torch.equal(x, y)
+    for x, y in zip(a[1:], b[1:]):
+        assert torch.equal(x, y)
+
+
 def test_out_of_order_and_capacity_errors_leave_state_unchanged():
     wl = SMALL["tiny"].replace(n_frames=2)
     st = make_state(wl)
