@@ -1858,8 +1858,10 @@ __device__ void merge_splits(const SelectArgs& a, int wg, float* lds) {
   const int lrow = gsub * 32 + (tid & 31);
   const size_t base = ((size_t)wg * GPW + gsub) * 32 + (tid & 31);   // = g*R + r
   // The partial outputs do not depend on the weights: the first MCH splits'
-  // loads are issued before the statistics, so they are all in flight at once.
-  constexpr int MCH = sizeof(T) == 2 ? 8 : 4;
+  // loads are issued before the statistics, so they are all in flight at once
+  // (9 per chunk: a frame's 17 splits at B = 4096 in two rounds, within the
+  // registers of 1024-thread work-groups).
+  constexpr int MCH = sizeof(T) == 2 ? 9 : 4;
   PV os[MCH];
   int8_t ep[MCH];
   auto load_chunk = [&](int s0) {
