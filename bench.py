@@ -83,6 +83,10 @@ def parse_args():
                    help="no GPU work: turn two rocprofv3 --pmc counter_collection.csv files "
                         "(FETCH_SIZE, WRITE_SIZE) of a run with --copy-calibration-mb into "
                         "profiles/attn_fwd_<workload>_traffic.json")
+    p.add_argument("--reference-rates", action="store_true",
+                   help="only measure the libraries' own reference rates on this GPU: torch's bf16 "
+                        "GEMM (hipBLASLt) and a read-only bf16 sum, as context for the roofline "
+                        "fractions")
     return p.parse_args()
 
 
@@ -144,6 +148,42 @@ def summarize_pmc(fetch_csv: str, write_csv: str, workload: str, copy_mb: int) -
     with open(path, "w") as fh:
         json.dump(rec, fh, indent=1)
     return rec
+
+
+def reference_rates(torch) -> dict:
+    """torch's bf16 GEMM and read-only bf16 sum on this GPU (HIP events, 20
+    repetitions after 3 warm-ups): the libraries' practical matrix-core and
+    streaming rates, context for the fractions of the published peaks."""
+    torch.cuda.set_device(0)
+
+    def timed(fn, reps=20):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / reps * 1e3   # us
+
+    gemm = []
+    for m, n, k in ((4096, 4096, 4096), (8192, 8192, 8192), (16384, 16384, 8192)):
+        a = torch.randn(m, k, dtype=torch.bfloat16, device="cuda")
+        b = torch.randn(k, n, dtype=torch.bfloat16, device="cuda")
+        us = timed(lambda: a @ b)
+        tf = 2.0 * m * n * k / us / 1e6
+        gemm.append({"m": m, "n": n, "k": k, "us": round(us, 1), "tflops": round(tf, 1),
+                     "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
+        del a, b
+    reads = []
+    for nbytes in (134_479_872, 500_000_000, 1_070_000_000, 4_000_000_000):
+        x = torch.ones(nbytes // 2, dtype=torch.bfloat16, device="cuda")
+        us = timed(lambda: x.sum(dtype=torch.float32))
+        reads.append({"bytes": nbytes, "us": round(us, 1), "gbs": round(nbytes / us / 1e3, 1)})
+        del x
+    return {"bf16_gemm": gemm, "bf16_sum_read": reads}
 
 
 def quadratic_comparison(skv, torch, np, wl):
@@ -360,6 +400,10 @@ def main():
     if args.summarize_pmc:
         print(json.dumps(summarize_pmc(*args.summarize_pmc, args.workload,
                                        args.copy_calibration_mb or 256)))
+        return
+    if args.reference_rates:
+        import torch
+        print(json.dumps({"reference_rates": reference_rates(torch)}))
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
