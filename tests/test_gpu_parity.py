@@ -16,7 +16,7 @@ import torch
 import kv_cache_compression_statekv_amd as skv
 from kv_cache_compression_statekv_amd.workload import CONFIGS, FrameStream, StreamConfig
 from gpu_helpers import (StepCheck, assert_step_ok, gpu_state_as_oracle, make_state,
-                         oracle_cfg, output_error, to_device, to_f64)
+                         oracle_cfg, output_error, selection_violations, to_device, to_f64)
 from oracle import OracleStream, frame_step
 
 pytestmark = pytest.mark.gpu
@@ -88,6 +88,38 @@ def test_full_size_sampled_frames(name, layer, frames, check):
                 if key in rep:
                     worst[key] = max(worst.get(key, 0.0), rep[key])
     print("worst", name, layer, worst, flush=True)
+
+
+# Free-running: the GPU and the oracle each carry their own state from frame 0
+# on the same seeded frames.  Until the kept sets first differ, both states are
+# the same, so every frame's output is compared and the first differing
+# selection must lie inside the 1e-6 band around the oracle's B-th score (a
+# legitimate divergence); after it the two streams may differ and the run stops.
+@pytest.mark.parametrize("name,frames", [("ragged_bf16_d64", 30), ("ivl3_1b", 64)])
+def test_free_running_stream(name, frames):
+    wl = (SMALL.get(name) or CONFIGS[name]).replace(n_frames=frames)
+    st = make_state(wl)
+    fs = FrameStream(wl)
+    orc = OracleStream(oracle_cfg(wl))
+    tol = 2e-2 if wl.dtype == "bf16" else 1e-5
+    first_divergence, worst = None, 0.0
+    for n in range(frames):
+        Q, K, V = fs.frame(n)
+        O = st.prefill_frame(*[to_device(x, wl.dtype) for x in (Q, K, V)], n=n)
+        res = orc.step(Q, K, V)
+        err = output_error(to_f64(O), res.O_exact)
+        worst = max(worst, err)
+        assert err < tol, (n, err)
+        _, _, pos = st.compressed_view()
+        kept = pos.cpu().numpy()
+        assert kept.size == res.state.pos.size
+        viol = selection_violations(res, kept, wl.budget)
+        assert not viol, (n, viol[:10])
+        if set(kept.tolist()) != set(res.state.pos.tolist()):
+            first_divergence = n
+            break
+    print(name, "frames", frames, "worst output error", worst,
+          "first (in-band) divergence", first_divergence, flush=True)
 
 
 # The largest pool the single-work-group selection takes: B + T = 32768
