@@ -2,6 +2,7 @@
 argument checks reject bad calls before touching the device.  No compute."""
 import ctypes
 import math
+import os
 
 import pytest
 
@@ -108,3 +109,29 @@ def test_null_arguments_are_rejected():
     assert lib.statekv_set_stream(None, None) == skv.STATEKV_EINVAL
     assert lib.statekv_kernel_times(None, None, None, 0, 0) == skv.STATEKV_EINVAL
     lib.statekv_destroy(None)
+
+
+def test_product_path_never_reaches_the_oracle():
+    # No module of the package imports the CPU oracle, and a missing library
+    # is an error rather than a silent fallback.
+    import ast
+    import glob
+    import kv_cache_compression_statekv_amd as skv
+    pkg = os.path.dirname(skv.__file__)
+    for path in glob.glob(os.path.join(pkg, "*.py")):
+        tree = ast.parse(open(path).read())
+        for node in ast.walk(tree):
+            names = []
+            if isinstance(node, ast.Import):
+                names = [a.name for a in node.names]
+            elif isinstance(node, ast.ImportFrom):
+                names = [node.module or ""]
+            assert not any(n.split(".")[0] == "oracle" for n in names), (path, names)
+
+
+def test_missing_library_is_an_error(monkeypatch, tmp_path):
+    import kv_cache_compression_statekv_amd as skv
+    monkeypatch.setattr(skv, "_lib", None)
+    monkeypatch.setattr(skv, "library_path", lambda: str(tmp_path / "libstatekv.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        skv.load_library(build_if_missing=False)
