@@ -60,6 +60,28 @@ def test_small_stream_every_frame(name):
         assert_step_ok(rep, wl.dtype)
 
 
+# Launch-shape overrides read at state creation change the split geometry
+# (hence the rounding order of the split merges), never the method: every frame
+# still matches the oracle.
+SHAPES = [
+    ("ragged_bf16_d64", {"STATEKV_ATTN_SPLITS": "1"}),
+    ("ragged_bf16_d64", {"STATEKV_ATTN_SPLITS": "3", "STATEKV_SCORE_RSPLITS": "1"}),
+    ("ragged_bf16_d128_yarn", {"STATEKV_SCORE_SLOTS": "8", "STATEKV_SCORE_RSPLITS": "64"}),
+]
+
+
+@pytest.mark.parametrize("name,env", SHAPES, ids=["one_split", "three_splits_one_rsplit",
+                                                  "few_score_slots"])
+def test_launch_shape_overrides(name, env, monkeypatch):
+    for k, v in env.items():
+        monkeypatch.setenv(k, v)
+    wl = SMALL[name]
+    chk = StepCheck(wl, flags=skv.FLAG_ALWAYS_SCORE)
+    for _ in range(wl.n_frames):
+        rep = chk.step(check=True)
+        assert_step_ok(rep, wl.dtype)
+
+
 # Full per-frame sizes of the five workloads, teacher-forced on sampled frames
 # (the fill boundary, the first evicting frames, later frames).
 FULL = [
