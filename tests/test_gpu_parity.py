@@ -117,7 +117,9 @@ def test_full_size_sampled_frames(name, layer, frames, check):
 # the same, so every frame's output is compared and the first differing
 # selection must lie inside the 1e-6 band around the oracle's B-th score (a
 # legitimate divergence); after it the two streams may differ and the run stops.
-@pytest.mark.parametrize("name,frames", [("ragged_bf16_d64", 30), ("ivl3_1b", 64)])
+@pytest.mark.parametrize("name,frames", [("ragged_bf16_d64", 30), ("ragged_bf16_d128_yarn", 20),
+                                         ("f32_d128_mha", 20), ("bf16_g16_b_lt_t", 12),
+                                         ("bf16_t1_b1", 40), ("ivl3_1b", 64)])
 def test_free_running_stream(name, frames):
     wl = (SMALL.get(name) or CONFIGS[name]).replace(n_frames=frames)
     st = make_state(wl)
