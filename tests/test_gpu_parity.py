@@ -146,6 +146,41 @@ def test_free_running_stream(name, frames):
           "first (in-band) divergence", first_divergence, flush=True)
 
 
+# Everything is allocated when the state is created: evicting frames and text
+# tokens leave the device's free memory unchanged.  A first state runs every
+# kernel once beforehand, so that the runtime's lazy loading of code objects
+# happens outside the measured region; inputs and outputs are staged before it.
+def test_frames_and_text_allocate_nothing():
+    import ctypes
+    wl = SMALL["ragged_bf16_d64"].replace(n_frames=12)
+    fs = FrameStream(wl)
+    frames = [[to_device(x, wl.dtype) for x in fs.frame(n)] for n in range(wl.n_frames)]
+    gen = torch.Generator().manual_seed(7)
+    t, Hq, Hkv, d = 2, wl.n_q_heads, wl.n_kv_heads, wl.head_dim
+    text = [torch.randn((t, h, d), generator=gen).to(torch.bfloat16).cuda() for h in (Hq, Hkv, Hkv)]
+    O = torch.empty((wl.tokens_per_frame, Hq, d), dtype=torch.bfloat16, device="cuda")
+    Ot = torch.empty((t, Hq, d), dtype=torch.bfloat16, device="cuda")
+    hip = skv._hip_runtime()
+
+    def free_bytes():
+        torch.cuda.synchronize()
+        free, total = ctypes.c_size_t(), ctypes.c_size_t()
+        assert hip.hipMemGetInfo(ctypes.byref(free), ctypes.byref(total)) == 0
+        return free.value
+
+    for st in (make_state(wl, max_text=4 * t), make_state(wl, max_text=4 * t)):
+        st.prefill_frame(*frames[0], n=0, out=O)
+        before = free_bytes()
+        for n in range(1, wl.n_frames):
+            st.prefill_frame(*frames[n], n=n, out=O)
+        st.decode(*text, out=Ot)
+        st.decode(*text, out=Ot)
+        after = free_bytes()
+    assert after == before, (before, after)
+    _, _, pos = st.compressed_view()
+    assert pos.numel() == wl.budget
+
+
 # The largest pool the single-work-group selection takes: B + T = 32768
 # candidates (32 rows per selection thread), teacher-forced at the fill
 # boundary and on the first evicting frames.
