@@ -6,9 +6,11 @@ to D, attention over [compressed state; frame], scores, Top-B, gather) on one
 frame of the synthetic stream.  Default workload: the InternVL3-1B-like layer
 (bf16, 14 query / 2 KV heads, d = 64, T = 256, B = 4096); the stream generator
 is the seeded one of the tests, extended past its 64 frames when more steps
-are asked for.  All frames are resident in HBM before timing starts; W
-warm-up frames (the first B/T = 16 fill the state) precede K timed steps, so
-every timed step evicts T tokens (constant work per frame).
+are asked for.  All frames are resident in HBM before timing starts.  Setup
+runs the B/T = 16 frames that fill the state (a step is an evicting frame
+step, so the fill is part of building its state, like loading weights); then
+W untimed warm-up steps and K timed steps follow, every one of them evicting
+T tokens (constant work per frame).
 
 --layers L steps a stack of L independent layers of the workload's shape
 (each with its own seeded stream) through one launch per kernel; value is
@@ -44,7 +46,9 @@ def parse_args():
     p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=512, help="timed frame steps (K)")
-    p.add_argument("--warmup", type=int, default=16, help="untimed frames before timing (W)")
+    p.add_argument("--warmup", type=int, default=16,
+                   help="untimed evicting steps before timing (W), after the B/T frames that "
+                        "fill the state")
     p.add_argument("--workload", default="ivl3_1b")
     p.add_argument("--distinct-frames", type=int, default=0,
                    help="frames drawn from the generator; later steps reuse them cyclically "
@@ -431,12 +435,12 @@ def main():
         return
     T, Hq, Hkv, d, B = wl.tokens_per_frame, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.budget
     L = args.layers
-    fill = math.ceil(B / T)
-    W = max(args.warmup, fill)
+    fill = math.ceil(B / T)     # frames that fill the state (setup, not steps)
+    W = args.warmup
     K = args.steps
     timing_pass = 0 if args.no_kernel_timing else K
     latency_pass = K            # per-step events, no kernel timing: flatness
-    total = W + K + latency_pass + timing_pass
+    total = fill + W + K + latency_pass + timing_pass
     tdtype = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
@@ -480,11 +484,11 @@ def main():
         if rc:
             raise skv.StateKVError(rc, f"statekv_prefill_frame({n})")
 
-    for n in range(W):
+    for n in range(fill + W):
         step(n)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for n in range(W, W + K):
+    for n in range(fill + W, fill + W + K):
         step(n)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -495,7 +499,7 @@ def main():
     # flatness).  Third pass: per-kernel execution times from start / stop
     # events that each dispatch records.
     stream = torch.cuda.current_stream()
-    n0 = W + K
+    n0 = fill + W + K
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(latency_pass + 1)]
     evs[0].record(stream)
     for i in range(latency_pass):
@@ -516,6 +520,7 @@ def main():
                 kernels[name] = {"avg_us": 1e3 * ms / cnt, "launches": cnt}
         st.set_flags(skv.FLAG_RECENT_WINDOW if args.recent_window else 0)
 
+    merge_kernel = "select_merge"    # the launch that merges pass 1's key splits
     pairs = pair_count(T, B)
     attn_flops = 4.0 * Hq * d * pairs * L             # QK^T + PV, causal-counted, all layers
     # + QK^T recomputed by the score pass (skipped by the recency window)
@@ -528,8 +533,13 @@ def main():
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                     "traffic": load_traffic("attn_fwd", args.workload) if L == 1 else None}
-        t_passes = sum(kernels[k]["avg_us"] for k in ("attn_fwd", "attn_score") if k in kernels) * 1e-6
+        # Attention passes: pass 1, the score pass and the merge of pass 1's key
+        # splits.  The merge runs in the launch named by merge_kernel, whose whole
+        # time is counted (conservative when it shares the launch with other work).
+        passes = ["attn_fwd", "attn_score", merge_kernel]
+        t_passes = sum(kernels[k]["avg_us"] for k in passes if k in kernels) * 1e-6
         extra["attention_passes_mfma_frac"] = round(executed_flops / t_passes / 1e12 / PEAK_BF16_TFLOPS, 4)
+        extra["attention_passes_kernels"] = [k for k in passes if k in kernels]
         t_step_kernels = sum(v["avg_us"] for v in kernels.values()) * 1e-6
         extra["kernel_sum_us_per_step"] = round(t_step_kernels * 1e6, 2)
     if kernels.get("rope_append", {}).get("avg_us"):
@@ -623,6 +633,7 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": W,
+        "fill_frames": fill,
         "ms_per_step": round(1e3 * elapsed / K, 5),
         "stack_steps_per_s": round(K / elapsed, 2),
         "higher_is_better": True,

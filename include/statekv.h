@@ -128,7 +128,14 @@ typedef struct statekv_scores_view {
 int statekv_create(const statekv_layer_cfg* cfg, int32_t budget_B, float alpha,
                    statekv_state** out);
 
-/* Launch subsequent work on hip_stream (a hipStream_t; NULL = default stream). */
+/* Launch subsequent work on hip_stream (a hipStream_t on the state's device;
+ * NULL = default stream).  The new stream is ordered after all work already
+ * queued for the state on the old one (an event recorded on the old stream,
+ * waited on by the new one; the event is created with the state, so this call
+ * allocates nothing), so frames may move between streams without a host
+ * synchronisation.  Inputs written on another stream must be ordered before a
+ * call by the caller.  Errors: EINVAL (null state), EDEVICE; on error the state
+ * keeps its old stream. */
 int statekv_set_stream(statekv_state* s, void* hip_stream);
 
 /*

@@ -219,6 +219,22 @@ class StateKV:
     def set_flags(self, flags: int):
         self._check(self._lib.statekv_set_flags(self._h, flags), "statekv_set_flags")
 
+    # -- stream ordering ------------------------------------------------------
+    def _launch(self, fn, tensors):
+        """Run a library call on the state's stream, ordered after the work queued
+        on torch's current stream (which produced the inputs); the current stream
+        then waits for the call, so its output is ready there, and the tensors are
+        recorded on the state's stream for the caching allocator."""
+        cur = torch.cuda.current_stream(self.device)
+        if cur == self.stream:
+            fn()
+            return
+        self.stream.wait_stream(cur)
+        fn()
+        cur.wait_stream(self.stream)
+        for t in tensors:
+            t.record_stream(self.stream)
+
     # -- the frame step -------------------------------------------------------
     def _shape(self, tokens: int, heads: int):
         one = (tokens, heads, self.d)
@@ -233,7 +249,8 @@ class StateKV:
 
     def prefill_frame(self, Q, K, V, n: int, out=None) -> torch.Tensor:
         """Run frame n; returns O [T][Hq][d] ([L][T][Hq][d] for a stack), written
-        asynchronously on the state's stream."""
+        asynchronously on the state's stream.  When torch's current stream is not
+        the state's, the step is ordered after it and it waits for the step."""
         self._frame_tensor(Q, self.Hq, "Q")
         self._frame_tensor(K, self.Hkv, "K")
         self._frame_tensor(V, self.Hkv, "V")
@@ -241,9 +258,10 @@ class StateKV:
             out = torch.empty(self._shape(self.T, self.Hq), dtype=self.torch_dtype, device=Q.device)
         else:
             self._frame_tensor(out, self.Hq, "out")
-        self._check(self._lib.statekv_prefill_frame(self._h, Q.data_ptr(), K.data_ptr(),
-                                                    V.data_ptr(), n, out.data_ptr()),
-                    "statekv_prefill_frame")
+        self._launch(lambda: self._check(
+            self._lib.statekv_prefill_frame(self._h, Q.data_ptr(), K.data_ptr(), V.data_ptr(), n,
+                                            out.data_ptr()),
+            "statekv_prefill_frame"), (Q, K, V, out))
         return out
 
     # -- the text phase ---------------------------------------------------------
@@ -261,9 +279,10 @@ class StateKV:
             out = torch.empty(self._shape(t, self.Hq), dtype=self.torch_dtype, device=Q.device)
         else:
             self._frame_tensor(out, self.Hq, "out", t)
-        self._check(self._lib.statekv_decode(self._h, Q.data_ptr(), K.data_ptr(), V.data_ptr(),
-                                             t, out.data_ptr()),
-                    "statekv_decode")
+        self._launch(lambda: self._check(
+            self._lib.statekv_decode(self._h, Q.data_ptr(), K.data_ptr(), V.data_ptr(), t,
+                                     out.data_ptr()),
+            "statekv_decode"), (Q, K, V, out))
         return out
 
     # -- views (copied into new tensors) ------------------------------------------

@@ -200,7 +200,6 @@ int attn_rows_per_wg(Dt dt, int d);
 // Keys per LDS block of pass 1 (key splits are whole blocks).
 int attn_block_keys(Dt dt, int d);
 int score_keys_per_wg(Dt dt, int waves);
-int score_waves_forced(Dt dt);
 // Score work-groups resident per CU (occupancy of the instantiation in use).
 int score_wgs_per_cu(Dt dt, int d);
 int score8_wgs_per_cu(int d);

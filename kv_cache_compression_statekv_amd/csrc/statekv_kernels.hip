@@ -2011,30 +2011,9 @@ __global__ __launch_bounds__(256) void score_view_kernel(ScoreViewArgs a) {
 static constexpr int kKtBf16 = 2;  // key tiles per wave in the score pass
 static constexpr int kKtF32 = 1;
 
-// Pass-1 shape: bf16 uses 8 waves of one 32-query tile each (two waves per
-// SIMD, so one wave's matrix work overlaps the other's softmax); fp32 (tiny
-// shapes) uses 4 waves.  STATEKV_ATTN_WAVES=4 selects 4 waves of two tiles.
-static int attn_variant() {
-  static int v = -1;
-  if (v < 0) {
-    const char* e = getenv("STATEKV_ATTN_WAVES");
-    v = (e && atoi(e) == 4) ? 4 : 8;
-  }
-  return v;
-}
-
 // Register stages of pass 1's block prefetch: 2 for d = 128 (measured a few
-// percent faster on the long-pool shapes), 1 for d = 64 (no gain);
-// STATEKV_ATTN_PF = 1, 2 or 4 overrides.
-static int attn_prefetch(int d) {
-  static int v = -1;
-  if (v < 0) {
-    const char* e = getenv("STATEKV_ATTN_PF");
-    const int x = e ? atoi(e) : 0;
-    v = (x == 1 || x == 2 || x == 4) ? x : 0;
-  }
-  return v ? v : (d == 128 ? 2 : 1);
-}
+// percent faster on the long-pool shapes), 1 for d = 64 (no gain).
+static constexpr int attn_prefetch(int d) { return d == 128 ? 2 : 1; }
 
 // Compute units of the current device (0 if unknown).
 static int device_cus() {
@@ -2053,52 +2032,30 @@ static int device_cus() {
 // stages per LDS byte).
 int attn_block_keys(Dt, int) { return kAttnBN; }
 
-int attn_rows_per_wg(Dt dt, int) {
-  if (dt != Dt::BF16) return 4 * 32;
-  return attn_variant() == 4 ? 4 * 32 * 2 : 8 * 32;
-}
+// Pass-1 shape: bf16 uses 8 waves of one 32-query tile each (two waves per
+// SIMD, so one wave's matrix work overlaps the other's softmax); fp32 (tiny
+// shapes) uses 4 waves.
+int attn_rows_per_wg(Dt dt, int) { return dt != Dt::BF16 ? 4 * 32 : 8 * 32; }
 // Score pass shape: 4 waves (256 keys per work-group), or for bf16 8 waves
 // (512 keys), which halves the Q traffic: faster when the whole grid is
 // resident at once (a single layer at B = 4096: 9.9 -> 9.4 us), slower on the
 // long-pool shapes and stacks, whose grids take several rounds (stress shape
-// 69 -> 78 us).  The runtime picks per frame; STATEKV_SCORE_WAVES = 4 or 8
-// forces one.  Returns 0 when not forced.
-int score_waves_forced(Dt dt) {
-  static int v = -1;
-  if (v < 0) {
-    const char* e = getenv("STATEKV_SCORE_WAVES");
-    const int x = e ? atoi(e) : 0;
-    v = (x == 4 || x == 8) ? x : 0;
-  }
-  return dt == Dt::BF16 ? v : 4;
-}
+// 69 -> 78 us).  The runtime picks per frame.
 // Register stages of the score pass's Q-tile prefetch (4-wave kernel): 4 for
 // d = 128 (5-7 % faster on the long-pool shapes), 2 for d = 64, where it
 // leaves room for three waves per SIMD (16 % faster on the 28-layer ivl3_1b
-// stack); STATEKV_SCORE_PF = 1, 2 or 4 overrides.
-static int score_prefetch(int d) {
-  static int v = -1;
-  if (v < 0) {
-    const char* e = getenv("STATEKV_SCORE_PF");
-    const int x = e ? atoi(e) : 0;
-    v = (x == 1 || x == 2 || x == 4) ? x : 0;
-  }
-  return v ? v : (d == 64 ? 2 : 4);
-}
+// stack).
+static constexpr int score_prefetch(int d) { return d == 64 ? 2 : 4; }
 
 // Work-groups of the score kernel that fit on one CU at once (0 if unknown).
 int score_wgs_per_cu(Dt dt, int d) {
   int n = 0;
   hipError_t e = hipSuccess;
   if (dt == Dt::BF16) {
-    const int pf = score_prefetch(d);
-#define STATEKV_OCC(DD, PF) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_score_kernel<BF16, DD, kKtBf16, 4, PF>, 256, 0)
-    if (d == 64) {
-      if (pf == 4) STATEKV_OCC(64, 4); else if (pf == 2) STATEKV_OCC(64, 2); else STATEKV_OCC(64, 1);
-    } else {
-      if (pf == 4) STATEKV_OCC(128, 4); else if (pf == 2) STATEKV_OCC(128, 2); else STATEKV_OCC(128, 1);
-    }
-#undef STATEKV_OCC
+    e = d == 64 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                      &n, attn_score_kernel<BF16, 64, kKtBf16, 4, score_prefetch(64)>, 256, 0)
+                : hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                      &n, attn_score_kernel<BF16, 128, kKtBf16, 4, score_prefetch(128)>, 256, 0);
   }
   return e == hipSuccess ? n : 0;
 }
@@ -2141,23 +2098,12 @@ hipError_t launch_attn(Dt dt, int d, const AttnArgs& a, int row_tiles, int split
                        const LaunchTiming& tm) {
   const dim3 grid(row_tiles, a.Hkv, splits);
   if (dt == Dt::BF16) {
-    if (attn_variant() == 4) {
-      if (d == 64) hipExtLaunchKernelGGL((attn_fwd_kernel<BF16, 64, 2, 4>), grid, dim3(256), 0, s, tm.start, tm.stop, 0, a);
-      else hipExtLaunchKernelGGL((attn_fwd_kernel<BF16, 128, 2, 4>), grid, dim3(256), 0, s, tm.start, tm.stop, 0, a);
-    } else {
-      const int pf = attn_prefetch(d);
-      if (d == 64 && (long)row_tiles * a.Hkv * splits > device_cus()) {
-        hipExtLaunchKernelGGL((attn_fwd_kernel<BF16, 64, 1, 8, 1, kAttnBN, 4>), grid, dim3(512), 0, s, tm.start, tm.stop, 0, a);
-      } else if (d == 64) {
-        if (pf == 4) hipExtLaunchKernelGGL((attn_fwd_kernel<BF16, 64, 1, 8, 4>), grid, dim3(512), 0, s, tm.start, tm.stop, 0, a);
-        else if (pf == 2) hipExtLaunchKernelGGL((attn_fwd_kernel<BF16, 64, 1, 8, 2>), grid, dim3(512), 0, s, tm.start, tm.stop, 0, a);
-        else hipExtLaunchKernelGGL((attn_fwd_kernel<BF16, 64, 1, 8, 1>), grid, dim3(512), 0, s, tm.start, tm.stop, 0, a);
-      } else {
-        if (pf == 4) hipExtLaunchKernelGGL((attn_fwd_kernel<BF16, 128, 1, 8, 4>), grid, dim3(512), 0, s, tm.start, tm.stop, 0, a);
-        else if (pf == 2) hipExtLaunchKernelGGL((attn_fwd_kernel<BF16, 128, 1, 8, 2>), grid, dim3(512), 0, s, tm.start, tm.stop, 0, a);
-        else hipExtLaunchKernelGGL((attn_fwd_kernel<BF16, 128, 1, 8, 1>), grid, dim3(512), 0, s, tm.start, tm.stop, 0, a);
-      }
-    }
+    if (d == 64 && (long)row_tiles * a.Hkv * splits > device_cus())
+      hipExtLaunchKernelGGL((attn_fwd_kernel<BF16, 64, 1, 8, 1, kAttnBN, 4>), grid, dim3(512), 0, s, tm.start, tm.stop, 0, a);
+    else if (d == 64)
+      hipExtLaunchKernelGGL((attn_fwd_kernel<BF16, 64, 1, 8, attn_prefetch(64)>), grid, dim3(512), 0, s, tm.start, tm.stop, 0, a);
+    else
+      hipExtLaunchKernelGGL((attn_fwd_kernel<BF16, 128, 1, 8, attn_prefetch(128)>), grid, dim3(512), 0, s, tm.start, tm.stop, 0, a);
   } else {
     if (d == 64) hipExtLaunchKernelGGL((attn_fwd_kernel<F32, 64, 1, 4>), grid, dim3(256), 0, s, tm.start, tm.stop, 0, a);
     else hipExtLaunchKernelGGL((attn_fwd_kernel<F32, 128, 1, 4>), grid, dim3(256), 0, s, tm.start, tm.stop, 0, a);
@@ -2173,14 +2119,8 @@ hipError_t launch_score(Dt dt, int d, const ScoreArgs& a, int key_blocks, int rs
       if (d == 64) hipExtLaunchKernelGGL((attn_score_kernel<BF16, 64, kKtBf16, 8>), grid, dim3(512), 0, s, tm.start, tm.stop, 0, a);
       else hipExtLaunchKernelGGL((attn_score_kernel<BF16, 128, kKtBf16, 8>), grid, dim3(512), 0, s, tm.start, tm.stop, 0, a);
     } else {
-      const int pf = score_prefetch(d);
-#define STATEKV_SCORE(DD, PF) hipExtLaunchKernelGGL((attn_score_kernel<BF16, DD, kKtBf16, 4, PF>), grid, dim3(256), 0, s, tm.start, tm.stop, 0, a)
-      if (d == 64) {
-        if (pf == 4) STATEKV_SCORE(64, 4); else if (pf == 2) STATEKV_SCORE(64, 2); else STATEKV_SCORE(64, 1);
-      } else {
-        if (pf == 4) STATEKV_SCORE(128, 4); else if (pf == 2) STATEKV_SCORE(128, 2); else STATEKV_SCORE(128, 1);
-      }
-#undef STATEKV_SCORE
+      if (d == 64) hipExtLaunchKernelGGL((attn_score_kernel<BF16, 64, kKtBf16, 4, score_prefetch(64)>), grid, dim3(256), 0, s, tm.start, tm.stop, 0, a);
+      else hipExtLaunchKernelGGL((attn_score_kernel<BF16, 128, kKtBf16, 4, score_prefetch(128)>), grid, dim3(256), 0, s, tm.start, tm.stop, 0, a);
     }
   } else {
     if (d == 64) hipExtLaunchKernelGGL((attn_score_kernel<F32, 64, kKtF32, 4>), grid, dim3(256), 0, s, tm.start, tm.stop, 0, a);
@@ -2210,30 +2150,15 @@ constexpr int kDecodeWavesF32 = 2;
 int decode_block_keys(Dt dt) { return 32 * (dt == Dt::BF16 ? kDecodeWavesBf16 : kDecodeWavesF32); }
 
 // Register stages of the text-phase kernel's block prefetch: 2 for d = 128
-// (about 6 % more bandwidth on the long caches), 1 for d = 64;
-// STATEKV_DECODE_PF = 1 .. 4 overrides.
-static int decode_prefetch(int d) {
-  static int v = -1;
-  if (v < 0) {
-    const char* e = getenv("STATEKV_DECODE_PF");
-    const int x = e ? atoi(e) : 0;
-    v = (x >= 1 && x <= 4) ? x : 0;
-  }
-  return v ? v : (d == 128 ? 2 : 1);
-}
+// (about 6 % more bandwidth on the long caches), 1 for d = 64.
+static constexpr int decode_prefetch(int d) { return d == 128 ? 2 : 1; }
 
 hipError_t launch_decode(Dt dt, int d, const DecodeArgs& a, hipStream_t s, const LaunchTiming& tm) {
   const dim3 grid(a.L * a.Hkv, a.S);
   if (dt == Dt::BF16) {
     const dim3 block(64 * kDecodeWavesBf16);
-    const int pf = decode_prefetch(d);
-#define STATEKV_DEC(DD, PF) hipExtLaunchKernelGGL((decode_attn_kernel<BF16, DD, kDecodeWavesBf16, PF>), grid, block, 0, s, tm.start, tm.stop, 0, a)
-    if (d == 64) {
-      if (pf == 4) STATEKV_DEC(64, 4); else if (pf == 3) STATEKV_DEC(64, 3); else if (pf == 2) STATEKV_DEC(64, 2); else STATEKV_DEC(64, 1);
-    } else {
-      if (pf == 4) STATEKV_DEC(128, 4); else if (pf == 3) STATEKV_DEC(128, 3); else if (pf == 2) STATEKV_DEC(128, 2); else STATEKV_DEC(128, 1);
-    }
-#undef STATEKV_DEC
+    if (d == 64) hipExtLaunchKernelGGL((decode_attn_kernel<BF16, 64, kDecodeWavesBf16, decode_prefetch(64)>), grid, block, 0, s, tm.start, tm.stop, 0, a);
+    else hipExtLaunchKernelGGL((decode_attn_kernel<BF16, 128, kDecodeWavesBf16, decode_prefetch(128)>), grid, block, 0, s, tm.start, tm.stop, 0, a);
   } else {
     const dim3 block(64 * kDecodeWavesF32);
     if (d == 64) hipExtLaunchKernelGGL((decode_attn_kernel<F32, 64, kDecodeWavesF32>), grid, block, 0, s, tm.start, tm.stop, 0, a);

@@ -56,6 +56,7 @@ struct statekv_state {
   int64_t det_ls;        // elements of dk / dv per layer
   int device;
   hipStream_t stream;
+  hipEvent_t stream_ev;  // orders a newly set stream after the work queued on the old one
 
   // launch geometry
   int attn_tiles, attn_splits_max;
@@ -148,6 +149,7 @@ void release(statekv_state* s) {
       if (e[0]) (void)hipEventDestroy(e[0]);
       if (e[1]) (void)hipEventDestroy(e[1]);
     }
+  if (s->stream_ev) (void)hipEventDestroy(s->stream_ev);
 }
 
 // Add a finished (start, stop) pair of ring slot r, kernel k to the sums.
@@ -211,8 +213,7 @@ void attn_geometry(const statekv_state* s, int P, int* splits, int* kps) {
 constexpr int kScoreWGRows = 48;
 
 void score_geometry(const statekv_state* s, int P, int* key_blocks, int* rsplits, int* rps, int* waves) {
-  const int forced = score_waves_forced(s->dt);
-  const int w0 = forced ? forced : 4;
+  const int w0 = 4;
   const int kb = ceil_div(P, score_keys_per_wg(s->dt, w0));
   const int base = kb * s->HkvAll;
   const int rs_lo = ceil_div(s->R, kScoreMaxRows);   // rows per work-group fit the LDS statistics
@@ -238,7 +239,7 @@ void score_geometry(const statekv_state* s, int P, int* key_blocks, int* rsplits
   }
   int r = ceil_div(ceil_div(s->R, rs), 32) * 32;
   int w = w0, kbw = kb;
-  if (!forced && s->dt == Dt::BF16 && s->score_slots8 > 0) {
+  if (s->dt == Dt::BF16 && s->score_slots8 > 0) {
     const int kb8 = ceil_div(P, score_keys_per_wg(s->dt, 8));
     const int rs8 = std::min(s->score_slots8 / (kb8 * s->HkvAll), std::min(s->score_rsplits_max, ceil_div(s->R, 32)));
     if (rs8 >= rs_lo) {
@@ -516,6 +517,7 @@ int statekv_create(const statekv_layer_cfg* cfg, int32_t budget_B, float alpha,
   if (!rc) rc = check(hipMemset(s->ppos, 0, Ls * s->cap * sizeof(int32_t)));
   if (!rc) rc = check(hipMemset(s->move_count, 0, Ls * sizeof(int32_t)));
   if (!rc) rc = check(hipDeviceSynchronize());
+  if (!rc) rc = check(hipEventCreateWithFlags(&s->stream_ev, hipEventDisableTiming));
   if (!rc) {
     s->ev_ok = true;
     for (auto& ring : s->ev)
@@ -541,7 +543,15 @@ int statekv_create(const statekv_layer_cfg* cfg, int32_t budget_B, float alpha,
 
 int statekv_set_stream(statekv_state* s, void* hip_stream) {
   if (!s) return STATEKV_EINVAL;
-  s->stream = (hipStream_t)hip_stream;
+  const hipStream_t next = (hipStream_t)hip_stream;
+  if (next == s->stream) return STATEKV_OK;
+  // Work already queued on the old stream (earlier frames, pending moves)
+  // completes before anything later queued on the new one starts.
+  int rc = check(hipSetDevice(s->device));
+  if (!rc) rc = check(hipEventRecord(s->stream_ev, s->stream));
+  if (!rc) rc = check(hipStreamWaitEvent(next, s->stream_ev, 0));
+  if (rc) return rc;
+  s->stream = next;
   return STATEKV_OK;
 }
 

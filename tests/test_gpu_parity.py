@@ -7,7 +7,7 @@ compressed state before that frame.  Bars:
   * rotated K and V appended to D, and every kept state row: bit-exact;
   * kept index sets: identical except candidates whose oracle score is within
     1e-6 relative of the B-th score;
-  * scores (when computed): relative error below 1e-5, summing to 1.
+  * scores (when computed): relative error below 1e-6, summing to 1.
 """
 import numpy as np
 import pytest
@@ -106,7 +106,7 @@ def test_full_size_sampled_frames(name, layer, frames, check):
         if rep is not None:
             print(name, layer, rep, flush=True)
             assert_step_ok(rep, wl.dtype)
-            for key in ("out_err", "score_rel_max"):
+            for key in ("out_err", "score_rel_max", "score_rel_p99", "score_rel_p50"):
                 if key in rep:
                     worst[key] = max(worst.get(key, 0.0), rep[key])
     print("worst", name, layer, worst, flush=True)
@@ -306,6 +306,57 @@ def test_side_stream_run_matches_default_stream():
     for x, y in zip(a[0], b[0]):
         assert torch.equal(x, y)
     for x, y in zip(a[1:], b[1:]):
+        assert torch.equal(x, y)
+
+
+def _run_bits(st, wl, frames_on):
+    """Steps every frame of wl with the inputs uploaded, and the output read, on
+    the stream frames_on(n) returns; returns the outputs and the final state."""
+    fs = FrameStream(wl)
+    outs = []
+    for n in range(wl.n_frames):
+        with torch.cuda.stream(frames_on(n)):
+            x = [to_device(a, wl.dtype) for a in fs.frame(n)]
+            outs.append(st.prefill_frame(*x, n=n).cpu())
+    k, v, pos = st.compressed_view()
+    return outs, (k.cpu(), v.cpu(), pos.cpu())
+
+
+def test_state_stream_differs_from_current_stream():
+    """A state created on the default stream, stepped while torch's current
+    stream is a side stream (inputs produced and outputs read there): the
+    binding orders the state's stream after the side stream and the side stream
+    after the step, so the bits equal an all-default-stream run."""
+    wl = SMALL["ragged_bf16_d64"]
+    default = torch.cuda.current_stream()
+    ref = _run_bits(make_state(wl), wl, lambda n: default)
+    side = torch.cuda.Stream()
+    st = make_state(wl)                       # state stream: the default stream
+    assert st.stream == default
+    got = _run_bits(st, wl, lambda n: side)
+    for x, y in zip(ref[0], got[0]):
+        assert torch.equal(x, y)
+    for x, y in zip(ref[1], got[1]):
+        assert torch.equal(x, y)
+
+
+def test_set_stream_between_frames():
+    """statekv_set_stream between frames (alternating two side streams, no host
+    synchronisation): the new stream is ordered after the old one's work."""
+    wl = SMALL["ragged_bf16_d64"]
+    default = torch.cuda.current_stream()
+    ref = _run_bits(make_state(wl), wl, lambda n: default)
+    sides = [torch.cuda.Stream(), torch.cuda.Stream()]
+    st = make_state(wl)
+
+    def on(n):
+        st.set_stream(sides[n % 2])
+        return sides[n % 2]
+
+    got = _run_bits(st, wl, on)
+    for x, y in zip(ref[0], got[0]):
+        assert torch.equal(x, y)
+    for x, y in zip(ref[1], got[1]):
         assert torch.equal(x, y)
 
 
