@@ -57,6 +57,8 @@ extern "C" {
 #define STATEKV_ENOMEM     -4  /* device allocation failed */
 #define STATEKV_EDEVICE    -5  /* the HIP runtime reported an error */
 #define STATEKV_ENONFINITE -6  /* an input frame held NaN or Inf */
+#define STATEKV_ESCRATCH   -7  /* statekv_prefill_frame_static: the frame step needs more
+                                  working memory than STATEKV_STATIC_SCRATCH_BYTES */
 
 #define STATEKV_DTYPE_BF16  1
 #define STATEKV_DTYPE_F32   2
@@ -156,6 +158,30 @@ int statekv_set_stream(statekv_state* s, void* hip_stream);
  */
 int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K,
                           const void* V, int32_t n, void* O);
+
+/* Bytes of the static device scratch behind statekv_prefill_frame_static (per device). */
+#define STATEKV_STATIC_SCRATCH_BYTES (32u << 20)
+
+/*
+ * The frame step of statekv_prefill_frame, for callers that cannot allocate
+ * device memory at the time of the call (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): same arguments, same
+ * results (bit-identical), but the step's working buffers (rotated queries,
+ * the key-split partial outputs and their statistics) live in one static
+ * device array of STATEKV_STATIC_SCRATCH_BYTES per device instead of the
+ * state's own.  Calls nothing that allocates.  The array's address on the
+ * state's device is resolved when a state is first created there (or, failing
+ * that, on the first call).  Every call on one device shares that array and
+ * leaves its contents behind (nothing in it needs to start cleared): calls that
+ * overlap on one device, on different streams or states, race and must not be
+ * issued.  Errors: those of statekv_prefill_frame, and ESCRATCH (nothing
+ * enqueued, state unchanged) when the state's shapes need more working memory
+ * than the array holds: (rotated queries + split partials + statistics) of all
+ * L layers; e.g. the single-layer Hq=14/Hkv=2/d=64/T=256/B=4096 step uses about
+ * 9 MB.
+ */
+int statekv_prefill_frame_static(statekv_state* s, const void* Q, const void* K,
+                                 const void* V, int32_t n, void* O);
 
 /*
  * Compressed state C after the last frame: k, v are [Hkv][count][d] with

@@ -26,6 +26,8 @@ STATEKV_ECAPACITY = -3
 STATEKV_ENOMEM = -4
 STATEKV_EDEVICE = -5
 STATEKV_ENONFINITE = -6
+STATEKV_ESCRATCH = -7
+STATIC_SCRATCH_BYTES = 32 << 20
 
 DTYPE_BF16 = 1
 DTYPE_F32 = 2
@@ -119,6 +121,7 @@ def load_library(build_if_missing: bool = True) -> ctypes.CDLL:
     lib.statekv_create.argtypes = [ctypes.POINTER(LayerCfg), I32, F32, ctypes.POINTER(P)]
     lib.statekv_set_stream.argtypes = [P, P]
     lib.statekv_prefill_frame.argtypes = [P, P, P, P, I32, P]
+    lib.statekv_prefill_frame_static.argtypes = [P, P, P, P, I32, P]
     lib.statekv_decode.argtypes = [P, P, P, P, I32, P]
     lib.statekv_compressed_view.argtypes = [P, ctypes.POINTER(View)]
     lib.statekv_detailed_view.argtypes = [P, ctypes.POINTER(View)]
@@ -129,7 +132,8 @@ def load_library(build_if_missing: bool = True) -> ctypes.CDLL:
     lib.statekv_destroy.restype = None
     lib.statekv_strerror.argtypes = [ctypes.c_int]
     lib.statekv_strerror.restype = ctypes.c_char_p
-    for name in ("statekv_create", "statekv_set_stream", "statekv_prefill_frame", "statekv_decode",
+    for name in ("statekv_create", "statekv_set_stream", "statekv_prefill_frame",
+                 "statekv_prefill_frame_static", "statekv_decode",
                  "statekv_compressed_view", "statekv_detailed_view", "statekv_scores",
                  "statekv_set_flags", "statekv_kernel_times"):
         getattr(lib, name).restype = ctypes.c_int

@@ -42,8 +42,27 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 using namespace statekv;
+
+// Working memory of statekv_prefill_frame_static: the per-step buffers of a
+// frame step (rotated queries, pass-1 partials and split statistics) for
+// callers that cannot allocate.  Every device the library runs on holds its own
+// copy until the process ends; its address on a device is resolved once, with
+// that device current (hipGetSymbolAddress), and only that address is handed
+// to kernels.  Calls that overlap on one device share it and race.
+static __device__ __align__(256) unsigned char scratch[STATEKV_STATIC_SCRATCH_BYTES];
+
+// Per-step working buffers of a frame step: written and read within one
+// step, so nothing in them needs clearing between steps.
+struct StepScratch {
+  void* qrot;      // [L*Hkv][G*T][d] rotated queries
+  void* opart;     // pass-1 partial outputs, whole groups of 32 rows
+  int8_t* epart;   // exponents of the fp16 partials
+  float* mpart;    // split maxima
+  double* lpart;   // split row sums
+};
 
 struct statekv_state {
   statekv_layer_cfg cfg;
@@ -72,11 +91,7 @@ struct statekv_state {
   int32_t* ppos;
   void* dk;
   void* dv;
-  void* qrot;
-  void* opart;
-  int8_t* epart;
-  float* mpart;
-  double* lpart;
+  StepScratch work;  // the state's own per-step buffers
   float2* rope_tab;
   unsigned long long* colsum;
   float* scores;
@@ -138,8 +153,8 @@ int alloc(P** p, size_t bytes) {
 }
 
 void release(statekv_state* s) {
-  void* bufs[] = {s->kpool, s->vpool, s->ppos, s->dk, s->dv, s->qrot, s->opart, s->epart, s->mpart,
-                  s->lpart, s->rope_tab, s->colsum, s->scores, s->score_pos, s->keep_flag,
+  void* bufs[] = {s->kpool, s->vpool, s->ppos, s->dk, s->dv, s->work.qrot, s->work.opart,
+                  s->work.epart, s->work.mpart, s->work.lpart, s->rope_tab, s->colsum, s->scores, s->score_pos, s->keep_flag,
                   s->move_dst, s->move_src, s->move_count, s->evicted_pos, s->inv_freq,
                   s->nonfinite, s->dec_opart, s->dec_mpart, s->dec_lpart};
   for (void* b : bufs)
@@ -182,6 +197,56 @@ void scaled_inv_freq(int d, double base, double alpha, int orig_ctx, double* out
 }
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Byte sizes of the per-step buffers (StepScratch order) for the state's
+// shapes and its split stride stat_ss.
+void step_scratch_sizes(const statekv_state* s, size_t (&bytes)[5]) {
+  const size_t E = s->esize, D = s->D, S = s->stat_ss;
+  const size_t rows_all = (size_t)s->HkvAll * s->R;
+  const size_t stat_rows = (rows_all + 31) / 32 * 32;   // whole groups of 32 rows
+  bytes[0] = rows_all * D * E;
+  bytes[1] = (S * rows_all + 31) / 32 * 32 * D * E;
+  bytes[2] = S * rows_all * sizeof(int8_t);
+  bytes[3] = stat_rows * S * sizeof(float);
+  bytes[4] = stat_rows * S * sizeof(double);
+}
+
+// Lays the per-step buffers out from base (256-byte aligned pieces); returns
+// the bytes they span.
+size_t carve_step_scratch(const statekv_state* s, char* base, StepScratch* w) {
+  size_t bytes[5];
+  step_scratch_sizes(s, bytes);
+  size_t off[5], at = 0;
+  for (int i = 0; i < 5; ++i) {
+    off[i] = at;
+    at += (bytes[i] + 255) / 256 * 256;
+  }
+  if (w) {
+    w->qrot = base + off[0];
+    w->opart = base + off[1];
+    w->epart = reinterpret_cast<int8_t*>(base + off[2]);
+    w->mpart = reinterpret_cast<float*>(base + off[3]);
+    w->lpart = reinterpret_cast<double*>(base + off[4]);
+  }
+  return at;
+}
+
+// Device address of the static scratch array, per device.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Resolves the address of `scratch` on `device`, which must be current;
+// once per device.
+int resolve_static_scratch(int device) {
+  if (device < 0 || device >= kMaxDevices) return STATEKV_EDEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[device]) return STATEKV_OK;
+  void* p = nullptr;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return STATEKV_EDEVICE;
+  g_scratch_ptr[device] = p;
+  return STATEKV_OK;
+}
 
 // Pass 1 runs best with one work-group (8 waves) per compute unit: about 256
 // work-groups; the score pass with about 8 waves per compute unit.
@@ -369,6 +434,7 @@ const char* statekv_strerror(int code) {
     case STATEKV_ENOMEM: return "device memory allocation failed";
     case STATEKV_EDEVICE: return "HIP runtime error";
     case STATEKV_ENONFINITE: return "an input frame held NaN or Inf";
+    case STATEKV_ESCRATCH: return "the frame step needs more working memory than the static scratch holds";
     default: return "unknown error";
   }
 }
@@ -469,22 +535,21 @@ int statekv_create(const statekv_layer_cfg* cfg, int32_t budget_B, float alpha,
     decode_geometry(s, all_positions, &sp, &kp);
     if (sp > 1) dec_rows = (size_t)sp * s->HkvAll * 32;
   }
-  const size_t rows_all = (size_t)s->HkvAll * s->R;
   // Text chunks of more than 32 query rows per KV head run through pass 1
   // over D and may use up to kMaxSplits key splits.
   s->stat_ss = c.max_text > 0 ? kMaxSplits : s->attn_splits_max;
-  const size_t S = s->stat_ss;
+  size_t wbytes[5];
+  step_scratch_sizes(s, wbytes);
   rc = alloc(&s->kpool, pool_bytes);
   if (!rc) rc = alloc(&s->vpool, pool_bytes);
   if (!rc) rc = alloc(&s->ppos, Ls * s->cap * sizeof(int32_t));
   if (!rc) rc = alloc(&s->dk, det_bytes);
   if (!rc) rc = alloc(&s->dv, det_bytes);
-  if (!rc) rc = alloc(&s->qrot, rows_all * D * E);
-  if (!rc) rc = alloc(&s->opart, (S * rows_all + 31) / 32 * 32 * D * E);  // whole 32-row groups
-  if (!rc) rc = alloc(&s->epart, S * rows_all * sizeof(int8_t));
-  const size_t stat_rows = (rows_all + 31) / 32 * 32;   // whole groups of 32 rows
-  if (!rc) rc = alloc(&s->mpart, stat_rows * S * sizeof(float));
-  if (!rc) rc = alloc(&s->lpart, stat_rows * S * sizeof(double));
+  if (!rc) rc = alloc(&s->work.qrot, wbytes[0]);
+  if (!rc) rc = alloc(&s->work.opart, wbytes[1]);
+  if (!rc) rc = alloc(&s->work.epart, wbytes[2]);
+  if (!rc) rc = alloc(&s->work.mpart, wbytes[3]);
+  if (!rc) rc = alloc(&s->work.lpart, wbytes[4]);
   if (!rc) rc = alloc(&s->rope_tab, (size_t)all_positions * (D / 2) * sizeof(float2));
   if (!rc) rc = alloc(&s->colsum, 2 * Ls * s->cap * sizeof(unsigned long long));
   if (!rc) rc = alloc(&s->scores, Ls * s->cap * sizeof(float));
@@ -518,6 +583,9 @@ int statekv_create(const statekv_layer_cfg* cfg, int32_t budget_B, float alpha,
   if (!rc) rc = check(hipMemset(s->move_count, 0, Ls * sizeof(int32_t)));
   if (!rc) rc = check(hipDeviceSynchronize());
   if (!rc) rc = check(hipEventCreateWithFlags(&s->stream_ev, hipEventDisableTiming));
+  // The static scratch of statekv_prefill_frame_static on this device (a
+  // failure here is reported by that entry point, which retries).
+  if (!rc) (void)resolve_static_scratch(s->device);
   if (!rc) {
     s->ev_ok = true;
     for (auto& ring : s->ev)
@@ -563,21 +631,33 @@ int statekv_set_flags(statekv_state* s, uint32_t flags) {
   return STATEKV_OK;
 }
 
-int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const void* V,
-                          int32_t n, void* O) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks of a frame step; 0 if the frame may run.
+int check_frame(const statekv_state* s, const void* Q, const void* K, const void* V, int32_t n,
+                const void* O) {
   if (!s || !Q || !K || !V || !O) return STATEKV_EINVAL;
   if (n != s->frames_done || s->text_done > 0) return STATEKV_EORDER;
   if (n >= s->cfg.max_frames) return STATEKV_ECAPACITY;
-  int rc = check(hipSetDevice(s->device));
-  if (rc) return rc;
+  const int P = s->count + s->T;
+  const bool scored = (P > s->B && !(s->flags & STATEKV_FLAG_RECENT_WINDOW)) ||
+                      (s->flags & STATEKV_FLAG_ALWAYS_SCORE);
+  return STATEKV_OK;
+}
 
+// The frame step (arguments already checked, device current) with its
+// per-step buffers in w.
+int frame_step(statekv_state* s, const void* Q, const void* K, const void* V, int32_t n, void* O,
+               const StepScratch& w) {
+  int rc = STATEKV_OK;
   const int k0 = s->count;
   const int P = k0 + s->T;
   const hipStream_t st = s->stream;
   const bool evict = P > s->B;
   const bool recent = (s->flags & STATEKV_FLAG_RECENT_WINDOW) != 0;
   const bool scored = (evict && !recent) || (s->flags & STATEKV_FLAG_ALWAYS_SCORE);
-  if (scored && P > kMaxPool) return STATEKV_EINVAL;   // beyond the selection's pool limit
   // Rows of this frame: right after the state, or, while the previous
   // frame's moves are pending, the region its rows do not occupy.
   const int F = s->moves_pending ? (s->frame_base == (int)s->B + s->T ? (int)s->B : (int)s->B + s->T) : k0;
@@ -590,7 +670,7 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const 
     a.k = K;
     a.v = V;
     a.table = s->rope_tab;
-    a.qrot = s->qrot;
+    a.qrot = w.qrot;
     a.kpool = s->kpool;
     a.vpool = s->vpool;
     a.pool_pos = s->ppos;
@@ -616,13 +696,13 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const 
   {
     KernelTimer tm(s, STATEKV_K_ATTN);
     AttnArgs a{};
-    a.qrot = s->qrot;
+    a.qrot = w.qrot;
     a.kpool = s->kpool;
     a.vpool = s->vpool;
-    a.opart = s->opart;
-    a.epart = s->epart;
-    a.mpart = s->mpart;
-    a.lpart = s->lpart;
+    a.opart = w.opart;
+    a.epart = w.epart;
+    a.mpart = w.mpart;
+    a.lpart = w.lpart;
     a.c_hi = s->c_hi;
     a.R = s->R;
     a.G = s->G;
@@ -646,10 +726,10 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const 
     score_geometry(s, P, &key_blocks, &rsplits, &rps, &waves);
     KernelTimer tm(s, STATEKV_K_SCORE);
     ScoreArgs a{};
-    a.qrot = s->qrot;
+    a.qrot = w.qrot;
     a.kpool = s->kpool;
-    a.mpart = s->mpart;
-    a.lpart = s->lpart;
+    a.mpart = w.mpart;
+    a.lpart = w.lpart;
     a.S = splits;
     a.ss = s->stat_ss;
     a.colsum = s->colsum + (size_t)s->colsum_next * s->L * s->cap;
@@ -688,10 +768,10 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const 
     a.mode = evict ? kSelEvict : (scored ? kSelScores : kSelMerge);
     a.recent = recent ? 1 : 0;
     a.score_scale = 1.0 / ((double)(1ull << kScoreFracBits) * (double)s->Hq * (double)s->T);
-    a.opart = s->opart;
-    a.epart = s->epart;
-    a.mpart = s->mpart;
-    a.lpart = s->lpart;
+    a.opart = w.opart;
+    a.epart = w.epart;
+    a.mpart = w.mpart;
+    a.lpart = w.lpart;
     a.out = O;
     a.Hkv = s->HkvAll;
     a.R = s->R;
@@ -726,6 +806,32 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const 
   s->frames_done = n + 1;
   s->ev_slot = (s->ev_slot + 1) % statekv_state::kRing;
   return STATEKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const void* V,
+                          int32_t n, void* O) {
+  int rc = check_frame(s, Q, K, V, n, O);
+  if (!rc) rc = check(hipSetDevice(s->device));
+  if (rc) return rc;
+  return frame_step(s, Q, K, V, n, O, s->work);
+}
+
+int statekv_prefill_frame_static(statekv_state* s, const void* Q, const void* K, const void* V,
+                                 int32_t n, void* O) {
+  int rc = check_frame(s, Q, K, V, n, O);
+  if (rc) return rc;
+  if (carve_step_scratch(s, nullptr, nullptr) > (size_t)STATEKV_STATIC_SCRATCH_BYTES)
+    return STATEKV_ESCRATCH;
+  rc = check(hipSetDevice(s->device));
+  if (!rc) rc = resolve_static_scratch(s->device);
+  if (rc) return rc;
+  StepScratch w;
+  carve_step_scratch(s, static_cast<char*>(g_scratch_ptr[s->device]), &w);
+  return frame_step(s, Q, K, V, n, O, w);
 }
 
 int statekv_decode(statekv_state* s, const void* Q, const void* K, const void* V, int32_t t,
@@ -800,7 +906,7 @@ int statekv_decode(statekv_state* s, const void* Q, const void* K, const void* V
       a.k = K;
       a.v = V;
       a.table = s->rope_tab;
-      a.qrot = s->qrot;
+      a.qrot = s->work.qrot;
       a.dk = s->dk;
       a.dv = s->dv;
       a.nonfinite = s->nonfinite;
@@ -822,13 +928,13 @@ int statekv_decode(statekv_state* s, const void* Q, const void* K, const void* V
     {
       KernelTimer tm(s, STATEKV_K_DEC_ATTN);
       AttnArgs a{};
-      a.qrot = s->qrot;
+      a.qrot = s->work.qrot;
       a.kpool = s->dk;
       a.vpool = s->dv;
-      a.opart = s->opart;
-      a.epart = s->epart;
-      a.mpart = s->mpart;
-      a.lpart = s->lpart;
+      a.opart = s->work.opart;
+      a.epart = s->work.epart;
+      a.mpart = s->work.mpart;
+      a.lpart = s->work.lpart;
       a.c_hi = s->c_hi;
       a.R = R;
       a.G = s->G;
@@ -851,10 +957,10 @@ int statekv_decode(statekv_state* s, const void* Q, const void* K, const void* V
       KernelTimer tm(s, STATEKV_K_DEC_MERGE);
       SelectArgs a{};
       a.mode = kSelMerge;
-      a.opart = s->opart;
-      a.epart = s->epart;
-      a.mpart = s->mpart;
-      a.lpart = s->lpart;
+      a.opart = s->work.opart;
+      a.epart = s->work.epart;
+      a.mpart = s->work.mpart;
+      a.lpart = s->work.lpart;
       a.out = O;
       a.Hkv = s->HkvAll;
       a.R = R;

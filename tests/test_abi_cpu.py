@@ -19,7 +19,7 @@ def test_every_declared_function_is_exported():
 
 
 def test_error_strings():
-    for code in range(0, -7, -1):
+    for code in range(0, -8, -1):
         assert skv.error_string(code) and skv.error_string(code) != "unknown error"
     assert skv.error_string(-99) == "unknown error"
 
@@ -99,6 +99,7 @@ def test_null_arguments_are_rejected():
     cfg = _cfg()
     assert lib.statekv_create(ctypes.byref(cfg), 64, 1.0, None) == skv.STATEKV_EINVAL
     assert lib.statekv_prefill_frame(None, None, None, None, 0, None) == skv.STATEKV_EINVAL
+    assert lib.statekv_prefill_frame_static(None, None, None, None, 0, None) == skv.STATEKV_EINVAL
     assert lib.statekv_decode(None, None, None, None, 1, None) == skv.STATEKV_EINVAL
     v = skv.View()
     assert lib.statekv_compressed_view(None, ctypes.byref(v)) == skv.STATEKV_EINVAL
