@@ -520,7 +520,7 @@ def main():
                 kernels[name] = {"avg_us": 1e3 * ms / cnt, "launches": cnt}
         st.set_flags(skv.FLAG_RECENT_WINDOW if args.recent_window else 0)
 
-    merge_kernel = "select_merge"    # the launch that merges pass 1's key splits
+    merge_kernel = "score_merge"     # the launch that merges pass 1's key splits
     pairs = pair_count(T, B)
     attn_flops = 4.0 * Hq * d * pairs * L             # QK^T + PV, causal-counted, all layers
     # + QK^T recomputed by the score pass (skipped by the recency window)
@@ -536,20 +536,20 @@ def main():
         # Attention passes: pass 1, the score pass and the merge of pass 1's key
         # splits.  The merge runs in the launch named by merge_kernel, whose whole
         # time is counted (conservative when it shares the launch with other work).
-        passes = ["attn_fwd", "attn_score", merge_kernel]
+        passes = ["attn_fwd", merge_kernel]
         t_passes = sum(kernels[k]["avg_us"] for k in passes if k in kernels) * 1e-6
         extra["attention_passes_mfma_frac"] = round(executed_flops / t_passes / 1e12 / PEAK_BF16_TFLOPS, 4)
         extra["attention_passes_kernels"] = [k for k in passes if k in kernels]
         t_step_kernels = sum(v["avg_us"] for v in kernels.values()) * 1e-6
         extra["kernel_sum_us_per_step"] = round(t_step_kernels * 1e6, 2)
-    if kernels.get("rope_append", {}).get("avg_us"):
+    if kernels.get("rope_select", {}).get("avg_us"):
         # RoPE + append (copy-like, HBM roofline): reads Q, K, V of the frame and
         # its rows of the cos/sin table; writes the rotated queries, the frame's
         # pool rows and its D rows (K and V).  The previous frame's moves (at
         # most T rows per KV head, K and V, read and written) are not counted.
         esz = 2 if wl.dtype == "bf16" else 4
         rope_bytes = L * ((Hq + 2 * Hkv) * T * d * esz + T * d * 4 + (Hq + 4 * Hkv) * T * d * esz)
-        gbs = rope_bytes / (kernels["rope_append"]["avg_us"] * 1e-6) / 1e9
+        gbs = rope_bytes / (kernels["rope_select"]["avg_us"] * 1e-6) / 1e9
         extra["hbm_rope_append"] = {"bytes": rope_bytes, "achieved_gbs": round(gbs, 1),
                                     "peak_gbs": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4),
                                     "note": "algorithmic bytes of the frame's RoPE and appends; "

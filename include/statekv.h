@@ -243,13 +243,17 @@ int statekv_decode(statekv_state* s, const void* Q, const void* K, const void* V
 /* Set option flags (STATEKV_FLAG_*).  Takes effect from the next frame. */
 int statekv_set_flags(statekv_state* s, uint32_t flags);
 
-/* Kernels of one step, in launch order, as indexed by statekv_kernel_times. */
-#define STATEKV_K_ROPE     0  /* virtual-position RoPE + append to D; the
-                                 previous frame's moves of kept rows into
-                                 evicted slots */
+/* Kernels of one step, in launch order, as indexed by statekv_kernel_times.
+ * A frame step is three launches: the frame launch, pass 1, and the score +
+ * merge launch.  The Top-B decision of a frame (and the moves of kept rows
+ * into evicted slots) is made in the next frame's frame launch, beside that
+ * frame's RoPE, or in a launch of its own when a view asks for the state. */
+#define STATEKV_K_ROPE     0  /* frame launch: the previous frame's Top-B decision
+                                 and moves; virtual-position RoPE + append to D */
 #define STATEKV_K_ATTN     1  /* fused attention, pass 1 (split over keys) */
-#define STATEKV_K_SCORE    2  /* recompute pass: per-key column sums */
-#define STATEKV_K_SELECT   3  /* Top-B decision; merge of the key splits into O */
+#define STATEKV_K_SCORE    2  /* merge of the key splits into O; recompute pass:
+                                 per-key column sums */
+#define STATEKV_K_SELECT   3  /* a pending Top-B decision made for a view */
 #define STATEKV_K_DEC_ROPE  4 /* text phase: RoPE of the text tokens + append to D */
 #define STATEKV_K_DEC_ATTN  5 /* text phase: attention over D, split over keys */
 #define STATEKV_K_DEC_MERGE 6 /* text phase: merge of the key splits into O */

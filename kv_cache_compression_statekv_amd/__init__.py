@@ -36,7 +36,7 @@ FLAG_ALWAYS_SCORE = 1
 FLAG_KERNEL_TIMING = 2
 FLAG_RECENT_WINDOW = 4
 
-KERNEL_NAMES = ["rope_append", "attn_fwd", "attn_score", "select_merge",
+KERNEL_NAMES = ["rope_select", "attn_fwd", "score_merge", "select_view",
                 "decode_rope", "decode_attn", "decode_merge"]
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),

@@ -13,7 +13,7 @@ constexpr int kAttnBN = 64;          // keys per LDS block in attention pass 1
 constexpr int kMaxSplits = 24;       // key splits of a frame's pass 1 (merges unroll over them)
 constexpr int kMaxMergeSplits = 512; // key splits of a text chunk's pass 1 (merged in a loop)
 constexpr int kScoreMaxRows = 512;   // rows of one score work-group (row statistics in LDS)
-constexpr int kSelectThreads = 1024;  // select launch: selection and merge work-groups
+constexpr int kSelectThreads = 1024;  // frame launch: selection and RoPE work-groups
 constexpr int kMaxPool = 32768;      // B + T limit of the single-work-group select
 constexpr int kSelectBins = 4096;
 constexpr int kSelCand = kSelectThreads;  // boundary candidates resolved by rank counting (one per thread)
@@ -33,27 +33,38 @@ struct RopeTableArgs {
   int32_t npos, half;
 };
 
-// Moves of a selection: row move_src[i] (a frame row at or beyond B) ->
-// slot move_dst[i] (< B) of every KV head, with its position; the position
-// the slot held is saved in evicted_pos[slot].  Pointers address layer 0 of
-// a stack; layer l's arrays follow at fixed strides: Hkv*cap rows (pools),
-// cap (pool_pos), B (evicted_pos), list_stride (move lists), 1 (move_count).
-struct MovesArgs {
+// Top-B decision of a scored (or evicting) frame and the moves it implies:
+// the evicted slots below B receive, in ascending order, the kept rows at or
+// beyond B (K and V of every KV head, and their positions; the position a slot
+// held is saved in evicted_pos[slot]).  One work-group per layer makes the
+// decision and performs its moves, in the next frame's first launch (beside
+// that frame's RoPE work-groups, which write the other frame region) or in a
+// launch of its own before a view of the state.  Pointers address layer 0 of a
+// stack; layer l's arrays follow at fixed strides: cap (colsum, pool_pos), B
+// (evicted_pos), list_stride (move lists), 1 (move_count), Hkv*cap rows (pools).
+struct SelArgs {
+  const unsigned long long* colsum;  // [cap] fixed-point column sums of the frame
+  int32_t* pool_pos;           // [cap] positions of the pool rows (by row)
+  int32_t* evicted_pos;        // [B] out
+  int32_t* move_dst;           // [T] out: evicted state slots (< B), ascending
+  int32_t* move_src;           // [T] out: rows of the kept frame tokens at or beyond B, ascending
+  int32_t* move_count;         // [1] out
   void* kpool;
   void* vpool;
-  int32_t* pool_pos;
-  int32_t* evicted_pos;        // [B] out
-  const int32_t* move_dst;
-  const int32_t* move_src;
-  const int32_t* move_count;
-  int32_t Hkv, cap, B, row_bytes, max_moves, list_stride;
+  int32_t P, B, mode;          // mode: kSelScores or kSelEvict
+  int32_t recent;              // 1: keep the B most recent candidates (positions), not the best scores
+  int32_t k0, foff;            // pool index -> row
+  double score_scale;          // 2^-kScoreFracBits / (Hq * T)
+  int32_t Hkv, cap, row_bytes, list_stride;   // Hkv: KV heads per layer
 };
+constexpr int kSelScores = 1;  // scores only, everything kept
+constexpr int kSelEvict = 2;   // scores (or positions) and Top-B
 
-// Arguments of the RoPE + append kernel for T tokens at stream positions
-// pos0..pos0+T-1 (a frame, or a chunk of text tokens).  Work-groups at or
-// beyond rope_blocks apply the previous frame's moves (mv.max_moves > 0):
-// they touch state slots below B and the previous frame's rows, never this
-// frame's.  Text tokens go to D only (kpool, vpool and pool_pos null).
+// Arguments of the frame launch: the RoPE + append work for T tokens at
+// stream positions pos0..pos0+T-1 (a frame, or a chunk of text tokens), and
+// in front of it (nsel = 1) the previous frame's selection work-group.  The
+// RoPE work-groups also clear the column sums this frame's score pass will
+// accumulate.  Text tokens go to D only (kpool, vpool and pool_pos null).
 // Layer l of a stack (grid y) finds its inputs and qrot T*H*d elements per
 // layer further, its pool Hkv*cap*d, pool_pos cap and D det_ls.
 struct RopeArgs {
@@ -70,7 +81,10 @@ struct RopeArgs {
   int32_t* nonfinite;     // set to 1 when an input element is NaN or Inf
   int32_t pos0, T, Hq, Hkv, G, cap, frame_base, rope_blocks;
   int64_t det_ls;         // elements between layers of dk / dv
-  MovesArgs mv;
+  unsigned long long* clear;  // [L][cap] column sums cleared (null: none)
+  int32_t clear_n;            // elements per layer
+  int32_t nsel;           // selection work-groups per layer in front of the RoPE ones (0 or 1)
+  SelArgs sel;
 };
 
 // Pool index j (state slots, then the frame's tokens) -> row of the pool
@@ -155,37 +169,32 @@ struct DecodeMergeArgs {
   int32_t R, G, Hq, Hkv, S, L;   // Hkv per layer
 };
 
-// Work-groups 0..L-1: scores and the Top-B decision of layer l (none in
-// kSelMerge mode); the others: the merge of the key splits of pass 1 into O
-// (independent of the selection).  Selection pointers address layer 0; layer
-// l's arrays follow cap (colsum, pool_pos, scores, keep_flag), list_stride
-// (move lists) and 1 (move_count) elements further.
-struct SelectArgs {
-  const unsigned long long* colsum;  // [cap] fixed-point column sums of this frame
-  // The other column-sum buffer, cleared by the merge work-groups for the
-  // next scored frame (null: nothing to clear); clear_n elements.
-  unsigned long long* colsum_clear;
-  int64_t clear_n;
-  const int32_t* pool_pos;     // [cap] positions of the pool rows (by row)
-  int32_t* move_dst;           // [T] out: evicted state slots (< B), ascending
-  int32_t* move_src;           // [T] out: rows of the kept frame tokens at or beyond B, ascending
-  int32_t* move_count;         // [1] out
-  int32_t P, B, mode;          // mode: kSelMerge, kSelScores or kSelEvict
-  int32_t recent;              // 1: keep the B most recent candidates (positions), not the best scores
-  int32_t k0, foff;            // pool index -> row
-  double score_scale;          // 2^-kScoreFracBits / (Hq * T)
+// Merge of the key splits of pass 1 into O, one work-group per group of 32
+// flat rows (flat row = g*R + r over the KV heads of all layers).
+struct MergeArgs {
   const void* opart;
   const int8_t* epart;
   const float* mpart;
   const double* lpart;
   void* out;                   // [L][T][Hq][d]
   int32_t Hkv, R, G, Hq, S, ss;   // Hkv: KV heads of all layers (layer-major)
-  int32_t L, lh, cap, list_stride;
+  int32_t lh;                  // KV heads per layer
   int64_t out_ls;              // elements of out between layers
 };
-constexpr int kSelMerge = 0;   // merge only (the pool fits in B and is not scored)
-constexpr int kSelScores = 1;  // scores, everything kept
-constexpr int kSelEvict = 2;   // scores and Top-B
+
+// The launch after pass 1: merge work-groups first (merge_wgs, a multiple of
+// the XCD count), then the score pass's (key block, KV head, row split)
+// work-groups.  Either part may be empty.
+// With fused = 1 there are no merge work-groups: the score work-groups whose
+// key block starts before k0 (the first mkb of each (KV head, row split))
+// also merge the split partials of their row range, mtpw (row, 4 dims) tasks
+// each, rows fastest; such a block's row statistics cover its whole range.
+struct ScoreMergeArgs {
+  ScoreArgs sc;
+  MergeArgs mg;
+  int32_t merge_wgs, key_blocks, rsplits;
+  int32_t fused, mkb, mtpw;
+};
 
 // Start / stop events that the dispatch itself records (kernel timing): the
 // elapsed time between them is the kernel's execution, without the launch
@@ -203,18 +212,23 @@ int score_keys_per_wg(Dt dt, int waves);
 // Score work-groups resident per CU (occupancy of the instantiation in use).
 int score_wgs_per_cu(Dt dt, int d);
 int score8_wgs_per_cu(int d);
-// Work-groups of the RoPE part of the RoPE kernel for T tokens.
+// Work-groups of the RoPE part of the frame launch for T tokens.
 int rope_blocks(int T, int Hq, int Hkv, int d, int esize);
 
 hipError_t launch_rope_table(const RopeTableArgs& a, hipStream_t s);
-hipError_t launch_rope(Dt dt, int d, const RopeArgs& a, int layers, hipStream_t s,
-                       const LaunchTiming& tm = {});
+// The frame launch (RoPE + append, the previous frame's selection); with
+// a.rope_blocks = 0 only the selection.
+hipError_t launch_frame(Dt dt, int d, const RopeArgs& a, int layers, hipStream_t s,
+                        const LaunchTiming& tm = {});
 hipError_t launch_attn(Dt dt, int d, const AttnArgs& a, int row_tiles, int splits, hipStream_t s,
                        const LaunchTiming& tm = {});
-hipError_t launch_score(Dt dt, int d, const ScoreArgs& a, int key_blocks, int rsplits, int waves,
-                        hipStream_t s, const LaunchTiming& tm);
-hipError_t launch_select(Dt dt, int d, const SelectArgs& a, hipStream_t s, const LaunchTiming& tm = {});
-hipError_t launch_moves(const MovesArgs& a, int layers, hipStream_t s);
+// Score pass (with `waves` waves per work-group) and merge in one launch.  The
+// merge rides on the score work-groups (fused) only where score_merge_fusable.
+hipError_t launch_score_merge(Dt dt, int d, const ScoreMergeArgs& a, int waves, hipStream_t s,
+                              const LaunchTiming& tm = {});
+// Work-groups of the merge for `rows` flat rows (a multiple of the XCD count).
+int merge_wgs(int64_t rows);
+inline bool score_merge_fusable(Dt dt, int d, int waves) { return dt == Dt::BF16 && d == 64 && waves == 8; }
 // Keys per block of the text-phase attention kernel.
 int decode_block_keys(Dt dt);
 hipError_t launch_decode(Dt dt, int d, const DecodeArgs& a, hipStream_t s, const LaunchTiming& tm = {});

@@ -7,14 +7,15 @@
 //                       the frame's K, V are appended to the detailed cache D.
 //   attn_fwd_kernel     关键设计 1: the frame's queries attend over
 //                       [Kbar_{n-1}; K_n] (bf16 MFMA, online softmax, split
-//                       over keys; the splits are merged by select_kernel).
-//   attn_score_kernel   关键设计 2: score of candidate j = attention weight paid
-//                       to j averaged over the frame's queries and query heads;
-//                       recomputed with the final row max / sum of pass 1.
-//   select_kernel       关键设计 2: TopK({s_j}, B), ties kept toward the older
-//                       token; its other work-groups merge the key splits of
-//                       the attention output.
-//   moves_kernel        关键设计 2: build C_n from the kept candidates (kept
+//                       over keys).
+//   score_merge_kernel  关键设计 1: merge of pass 1's key splits into the
+//                       output; 关键设计 2: score of candidate j = attention
+//                       weight paid to j averaged over the frame's queries and
+//                       query heads, recomputed with the final row max / sum.
+//   frame_kernel        关键设计 3 + flowchart node E: the RoPE work-groups
+//                       (rope_wg); 关键设计 2: in front of them, the previous
+//                       frame's TopK({s_j}, B), ties kept toward the older
+//                       token, and C_n built from the kept candidates (kept
 //                       frame rows move into the evicted slots).
 //   decode_attn_kernel  整体框架 / 关键设计 1, 3: after the frames, text
 //   decode_merge_kernel tokens attend over the whole detailed cache D at the
@@ -281,41 +282,6 @@ __device__ __forceinline__ int xcd_remap(int id, int n) {
   return xcd * q + min(xcd, r) + local;
 }
 
-// Layer l's slice of a stack's move arguments.
-__device__ __forceinline__ MovesArgs moves_layer(MovesArgs a, int l) {
-  const size_t pool_bytes = (size_t)a.Hkv * a.cap * a.row_bytes;
-  a.kpool = (char*)a.kpool + l * pool_bytes;
-  a.vpool = (char*)a.vpool + l * pool_bytes;
-  a.pool_pos += (size_t)l * a.cap;
-  a.evicted_pos += (size_t)l * a.B;
-  a.move_dst += (size_t)l * a.list_stride;
-  a.move_src += (size_t)l * a.list_stride;
-  a.move_count += l;
-  return a;
-}
-
-// One 16-byte chunk of a move: task t = (move i, KV head g, chunk c); K and V.
-// The move list holds slots below B and rows in [B, cap); clamping only
-// guards the copy against a malformed list.
-__device__ __forceinline__ void apply_move_chunk(const MovesArgs& a, size_t t) {
-  const int cpr = a.row_bytes / 16;
-  const int i = (int)(t / ((size_t)a.Hkv * cpr));
-  if (i >= min(*a.move_count, a.max_moves)) return;
-  const int rem = (int)(t - (size_t)i * a.Hkv * cpr);
-  const int g = rem / cpr, c = rem - g * cpr;
-  const int dst = min(max(a.move_dst[i], 0), a.B - 1);
-  const int src = min(max(a.move_src[i], a.B), a.cap - 1);
-  const size_t so = ((size_t)g * a.cap + src) * a.row_bytes + (size_t)c * 16;
-  const size_t dof = ((size_t)g * a.cap + dst) * a.row_bytes + (size_t)c * 16;
-  *reinterpret_cast<u32x4_t*>((char*)a.kpool + dof) = *reinterpret_cast<const u32x4_t*>((const char*)a.kpool + so);
-  *reinterpret_cast<u32x4_t*>((char*)a.vpool + dof) = *reinterpret_cast<const u32x4_t*>((const char*)a.vpool + so);
-  if (g == 0 && c == 0) {
-    a.evicted_pos[dst] = a.pool_pos[dst];
-    a.pool_pos[dst] = a.pool_pos[src];
-  }
-}
-
-
 // Four rotation pairs of one (token, head): x1 = x[k..k+4), x2 = x[k+d/2..).
 template <class E> struct Vec4;
 template <> struct Vec4<BF16> {
@@ -356,19 +322,19 @@ __host__ __device__ inline int64_t rope_v_tasks(int T, int Hkv, int d, int esize
   return (int64_t)T * Hkv * (d * esize / 16);
 }
 
+// The RoPE + append work of RoPE work-group `wg` (kSelectThreads tasks) of
+// layer `layer`; it also clears its share of the layer's column sums.
 template <class E, int D>
-__global__ __launch_bounds__(256) void rope_append_kernel(RopeArgs a0) {
+__device__ void rope_wg(const RopeArgs& a0, size_t layer, int wg) {
   typedef typename E::T T;
   constexpr int HALF = D / 2;
   constexpr int CH = HALF / kRopePairsPerTask;   // tasks per head
   constexpr int VEC = 16 / (int)sizeof(T);
   constexpr int VCH = D / VEC;                   // value chunks per head
   const int tid = threadIdx.x;
-  // Layer blockIdx.y of a stack: its slice of every array.
-  const size_t layer = blockIdx.y;
-  if ((int)blockIdx.x >= a0.rope_blocks) {   // the previous frame's moves
-    apply_move_chunk(moves_layer(a0.mv, (int)layer), (size_t)(blockIdx.x - a0.rope_blocks) * 256 + tid);
-    return;
+  if (a0.clear) {
+    unsigned long long* c = a0.clear + layer * a0.cap;
+    for (int i = wg * kSelectThreads + tid; i < a0.clear_n; i += a0.rope_blocks * kSelectThreads) c[i] = 0ull;
   }
   RopeArgs a = a0;
   {
@@ -389,7 +355,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeArgs a0) {
   const int nh = a.Hq + a.Hkv;
   const int64_t nqk = rope_qk_tasks(a.T, a.Hq, a.Hkv, D);
   const int64_t nv = rope_v_tasks(a.T, a.Hkv, D, (int)sizeof(T));
-  const int64_t t = (int64_t)blockIdx.x * 256 + tid;
+  const int64_t t = (int64_t)wg * kSelectThreads + tid;
   bool finite = true;
   if (t < nqk) {
     const int c = (int)(t % CH);
@@ -1355,8 +1321,25 @@ __global__ __launch_bounds__(kDecodeMergeThreads) void decode_merge_kernel(Decod
 // key's fixed-point total.  Every sum has a fixed order (or is an integer
 // sum), so the scores are deterministic.
 // ---------------------------------------------------------------------------
-template <class E, int D, int KT, int NW, int NPF = 1>
-__global__ __launch_bounds__(64 * NW, 1) void attn_score_kernel(ScoreArgs a) {
+constexpr int16_t kNoWeight = -32768;
+// Exponent of a merge weight 2^(ms - m) <= 1 (an integer); exponents below the
+// fp32 range give weight 0 either way.
+__device__ __forceinline__ int16_t weight_exp(float e) { return (int16_t)max(-1000, (int)e); }
+
+// LDS bytes of one score work-group: two Q tiles, row statistics.
+template <class E, int D>
+constexpr int score_lds_bytes() {
+  return 2 * 32 * (D + 16 / (int)sizeof(typename E::T)) * (int)sizeof(typename E::T) + 3 * kScoreMaxRows * 4;
+}
+
+// Score work-group `wid` of `nwg` (logical (key block, KV head, row split),
+// key_blocks x a.Hkv x row splits), LDS at smem (score_lds_bytes).
+// FM: this instantiation can merge split partials in its score work-groups
+// (ScoreMergeArgs::fused); the merge's registers fit beside the score pass's
+// only in some shapes.
+template <class E, int D, int KT, int NW, int NPF, bool FM>
+__device__ void score_wg(const ScoreArgs& a, int wid, int nwg, int key_blocks, const ScoreMergeArgs& fm,
+                         char* smem) {
   typedef typename E::T T;
   typedef Mma<E> M;
   constexpr int RT = 32;
@@ -1367,20 +1350,19 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_score_kernel(ScoreArgs a) {
   constexpr int BNK = NW * 32 * KT;
   constexpr int CPR = D / EPV;                       // 16-byte chunks per Q row
   constexpr int QCH = (RT * CPR + NT - 1) / NT;
-  __shared__ __attribute__((aligned(16))) T Qs[2][RT * QSTR];
-  __shared__ __attribute__((aligned(16))) float sm[kScoreMaxRows];
-  __shared__ __attribute__((aligned(16))) float sr[kScoreMaxRows];
-  __shared__ __attribute__((aligned(16))) int slim[kScoreMaxRows];
+  T* const Qs0 = reinterpret_cast<T*>(smem);         // [2][RT * QSTR]
+  float* const sm = reinterpret_cast<float*>(smem + 2 * RT * QSTR * sizeof(T));
+  float* const sr = sm + kScoreMaxRows;
+  int* const slim = reinterpret_cast<int*>(sr + kScoreMaxRows);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, hh = lane >> 5;
   // Logical (key block, KV head, row split); the key blocks of one (head,
   // row split) share its Q rows and run on one XCD.
-  const int wl = xcd_remap(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z),
-                           gridDim.x * gridDim.y * gridDim.z);
-  const int kblock = wl % gridDim.x, wrest = wl / gridDim.x;
-  const int g = wrest % gridDim.y, rsplit = wrest / gridDim.y;
+  const int wl = xcd_remap(wid, nwg);
+  const int kblock = wl % key_blocks, wrest = wl / key_blocks;
+  const int g = wrest % a.Hkv, rsplit = wrest / a.Hkv;
   const int key_wg = kblock * BNK;
   const int key_w = key_wg + wave * 32 * KT;
 
@@ -1428,13 +1410,47 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_score_kernel(ScoreArgs a) {
     for (int j = 0; j < QCH; ++j) {
       const int t = tid + j * NT;
       const int rr = t / CPR, cc = t - rr * CPR;
-      if (t < RT * CPR) *reinterpret_cast<u32x4_t*>(&Qs[buf][rr * QSTR + cc * EPV]) = q[j];
+      if (t < RT * CPR) *reinterpret_cast<u32x4_t*>(&Qs0[buf * RT * QSTR + rr * QSTR + cc * EPV]) = q[j];
     }
   };
 
 #pragma unroll
   for (int i = 0; i < NPF; ++i)
     if (i < ntile) load_tile(qr[i], rstart + i * RT);
+
+  // Fused merge: task tid of this work-group's slice, (row, 4 dims) of the
+  // rows [r0, r1) (rows fastest).  Its loads are in flight while the row
+  // statistics are merged; the merge itself uses those statistics (this key
+  // block starts before k0, so rstart = r0 and they cover every row).
+  typedef typename PartialOut<E>::V PV;
+  constexpr int MCPR = D / 4;
+  PV mo[kMaxSplits];
+  int8_t me[kMaxSplits];
+  float mm[kMaxSplits];
+  int m_row = -1, m_c = 0;
+  if (FM && fm.fused && kblock < fm.mkb && tid < fm.mtpw) {
+    const int nrow_m = r1 - r0;
+    const int t = kblock * fm.mtpw + tid;
+    if (t < nrow_m * MCPR) {
+      m_row = r0 + t % nrow_m;
+      m_c = t / nrow_m;
+    }
+  }
+  if (FM && m_row >= 0) {
+    const MergeArgs& mg = fm.mg;
+    const size_t nrows = (size_t)mg.Hkv * mg.R;
+    const size_t base = (size_t)g * mg.R + m_row;
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplits; ++sp) {
+      mm[sp] = -INFINITY;
+      if (sp < mg.S) {
+        const size_t ri = sp * nrows + base;
+        mo[sp] = reinterpret_cast<const PV*>(mg.opart)[opart_group(ri, D) + (size_t)m_c * 32 + (ri & 31)];
+        me[sp] = sizeof(T) == 2 ? mg.epart[ri] : (int8_t)0;
+        mm[sp] = mg.mpart[stat_index(base, sp, mg.ss)];
+      }
+    }
+  }
   // Row statistics of the work-group's rows (padded to whole tiles), from the
   // key-split partials of pass 1: m = max_s m_s, l = sum_s 2^(m_s - m) l_s
   // (exact powers of two, fp64 sum).  Padding rows get 1/l = 0.
@@ -1458,6 +1474,38 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_score_kernel(ScoreArgs a) {
 
   if (ntile > 0) store_tile(qr[0], 0);
   __syncthreads();
+  if (FM && m_row >= 0) {
+    // m and 1/l of the row, as the split merge forms them; the same weights,
+    // arithmetic and order as merge_group, so O does not depend on which
+    // work-groups merge it.
+    const MergeArgs& mg = fm.mg;
+    const float m = sm[m_row - rstart];
+    const float inv = sr[m_row - rstart];
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplits; ++sp) {
+      if (sp < mg.S && mm[sp] != -INFINITY) {
+        const float w = ldexpf(1.f, weight_exp(mm[sp] - m));
+        if (w != 0.f) {
+          const f32x4_t o4 = PartialOut<E>::unpack(mo[sp]);
+          const float wo = sizeof(T) == 2 ? ldexpf(w, (int)me[sp]) : w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[e] = fmaf(wo, o4[e], acc[e]);
+        }
+      }
+    }
+    const int layer = g / mg.lh;
+    const int tok = m_row / mg.G;
+    const int h = (g - layer * mg.lh) * mg.G + (m_row - tok * mg.G);
+    T* out = (T*)mg.out + (size_t)layer * mg.out_ls + ((size_t)tok * mg.Hq + h) * D + m_c * 4;
+    if constexpr (sizeof(T) == 2) {
+      const u32x2_t v = {(uint32_t)f32_to_bf16(acc[0] * inv) | ((uint32_t)f32_to_bf16(acc[1] * inv) << 16),
+                         (uint32_t)f32_to_bf16(acc[2] * inv) | ((uint32_t)f32_to_bf16(acc[3] * inv) << 16)};
+      *reinterpret_cast<u32x2_t*>(out) = v;
+    } else {
+      *reinterpret_cast<f32x4_t*>(out) = acc * inv;
+    }
+  }
   for (int it0 = 0; it0 < ntile; it0 += NPF)
 #pragma unroll
   for (int ip = 0; ip < NPF; ++ip) {
@@ -1473,7 +1521,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_score_kernel(ScoreArgs a) {
     for (int kt = 0; kt < KT; ++kt) acc[kt] = f32x16_t{};
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      const typename M::Frag af = M::ld(&Qs[buf][col * QSTR + ks * M::KS + hh * M::KL]);
+      const typename M::Frag af = M::ld(&Qs0[buf * RT * QSTR + col * QSTR + ks * M::KS + hh * M::KL]);
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) acc[kt] = M::mma(af, kf[kt][ks], acc[kt]);
     }
@@ -1488,29 +1536,37 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_score_kernel(ScoreArgs a) {
     for (int kt = 0; kt < KT; ++kt) {
       const int key_t0 = key_w + kt * 32;
       const int key = key_t0 + col;
-      float sum = 0.f;
+      // The lane's 16 weights of this key summed as a tree (four partial sums
+      // over the row groups, then pairwise): fewer roundings in series than a
+      // running sum.
+      float part[4];
       if (key_t0 + 31 >= a.k0) {  // tile holds frame keys: causal visibility per row
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int4 lv = *reinterpret_cast<const int4*>(&slim[ro + 8 * j + 4 * hh]);
           const int lvv[4] = {lv.x, lv.y, lv.z, lv.w};
+          float pq[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const float x = acc[kt][4 * j + q];
             const float p = fast_exp2(fmaf(x, a.c_lo, fmaf(x, a.c_hi, -mv[j][q]))) * rv[j][q];
-            sum += key < lvv[q] ? p : 0.f;
+            pq[q] = key < lvv[q] ? p : 0.f;
           }
+          part[j] = (pq[0] + pq[1]) + (pq[2] + pq[3]);
         }
       } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 4; ++j) {
+          float pq[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const float x = acc[kt][4 * j + q];
-            sum += fast_exp2(fmaf(x, a.c_lo, fmaf(x, a.c_hi, -mv[j][q]))) * rv[j][q];
+            pq[q] = fast_exp2(fmaf(x, a.c_lo, fmaf(x, a.c_hi, -mv[j][q]))) * rv[j][q];
           }
+          part[j] = (pq[0] + pq[1]) + (pq[2] + pq[3]);
+        }
       }
-      cs[kt] += (double)sum;
+      cs[kt] += (double)((part[0] + part[1]) + (part[2] + part[3]));
     }
     if (it + 1 < ntile) store_tile(qr[(ip + 1) % NPF], buf ^ 1);
     __syncthreads();
@@ -1528,7 +1584,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_score_kernel(ScoreArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Top-B selection (work-group 0 of select_kernel, 1024 threads).  With the
+// Top-B selection (work-group 0 of frame_kernel, 1024 threads).  With the
 // recency window the selection value is the position instead of the score, so
 // the same steps evict the oldest tokens.
 // Scores s_j = (fixed-point column sum) / (Hq*T), rounded to fp32.  The pool
@@ -1601,7 +1657,6 @@ __device__ int block_excl_scan(int v, int* sh, int* total) {
 }
 
 struct SelectShared {
-  uint32_t val[kMaxPool];  // score bits of the pool rows; bit 31 = evicted
   int hist[kSelectBins];
   uint32_t cand_v[kSelCand];
   uint32_t cand_np[kSelCand];
@@ -1663,7 +1718,9 @@ __device__ int refine_boundary(SelectShared& sh, int P, uint32_t& lo, uint32_t& 
   return sh.cnt;
 }
 
-__device__ void select_top_b(const SelectArgs& a, SelectShared& sh) {
+// val: [P] words of dynamic LDS, the score bits of the pool rows (bit 31 set
+// once a row is evicted).
+__device__ void select_top_b(const SelArgs& a, SelectShared& sh, uint32_t* val) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // Row j*kSelectThreads + tid of the pool belongs to thread tid, so that every
   // global access of a wave is contiguous.  No global store precedes a
@@ -1697,7 +1754,7 @@ __device__ void select_top_b(const SelectArgs& a, SelectShared& sh) {
         // position (older tokens have smaller values and are evicted first).
         const uint32_t fb = a.recent ? (uint32_t)fx[j]
                                      : __float_as_uint((float)((double)fx[j] * a.score_scale));
-        sh.val[idx] = fb;
+        val[idx] = fb;
         flo = min(flo, fb);
         fhi = max(fhi, fb);
       }
@@ -1724,7 +1781,7 @@ __device__ void select_top_b(const SelectArgs& a, SelectShared& sh) {
     int cnt;
     do {
       cnt = refine_boundary(sh, a.P, lo, hi, need, [&](int idx, uint32_t& v) {
-        v = sh.val[idx];
+        v = val[idx];
         return true;
       });
     } while (cnt > kSelCand && lo != hi);
@@ -1736,7 +1793,7 @@ __device__ void select_top_b(const SelectArgs& a, SelectShared& sh) {
       const uint32_t tied = lo;
       do {
         cnt = refine_boundary(sh, a.P, plo, phi, need, [&](int idx, uint32_t& v) {
-          if (sh.val[idx] != tied) return false;
+          if (val[idx] != tied) return false;
           v = ~(uint32_t)a.pool_pos[pool_row(idx, a.k0, a.foff)];
           return true;
         });
@@ -1746,7 +1803,7 @@ __device__ void select_top_b(const SelectArgs& a, SelectShared& sh) {
     // Rows below the boundary are evicted (bit 31 of their entry); the
     // candidates are collected.
     for (int idx = tid; idx < a.P; idx += kSelectThreads) {
-      const uint32_t v = sh.val[idx];
+      const uint32_t v = val[idx];
       bool ev = v < lo;
       bool cand = v >= lo && v <= hi;
       if (cand && tie_stage) {
@@ -1761,7 +1818,7 @@ __device__ void select_top_b(const SelectArgs& a, SelectShared& sh) {
           sh.cand_idx[slot] = idx;
         }
       }
-      if (ev) sh.val[idx] = v | 0x80000000u;
+      if (ev) val[idx] = v | 0x80000000u;
     }
     __syncthreads();
     // Rank of each candidate among the candidates: by score bits, and by ~pos
@@ -1776,7 +1833,7 @@ __device__ void select_top_b(const SelectArgs& a, SelectShared& sh) {
         rank += o < mine ? 1 : 0;
         eq += o == mine ? 1 : 0;
       }
-      if (eq == 1 && rank < need) sh.val[sh.cand_idx[tid]] |= 0x80000000u;
+      if (eq == 1 && rank < need) val[sh.cand_idx[tid]] |= 0x80000000u;
       if (eq > 1) sh.any_tie = 1;
     }
     __syncthreads();
@@ -1790,7 +1847,7 @@ __device__ void select_top_b(const SelectArgs& a, SelectShared& sh) {
       if (tid < nc && eq > 1) {
         for (int c = 0; c < nc; ++c)
           rank += (sh.cand_v[c] == mine && sh.cand_np[c] < np) ? 1 : 0;
-        if (rank < need) sh.val[sh.cand_idx[tid]] |= 0x80000000u;
+        if (rank < need) val[sh.cand_idx[tid]] |= 0x80000000u;
       }
       __syncthreads();
     }
@@ -1805,7 +1862,7 @@ __device__ void select_top_b(const SelectArgs& a, SelectShared& sh) {
   const int i1 = min(a.P, i0 + C);
   int holes = 0, movers = 0;
   for (int idx = i0; idx < i1; ++idx) {
-    const uint32_t ev = sh.val[idx] >> 31;
+    const uint32_t ev = val[idx] >> 31;
     holes += (idx < a.B && ev) ? 1 : 0;
     movers += (idx >= a.B && !ev) ? 1 : 0;
   }
@@ -1821,162 +1878,219 @@ __device__ void select_top_b(const SelectArgs& a, SelectShared& sh) {
   if (holes | movers) {
     int bh = base & 0xffff, bm = base >> 16;
     for (int idx = i0; idx < i1; ++idx) {
-      const uint32_t ev = sh.val[idx] >> 31;
+      const uint32_t ev = val[idx] >> 31;
       if (idx < a.B && ev && bh < a.list_stride) a.move_dst[bh++] = idx;
       if (idx >= a.B && !ev && bm < a.list_stride) a.move_src[bm++] = pool_row(idx, a.k0, a.foff);
     }
   }
-  if (tid == 0) *a.move_count = min(min(total & 0xffff, total >> 16), a.list_stride);
+  const int moves = min(min(total & 0xffff, total >> 16), a.list_stride);
+  if (tid == 0) *a.move_count = moves;
+  if (moves == 0) return;
+  // The moves themselves: K and V of every KV head, 16 bytes per task, and the
+  // positions.  The list was written by this work-group before the barrier.
+  __syncthreads();
+  const int cpr = a.row_bytes / 16;
+  const int per_move = a.Hkv * cpr;
+  for (int t = tid; t < moves * per_move; t += kSelectThreads) {
+    const int i = t / per_move;
+    const int rem = t - i * per_move;
+    const int g = rem / cpr, c = rem - g * cpr;
+    const int dst = min(max(a.move_dst[i], 0), a.B - 1);
+    const int src = min(max(a.move_src[i], a.B), a.cap - 1);
+    const size_t so = ((size_t)g * a.cap + src) * a.row_bytes + (size_t)c * 16;
+    const size_t dof = ((size_t)g * a.cap + dst) * a.row_bytes + (size_t)c * 16;
+    const u32x4_t kv = *reinterpret_cast<const u32x4_t*>((const char*)a.kpool + so);
+    const u32x4_t vv = *reinterpret_cast<const u32x4_t*>((const char*)a.vpool + so);
+    *reinterpret_cast<u32x4_t*>((char*)a.kpool + dof) = kv;
+    *reinterpret_cast<u32x4_t*>((char*)a.vpool + dof) = vv;
+  }
+  for (int i = tid; i < moves; i += kSelectThreads) {
+    const int dst = min(max(a.move_dst[i], 0), a.B - 1);
+    const int src = min(max(a.move_src[i], a.B), a.cap - 1);
+    a.evicted_pos[dst] = a.pool_pos[dst];
+    a.pool_pos[dst] = a.pool_pos[src];
+  }
 }
 
 // Merge of the key splits of pass 1:
 //   m = max_s m_s,  l = sum_s 2^(m_s - m) l_s,  O = sum_s 2^(m_s - m) O_s / l,
-// one thread per (row, 4 dims), written to O [T][Hq][d].  A work-group covers
-// whole groups of 32 rows with rows fastest, matching the lane-order layout
-// of the partials; one thread per row merges the row's split statistics into
-// LDS (weights 2^(m_s - m), exact powers of two, and 1/l), which the row's
-// other threads read.  Partials of splits that saw no key of a row were never
-// written, so they are selected out, not multiplied.  Up to kMaxSplits splits
-// (a frame) the statistics sit in registers; more (a text chunk over a long
-// cache, up to kMaxMergeSplits) are merged in two loops over the splits with
-// the same arithmetic in the same order.
-template <class E, int D>
-__device__ void merge_splits(const SelectArgs& a, int wg, float* lds) {
+// for one group of 32 flat rows (flat row = g*R + r), written to O [T][Hq][d].
+// A task is (row, 4 dims) with rows fastest, matching the lane-order layout of
+// the partials; a work-group of NT threads takes TPT tasks per thread.  One
+// thread per row merges the row's split statistics into LDS (weights
+// 2^(m_s - m), exact powers of two, and 1/l), which the row's other tasks
+// read.  Partials of splits that saw no key of a row were never written, so
+// they are selected out, not multiplied.  Up to kMaxSplits splits (a frame)
+// the statistics sit in registers; more (a text chunk over a long cache, up to
+// kMaxMergeSplits) are merged in two loops over the splits with the same
+// arithmetic in the same order.  LDS: merge_lds_bytes(S).
+// LDS bytes of a merge work-group for S splits.
+__host__ __device__ inline int merge_lds_bytes(int S) {
+  return 32 * 4 + 32 * (S <= kMaxSplits ? kMaxSplits : S) * 2;
+}
+
+template <class E, int D, int NT>
+__device__ void merge_group(const MergeArgs& a, int grp, float* lds) {
   typedef typename E::T T;
   constexpr int CPR = D / 4;
-  constexpr int GPW = kSelectThreads / (32 * CPR);   // row groups per work-group
-  static_assert(GPW >= 1 && GPW * 32 * CPR == kSelectThreads, "merge work-group shape");
-  static_assert(GPW * 32 * (kMaxMergeSplits + 1) * sizeof(float) <= sizeof(SelectShared), "merge weights in LDS");
+  constexpr int TASKS = 32 * CPR;
+  constexpr int TPT = (TASKS + NT - 1) / NT;      // tasks per thread
+  // Partial loads in flight per task (a frame's 17 splits at B = 4096 arrive
+  // in two rounds with one task per thread).
+  constexpr int MCH = sizeof(T) == 2 ? (TPT == 1 ? 9 : (TPT == 2 ? 5 : 3)) : (TPT == 1 ? 4 : 2);
   const int wstr = a.S <= kMaxSplits ? kMaxSplits : a.S;   // weights per row
-  float* wts = lds;                                   // [GPW*32][wstr]
-  float* rinv = lds + GPW * 32 * wstr;                // [GPW*32]
+  // Weights are exact powers of two, kept as their exponents (kNoWeight: the
+  // split saw no key of the row).
+  float* rinv = lds;                                        // [32]
+  int16_t* wexp = reinterpret_cast<int16_t*>(lds + 32);     // [32][wstr]
   typedef typename PartialOut<E>::V PV;
   const int tid = threadIdx.x;
   const size_t nrows = (size_t)a.Hkv * a.R;
-  const int gsub = (tid >> 5) / CPR;
-  const int c = (tid >> 5) - gsub * CPR;
-  const int lrow = gsub * 32 + (tid & 31);
-  const size_t base = ((size_t)wg * GPW + gsub) * 32 + (tid & 31);   // = g*R + r
-  // The partial outputs do not depend on the weights: the first MCH splits'
-  // loads are issued before the statistics, so they are all in flight at once
-  // (9 per chunk: a frame's 17 splits at B = 4096 in two rounds, within the
-  // registers of 1024-thread work-groups).
-  constexpr int MCH = sizeof(T) == 2 ? 9 : 4;
-  PV os[MCH];
-  int8_t ep[MCH];
+  const size_t row0 = (size_t)grp * 32;
+  PV os[TPT][MCH];
+  int8_t ep[TPT][MCH];
   auto load_chunk = [&](int s0) {
 #pragma unroll
-    for (int j = 0; j < MCH; ++j) {
-      const int sp = s0 + j;
-      if (sp < a.S && base < nrows) {
-        const size_t ri = sp * nrows + base;
-        os[j] = reinterpret_cast<const PV*>(a.opart)[opart_group(ri, D) + (size_t)c * 32 + (ri & 31)];
-        ep[j] = sizeof(T) == 2 ? a.epart[ri] : (int8_t)0;
+    for (int u = 0; u < TPT; ++u) {
+      const int task = tid + u * NT;
+      const int rr = task & 31, c = task >> 5;
+      const size_t base = row0 + rr;
+#pragma unroll
+      for (int j = 0; j < MCH; ++j) {
+        const int sp = s0 + j;
+        if (task < TASKS && sp < a.S && base < nrows) {
+          const size_t ri = sp * nrows + base;
+          os[u][j] = reinterpret_cast<const PV*>(a.opart)[opart_group(ri, D) + (size_t)c * 32 + (ri & 31)];
+          ep[u][j] = sizeof(T) == 2 ? a.epart[ri] : (int8_t)0;
+        }
       }
     }
   };
   load_chunk(0);
-  if (c == 0 && a.S > kMaxSplits) {
-    float inv = 0.f;
-    if (base < nrows) {
-      float m = -INFINITY;
-      for (int sp = 0; sp < a.S; ++sp) m = fmaxf(m, a.mpart[stat_index(base, sp, a.ss)]);
-      double l = 0.0;
-      for (int sp = 0; sp < a.S; ++sp) {
-        const float ms = a.mpart[stat_index(base, sp, a.ss)];
-        float w = 0.f;
-        if (ms != -INFINITY) {
-          w = ldexpf(1.f, (int)(ms - m));
-          l += ldexp(a.lpart[stat_index(base, sp, a.ss)], (int)(ms - m));
+  if (tid < 32) {
+    const size_t base = row0 + tid;
+    if (a.S > kMaxSplits) {
+      float inv = 0.f;
+      if (base < nrows) {
+        float m = -INFINITY;
+        for (int sp = 0; sp < a.S; ++sp) m = fmaxf(m, a.mpart[stat_index(base, sp, a.ss)]);
+        double l = 0.0;
+        for (int sp = 0; sp < a.S; ++sp) {
+          const float ms = a.mpart[stat_index(base, sp, a.ss)];
+          int16_t we = kNoWeight;
+          if (ms != -INFINITY) {
+            we = weight_exp(ms - m);
+            l += ldexp(a.lpart[stat_index(base, sp, a.ss)], (int)(ms - m));
+          }
+          wexp[tid * wstr + sp] = we;
         }
-        wts[lrow * wstr + sp] = w;
+        inv = (float)(1.0 / l);
+      } else {
+        for (int sp = 0; sp < a.S; ++sp) wexp[tid * wstr + sp] = kNoWeight;
       }
-      inv = (float)(1.0 / l);
+      rinv[tid] = inv;
     } else {
-      for (int sp = 0; sp < a.S; ++sp) wts[lrow * wstr + sp] = 0.f;
+      int16_t w[kMaxSplits];
+      float inv = 0.f;
+#pragma unroll
+      for (int sp = 0; sp < kMaxSplits; ++sp) w[sp] = kNoWeight;
+      if (base < nrows) {
+        float ms[kMaxSplits];
+        double ls[kMaxSplits];
+        load_split_stats(a.mpart, a.lpart, base, a.S, a.ss, ms, ls);
+        float m;
+        double l;
+        merge_split_stats(ms, ls, m, l);
+#pragma unroll
+        for (int sp = 0; sp < kMaxSplits; ++sp) w[sp] = ms[sp] != -INFINITY ? weight_exp(ms[sp] - m) : kNoWeight;
+        inv = (float)(1.0 / l);
+      }
+#pragma unroll
+      for (int sp = 0; sp < kMaxSplits; ++sp) wexp[tid * kMaxSplits + sp] = w[sp];
+      rinv[tid] = inv;
     }
-    rinv[lrow] = inv;
-  } else if (c == 0) {
-    float w[kMaxSplits];
-    float inv = 0.f;
-#pragma unroll
-    for (int sp = 0; sp < kMaxSplits; ++sp) w[sp] = 0.f;
-    if (base < nrows) {
-      float ms[kMaxSplits];
-      double ls[kMaxSplits];
-      load_split_stats(a.mpart, a.lpart, base, a.S, a.ss, ms, ls);
-      float m;
-      double l;
-      merge_split_stats(ms, ls, m, l);
-#pragma unroll
-      for (int sp = 0; sp < kMaxSplits; ++sp) w[sp] = ms[sp] != -INFINITY ? ldexpf(1.f, (int)(ms[sp] - m)) : 0.f;
-      inv = (float)(1.0 / l);
-    }
-#pragma unroll
-    for (int sp = 0; sp < kMaxSplits; ++sp) wts[lrow * kMaxSplits + sp] = w[sp];
-    rinv[lrow] = inv;
   }
   __syncthreads();
-  if (base >= nrows) return;
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4_t acc[TPT];
+#pragma unroll
+  for (int u = 0; u < TPT; ++u) acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < a.S; s0 += MCH) {
     if (s0 > 0) load_chunk(s0);
 #pragma unroll
-    for (int j = 0; j < MCH; ++j) {
-      const int sp = s0 + j;
-      // Splits that saw no key of the row have weight 0 and unwritten partials.
-      const float w = sp < a.S ? wts[lrow * wstr + sp] : 0.f;
-      if (w != 0.f) {
-        const f32x4_t o4 = PartialOut<E>::unpack(os[j]);
-        const float wo = sizeof(T) == 2 ? ldexpf(w, (int)ep[j]) : w;
+    for (int u = 0; u < TPT; ++u) {
+      const int rr = (tid + u * NT) & 31;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] = fmaf(wo, o4[e], acc[e]);
+      for (int j = 0; j < MCH; ++j) {
+        const int sp = s0 + j;
+        // Splits that saw no key of the row have weight 0 and unwritten partials.
+        const int we = sp < a.S ? wexp[rr * wstr + sp] : kNoWeight;
+        const float w = we == kNoWeight ? 0.f : ldexpf(1.f, we);
+        if (w != 0.f) {
+          const f32x4_t o4 = PartialOut<E>::unpack(os[u][j]);
+          const float wo = sizeof(T) == 2 ? ldexpf(w, (int)ep[u][j]) : w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[u][e] = fmaf(wo, o4[e], acc[u][e]);
+        }
       }
     }
   }
-  const float inv = rinv[lrow];
-  const int g = (int)(base / a.R), r = (int)(base - (size_t)g * a.R);
-  const int layer = g / a.lh;
-  const int tok = r / a.G;
-  const int h = (g - layer * a.lh) * a.G + (r - tok * a.G);
-  T* out = (T*)a.out + (size_t)layer * a.out_ls + ((size_t)tok * a.Hq + h) * D + c * 4;
-  if constexpr (sizeof(T) == 2) {
-    const u32x2_t v = {(uint32_t)f32_to_bf16(acc[0] * inv) | ((uint32_t)f32_to_bf16(acc[1] * inv) << 16),
-                       (uint32_t)f32_to_bf16(acc[2] * inv) | ((uint32_t)f32_to_bf16(acc[3] * inv) << 16)};
-    *reinterpret_cast<u32x2_t*>(out) = v;
-  } else {
-    *reinterpret_cast<f32x4_t*>(out) = acc * inv;
+#pragma unroll
+  for (int u = 0; u < TPT; ++u) {
+    const int task = tid + u * NT;
+    const int rr = task & 31, c = task >> 5;
+    const size_t base = row0 + rr;
+    if (task >= TASKS || base >= nrows) continue;
+    const float inv = rinv[rr];
+    const int g = (int)(base / a.R), r = (int)(base - (size_t)g * a.R);
+    const int layer = g / a.lh;
+    const int tok = r / a.G;
+    const int h = (g - layer * a.lh) * a.G + (r - tok * a.G);
+    T* out = (T*)a.out + (size_t)layer * a.out_ls + ((size_t)tok * a.Hq + h) * D + c * 4;
+    if constexpr (sizeof(T) == 2) {
+      const u32x2_t v = {(uint32_t)f32_to_bf16(acc[u][0] * inv) | ((uint32_t)f32_to_bf16(acc[u][1] * inv) << 16),
+                         (uint32_t)f32_to_bf16(acc[u][2] * inv) | ((uint32_t)f32_to_bf16(acc[u][3] * inv) << 16)};
+      *reinterpret_cast<u32x2_t*>(out) = v;
+    } else {
+      *reinterpret_cast<f32x4_t*>(out) = acc[u] * inv;
+    }
   }
 }
 
+// The frame launch: per layer (grid y), work-group 0 makes the previous
+// frame's Top-B decision and its moves when nsel = 1; the others rotate and
+// append this frame's tokens.  Dynamic LDS: the selection's P score words.
 template <class E, int D>
-__global__ __launch_bounds__(kSelectThreads, 1) void select_kernel(SelectArgs a) {
-  __shared__ SelectShared sh;   // the selection's state, or the merge's statistics
-  const int nsel = a.mode != kSelMerge ? a.L : 0;   // one selection work-group per layer
-  if ((int)blockIdx.x >= nsel) {
-    const int wg = blockIdx.x - nsel;
-    if (a.colsum_clear) {   // the next scored frame's column sums start at zero
-      const size_t stride = (size_t)(gridDim.x - nsel) * kSelectThreads;
-      for (size_t i = (size_t)wg * kSelectThreads + threadIdx.x; i < (size_t)a.clear_n; i += stride)
-        a.colsum_clear[i] = 0ull;
-    }
-    merge_splits<E, D>(a, wg, reinterpret_cast<float*>(sh.val));
+__global__ __launch_bounds__(kSelectThreads) void frame_kernel(RopeArgs a) {
+  const size_t layer = blockIdx.y;
+  if ((int)blockIdx.x < a.nsel) {
+    __shared__ SelectShared sh;
+    extern __shared__ __attribute__((aligned(16))) uint32_t sel_val[];
+    SelArgs b = a.sel;
+    const size_t pool_bytes = (size_t)b.Hkv * b.cap * b.row_bytes;
+    b.colsum += layer * b.cap;
+    b.pool_pos += layer * b.cap;
+    b.evicted_pos += layer * b.B;
+    b.move_dst += layer * b.list_stride;
+    b.move_src += layer * b.list_stride;
+    b.move_count += layer;
+    b.kpool = (char*)b.kpool + layer * pool_bytes;
+    b.vpool = (char*)b.vpool + layer * pool_bytes;
+    select_top_b(b, sh, sel_val);
     return;
   }
-  SelectArgs b = a;
-  const size_t l = blockIdx.x;
-  b.colsum += l * a.cap;
-  b.pool_pos += l * a.cap;
-  b.move_dst += l * a.list_stride;
-  b.move_src += l * a.list_stride;
-  b.move_count += l;
-  select_top_b(b, sh);
+  rope_wg<E, D>(a, layer, (int)blockIdx.x - a.nsel);
 }
 
-// Moves of a selection outside a frame step (before a view), 16 bytes per
-// thread: K and V of every KV head.
-__global__ __launch_bounds__(256) void moves_kernel(MovesArgs a) {
-  apply_move_chunk(moves_layer(a, blockIdx.y), (size_t)blockIdx.x * blockDim.x + threadIdx.x);
+// The launch after pass 1: merge work-groups first, then the score pass.
+template <class E, int D, int KT, int NW, int NPF = 1, bool FM = false>
+__global__ __launch_bounds__(64 * NW, 1) void score_merge_kernel(ScoreMergeArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int wg = blockIdx.x;
+  if (wg < a.merge_wgs) {
+    merge_group<E, D, 64 * NW>(a.mg, wg, reinterpret_cast<float*>(smem));
+    return;
+  }
+  score_wg<E, D, KT, NW, NPF, FM>(a.sc, wg - a.merge_wgs, (int)gridDim.x - a.merge_wgs, a.key_blocks, a, smem);
 }
 
 // The scores view of the last scored pool (one thread per candidate, layer
@@ -2047,15 +2161,17 @@ int attn_rows_per_wg(Dt dt, int) { return dt != Dt::BF16 ? 4 * 32 : 8 * 32; }
 // stack).
 static constexpr int score_prefetch(int d) { return d == 64 ? 2 : 4; }
 
-// Work-groups of the score kernel that fit on one CU at once (0 if unknown).
+// Work-groups of the (4-wave) score kernel that fit on one CU at once (0 if unknown).
 int score_wgs_per_cu(Dt dt, int d) {
   int n = 0;
   hipError_t e = hipSuccess;
   if (dt == Dt::BF16) {
     e = d == 64 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                      &n, attn_score_kernel<BF16, 64, kKtBf16, 4, score_prefetch(64)>, 256, 0)
+                      &n, score_merge_kernel<BF16, 64, kKtBf16, 4, score_prefetch(64)>, 256,
+                      score_lds_bytes<BF16, 64>())
                 : hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                      &n, attn_score_kernel<BF16, 128, kKtBf16, 4, score_prefetch(128)>, 256, 0);
+                      &n, score_merge_kernel<BF16, 128, kKtBf16, 4, score_prefetch(128)>, 256,
+                      score_lds_bytes<BF16, 128>());
   }
   return e == hipSuccess ? n : 0;
 }
@@ -2063,11 +2179,18 @@ int score_wgs_per_cu(Dt dt, int d) {
 int score8_wgs_per_cu(int d) {
   int n = 0;
   const hipError_t e = d == 64
-      ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_score_kernel<BF16, 64, kKtBf16, 8>, 512, 0)
-      : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_score_kernel<BF16, 128, kKtBf16, 8>, 512, 0);
+      ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, score_merge_kernel<BF16, 64, kKtBf16, 8>, 512,
+                                                     score_lds_bytes<BF16, 64>())
+      : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, score_merge_kernel<BF16, 128, kKtBf16, 8>, 512,
+                                                     score_lds_bytes<BF16, 128>());
   return e == hipSuccess ? n : 0;
 }
 int score_keys_per_wg(Dt dt, int waves) { return waves * 32 * (dt == Dt::BF16 ? kKtBf16 : kKtF32); }
+
+int merge_wgs(int64_t rows) {
+  const int64_t groups = (rows + 31) / 32;
+  return (int)((groups + kXcds - 1) / kXcds * kXcds);
+}
 
 hipError_t launch_rope_table(const RopeTableArgs& a, hipStream_t s) {
   const size_t total = (size_t)a.npos * a.half;
@@ -2075,23 +2198,31 @@ hipError_t launch_rope_table(const RopeTableArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Work-groups of the RoPE part of a launch for T tokens (before the move
-// work-groups).
+// Work-groups of the RoPE part of a launch for T tokens (after the selection
+// work-group).
 int rope_blocks(int T, int Hq, int Hkv, int d, int esize) {
-  return (int)((rope_qk_tasks(T, Hq, Hkv, d) + rope_v_tasks(T, Hkv, d, esize) + 255) / 256);
+  return (int)((rope_qk_tasks(T, Hq, Hkv, d) + rope_v_tasks(T, Hkv, d, esize) + kSelectThreads - 1) /
+               kSelectThreads);
 }
 
-hipError_t launch_rope(Dt dt, int d, const RopeArgs& a, int layers, hipStream_t s, const LaunchTiming& tm) {
-  const size_t move_tasks = a.mv.max_moves > 0 ? (size_t)a.mv.max_moves * a.Hkv * (a.mv.row_bytes / 16) : 0;
-  const dim3 blocks(a.rope_blocks + (int)((move_tasks + 255) / 256), layers);
-  if (dt == Dt::BF16) {
-    if (d == 64) hipExtLaunchKernelGGL((rope_append_kernel<BF16, 64>), dim3(blocks), dim3(256), 0, s, tm.start, tm.stop, 0, a);
-    else hipExtLaunchKernelGGL((rope_append_kernel<BF16, 128>), dim3(blocks), dim3(256), 0, s, tm.start, tm.stop, 0, a);
-  } else {
-    if (d == 64) hipExtLaunchKernelGGL((rope_append_kernel<F32, 64>), dim3(blocks), dim3(256), 0, s, tm.start, tm.stop, 0, a);
-    else hipExtLaunchKernelGGL((rope_append_kernel<F32, 128>), dim3(blocks), dim3(256), 0, s, tm.start, tm.stop, 0, a);
-  }
+template <class E, int D>
+static hipError_t launch_frame_t(const RopeArgs& a, int layers, hipStream_t s, const LaunchTiming& tm) {
+  const dim3 grid(a.nsel + a.rope_blocks, layers);
+  const size_t lds = a.nsel ? (size_t)a.sel.P * sizeof(uint32_t) : 0;
+  // The selection's LDS may exceed the default dynamic limit (a failure here
+  // surfaces as a launch error below).
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&frame_kernel<E, D>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     kMaxPool * (int)sizeof(uint32_t));
+  (void)attr;
+  hipExtLaunchKernelGGL((frame_kernel<E, D>), grid, dim3(kSelectThreads), lds, s, tm.start, tm.stop, 0, a);
   return hipGetLastError();
+}
+
+hipError_t launch_frame(Dt dt, int d, const RopeArgs& a, int layers, hipStream_t s, const LaunchTiming& tm) {
+  if (a.nsel + a.rope_blocks == 0) return hipSuccess;
+  if (dt == Dt::BF16) return d == 64 ? launch_frame_t<BF16, 64>(a, layers, s, tm) : launch_frame_t<BF16, 128>(a, layers, s, tm);
+  return d == 64 ? launch_frame_t<F32, 64>(a, layers, s, tm) : launch_frame_t<F32, 128>(a, layers, s, tm);
 }
 
 hipError_t launch_attn(Dt dt, int d, const AttnArgs& a, int row_tiles, int splits, hipStream_t s,
@@ -2111,36 +2242,28 @@ hipError_t launch_attn(Dt dt, int d, const AttnArgs& a, int row_tiles, int split
   return hipGetLastError();
 }
 
-hipError_t launch_score(Dt dt, int d, const ScoreArgs& a, int key_blocks, int rsplits, int waves,
-                        hipStream_t s, const LaunchTiming& tm) {
-  const dim3 grid(key_blocks, a.Hkv, rsplits);
-  if (dt == Dt::BF16) {
-    if (waves == 8) {
-      if (d == 64) hipExtLaunchKernelGGL((attn_score_kernel<BF16, 64, kKtBf16, 8>), grid, dim3(512), 0, s, tm.start, tm.stop, 0, a);
-      else hipExtLaunchKernelGGL((attn_score_kernel<BF16, 128, kKtBf16, 8>), grid, dim3(512), 0, s, tm.start, tm.stop, 0, a);
-    } else {
-      if (d == 64) hipExtLaunchKernelGGL((attn_score_kernel<BF16, 64, kKtBf16, 4, score_prefetch(64)>), grid, dim3(256), 0, s, tm.start, tm.stop, 0, a);
-      else hipExtLaunchKernelGGL((attn_score_kernel<BF16, 128, kKtBf16, 4, score_prefetch(128)>), grid, dim3(256), 0, s, tm.start, tm.stop, 0, a);
-    }
-  } else {
-    if (d == 64) hipExtLaunchKernelGGL((attn_score_kernel<F32, 64, kKtF32, 4>), grid, dim3(256), 0, s, tm.start, tm.stop, 0, a);
-    else hipExtLaunchKernelGGL((attn_score_kernel<F32, 128, kKtF32, 4>), grid, dim3(256), 0, s, tm.start, tm.stop, 0, a);
-  }
+template <class E, int D, int KT, int NW, int NPF, bool FM = false>
+static hipError_t launch_sm_t(const ScoreMergeArgs& a, hipStream_t s, const LaunchTiming& tm) {
+  const int score_wgs = a.key_blocks * a.sc.Hkv * a.rsplits;
+  const int grid = a.merge_wgs + score_wgs;
+  if (grid == 0) return hipSuccess;
+  size_t lds = a.merge_wgs ? (size_t)merge_lds_bytes(a.mg.S) : 0;
+  if (score_wgs) lds = std::max(lds, (size_t)score_lds_bytes<E, D>());
+  hipExtLaunchKernelGGL((score_merge_kernel<E, D, KT, NW, NPF, FM>), dim3(grid), dim3(64 * NW), lds, s, tm.start,
+                        tm.stop, 0, a);
   return hipGetLastError();
 }
 
-hipError_t launch_select(Dt dt, int d, const SelectArgs& a, hipStream_t s, const LaunchTiming& tm) {
-  const size_t mthreads = ((size_t)a.Hkv * a.R + 31) / 32 * 32 * (d / 4);   // whole 32-row groups
-  const int nsel = a.mode != kSelMerge ? a.L : 0;
-  const dim3 grid((unsigned)(nsel + (mthreads + kSelectThreads - 1) / kSelectThreads)), block(kSelectThreads);
+hipError_t launch_score_merge(Dt dt, int d, const ScoreMergeArgs& a, int waves, hipStream_t s,
+                              const LaunchTiming& tm) {
   if (dt == Dt::BF16) {
-    if (d == 64) hipExtLaunchKernelGGL((select_kernel<BF16, 64>), grid, block, 0, s, tm.start, tm.stop, 0, a);
-    else hipExtLaunchKernelGGL((select_kernel<BF16, 128>), grid, block, 0, s, tm.start, tm.stop, 0, a);
-  } else {
-    if (d == 64) hipExtLaunchKernelGGL((select_kernel<F32, 64>), grid, block, 0, s, tm.start, tm.stop, 0, a);
-    else hipExtLaunchKernelGGL((select_kernel<F32, 128>), grid, block, 0, s, tm.start, tm.stop, 0, a);
+    if (waves == 8 && d == 64 && a.fused) return launch_sm_t<BF16, 64, kKtBf16, 8, 1, true>(a, s, tm);
+    if (waves == 8)
+      return d == 64 ? launch_sm_t<BF16, 64, kKtBf16, 8, 1>(a, s, tm) : launch_sm_t<BF16, 128, kKtBf16, 8, 1>(a, s, tm);
+    return d == 64 ? launch_sm_t<BF16, 64, kKtBf16, 4, score_prefetch(64)>(a, s, tm)
+                   : launch_sm_t<BF16, 128, kKtBf16, 4, score_prefetch(128)>(a, s, tm);
   }
-  return hipGetLastError();
+  return d == 64 ? launch_sm_t<F32, 64, kKtF32, 4, 1>(a, s, tm) : launch_sm_t<F32, 128, kKtF32, 4, 1>(a, s, tm);
 }
 
 // Waves of the text-phase attention kernel: 4 (bf16) or 2 (fp32, whose
@@ -2177,12 +2300,6 @@ hipError_t launch_decode_merge(Dt dt, int d, const DecodeMergeArgs& a, hipStream
     if (d == 64) hipExtLaunchKernelGGL((decode_merge_kernel<F32, 64>), grid, block, 0, s, tm.start, tm.stop, 0, a);
     else hipExtLaunchKernelGGL((decode_merge_kernel<F32, 128>), grid, block, 0, s, tm.start, tm.stop, 0, a);
   }
-  return hipGetLastError();
-}
-
-hipError_t launch_moves(const MovesArgs& a, int layers, hipStream_t s) {
-  const size_t total = (size_t)a.max_moves * a.Hkv * (a.row_bytes / 16);
-  hipLaunchKernelGGL(moves_kernel, dim3((unsigned)((total + 255) / 256), layers), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -91,7 +91,10 @@ struct statekv_state {
   int32_t* ppos;
   void* dk;
   void* dv;
-  StepScratch work;  // the state's own per-step buffers
+  // The state's own per-step buffers, two sets used by alternate frames: a
+  // frame's pass 1 then never writes the lines the previous frame's merge and
+  // score pass have just read on other XCDs (measured 2 us faster at B = 4096).
+  StepScratch work[2];
   float2* rope_tab;
   unsigned long long* colsum;
   float* scores;
@@ -113,10 +116,12 @@ struct statekv_state {
   int frames_done;
   int text_done;     // text tokens appended to D by statekv_decode
 
-  // rows of the last frame; moves of its selection not yet performed
+  // Rows of the last frame, and its Top-B decision (with the moves it
+  // implies) when not yet made: it runs in the next frame's first launch, or
+  // in a launch of its own before a view of the state.
   int frame_base;
-  mutable bool moves_pending;
-  int pending_max_moves;
+  mutable bool sel_pending;
+  int sel_P, sel_k0, sel_foff, sel_mode, sel_recent, sel_colsum;
 
   // scores of the last frame that computed them
   int score_frame, score_pool, score_k0, score_foff;
@@ -153,8 +158,13 @@ int alloc(P** p, size_t bytes) {
 }
 
 void release(statekv_state* s) {
-  void* bufs[] = {s->kpool, s->vpool, s->ppos, s->dk, s->dv, s->work.qrot, s->work.opart,
-                  s->work.epart, s->work.mpart, s->work.lpart, s->rope_tab, s->colsum, s->scores, s->score_pos, s->keep_flag,
+  for (StepScratch& w : s->work) {
+    void* wb[] = {w.qrot, w.opart, w.epart, w.mpart, w.lpart};
+    for (void* b : wb)
+      if (b) (void)hipFree(b);
+  }
+  void* bufs[] = {s->kpool, s->vpool, s->ppos, s->dk, s->dv, s->rope_tab, s->colsum, s->scores,
+                  s->score_pos, s->keep_flag,
                   s->move_dst, s->move_src, s->move_count, s->evicted_pos, s->inv_freq,
                   s->nonfinite, s->dec_opart, s->dec_mpart, s->dec_lpart};
   for (void* b : bufs)
@@ -382,29 +392,44 @@ struct KernelTimer {
   }
 };
 
-MovesArgs moves_args(const statekv_state* s, int max_moves) {
-  MovesArgs a{};
-  a.kpool = s->kpool;
-  a.vpool = s->vpool;
+// The pending selection of the last frame (layer 0's arrays; the kernel
+// offsets the other layers).
+SelArgs sel_args(const statekv_state* s) {
+  SelArgs a{};
+  a.colsum = s->colsum + (size_t)s->sel_colsum * s->L * s->cap;
   a.pool_pos = s->ppos;
   a.evicted_pos = s->evicted_pos;
   a.move_dst = s->move_dst;
   a.move_src = s->move_src;
   a.move_count = s->move_count;
+  a.kpool = s->kpool;
+  a.vpool = s->vpool;
+  a.P = s->sel_P;
+  a.B = s->B;
+  a.mode = s->sel_mode;
+  a.recent = s->sel_recent;
+  a.k0 = s->sel_k0;
+  a.foff = s->sel_foff;
+  a.score_scale = 1.0 / ((double)(1ull << kScoreFracBits) * (double)s->Hq * (double)s->T);
   a.Hkv = s->Hkv;
   a.cap = s->cap;
-  a.B = s->B;
   a.row_bytes = s->D * s->esize;
-  a.max_moves = max_moves;
   a.list_stride = s->T;
   return a;
 }
 
-// Performs the moves of the last selection if no frame step has yet.
-int apply_pending_moves(const statekv_state* s) {
-  if (!s->moves_pending) return STATEKV_OK;
-  const int rc = check(launch_moves(moves_args(s, s->pending_max_moves), s->L, s->stream));
-  if (!rc) s->moves_pending = false;
+// Makes the last frame's pending Top-B decision and its moves (one launch of
+// the selection work-groups alone).
+int resolve_pending_selection(const statekv_state* s) {
+  if (!s->sel_pending) return STATEKV_OK;
+  RopeArgs a{};
+  a.nsel = 1;
+  a.sel = sel_args(s);
+  a.cap = s->cap;
+  KernelTimer tm(const_cast<statekv_state*>(s), STATEKV_K_SELECT);
+  const int rc = check(launch_frame(s->dt, s->D, a, s->L, s->stream, tm.lt));
+  tm.done();
+  if (!rc) s->sel_pending = false;
   return rc;
 }
 
@@ -545,11 +570,13 @@ int statekv_create(const statekv_layer_cfg* cfg, int32_t budget_B, float alpha,
   if (!rc) rc = alloc(&s->ppos, Ls * s->cap * sizeof(int32_t));
   if (!rc) rc = alloc(&s->dk, det_bytes);
   if (!rc) rc = alloc(&s->dv, det_bytes);
-  if (!rc) rc = alloc(&s->work.qrot, wbytes[0]);
-  if (!rc) rc = alloc(&s->work.opart, wbytes[1]);
-  if (!rc) rc = alloc(&s->work.epart, wbytes[2]);
-  if (!rc) rc = alloc(&s->work.mpart, wbytes[3]);
-  if (!rc) rc = alloc(&s->work.lpart, wbytes[4]);
+  for (StepScratch& w : s->work) {
+    if (!rc) rc = alloc(&w.qrot, wbytes[0]);
+    if (!rc) rc = alloc(&w.opart, wbytes[1]);
+    if (!rc) rc = alloc(&w.epart, wbytes[2]);
+    if (!rc) rc = alloc(&w.mpart, wbytes[3]);
+    if (!rc) rc = alloc(&w.lpart, wbytes[4]);
+  }
   if (!rc) rc = alloc(&s->rope_tab, (size_t)all_positions * (D / 2) * sizeof(float2));
   if (!rc) rc = alloc(&s->colsum, 2 * Ls * s->cap * sizeof(unsigned long long));
   if (!rc) rc = alloc(&s->scores, Ls * s->cap * sizeof(float));
@@ -652,17 +679,22 @@ int check_frame(const statekv_state* s, const void* Q, const void* K, const void
 int frame_step(statekv_state* s, const void* Q, const void* K, const void* V, int32_t n, void* O,
                const StepScratch& w) {
   int rc = STATEKV_OK;
-  const int k0 = s->count;
+  const int k0 = s->count;   // the state after the last frame's (possibly pending) selection
   const int P = k0 + s->T;
   const hipStream_t st = s->stream;
   const bool evict = P > s->B;
   const bool recent = (s->flags & STATEKV_FLAG_RECENT_WINDOW) != 0;
   const bool scored = (evict && !recent) || (s->flags & STATEKV_FLAG_ALWAYS_SCORE);
-  // Rows of this frame: right after the state, or, while the previous
-  // frame's moves are pending, the region its rows do not occupy.
-  const int F = s->moves_pending ? (s->frame_base == (int)s->B + s->T ? (int)s->B : (int)s->B + s->T) : k0;
+  // Rows of this frame: right after the state, or, while the last frame's
+  // evictions are pending (its kept rows at or beyond B are about to move),
+  // the frame region its rows do not occupy.
+  const bool prev_moves = s->sel_pending && s->sel_mode == kSelEvict;
+  const int F = prev_moves ? (s->frame_base == (int)s->B + s->T ? (int)s->B : (int)s->B + s->T) : k0;
   const int foff = F - k0;
+  const size_t cs_n = (size_t)s->L * s->cap;
 
+  // 1. The last frame's Top-B decision and moves, beside this frame's RoPE and
+  //    appends (disjoint rows), which also clear this frame's column sums.
   {
     KernelTimer tm(s, STATEKV_K_ROPE);
     RopeArgs a{};
@@ -686,11 +718,20 @@ int frame_step(statekv_state* s, const void* Q, const void* K, const void* V, in
     a.frame_base = F;
     a.rope_blocks = rope_blocks(s->T, s->Hq, s->Hkv, s->D, s->esize);
     a.det_ls = s->det_ls;
-    a.mv = moves_args(s, s->moves_pending ? s->pending_max_moves : 0);
-    rc = check(launch_rope(s->dt, s->D, a, s->L, st, tm.lt));
+    if (scored) {
+      a.clear = s->colsum + (size_t)s->colsum_next * cs_n;
+      a.clear_n = P;
+    }
+    if (s->sel_pending) {
+      a.nsel = 1;
+      a.sel = sel_args(s);
+    }
+    rc = check(launch_frame(s->dt, s->D, a, s->L, st, tm.lt));
     tm.done();
     if (rc) return rc;
+    s->sel_pending = false;
   }
+  // 2. Attention pass 1, split over keys.
   int splits, kps;
   attn_geometry(s, P, &splits, &kps);
   {
@@ -721,75 +762,80 @@ int frame_step(statekv_state* s, const void* Q, const void* K, const void* V, in
     tm.done();
     if (rc) return rc;
   }
-  if (scored) {
-    int key_blocks, rsplits, rps, waves;
-    score_geometry(s, P, &key_blocks, &rsplits, &rps, &waves);
-    KernelTimer tm(s, STATEKV_K_SCORE);
-    ScoreArgs a{};
-    a.qrot = w.qrot;
-    a.kpool = s->kpool;
-    a.mpart = w.mpart;
-    a.lpart = w.lpart;
-    a.S = splits;
-    a.ss = s->stat_ss;
-    a.colsum = s->colsum + (size_t)s->colsum_next * s->L * s->cap;
-    a.c_hi = s->c_hi;
-    a.c_lo = s->c_lo;
-    a.R = s->R;
-    a.G = s->G;
-    a.cap = s->cap;
-    a.P = P;
-    a.k0 = k0;
-    a.foff = foff;
-    a.rps = rps;
-    a.Hkv = s->HkvAll;
-    a.lh = s->Hkv;
-    rc = check(launch_score(s->dt, s->D, a, key_blocks, rsplits, waves, st, tm.lt));
-    tm.done();
-    if (rc) return rc;
-  }
+  // 3. The merge of the key splits into O and, for a scored frame, the score pass.
   {
-    KernelTimer tm(s, STATEKV_K_SELECT);
-    SelectArgs a{};
-    const size_t cs_n = (size_t)s->L * s->cap;
-    a.colsum = s->colsum + (size_t)s->colsum_next * cs_n;
+    KernelTimer tm(s, STATEKV_K_SCORE);
+    ScoreMergeArgs a{};
+    MergeArgs& m = a.mg;
+    m.opart = w.opart;
+    m.epart = w.epart;
+    m.mpart = w.mpart;
+    m.lpart = w.lpart;
+    m.out = O;
+    m.Hkv = s->HkvAll;
+    m.R = s->R;
+    m.G = s->G;
+    m.Hq = s->Hq;
+    m.S = splits;
+    m.ss = s->stat_ss;
+    m.lh = s->Hkv;
+    m.out_ls = (int64_t)s->T * s->Hq * s->D;
+    a.merge_wgs = merge_wgs((int64_t)s->HkvAll * s->R);
+    int waves = s->dt == Dt::BF16 ? 8 : 4;
     if (scored) {
-      a.colsum_clear = s->colsum + (size_t)(s->colsum_next ^ 1) * cs_n;
-      a.clear_n = (int64_t)cs_n;
+      int key_blocks, rsplits, rps;
+      score_geometry(s, P, &key_blocks, &rsplits, &rps, &waves);
+      ScoreArgs& c = a.sc;
+      c.qrot = w.qrot;
+      c.kpool = s->kpool;
+      c.mpart = w.mpart;
+      c.lpart = w.lpart;
+      c.S = splits;
+      c.ss = s->stat_ss;
+      c.colsum = s->colsum + (size_t)s->colsum_next * cs_n;
+      c.c_hi = s->c_hi;
+      c.c_lo = s->c_lo;
+      c.R = s->R;
+      c.G = s->G;
+      c.cap = s->cap;
+      c.P = P;
+      c.k0 = k0;
+      c.foff = foff;
+      c.rps = rps;
+      c.Hkv = s->HkvAll;
+      c.lh = s->Hkv;
+      a.key_blocks = key_blocks;
+      a.rsplits = rsplits;
+      // The merge rides on the score work-groups whose key block starts
+      // before k0, each taking an equal slice of its row range's (row, 4
+      // dims) tasks, when a slice fits in one task per thread.
+      const int bnk = score_keys_per_wg(s->dt, waves);
+      const int mkb = std::min(key_blocks, ceil_div(k0, bnk));
+      if (mkb > 0 && score_merge_fusable(s->dt, s->D, waves)) {
+        const int mtpw = ceil_div(ceil_div(rps * (s->D / 4), mkb), 32) * 32;
+        if (mtpw <= 64 * waves) {
+          a.fused = 1;
+          a.mkb = mkb;
+          a.mtpw = mtpw;
+          a.merge_wgs = 0;
+        }
+      }
     }
-    a.pool_pos = s->ppos;
-    a.move_dst = s->move_dst;
-    a.move_src = s->move_src;
-    a.move_count = s->move_count;
-    a.P = P;
-    a.B = s->B;
-    a.k0 = k0;
-    a.foff = foff;
-    a.mode = evict ? kSelEvict : (scored ? kSelScores : kSelMerge);
-    a.recent = recent ? 1 : 0;
-    a.score_scale = 1.0 / ((double)(1ull << kScoreFracBits) * (double)s->Hq * (double)s->T);
-    a.opart = w.opart;
-    a.epart = w.epart;
-    a.mpart = w.mpart;
-    a.lpart = w.lpart;
-    a.out = O;
-    a.Hkv = s->HkvAll;
-    a.R = s->R;
-    a.G = s->G;
-    a.Hq = s->Hq;
-    a.S = splits;
-    a.ss = s->stat_ss;
-    a.L = s->L;
-    a.lh = s->Hkv;
-    a.cap = s->cap;
-    a.list_stride = s->T;
-    a.out_ls = (int64_t)s->T * s->Hq * s->D;
-    rc = check(launch_select(s->dt, s->D, a, st, tm.lt));
+    rc = check(launch_score_merge(s->dt, s->D, a, waves, st, tm.lt));
     tm.done();
     if (rc) return rc;
   }
-  s->moves_pending = evict;
-  s->pending_max_moves = evict ? std::min(P - (int)s->B, (int)s->B) : 0;
+  // The Top-B decision of this frame waits for the next frame's first launch
+  // (or a view of the state).
+  if (evict || scored) {
+    s->sel_pending = true;
+    s->sel_P = P;
+    s->sel_k0 = k0;
+    s->sel_foff = foff;
+    s->sel_mode = evict ? kSelEvict : kSelScores;
+    s->sel_recent = recent ? 1 : 0;
+    s->sel_colsum = scored ? s->colsum_next : 0;
+  }
   s->frame_base = F;
   if (scored) {
     s->colsum_last = s->colsum_next;
@@ -800,7 +846,7 @@ int frame_step(statekv_state* s, const void* Q, const void* K, const void* V, in
     s->score_foff = foff;
     s->score_evicted = evict;
   } else if (evict) {
-    s->score_frame = -1;   // the pool has changed: earlier scores no longer describe it
+    s->score_frame = -1;   // the pool changes: earlier scores no longer describe it
   }
   s->count = evict ? (int)s->B : P;
   s->frames_done = n + 1;
@@ -817,7 +863,7 @@ int statekv_prefill_frame(statekv_state* s, const void* Q, const void* K, const 
   int rc = check_frame(s, Q, K, V, n, O);
   if (!rc) rc = check(hipSetDevice(s->device));
   if (rc) return rc;
-  return frame_step(s, Q, K, V, n, O, s->work);
+  return frame_step(s, Q, K, V, n, O, s->work[n & 1]);
 }
 
 int statekv_prefill_frame_static(statekv_state* s, const void* Q, const void* K, const void* V,
@@ -906,7 +952,7 @@ int statekv_decode(statekv_state* s, const void* Q, const void* K, const void* V
       a.k = K;
       a.v = V;
       a.table = s->rope_tab;
-      a.qrot = s->work.qrot;
+      a.qrot = s->work[0].qrot;
       a.dk = s->dk;
       a.dv = s->dv;
       a.nonfinite = s->nonfinite;
@@ -918,8 +964,7 @@ int statekv_decode(statekv_state* s, const void* Q, const void* K, const void* V
       a.cap = s->cap;
       a.rope_blocks = rope_blocks(t, s->Hq, s->Hkv, s->D, s->esize);
       a.det_ls = s->det_ls;
-      a.mv = moves_args(s, 0);
-      rc = check(launch_rope(s->dt, s->D, a, s->L, st, tm.lt));
+      rc = check(launch_frame(s->dt, s->D, a, s->L, st, tm.lt));
       tm.done();
       if (rc) return rc;
     }
@@ -928,13 +973,13 @@ int statekv_decode(statekv_state* s, const void* Q, const void* K, const void* V
     {
       KernelTimer tm(s, STATEKV_K_DEC_ATTN);
       AttnArgs a{};
-      a.qrot = s->work.qrot;
+      a.qrot = s->work[0].qrot;
       a.kpool = s->dk;
       a.vpool = s->dv;
-      a.opart = s->work.opart;
-      a.epart = s->work.epart;
-      a.mpart = s->work.mpart;
-      a.lpart = s->work.lpart;
+      a.opart = s->work[0].opart;
+      a.epart = s->work[0].epart;
+      a.mpart = s->work[0].mpart;
+      a.lpart = s->work[0].lpart;
       a.c_hi = s->c_hi;
       a.R = R;
       a.G = s->G;
@@ -955,23 +1000,23 @@ int statekv_decode(statekv_state* s, const void* Q, const void* K, const void* V
     }
     {
       KernelTimer tm(s, STATEKV_K_DEC_MERGE);
-      SelectArgs a{};
-      a.mode = kSelMerge;
-      a.opart = s->work.opart;
-      a.epart = s->work.epart;
-      a.mpart = s->work.mpart;
-      a.lpart = s->work.lpart;
-      a.out = O;
-      a.Hkv = s->HkvAll;
-      a.R = R;
-      a.G = s->G;
-      a.Hq = s->Hq;
-      a.S = splits;
-      a.ss = splits;
-      a.L = s->L;
-      a.lh = s->Hkv;
-      a.out_ls = (int64_t)t * s->Hq * s->D;
-      rc = check(launch_select(s->dt, s->D, a, st, tm.lt));
+      ScoreMergeArgs a{};
+      MergeArgs& m = a.mg;
+      m.opart = s->work[0].opart;
+      m.epart = s->work[0].epart;
+      m.mpart = s->work[0].mpart;
+      m.lpart = s->work[0].lpart;
+      m.out = O;
+      m.Hkv = s->HkvAll;
+      m.R = R;
+      m.G = s->G;
+      m.Hq = s->Hq;
+      m.S = splits;
+      m.ss = splits;
+      m.lh = s->Hkv;
+      m.out_ls = (int64_t)t * s->Hq * s->D;
+      a.merge_wgs = merge_wgs((int64_t)s->HkvAll * R);
+      rc = check(launch_score_merge(s->dt, s->D, a, s->dt == Dt::BF16 ? 8 : 4, st, tm.lt));
       tm.done();
       if (rc) return rc;
     }
@@ -984,7 +1029,7 @@ int statekv_decode(statekv_state* s, const void* Q, const void* K, const void* V
 int statekv_compressed_view(const statekv_state* s, statekv_view* out) {
   if (!s || !out) return STATEKV_EINVAL;
   int rc = check(hipSetDevice(s->device));
-  if (!rc) rc = apply_pending_moves(s);
+  if (!rc) rc = resolve_pending_selection(s);
   if (!rc) rc = sync_state(s);
   if (!rc) rc = read_nonfinite(s);
   if (rc) return rc;
@@ -1038,7 +1083,7 @@ int statekv_scores(const statekv_state* s, statekv_scores_view* out) {
   // Scores from the frame's column sums, keep flags from its move list, and
   // positions at scoring time: those of the pool rows, except in the slots
   // that the selection's moves have filled since.
-  rc = apply_pending_moves(s);
+  rc = resolve_pending_selection(s);
   if (!rc) {
     ScoreViewArgs a{};
     a.colsum = s->colsum + (size_t)s->colsum_last * s->L * s->cap;

@@ -17,8 +17,13 @@ OUT_TOL = {"bf16": 2e-2, "f32": 1e-5}
 # the B-th score.
 BAND = 1e-6
 # Scores: relative error of every candidate's fp32 score against the oracle's
-# fp64 mean attention.
-SCORE_TOL = 1e-6
+# fp64 mean attention.  bf16 inputs: products are exact in fp32, so a weight's
+# error comes from the fp32 sums and the exponent argument; measured below
+# 7e-7.  fp32 inputs (the tiny and MHA test streams): every product of the
+# logit is rounded too, and a weight 2^a of a low-scoring key carries about
+# ln2 * |a| * 2^-24 from its fp32 argument (|a| up to ~20 in these streams);
+# measured up to 1.9e-6, so the bar is 3e-6.
+SCORE_TOL = {"bf16": 1e-6, "f32": 3e-6}
 
 
 def oracle_cfg(wl: StreamConfig) -> LayerConfig:
@@ -163,7 +168,8 @@ class StepCheck:
         return rep
 
 
-def assert_step_ok(rep, dtype: str, score_tol: float = SCORE_TOL):
+def assert_step_ok(rep, dtype: str, score_tol: float | None = None):
+    score_tol = SCORE_TOL[dtype] if score_tol is None else score_tol
     assert rep["out_err"] <= OUT_TOL[dtype], rep
     assert rep["d_k_exact"] and rep["d_v_exact"], rep
     assert rep["state_size"][0] == rep["state_size"][1], rep
