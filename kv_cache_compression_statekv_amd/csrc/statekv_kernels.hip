@@ -1288,7 +1288,6 @@ __global__ __launch_bounds__(kDecodeMergeThreads) void decode_merge_kernel(Decod
   __syncthreads();
   if (tid >= CPR) return;
   acc = redo[0][c];
-#pragma unroll 8
   for (int j = 1; j < SG; ++j) acc += redo[j][c];
   double l = wl[0];
 #pragma unroll
@@ -1656,6 +1655,9 @@ __device__ int block_excl_scan(int v, int* sh, int* total) {
   return before + inc - v;
 }
 
+// Moves kept in LDS (the histogram's space) when the list holds at most this many.
+constexpr int kSelListMax = kSelectBins / 2;
+
 struct SelectShared {
   int hist[kSelectBins];
   uint32_t cand_v[kSelCand];
@@ -1871,45 +1873,90 @@ __device__ void select_top_b(const SelArgs& a, SelectShared& sh, uint32_t* val) 
 
   // Outputs: the move list only.  Scores, keep flags and positions of the
   // scored pool are rebuilt on request from the column sums and the move
-  // list, and the merge work-groups clear the other column-sum buffer.
-  // With unique positions exactly P - B rows are evicted, so at most
+  // list.  With unique positions exactly P - B rows are evicted, so at most
   // min(T, B) moves exist; the writes are still bounded by the lists'
-  // capacity, so inconsistent inputs cannot write past them.
+  // capacity, so inconsistent inputs cannot write past them.  When the list
+  // fits in LDS (the histogram's space, free by now) it goes there, and every
+  // global store waits until after the barrier below (which would otherwise
+  // wait for them).
+  const bool lds_list = a.list_stride <= kSelListMax;
+  int* l_dst = sh.hist;
+  int* l_src = sh.hist + kSelListMax;
   if (holes | movers) {
     int bh = base & 0xffff, bm = base >> 16;
     for (int idx = i0; idx < i1; ++idx) {
       const uint32_t ev = val[idx] >> 31;
-      if (idx < a.B && ev && bh < a.list_stride) a.move_dst[bh++] = idx;
-      if (idx >= a.B && !ev && bm < a.list_stride) a.move_src[bm++] = pool_row(idx, a.k0, a.foff);
+      if (idx < a.B && ev && bh < a.list_stride) {
+        if (lds_list) l_dst[bh] = idx;
+        else a.move_dst[bh] = idx;
+        ++bh;
+      }
+      if (idx >= a.B && !ev && bm < a.list_stride) {
+        const int row = pool_row(idx, a.k0, a.foff);
+        if (lds_list) l_src[bm] = row;
+        else a.move_src[bm] = row;
+        ++bm;
+      }
     }
   }
   const int moves = min(min(total & 0xffff, total >> 16), a.list_stride);
-  if (tid == 0) *a.move_count = moves;
-  if (moves == 0) return;
-  // The moves themselves: K and V of every KV head, 16 bytes per task, and the
-  // positions.  The list was written by this work-group before the barrier.
+  if (moves == 0) {
+    if (tid == 0) *a.move_count = 0;
+    return;
+  }
   __syncthreads();
+  // The moves: K and V of every KV head (16 bytes per task), and the
+  // positions.  A round issues all its loads before its stores: one memory
+  // round trip per round (one round for a frame of up to 1024 moves of
+  // 4 * 1024 chunks).
   const int cpr = a.row_bytes / 16;
   const int per_move = a.Hkv * cpr;
-  for (int t = tid; t < moves * per_move; t += kSelectThreads) {
-    const int i = t / per_move;
-    const int rem = t - i * per_move;
-    const int g = rem / cpr, c = rem - g * cpr;
-    const int dst = min(max(a.move_dst[i], 0), a.B - 1);
-    const int src = min(max(a.move_src[i], a.B), a.cap - 1);
-    const size_t so = ((size_t)g * a.cap + src) * a.row_bytes + (size_t)c * 16;
-    const size_t dof = ((size_t)g * a.cap + dst) * a.row_bytes + (size_t)c * 16;
-    const u32x4_t kv = *reinterpret_cast<const u32x4_t*>((const char*)a.kpool + so);
-    const u32x4_t vv = *reinterpret_cast<const u32x4_t*>((const char*)a.vpool + so);
-    *reinterpret_cast<u32x4_t*>((char*)a.kpool + dof) = kv;
-    *reinterpret_cast<u32x4_t*>((char*)a.vpool + dof) = vv;
+  const int tasks = moves * per_move;
+  constexpr int kMoveRound = 4;
+  for (int t0 = 0, mp0 = 0; t0 < tasks || mp0 < moves; t0 += kMoveRound * kSelectThreads, mp0 += kSelectThreads) {
+    u32x4_t kv[kMoveRound], vv[kMoveRound];
+    size_t dof[kMoveRound];
+#pragma unroll
+    for (int m = 0; m < kMoveRound; ++m) {
+      const int t = t0 + tid + m * kSelectThreads;
+      dof[m] = ~(size_t)0;
+      if (t < tasks) {
+        const int mi = t / per_move;
+        const int rem = t - mi * per_move;
+        const int g = rem / cpr, c = rem - g * cpr;
+        const int dst = min(max(lds_list ? l_dst[mi] : a.move_dst[mi], 0), a.B - 1);
+        const int src = min(max(lds_list ? l_src[mi] : a.move_src[mi], a.B), a.cap - 1);
+        const size_t so = ((size_t)g * a.cap + src) * a.row_bytes + (size_t)c * 16;
+        dof[m] = ((size_t)g * a.cap + dst) * a.row_bytes + (size_t)c * 16;
+        kv[m] = *reinterpret_cast<const u32x4_t*>((const char*)a.kpool + so);
+        vv[m] = *reinterpret_cast<const u32x4_t*>((const char*)a.vpool + so);
+      }
+    }
+    // One position move per thread and round.
+    const int mp = mp0 + tid;
+    int pdst = -1, psrc = 0, pd = 0, ps = 0;
+    if (mp < moves) {
+      pdst = min(max(lds_list ? l_dst[mp] : a.move_dst[mp], 0), a.B - 1);
+      psrc = min(max(lds_list ? l_src[mp] : a.move_src[mp], a.B), a.cap - 1);
+      pd = a.pool_pos[pdst];
+      ps = a.pool_pos[psrc];
+    }
+#pragma unroll
+    for (int m = 0; m < kMoveRound; ++m) {
+      if (dof[m] == ~(size_t)0) continue;
+      *reinterpret_cast<u32x4_t*>((char*)a.kpool + dof[m]) = kv[m];
+      *reinterpret_cast<u32x4_t*>((char*)a.vpool + dof[m]) = vv[m];
+    }
+    if (pdst >= 0) {
+      a.evicted_pos[pdst] = pd;
+      a.pool_pos[pdst] = ps;
+      if (lds_list) {
+        a.move_dst[mp] = pdst;
+        a.move_src[mp] = psrc;
+      }
+    }
   }
-  for (int i = tid; i < moves; i += kSelectThreads) {
-    const int dst = min(max(a.move_dst[i], 0), a.B - 1);
-    const int src = min(max(a.move_src[i], a.B), a.cap - 1);
-    a.evicted_pos[dst] = a.pool_pos[dst];
-    a.pool_pos[dst] = a.pool_pos[src];
-  }
+  if (tid == 0) *a.move_count = moves;
 }
 
 // Merge of the key splits of pass 1:
