@@ -552,8 +552,9 @@ def main():
         gbs = rope_bytes / (kernels["rope_select"]["avg_us"] * 1e-6) / 1e9
         extra["hbm_rope_append"] = {"bytes": rope_bytes, "achieved_gbs": round(gbs, 1),
                                     "peak_gbs": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4),
-                                    "note": "algorithmic bytes of the frame's RoPE and appends; "
-                                            "latency-bound at these sizes"}
+                                    "note": "algorithmic bytes of the frame's RoPE and appends over "
+                                            "the frame launch, which also makes the previous frame's "
+                                            "Top-B decision and moves; latency-bound at these sizes"}
     if lat:
         lat_a = np.array(lat)
         idx = np.arange(lat_a.size)
