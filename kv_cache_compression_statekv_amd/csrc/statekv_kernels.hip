@@ -2,8 +2,8 @@
 //
 // Paper note "Linear Scaling Video VLMs for Long Video Understanding"
 // (papernotes.org, ECCV 2026), section 方法详解:
-//   rope_append_kernel  关键设计 3: RoPE at the virtual position nT + i with the
-//                       fixed scaled frequencies; 整体框架 / flowchart node E:
+//   rope_wg             关键设计 3: RoPE at the virtual position nT + i with the
+//   (in frame_kernel)   fixed scaled frequencies; 整体框架 / flowchart node E:
 //                       the frame's K, V are appended to the detailed cache D.
 //   attn_fwd_kernel     关键设计 1: the frame's queries attend over
 //                       [Kbar_{n-1}; K_n] (bf16 MFMA, online softmax, split
@@ -20,8 +20,9 @@
 //   decode_attn_kernel  整体框架 / 关键设计 1, 3: after the frames, text
 //   decode_merge_kernel tokens attend over the whole detailed cache D at the
 //                       continuing virtual positions (split over keys, then
-//                       merged).  Longer text chunks reuse the RoPE kernel,
-//                       attn_fwd_kernel (with D's strides) and the merge.
+//                       merged).  Longer text chunks reuse the frame launch's
+//                       RoPE work-groups, attn_fwd_kernel (with D's strides)
+//                       and the merge.
 //
 // Matrix-core tiles use v_mfma_f32_32x32x16_bf16 (bf16 storage) or
 // v_mfma_f32_32x32x2_f32 (fp32 storage).  Accumulator layout of a 32x32 tile:
@@ -439,6 +440,13 @@ __device__ void rope_wg(const RopeArgs& a0, size_t layer, int wg) {
 // row sum l only needs the weights near the maximum, whose exponent error
 // c_lo*x is common to them, so it stays within about 1e-7 of the exact sum.
 // ---------------------------------------------------------------------------
+// Raw buffer resource over [base, base + 2^32): loads address base + a
+// 32-bit byte offset, with the base in scalar registers.  Word 3 selects a
+// 32-bit data format, which untyped loads need to return data.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, -1, 0x00020000);
+}
+
 template <class E, int D, int NT, int BN_ = kAttnBN>
 struct AttnStage {
   typedef typename E::T T;
@@ -458,66 +466,85 @@ struct AttnStage {
   u32x4_t vr[VCH];
 
   // Key j of the block is row pool_row(j, k0, foff) of kbase / vbase; rows
-  // are rs elements apart (rs < 2^24).  Row kb + r of the block sits at
-  // (kb + r) * rs, plus foff * rs from key k0 on: the block's part is uniform
-  // (scalar arithmetic) and a thread's r * rs (r < BN) is a 24-bit product
-  // that does not change from block to block.  Keys at or beyond kend (the
-  // last block of a range) read the row of key kend - 1 instead: the softmax
-  // masks them, so these finite rows only fill the tile, and no load needs a
-  // branch.
-  __device__ __forceinline__ void load(const T* kbase, const T* vbase, int kb, int kend, int k0,
-                                       int foff, size_t rs, int tid) {
-    constexpr int CPR = D / EPV;
-    const int64_t blk = (int64_t)kb * (int64_t)rs;
-    const int64_t fo = (int64_t)foff * (int64_t)rs;
-    const uint32_t rs32 = (uint32_t)rs;
-    const int rlast = kend - 1 - kb;   // last valid row of the block (>= 0)
-    // Whole block on one side of k0 (nearly every block): one uniform base.
-    if (kb + BN <= kend && (kb + BN <= k0 || kb >= k0)) {
-      const int64_t ub = blk + (kb >= k0 ? fo : 0);
-      load_rows(kbase + ub, vbase + ub, [&](int rr) -> int64_t { return (int64_t)__umul24((uint32_t)rr, rs32); },
-                tid);
-    } else {
-      load_rows(kbase + blk, vbase + blk, [&](int rr) -> int64_t {
-        const int rc = min(rr, rlast);
-        return (int64_t)__umul24((uint32_t)rc, rs32) + (kb + rc >= k0 ? fo : 0);
-      }, tid);
-    }
-  }
-
-  // Row r of the block is at kb_ + row_off(r) (keys) and vb_ + row_off(r).
+  // are rs elements apart (rs < 2^24).  Loads are buffer loads: the block's
+  // base is a scalar resource (kbase / vbase advanced by the block's first
+  // row) and each lane adds a byte offset.  Row kb + r of the block sits at
+  // (kb + r) * rs, plus foff * rs from key k0 on.  When the whole block lies
+  // on one side of k0 (nearly every block) the lane offsets r * rs do not
+  // change from block to block: they are formed once (off_uniform) and no
+  // vector instruction is spent on addresses in the loop.  Keys at or beyond
+  // kend (the last block of a range) read the row of key kend - 1 instead:
+  // the softmax masks them, so these finite rows only fill the tile, and no
+  // load needs a branch.
+  struct Offsets {
+    uint32_t k[KCH];
+    uint32_t v[VCH];
+  };
   template <class RowOff>
-  __device__ __forceinline__ void load_rows(const T* kb_, const T* vb_, RowOff row_off, int tid) {
+  __device__ __forceinline__ static void offsets(Offsets& o, RowOff row_off, int tid) {
     constexpr int CPR = D / EPV;
-    const T* kbase = kb_;
-    const T* vbase = vb_;
 #pragma unroll
     for (int j = 0; j < KCH; ++j) {
       const int t = tid + j * NT;
       const int rr = t / CPR, cc = t - rr * CPR;
-      kr[j] = *reinterpret_cast<const u32x4_t*>(kbase + row_off(rr) + cc * EPV);
+      o.k[j] = row_off(rr) + (uint32_t)(cc * 16);
     }
     if constexpr (sizeof(T) == 2) {
       constexpr int NKQ = BN / KG;
 #pragma unroll
       for (int u = 0; u < VT_PER; ++u) {
-        const int t = tid + u * NT;
+        const int t = min(tid + u * NT, VTASKS - 1);
         const int kq = t % NKQ, dc = t / NKQ;
 #pragma unroll
-        for (int j = 0; j < KG; ++j) {
-          vr[u * KG + j] = u32x4_t{0u, 0u, 0u, 0u};
-          if (VTASKS % NT == 0 || t < VTASKS)
-            vr[u * KG + j] = *reinterpret_cast<const u32x4_t*>(vbase + row_off(kq * KG + j) + dc * 8);
-        }
+        for (int j = 0; j < KG; ++j) o.v[u * KG + j] = row_off(kq * KG + j) + (uint32_t)(dc * 16);
       }
     } else {
 #pragma unroll
       for (int j = 0; j < VCH; ++j) {
         const int t = tid + j * NT;
         const int rr = t % BN, cc = t / BN;
-        vr[j] = *reinterpret_cast<const u32x4_t*>(vbase + row_off(rr) + cc * 4);
+        o.v[j] = row_off(rr) + (uint32_t)(cc * 16);
       }
     }
+  }
+  __device__ __forceinline__ static void off_uniform(Offsets& o, size_t rs, int tid) {
+    const uint32_t rb = (uint32_t)rs * (uint32_t)sizeof(T);
+    offsets(o, [&](int rr) -> uint32_t { return (uint32_t)rr * rb; }, tid);
+  }
+
+  __device__ __forceinline__ void load(const T* kbase, const T* vbase, int kb, int kend, int k0,
+                                       int foff, size_t rs, Offsets& ou, int tid) {
+    const int64_t blk = (int64_t)kb * (int64_t)rs;
+    const int64_t fo = (int64_t)foff * (int64_t)rs;
+    // Whole block on one side of k0 (nearly every block): one uniform base
+    // and the loop-invariant offsets.  Otherwise rows are clamped and the
+    // frame's rows shifted by foff one by one, in the same registers, which
+    // get their loop-invariant values back once the loads are issued.
+    if (kb + BN <= kend && (kb + BN <= k0 || kb >= k0)) {
+      const int64_t ub = blk + (kb >= k0 ? fo : 0);
+      load_rows(kbase + ub, vbase + ub, ou);
+    } else {
+      const uint32_t rb = (uint32_t)rs * (uint32_t)sizeof(T);
+      const uint32_t fob = (uint32_t)fo * (uint32_t)sizeof(T);
+      const int rlast = kend - 1 - kb;   // last valid row of the block (>= 0)
+      offsets(ou, [&](int rr) -> uint32_t {
+        const int rc = min(rr, rlast);
+        return (uint32_t)rc * rb + (kb + rc >= k0 ? fob : 0u);
+      }, tid);
+      load_rows(kbase + blk, vbase + blk, ou);
+      off_uniform(ou, rs, tid);
+    }
+  }
+
+  // Every thread loads (threads beyond the V^T tasks repeat the last task's
+  // rows and do not store them): no branch around the loads.
+  __device__ __forceinline__ void load_rows(const T* kb_, const T* vb_, const Offsets& o) {
+    const __amdgpu_buffer_rsrc_t kr_ = buffer_rsrc(kb_);
+    const __amdgpu_buffer_rsrc_t vr_ = buffer_rsrc(vb_);
+#pragma unroll
+    for (int j = 0; j < KCH; ++j) kr[j] = __builtin_amdgcn_raw_buffer_load_b128(kr_, o.k[j], 0, 0);
+#pragma unroll
+    for (int j = 0; j < VCH; ++j) vr[j] = __builtin_amdgcn_raw_buffer_load_b128(vr_, o.v[j], 0, 0);
   }
 
   __device__ __forceinline__ void store(T* Ks, T* Vt, int tid) const {
@@ -735,11 +762,17 @@ void attn_fwd_kernel(AttnArgs a) {
   // compute, so short splits (a few blocks per work-group) have all their
   // loads in flight at once.  Blocks pass through two LDS buffers.
   Stage st[NPF];
+  typename Stage::Offsets so;
+  Stage::off_uniform(so, rs, tid);
   const int nblk = kend > kbeg ? (kend - kbeg + BN - 1) / BN : 0;
 #pragma unroll
   for (int i = 0; i < NPF; ++i)
-    if (i < nblk) st[i].load(kbase, vbase, kbeg + i * BN, kend, a.k0, a.foff, rs, tid);
+    if (i < nblk) st[i].load(kbase, vbase, kbeg + i * BN, kend, a.k0, a.foff, rs, so, tid);
   if (nblk > 0) st[0].store(Ks[0], Vt[0], tid);
+  // Every load issued so far (the query fragments and block 0) has arrived
+  // here on every path; saying so keeps the compiler from waiting for the
+  // loop's own prefetch loads before the first matrix instruction of a block.
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   __syncthreads();
 
   auto compute = [&](int kb, int buf) {
@@ -896,10 +929,10 @@ void attn_fwd_kernel(AttnArgs a) {
           // beside this block's compute: that buffer was last read before the
           // previous barrier, and the barrier below publishes it.
           if (b + 1 < nblk) st[(i + 1) % NPF].store(Ks[buf ^ 1], Vt[buf ^ 1], tid);
-          if (b + NPF < nblk) st[i].load(kbase, vbase, kb + NPF * BN, kend, a.k0, a.foff, rs, tid);
+          if (b + NPF < nblk) st[i].load(kbase, vbase, kb + NPF * BN, kend, a.k0, a.foff, rs, so, tid);
           compute(kb, buf);
         } else {
-          if (b + NPF < nblk) st[i].load(kbase, vbase, kb + NPF * BN, kend, a.k0, a.foff, rs, tid);
+          if (b + NPF < nblk) st[i].load(kbase, vbase, kb + NPF * BN, kend, a.k0, a.foff, rs, so, tid);
           compute(kb, buf);
           if (b + 1 < nblk) st[(i + 1) % NPF].store(Ks[buf ^ 1], Vt[buf ^ 1], tid);
         }
@@ -1026,11 +1059,13 @@ __global__ __launch_bounds__(64 * NW, NPF > 1 ? 1 : 2) void decode_attn_kernel(D
   // NPF register stages: block b's loads are issued NPF blocks ahead of its
   // compute (more bytes in flight per CU for the HBM stream).
   Stage st[NPF];
+  typename Stage::Offsets so;
+  Stage::off_uniform(so, rs, tid);
   const int nblk = dend > kbeg ? (dend - kbeg + BN - 1) / BN : 0;
   bool finite = true;
 #pragma unroll
   for (int i = 0; i < NPF; ++i)
-    if (i < nblk) st[i].load(kbase, vbase, kbeg + i * BN, dend, a.k0, 0, rs, tid);
+    if (i < nblk) st[i].load(kbase, vbase, kbeg + i * BN, dend, a.k0, 0, rs, so, tid);
 
   typename M::Frag qf[NKS];
   {
@@ -1149,7 +1184,7 @@ __global__ __launch_bounds__(64 * NW, NPF > 1 ? 1 : 2) void decode_attn_kernel(D
         if (b > 0) __syncthreads();   // every wave is done with the previous block
         st[i].store(Ks, Vt, tid);
         __syncthreads();
-        if (b + NPF < nblk) st[i].load(kbase, vbase, kb + NPF * BN, dend, a.k0, 0, rs, tid);
+        if (b + NPF < nblk) st[i].load(kbase, vbase, kb + NPF * BN, dend, a.k0, 0, rs, so, tid);
         if (kb + wave * 32 < dend) subtile(kb + wave * 32, Ks, Vt, VSTR, wave * 32, lim_d, full_end_d);
       }
     }
@@ -1394,15 +1429,22 @@ __device__ void score_wg(const ScoreArgs& a, int wid, int nwg, int key_blocks, c
   // NPF tiles' loads are issued before the row statistics are merged, so the
   // two latencies overlap.
   u32x4_t qr[NPF][QCH];
-  auto load_tile = [&](u32x4_t (&q)[QCH], int rt) {
+  // Tile loads are buffer loads from the tile's first row: rows at or beyond
+  // r1 lie past the resource's extent and read as zero, and threads without a
+  // chunk (t >= RT * CPR) use an offset past any extent, so no load needs a
+  // branch and the lane offsets are formed once.
+  uint32_t qoff[QCH];
 #pragma unroll
-    for (int j = 0; j < QCH; ++j) {
-      const int t = tid + j * NT;
-      const int rr = t / CPR, cc = t - rr * CPR;
-      const int r = rt + rr;
-      q[j] = u32x4_t{0u, 0u, 0u, 0u};
-      if (t < RT * CPR && r < r1) q[j] = *reinterpret_cast<const u32x4_t*>(qbase + (size_t)r * D + cc * EPV);
-    }
+  for (int j = 0; j < QCH; ++j) {
+    const int t = tid + j * NT;
+    const int rr = t / CPR, cc = t - rr * CPR;
+    qoff[j] = t < RT * CPR ? (uint32_t)(rr * D * (int)sizeof(T) + cc * 16) : 0x80000000u;
+  }
+  auto load_tile = [&](u32x4_t (&q)[QCH], int rt) {
+    const __amdgpu_buffer_rsrc_t rsq = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<T*>(qbase + (size_t)rt * D), (short)0, max(r1 - rt, 0) * D * (int)sizeof(T), 0x00020000);
+#pragma unroll
+    for (int j = 0; j < QCH; ++j) q[j] = __builtin_amdgcn_raw_buffer_load_b128(rsq, qoff[j], 0, 0);
   };
   auto store_tile = [&](const u32x4_t (&q)[QCH], int buf) {
 #pragma unroll
@@ -1413,9 +1455,11 @@ __device__ void score_wg(const ScoreArgs& a, int wid, int nwg, int key_blocks, c
     }
   };
 
+  // Tiles past the last one read as zero (no rows in their extent), so every
+  // stage is loaded unconditionally and the compiler knows which loads each
+  // wait is for.
 #pragma unroll
-  for (int i = 0; i < NPF; ++i)
-    if (i < ntile) load_tile(qr[i], rstart + i * RT);
+  for (int i = 0; i < NPF; ++i) load_tile(qr[i], rstart + i * RT);
 
   // Fused merge: task tid of this work-group's slice, (row, 4 dims) of the
   // rows [r0, r1) (rows fastest).  Its loads are in flight while the row
@@ -1472,6 +1516,11 @@ __device__ void score_wg(const ScoreArgs& a, int wid, int nwg, int key_blocks, c
   }
 
   if (ntile > 0) store_tile(qr[0], 0);
+  // Every load issued so far has arrived on every path (the statistics were
+  // issued after the first tiles, and the merge needs its partials next);
+  // saying so keeps the compiler from waiting for the loop's own prefetch
+  // loads before the first matrix instruction of a tile.
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   __syncthreads();
   if (FM && m_row >= 0) {
     // m and 1/l of the row, as the split merge forms them; the same weights,
@@ -1512,7 +1561,7 @@ __device__ void score_wg(const ScoreArgs& a, int wid, int nwg, int key_blocks, c
     if (it >= ntile) break;
     const int buf = it & 1;
     const int ro = it * RT;   // tile offset inside the statistics arrays
-    if (it + NPF < ntile) load_tile(qr[ip], rstart + (it + NPF) * RT);
+    load_tile(qr[ip], rstart + (it + NPF) * RT);
     // S = Q K^T for the KT key tiles: Q fragments read once per k-slice and
     // fed to KT independent accumulation chains.
     f32x16_t acc[KT];
