@@ -536,6 +536,58 @@ struct AttnStage {
     }
   }
 
+  // The same block through 64-bit global addresses, for the text-phase
+  // kernel: its K and V come from D, a stream read once, and its registers
+  // are at their limit, so loop-invariant offsets would cost it more than the
+  // address arithmetic they save (measured 25 % slower per token at 131k keys).
+  __device__ __forceinline__ void load_global(const T* kbase, const T* vbase, int kb, int kend, size_t rs,
+                                              int tid) {
+    const int64_t blk = (int64_t)kb * (int64_t)rs;
+    const uint32_t rs32 = (uint32_t)rs;
+    const int rlast = kend - 1 - kb;   // last valid row of the block (>= 0)
+    if (kb + BN <= kend) {
+      load_rows_global(kbase + blk, vbase + blk,
+                       [&](int rr) -> int64_t { return (int64_t)__umul24((uint32_t)rr, rs32); }, tid);
+    } else {
+      load_rows_global(kbase + blk, vbase + blk, [&](int rr) -> int64_t {
+        return (int64_t)__umul24((uint32_t)min(rr, rlast), rs32);
+      }, tid);
+    }
+  }
+
+  // Row r of the block is at kb_ + row_off(r) (keys) and vb_ + row_off(r).
+  template <class RowOff>
+  __device__ __forceinline__ void load_rows_global(const T* kb_, const T* vb_, RowOff row_off, int tid) {
+    constexpr int CPR = D / EPV;
+#pragma unroll
+    for (int j = 0; j < KCH; ++j) {
+      const int t = tid + j * NT;
+      const int rr = t / CPR, cc = t - rr * CPR;
+      kr[j] = *reinterpret_cast<const u32x4_t*>(kb_ + row_off(rr) + cc * EPV);
+    }
+    if constexpr (sizeof(T) == 2) {
+      constexpr int NKQ = BN / KG;
+#pragma unroll
+      for (int u = 0; u < VT_PER; ++u) {
+        const int t = tid + u * NT;
+        const int kq = t % NKQ, dc = t / NKQ;
+#pragma unroll
+        for (int j = 0; j < KG; ++j) {
+          vr[u * KG + j] = u32x4_t{0u, 0u, 0u, 0u};
+          if (VTASKS % NT == 0 || t < VTASKS)
+            vr[u * KG + j] = *reinterpret_cast<const u32x4_t*>(vb_ + row_off(kq * KG + j) + dc * 8);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < VCH; ++j) {
+        const int t = tid + j * NT;
+        const int rr = t % BN, cc = t / BN;
+        vr[j] = *reinterpret_cast<const u32x4_t*>(vb_ + row_off(rr) + cc * 4);
+      }
+    }
+  }
+
   // Every thread loads (threads beyond the V^T tasks repeat the last task's
   // rows and do not store them): no branch around the loads.
   __device__ __forceinline__ void load_rows(const T* kb_, const T* vb_, const Offsets& o) {
@@ -1059,13 +1111,11 @@ __global__ __launch_bounds__(64 * NW, NPF > 1 ? 1 : 2) void decode_attn_kernel(D
   // NPF register stages: block b's loads are issued NPF blocks ahead of its
   // compute (more bytes in flight per CU for the HBM stream).
   Stage st[NPF];
-  typename Stage::Offsets so;
-  Stage::off_uniform(so, rs, tid);
   const int nblk = dend > kbeg ? (dend - kbeg + BN - 1) / BN : 0;
   bool finite = true;
 #pragma unroll
   for (int i = 0; i < NPF; ++i)
-    if (i < nblk) st[i].load(kbase, vbase, kbeg + i * BN, dend, a.k0, 0, rs, so, tid);
+    if (i < nblk) st[i].load_global(kbase, vbase, kbeg + i * BN, dend, rs, tid);
 
   typename M::Frag qf[NKS];
   {
@@ -1184,7 +1234,7 @@ __global__ __launch_bounds__(64 * NW, NPF > 1 ? 1 : 2) void decode_attn_kernel(D
         if (b > 0) __syncthreads();   // every wave is done with the previous block
         st[i].store(Ks, Vt, tid);
         __syncthreads();
-        if (b + NPF < nblk) st[i].load(kbase, vbase, kb + NPF * BN, dend, a.k0, 0, rs, so, tid);
+        if (b + NPF < nblk) st[i].load_global(kbase, vbase, kb + NPF * BN, dend, rs, tid);
         if (kb + wave * 32 < dend) subtile(kb + wave * 32, Ks, Vt, VSTR, wave * 32, lim_d, full_end_d);
       }
     }
