@@ -189,6 +189,15 @@ struct MergeArgs {
 // key block starts before k0 (the first mkb of each (KV head, row split))
 // also merge the split partials of their row range, mtpw (row, 4 dims) tasks
 // each, rows fastest; such a block's row statistics cover its whole range.
+// The launch after pass 1 under the recency policy: the frame's own eviction
+// decision (positions only) and moves, one work-group per layer, beside the
+// split merge (merge groups numbered across the stack's layers).
+struct SelectMergeArgs {
+  SelArgs sel;
+  MergeArgs mg;
+  int32_t layers;
+};
+
 struct ScoreMergeArgs {
   ScoreArgs sc;
   MergeArgs mg;
@@ -224,6 +233,8 @@ hipError_t launch_attn(Dt dt, int d, const AttnArgs& a, int row_tiles, int split
                        const LaunchTiming& tm = {});
 // Score pass (with `waves` waves per work-group) and merge in one launch.  The
 // merge rides on the score work-groups (fused) only where score_merge_fusable.
+hipError_t launch_select_merge(Dt dt, int d, const SelectMergeArgs& a, int merge_groups, hipStream_t s,
+                               const LaunchTiming& tm = {});
 hipError_t launch_score_merge(Dt dt, int d, const ScoreMergeArgs& a, int waves, hipStream_t s,
                               const LaunchTiming& tm = {});
 // Work-groups of the merge for `rows` flat rows (a multiple of the XCD count).

@@ -2205,26 +2205,45 @@ __device__ void merge_group(const MergeArgs& a, int grp, float* lds) {
 // The frame launch: per layer (grid y), work-group 0 makes the previous
 // frame's Top-B decision and its moves when nsel = 1; the others rotate and
 // append this frame's tokens.  Dynamic LDS: the selection's P score words.
+// The selection of layer `layer` of a stack (its slices of every array).
+__device__ void select_layer(SelArgs b, size_t layer, SelectShared& sh, uint32_t* val) {
+  const size_t pool_bytes = (size_t)b.Hkv * b.cap * b.row_bytes;
+  b.colsum += layer * b.cap;
+  b.pool_pos += layer * b.cap;
+  b.evicted_pos += layer * b.B;
+  b.move_dst += layer * b.list_stride;
+  b.move_src += layer * b.list_stride;
+  b.move_count += layer;
+  b.kpool = (char*)b.kpool + layer * pool_bytes;
+  b.vpool = (char*)b.vpool + layer * pool_bytes;
+  select_top_b(b, sh, val);
+}
+
 template <class E, int D>
 __global__ __launch_bounds__(kSelectThreads) void frame_kernel(RopeArgs a) {
   const size_t layer = blockIdx.y;
   if ((int)blockIdx.x < a.nsel) {
     __shared__ SelectShared sh;
     extern __shared__ __attribute__((aligned(16))) uint32_t sel_val[];
-    SelArgs b = a.sel;
-    const size_t pool_bytes = (size_t)b.Hkv * b.cap * b.row_bytes;
-    b.colsum += layer * b.cap;
-    b.pool_pos += layer * b.cap;
-    b.evicted_pos += layer * b.B;
-    b.move_dst += layer * b.list_stride;
-    b.move_src += layer * b.list_stride;
-    b.move_count += layer;
-    b.kpool = (char*)b.kpool + layer * pool_bytes;
-    b.vpool = (char*)b.vpool + layer * pool_bytes;
-    select_top_b(b, sh, sel_val);
+    select_layer(a.sel, layer, sh, sel_val);
     return;
   }
   rope_wg<E, D>(a, layer, (int)blockIdx.x - a.nsel);
+}
+
+// Recency policy, the launch after pass 1: work-group l < layers evicts the
+// oldest rows of layer l's pool and makes its moves (the merge reads only the
+// split partials, never the pool), the others merge the key splits into O.
+// Dynamic LDS: the selection's P score words, or the merge's weights.
+template <class E, int D>
+__global__ __launch_bounds__(kSelectThreads) void select_merge_kernel(SelectMergeArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
+  if ((int)blockIdx.x < a.layers) {
+    __shared__ SelectShared sh;
+    select_layer(a.sel, blockIdx.x, sh, dyn);
+    return;
+  }
+  merge_group<E, D, kSelectThreads>(a.mg, (int)blockIdx.x - a.layers, reinterpret_cast<float*>(dyn));
 }
 
 // The launch after pass 1: merge work-groups first, then the score pass.
@@ -2363,6 +2382,28 @@ static hipError_t launch_frame_t(const RopeArgs& a, int layers, hipStream_t s, c
   (void)attr;
   hipExtLaunchKernelGGL((frame_kernel<E, D>), grid, dim3(kSelectThreads), lds, s, tm.start, tm.stop, 0, a);
   return hipGetLastError();
+}
+
+template <class E, int D>
+static hipError_t launch_select_merge_t(const SelectMergeArgs& a, int merge_groups, hipStream_t s,
+                                        const LaunchTiming& tm) {
+  const size_t lds = std::max((size_t)a.sel.P * sizeof(uint32_t), (size_t)merge_lds_bytes(a.mg.S));
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_merge_kernel<E, D>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     kMaxPool * (int)sizeof(uint32_t));
+  (void)attr;
+  hipExtLaunchKernelGGL((select_merge_kernel<E, D>), dim3(a.layers + merge_groups), dim3(kSelectThreads), lds, s,
+                        tm.start, tm.stop, 0, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_select_merge(Dt dt, int d, const SelectMergeArgs& a, int merge_groups, hipStream_t s,
+                               const LaunchTiming& tm) {
+  if (dt == Dt::BF16)
+    return d == 64 ? launch_select_merge_t<BF16, 64>(a, merge_groups, s, tm)
+                   : launch_select_merge_t<BF16, 128>(a, merge_groups, s, tm);
+  return d == 64 ? launch_select_merge_t<F32, 64>(a, merge_groups, s, tm)
+                 : launch_select_merge_t<F32, 128>(a, merge_groups, s, tm);
 }
 
 hipError_t launch_frame(Dt dt, int d, const RopeArgs& a, int layers, hipStream_t s, const LaunchTiming& tm) {

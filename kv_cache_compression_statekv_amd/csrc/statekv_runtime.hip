@@ -394,9 +394,12 @@ struct KernelTimer {
 
 // The pending selection of the last frame (layer 0's arrays; the kernel
 // offsets the other layers).
-SelArgs sel_args(const statekv_state* s) {
+// Selection arguments for a pool of P candidates (state rows [0, k0), frame
+// rows from k0 + foff) in the given mode, scores from column-sum buffer
+// colsum_buf.
+SelArgs sel_args_for(const statekv_state* s, int P, int k0, int foff, int mode, int recent, int colsum_buf) {
   SelArgs a{};
-  a.colsum = s->colsum + (size_t)s->sel_colsum * s->L * s->cap;
+  a.colsum = s->colsum + (size_t)colsum_buf * s->L * s->cap;
   a.pool_pos = s->ppos;
   a.evicted_pos = s->evicted_pos;
   a.move_dst = s->move_dst;
@@ -404,18 +407,23 @@ SelArgs sel_args(const statekv_state* s) {
   a.move_count = s->move_count;
   a.kpool = s->kpool;
   a.vpool = s->vpool;
-  a.P = s->sel_P;
+  a.P = P;
   a.B = s->B;
-  a.mode = s->sel_mode;
-  a.recent = s->sel_recent;
-  a.k0 = s->sel_k0;
-  a.foff = s->sel_foff;
+  a.mode = mode;
+  a.recent = recent;
+  a.k0 = k0;
+  a.foff = foff;
   a.score_scale = 1.0 / ((double)(1ull << kScoreFracBits) * (double)s->Hq * (double)s->T);
   a.Hkv = s->Hkv;
   a.cap = s->cap;
   a.row_bytes = s->D * s->esize;
   a.list_stride = s->T;
   return a;
+}
+
+// The pending decision of the last frame.
+SelArgs sel_args(const statekv_state* s) {
+  return sel_args_for(s, s->sel_P, s->sel_k0, s->sel_foff, s->sel_mode, s->sel_recent, s->sel_colsum);
 }
 
 // Makes the last frame's pending Top-B decision and its moves (one launch of
@@ -676,6 +684,25 @@ int check_frame(const statekv_state* s, const void* Q, const void* K, const void
 
 // The frame step (arguments already checked, device current) with its
 // per-step buffers in w.
+// The split merge of a frame step into O.
+MergeArgs merge_args(const statekv_state* s, const StepScratch& w, void* O, int splits) {
+  MergeArgs m{};
+  m.opart = w.opart;
+  m.epart = w.epart;
+  m.mpart = w.mpart;
+  m.lpart = w.lpart;
+  m.out = O;
+  m.Hkv = s->HkvAll;
+  m.R = s->R;
+  m.G = s->G;
+  m.Hq = s->Hq;
+  m.S = splits;
+  m.ss = s->stat_ss;
+  m.lh = s->Hkv;
+  m.out_ls = (int64_t)s->T * s->Hq * s->D;
+  return m;
+}
+
 int frame_step(statekv_state* s, const void* Q, const void* K, const void* V, int32_t n, void* O,
                const StepScratch& w) {
   int rc = STATEKV_OK;
@@ -762,24 +789,24 @@ int frame_step(statekv_state* s, const void* Q, const void* K, const void* V, in
     tm.done();
     if (rc) return rc;
   }
-  // 3. The merge of the key splits into O and, for a scored frame, the score pass.
-  {
+  // 3. The merge of the key splits into O and, for a scored frame, the score
+  //    pass.  Under the recency policy an evicting frame's decision needs
+  //    positions only: it is made here, beside the merge, instead of waiting
+  //    for the next frame.
+  const bool decide_now = evict && recent && !scored;
+  if (decide_now) {
+    KernelTimer tm(s, STATEKV_K_SCORE);
+    SelectMergeArgs a{};
+    a.mg = merge_args(s, w, O, splits);
+    a.sel = sel_args_for(s, P, k0, foff, kSelEvict, 1, 0);
+    a.layers = s->L;
+    rc = check(launch_select_merge(s->dt, s->D, a, merge_wgs((int64_t)s->HkvAll * s->R), st, tm.lt));
+    tm.done();
+    if (rc) return rc;
+  } else {
     KernelTimer tm(s, STATEKV_K_SCORE);
     ScoreMergeArgs a{};
-    MergeArgs& m = a.mg;
-    m.opart = w.opart;
-    m.epart = w.epart;
-    m.mpart = w.mpart;
-    m.lpart = w.lpart;
-    m.out = O;
-    m.Hkv = s->HkvAll;
-    m.R = s->R;
-    m.G = s->G;
-    m.Hq = s->Hq;
-    m.S = splits;
-    m.ss = s->stat_ss;
-    m.lh = s->Hkv;
-    m.out_ls = (int64_t)s->T * s->Hq * s->D;
+    a.mg = merge_args(s, w, O, splits);
     a.merge_wgs = merge_wgs((int64_t)s->HkvAll * s->R);
     int waves = s->dt == Dt::BF16 ? 8 : 4;
     if (scored) {
@@ -825,9 +852,9 @@ int frame_step(statekv_state* s, const void* Q, const void* K, const void* V, in
     tm.done();
     if (rc) return rc;
   }
-  // The Top-B decision of this frame waits for the next frame's first launch
-  // (or a view of the state).
-  if (evict || scored) {
+  // Otherwise the Top-B decision of this frame waits for the next frame's
+  // first launch (or a view of the state).
+  if ((evict || scored) && !decide_now) {
     s->sel_pending = true;
     s->sel_P = P;
     s->sel_k0 = k0;
