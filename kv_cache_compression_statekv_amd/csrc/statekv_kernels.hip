@@ -429,9 +429,10 @@ __device__ void rope_wg(const RopeArgs& a0, size_t layer, int wg) {
 // S^T = K Q^T puts one query per lane column, so row max / row sum reduce
 // inside the lane plus one exchange with lane l^32.  O^T = V^T P^T reuses the
 // S^T accumulators directly as the B operand: for bf16 the eight keys a lane
-// supplies to one instruction are keys {16m + 8(t/4) + 4(l/32) + t%4}, so V^T
-// is written to LDS with bits 2 and 3 of the key index swapped inside each
-// group of 16, which makes those eight keys contiguous (one 16-byte read).
+// supplies to one instruction are keys {16m + 8(t/4) + 4(l/32) + t%4}.  V
+// stays row-major in LDS and gfx950's transposing LDS read (ds_read_b64_tr_b16)
+// gathers those keys of the lane's dimension, two reads per operand; fp32
+// streams write V^T to LDS instead.
 //
 // Visibility: key j is visible to a query of token i iff j < k0 + i + 1 (all
 // state keys, the frame's keys causally) and j lies in this split.  Blocks
@@ -447,19 +448,26 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base) 
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, -1, 0x00020000);
 }
 
-template <class E, int D, int NT, int BN_ = kAttnBN>
+// VROW (bf16 only): V kept row-major in LDS ([BN][VSTR], rows padded by 64
+// bytes so that the transposing reads of four rows by 32 lanes hit distinct
+// banks) and read as V^T by ds_read_b64_tr_b16; otherwise V^T is written to
+// LDS ([D][VSTR]) from registers.
+template <class E, int D, int NT, int BN_ = kAttnBN, bool VROW = false>
 struct AttnStage {
   typedef typename E::T T;
   static constexpr int BN = BN_;
   static constexpr int EPV = 16 / (int)sizeof(T);
   static constexpr int KSTR = D + EPV;
-  static constexpr int VSTR = BN + EPV;
+  static_assert(!VROW || sizeof(T) == 2, "row-major V needs 16-bit elements");
+  static constexpr int VSTR = VROW ? D + 32 : BN + EPV;
+  static constexpr int VSIZE = VROW ? BN * VSTR : D * VSTR;   // elements of one V buffer
+  static constexpr bool VROW_ = VROW;
   static constexpr int KCH = BN * (D / EPV) / NT;          // 16-byte K chunks / thread
   // bf16 V^T: tasks of KG consecutive keys x 8 dims
   static constexpr int KG = (BN / 4) * (D / 8) >= NT ? 4 : 2;
   static constexpr int VTASKS = (BN / KG) * (D / 8);
   static constexpr int VT_PER = (VTASKS + NT - 1) / NT;
-  static constexpr int VCH = sizeof(T) == 2 ? KG * VT_PER : KCH;
+  static constexpr int VCH = VROW ? KCH : (sizeof(T) == 2 ? KG * VT_PER : KCH);
   static_assert(KCH >= 1 && (BN * (D / EPV)) % NT == 0, "K staging shape");
 
   u32x4_t kr[KCH];
@@ -489,7 +497,14 @@ struct AttnStage {
       const int rr = t / CPR, cc = t - rr * CPR;
       o.k[j] = row_off(rr) + (uint32_t)(cc * 16);
     }
-    if constexpr (sizeof(T) == 2) {
+    if constexpr (VROW) {
+#pragma unroll
+      for (int j = 0; j < VCH; ++j) {
+        const int t = tid + j * NT;
+        const int rr = t / CPR, cc = t - rr * CPR;
+        o.v[j] = row_off(rr) + (uint32_t)(cc * 16);
+      }
+    } else if constexpr (sizeof(T) == 2) {
       constexpr int NKQ = BN / KG;
 #pragma unroll
       for (int u = 0; u < VT_PER; ++u) {
@@ -607,7 +622,14 @@ struct AttnStage {
       const int rr = t / CPR, cc = t - rr * CPR;
       *reinterpret_cast<u32x4_t*>(&Ks[rr * KSTR + cc * EPV]) = kr[j];
     }
-    if constexpr (sizeof(T) == 2) {
+    if constexpr (VROW) {
+#pragma unroll
+      for (int j = 0; j < VCH; ++j) {
+        const int t = tid + j * NT;
+        const int rr = t / CPR, cc = t - rr * CPR;
+        *reinterpret_cast<u32x4_t*>(&Vt[rr * VSTR + cc * EPV]) = vr[j];
+      }
+    } else if constexpr (sizeof(T) == 2) {
       constexpr int NKQ = BN / KG;
 #pragma unroll
       for (int u = 0; u < VT_PER; ++u) {
@@ -751,7 +773,7 @@ void attn_fwd_kernel(AttnArgs a) {
   typedef Mma<E> M;
   constexpr int NT = 64 * NW;
   constexpr int BN = BN_;
-  typedef AttnStage<E, D, NT, BN> Stage;
+  typedef AttnStage<E, D, NT, BN, sizeof(T) == 2> Stage;
   constexpr int NSUB = BN / 32;   // 32-key sub-tiles per block
   constexpr int KSTR = Stage::KSTR;
   constexpr int VSTR = Stage::VSTR;
@@ -759,11 +781,33 @@ void attn_fwd_kernel(AttnArgs a) {
   constexpr int NDT = D / 32;
   constexpr int BM = NW * 32 * QT;
   __shared__ __attribute__((aligned(16))) T Ks[2][BN * KSTR];
-  __shared__ __attribute__((aligned(16))) T Vt[2][D * VSTR];
+  __shared__ __attribute__((aligned(16))) T Vt[2][Stage::VSIZE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, hh = lane >> 5;
+  // MFMA operand V^T for dims [32 dt, 32 dt + 32) and the 16 keys from key0
+  // of an LDS block: this lane's row 32 dt + col and its 8 keys, in the order
+  // the P operand holds them (key key0 + 8 (t / 4) + 4 hh + t % 4 for t < 8).
+  // Row-major V (bf16): two transposing reads; lane s of each 16-lane group
+  // reads 4 dims of key key0 + 8 c + 4 hh + s / 4 and the read hands lane i of
+  // the group element i % 4 of lane 4 e + i / 4, i.e. key e of its own dim.
+  const int vlane = Stage::VROW_ ? (4 * hh + (lane & 15) / 4) * VSTR + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)
+                                 : col * VSTR + hh * 8;
+  auto v_operand = [&](const T* vt_, int key0, int dt) {
+    if constexpr (Stage::VROW_) {
+      typedef short s16x4_t __attribute__((ext_vector_type(4)));
+      typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+      const T* p = vt_ + key0 * VSTR + dt * 32 + vlane;
+      const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p));
+      const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p + 8 * VSTR));
+      const u32x4_t w = {__builtin_bit_cast(u32x2_t, lo)[0], __builtin_bit_cast(u32x2_t, lo)[1],
+                         __builtin_bit_cast(u32x2_t, hi)[0], __builtin_bit_cast(u32x2_t, hi)[1]};
+      return __builtin_bit_cast(bf16x8_t, w);
+    } else {
+      return *reinterpret_cast<const bf16x8_t*>(&vt_[dt * 32 * VSTR + key0 + vlane]);
+    }
+  };
   // Logical (row tile, KV head, split); the row tiles of one (head, split)
   // share its K/V blocks and run on one XCD.  Heaviest row tiles first (later
   // tokens see more keys).
@@ -863,8 +907,7 @@ void attn_fwd_kernel(AttnArgs a) {
         for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt) {
-            const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(
-                &vt_[(dt * 32 + col) * VSTR + sub * 32 + mm * 16 + hh * 8]);
+            const bf16x8_t af = v_operand(vt_, sub * 32 + mm * 16, dt);
 #pragma unroll
             for (int qt = 0; qt < QT; ++qt) o[qt][dt] = M::mma(af, pf[mm][qt], o[qt][dt]);
           }
@@ -948,8 +991,7 @@ void attn_fwd_kernel(AttnArgs a) {
             for (int t = 0; t < 8; ++t) pf[qt][t] = (__bf16)sacc[sub][qt][8 * mm + t];
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt) {
-            const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(
-                &vt_[(dt * 32 + col) * VSTR + sub * 32 + mm * 16 + hh * 8]);
+            const bf16x8_t af = v_operand(vt_, sub * 32 + mm * 16, dt);
 #pragma unroll
             for (int qt = 0; qt < QT; ++qt) o[qt][dt] = M::mma(af, pf[qt], o[qt][dt]);
           }
