@@ -1484,11 +1484,27 @@ __device__ void score_wg(const ScoreArgs& a, int wid, int nwg, int key_blocks, c
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, hh = lane >> 5;
-  // Logical (key block, KV head, row split); the key blocks of one (head,
-  // row split) share its Q rows and run on one XCD.
+  // Logical work-group order (consecutive ids run on one XCD and share its
+  // L2).  The 8-wave kernel (grids resident all at once): (key block, KV
+  // head, row split), the key blocks of one (head, row split) sharing its Q
+  // rows.  The 4-wave kernel (grids of several rounds, long pools): (row
+  // split, key block, KV head), consecutive ids sharing a key block's K and a
+  // head's key blocks sharing its Q tiles; with the key blocks fastest a
+  // head's K (4.3 MB at the stress shape) streamed through the L2 once per
+  // row split, and the launch fetched 157 MB instead of 55.
   const int wl = xcd_remap(wid, nwg);
-  const int kblock = wl % key_blocks, wrest = wl / key_blocks;
-  const int g = wrest % a.Hkv, rsplit = wrest / a.Hkv;
+  int kblock, g, rsplit;
+  if constexpr (NW == 4) {
+    rsplit = wl % fm.rsplits;
+    const int wrest = wl / fm.rsplits;
+    kblock = wrest % key_blocks;
+    g = wrest / key_blocks;
+  } else {
+    kblock = wl % key_blocks;
+    const int wrest = wl / key_blocks;
+    g = wrest % a.Hkv;
+    rsplit = wrest / a.Hkv;
+  }
   const int key_wg = kblock * BNK;
   const int key_w = key_wg + wave * 32 * KT;
 
