@@ -231,15 +231,19 @@ hipError_t launch_frame(Dt dt, int d, const RopeArgs& a, int layers, hipStream_t
                         const LaunchTiming& tm = {});
 hipError_t launch_attn(Dt dt, int d, const AttnArgs& a, int row_tiles, int splits, hipStream_t s,
                        const LaunchTiming& tm = {});
-// Score pass (with `waves` waves per work-group) and merge in one launch.  The
-// merge rides on the score work-groups (fused) only where score_merge_fusable.
+// Recency policy: the frame's decision and moves beside the split merge.
 hipError_t launch_select_merge(Dt dt, int d, const SelectMergeArgs& a, int merge_groups, hipStream_t s,
                                const LaunchTiming& tm = {});
+// Score pass (with `waves` waves per work-group) and merge in one launch.  The
+// merge rides on the score work-groups (fused) only where score_merge_fusable:
+// bf16 with 8 waves, the single-layer grids resident all at once, where
+// separate merge work-groups would push score work-groups into a second round
+// (the 4-wave kernel has no registers to spare for the merge at d = 128).
 hipError_t launch_score_merge(Dt dt, int d, const ScoreMergeArgs& a, int waves, hipStream_t s,
                               const LaunchTiming& tm = {});
 // Work-groups of the merge for `rows` flat rows (a multiple of the XCD count).
 int merge_wgs(int64_t rows);
-inline bool score_merge_fusable(Dt dt, int d, int waves) { return dt == Dt::BF16 && d == 64 && waves == 8; }
+inline bool score_merge_fusable(Dt dt, int, int waves) { return dt == Dt::BF16 && waves == 8; }
 // Keys per block of the text-phase attention kernel.
 int decode_block_keys(Dt dt);
 hipError_t launch_decode(Dt dt, int d, const DecodeArgs& a, hipStream_t s, const LaunchTiming& tm = {});

@@ -2502,7 +2502,9 @@ static hipError_t launch_sm_t(const ScoreMergeArgs& a, hipStream_t s, const Laun
 hipError_t launch_score_merge(Dt dt, int d, const ScoreMergeArgs& a, int waves, hipStream_t s,
                               const LaunchTiming& tm) {
   if (dt == Dt::BF16) {
-    if (waves == 8 && d == 64 && a.fused) return launch_sm_t<BF16, 64, kKtBf16, 8, 1, true>(a, s, tm);
+    if (waves == 8 && a.fused)
+      return d == 64 ? launch_sm_t<BF16, 64, kKtBf16, 8, 1, true>(a, s, tm)
+                     : launch_sm_t<BF16, 128, kKtBf16, 8, 1, true>(a, s, tm);
     if (waves == 8)
       return d == 64 ? launch_sm_t<BF16, 64, kKtBf16, 8, 1>(a, s, tm) : launch_sm_t<BF16, 128, kKtBf16, 8, 1>(a, s, tm);
     return d == 64 ? launch_sm_t<BF16, 64, kKtBf16, 4, score_prefetch(64)>(a, s, tm)
