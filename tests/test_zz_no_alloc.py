@@ -39,7 +39,11 @@ def _state_bits(st):
     return [k, v, pos, dk, dv] + ([sc["scores"], sc["keep_flag"]] if sc else [])
 
 
-def test_static_scratch_matches_allocating_entry_point():
+# Top-B with the scores kept for every frame, and the recency window, whose
+# decision and moves run in the launch after pass 1.
+@pytest.mark.parametrize("flags", [skv.FLAG_ALWAYS_SCORE, skv.FLAG_RECENT_WINDOW],
+                         ids=["topb_scores", "recent_window"])
+def test_static_scratch_matches_allocating_entry_point(flags):
     # The larger workload first: the InternVL3-1B-like layer (about 9 MB of
     # working buffers), then the smaller ragged one (about 1.5 MB), alternating.
     big = CONFIGS["ivl3_1b"].replace(n_frames=20)
@@ -49,7 +53,7 @@ def test_static_scratch_matches_allocating_entry_point():
         frames = [[to_device(a, wl.dtype) for a in fs.frame(n)] for n in range(wl.n_frames)]
         twins = [make_state(wl), make_state(wl)]    # [allocating, static]
         for st in twins:
-            st.set_flags(skv.FLAG_ALWAYS_SCORE)
+            st.set_flags(flags)
         shape = (wl.tokens_per_frame, wl.n_q_heads, wl.head_dim)
         outs = [torch.empty(shape, dtype=torch.bfloat16, device="cuda") for _ in twins]
         work.append((wl, frames, twins, outs))
