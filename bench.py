@@ -412,8 +412,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures the StateKV frame step on one GPU only; "
-              f"--gpus {args.gpus} (WORLD_SIZE={world}) is not supported: the step has no "
-              "multi-GPU path in this build.", file=sys.stderr)
+              f"--gpus {args.gpus} (WORLD_SIZE={world}) is not supported: the library has no "
+              "multi-GPU path (one state runs on one device).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
