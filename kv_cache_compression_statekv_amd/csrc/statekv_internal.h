@@ -80,6 +80,7 @@ struct RopeArgs {
   void* dv;               // [positions][Hkv][d]
   int32_t* nonfinite;     // set to 1 when an input element is NaN or Inf
   int32_t pos0, T, Hq, Hkv, G, cap, frame_base, rope_blocks;
+  int32_t rope_pairs;     // rotation pairs per RoPE task (rope_pairs_for)
   int64_t det_ls;         // elements between layers of dk / dv
   unsigned long long* clear;  // [L][cap] column sums cleared (null: none)
   int32_t clear_n;            // elements per layer
@@ -221,8 +222,12 @@ int score_keys_per_wg(Dt dt, int waves);
 // Score work-groups resident per CU (occupancy of the instantiation in use).
 int score_wgs_per_cu(Dt dt, int d);
 int score8_wgs_per_cu(int d);
+// Rotation pairs per RoPE task for a launch over `layers` layers of T
+// tokens: 4, or 16 bytes of each half of a head (8 for bf16) when the launch
+// is large enough to be bound by memory bandwidth rather than latency.
+int rope_pairs_for(int T, int Hq, int Hkv, int d, int esize, int layers);
 // Work-groups of the RoPE part of the frame launch for T tokens.
-int rope_blocks(int T, int Hq, int Hkv, int d, int esize);
+int rope_blocks(int T, int Hq, int Hkv, int d, int esize, int pairs);
 
 hipError_t launch_rope_table(const RopeTableArgs& a, hipStream_t s);
 // The frame launch (RoPE + append, the previous frame's selection); with

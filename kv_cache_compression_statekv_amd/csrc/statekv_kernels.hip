@@ -37,6 +37,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <type_traits>
 
 namespace statekv {
 namespace {
@@ -315,21 +316,21 @@ template <> struct Vec4<F32> {
 // values.  Short per-thread work keeps the launch's latency chain (load,
 // fp64 rotation, store) short; the value loads are issued by their own
 // threads, beside the rotations.
-constexpr int kRopePairsPerTask = 4;
-__host__ __device__ inline int64_t rope_qk_tasks(int T, int Hq, int Hkv, int d) {
-  return (int64_t)T * (Hq + Hkv) * (d / 2 / kRopePairsPerTask);
+__host__ __device__ inline int64_t rope_qk_tasks(int T, int Hq, int Hkv, int d, int pairs) {
+  return (int64_t)T * (Hq + Hkv) * (d / 2 / pairs);
 }
 __host__ __device__ inline int64_t rope_v_tasks(int T, int Hkv, int d, int esize) {
   return (int64_t)T * Hkv * (d * esize / 16);
 }
 
 // The RoPE + append work of RoPE work-group `wg` (kSelectThreads tasks) of
-// layer `layer`; it also clears its share of the layer's column sums.
-template <class E, int D>
-__device__ void rope_wg(const RopeArgs& a0, size_t layer, int wg) {
+// layer `layer`, RP rotation pairs per task; it also clears its share of the
+// layer's column sums.
+template <class E, int D, int RP>
+__device__ void rope_wg_t(const RopeArgs& a0, size_t layer, int wg) {
   typedef typename E::T T;
   constexpr int HALF = D / 2;
-  constexpr int CH = HALF / kRopePairsPerTask;   // tasks per head
+  constexpr int CH = HALF / RP;                  // tasks per head
   constexpr int VEC = 16 / (int)sizeof(T);
   constexpr int VCH = D / VEC;                   // value chunks per head
   const int tid = threadIdx.x;
@@ -354,7 +355,7 @@ __device__ void rope_wg(const RopeArgs& a0, size_t layer, int wg) {
     a.dv = (T*)a.dv + layer * a.det_ls;
   }
   const int nh = a.Hq + a.Hkv;
-  const int64_t nqk = rope_qk_tasks(a.T, a.Hq, a.Hkv, D);
+  const int64_t nqk = rope_qk_tasks(a.T, a.Hq, a.Hkv, D, RP);
   const int64_t nv = rope_v_tasks(a.T, a.Hkv, D, (int)sizeof(T));
   const int64_t t = (int64_t)wg * kSelectThreads + tid;
   bool finite = true;
@@ -363,7 +364,7 @@ __device__ void rope_wg(const RopeArgs& a0, size_t layer, int wg) {
     const int64_t rest = t / CH;
     const int hd = (int)(rest % nh);
     const int tok = (int)(rest / nh);
-    const int k = c * kRopePairsPerTask;
+    const int k = c * RP;
     const int pos = a.pos0 + tok;
     const T* src;
     T* dst0;
@@ -379,22 +380,25 @@ __device__ void rope_wg(const RopeArgs& a0, size_t layer, int wg) {
       if (a.kpool) dst1 = (T*)a.kpool + ((size_t)g * a.cap + a.frame_base + tok) * D;
       if (a.pool_pos && g == 0 && c == 0) a.pool_pos[a.frame_base + tok] = pos;
     }
-    float x1[kRopePairsPerTask], x2[kRopePairsPerTask];
-    Vec4<E>::load(src + k, x1);
-    Vec4<E>::load(src + k + HALF, x2);
+    typedef typename std::conditional<RP == 8, Vec8<E>, Vec4<E>>::type VP;
+    float x1[RP], x2[RP];
+    VP::load(src + k, x1);
+    VP::load(src + k + HALF, x2);
     const f32x4_t* tb = reinterpret_cast<const f32x4_t*>(a.table + (size_t)pos * HALF + k);
-    const f32x4_t cs4[2] = {tb[0], tb[1]};   // (cos, sin) of pairs k, k+1 and k+2, k+3
-    T y1[kRopePairsPerTask], y2[kRopePairsPerTask];
+    f32x4_t cs4[RP / 2];   // (cos, sin) of pairs k + 2 i and k + 2 i + 1
 #pragma unroll
-    for (int j = 0; j < kRopePairsPerTask; ++j) {
+    for (int i = 0; i < RP / 2; ++i) cs4[i] = tb[i];
+    T y1[RP], y2[RP];
+#pragma unroll
+    for (int j = 0; j < RP; ++j) {
       finite &= isfinite(x1[j]) && isfinite(x2[j]);
       rope_pair<E>(x1[j], x2[j], float2{cs4[j >> 1][2 * (j & 1)], cs4[j >> 1][2 * (j & 1) + 1]}, y1[j], y2[j]);
     }
-    Vec4<E>::store(dst0 + k, y1);
-    Vec4<E>::store(dst0 + k + HALF, y2);
+    VP::store(dst0 + k, y1);
+    VP::store(dst0 + k + HALF, y2);
     if (dst1) {
-      Vec4<E>::store(dst1 + k, y1);
-      Vec4<E>::store(dst1 + k + HALF, y2);
+      VP::store(dst1 + k, y1);
+      VP::store(dst1 + k + HALF, y2);
     }
   } else if (t < nqk + nv) {
     // Values: copied unrotated to the pool and to D, 16 bytes per task.
@@ -418,6 +422,12 @@ __device__ void rope_wg(const RopeArgs& a0, size_t layer, int wg) {
     *reinterpret_cast<u32x4_t*>((T*)a.dv + ((size_t)(a.pos0 + tok) * a.Hkv + g) * D + c * VEC) = v;
   }
   if (!finite) atomicOr(a.nonfinite, 1);
+}
+
+template <class E, int D>
+__device__ void rope_wg(const RopeArgs& a, size_t layer, int wg) {
+  if (sizeof(typename E::T) == 2 && a.rope_pairs == 8) rope_wg_t<E, D, 8>(a, layer, wg);
+  else rope_wg_t<E, D, 4>(a, layer, wg);
 }
 
 // ---------------------------------------------------------------------------
@@ -2421,10 +2431,19 @@ hipError_t launch_rope_table(const RopeTableArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Four pairs per task keep each thread's load, rotation and store chain short
+// (latency-bound launches: a single layer of a few hundred tokens); with more
+// than 2^20 such tasks in the launch (large frames, stacks) 16-byte accesses
+// move the bytes faster (28-layer qwen3vl_2b stack: 161 -> 135 us).
+int rope_pairs_for(int T, int Hq, int Hkv, int d, int esize, int layers) {
+  if (esize != 2) return 4;
+  return (int64_t)layers * rope_qk_tasks(T, Hq, Hkv, d, 4) > (int64_t(1) << 20) ? 8 : 4;
+}
+
 // Work-groups of the RoPE part of a launch for T tokens (after the selection
 // work-group).
-int rope_blocks(int T, int Hq, int Hkv, int d, int esize) {
-  return (int)((rope_qk_tasks(T, Hq, Hkv, d) + rope_v_tasks(T, Hkv, d, esize) + kSelectThreads - 1) /
+int rope_blocks(int T, int Hq, int Hkv, int d, int esize, int pairs) {
+  return (int)((rope_qk_tasks(T, Hq, Hkv, d, pairs) + rope_v_tasks(T, Hkv, d, esize) + kSelectThreads - 1) /
                kSelectThreads);
 }
 

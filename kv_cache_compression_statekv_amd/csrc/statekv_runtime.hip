@@ -743,7 +743,8 @@ int frame_step(statekv_state* s, const void* Q, const void* K, const void* V, in
     a.G = s->G;
     a.cap = s->cap;
     a.frame_base = F;
-    a.rope_blocks = rope_blocks(s->T, s->Hq, s->Hkv, s->D, s->esize);
+    a.rope_pairs = rope_pairs_for(s->T, s->Hq, s->Hkv, s->D, s->esize, s->L);
+    a.rope_blocks = rope_blocks(s->T, s->Hq, s->Hkv, s->D, s->esize, a.rope_pairs);
     a.det_ls = s->det_ls;
     if (scored) {
       a.clear = s->colsum + (size_t)s->colsum_next * cs_n;
@@ -989,7 +990,8 @@ int statekv_decode(statekv_state* s, const void* Q, const void* K, const void* V
       a.Hkv = s->Hkv;
       a.G = s->G;
       a.cap = s->cap;
-      a.rope_blocks = rope_blocks(t, s->Hq, s->Hkv, s->D, s->esize);
+      a.rope_pairs = rope_pairs_for(t, s->Hq, s->Hkv, s->D, s->esize, s->L);
+      a.rope_blocks = rope_blocks(t, s->Hq, s->Hkv, s->D, s->esize, a.rope_pairs);
       a.det_ls = s->det_ls;
       rc = check(launch_frame(s->dt, s->D, a, s->L, st, tm.lt));
       tm.done();
