@@ -36,6 +36,9 @@ def compile_command(out: str) -> list:
         # pools, the text-phase kernel 5 %).
         "-mllvm", "--amdgpu-mfma-vgpr-form",
         "-I", INCLUDE, "-I", CSRC,
+        # Every symbol resolved at link time: a declaration without its
+        # definition fails the build instead of the first load.
+        "-Wl,-z,defs",
         *[os.path.join(CSRC, s) for s in SOURCES],
         "-o", out,
     ]
