@@ -888,12 +888,15 @@ void attn_fwd_kernel(AttnArgs a) {
     if constexpr (sizeof(T) == 2) {
       // NSUB sub-tiles of 32 keys, software-pipelined inside the wave:
       //   QK(0); max(0);
-      //   for s: [PV(s-1), QK(s+1)] beside [exp(s), pack(s)]; rescale(s); max(s+1)
-      //   PV(NSUB-1)
+      //   for s: rescale(s-1); [PV(s-1), QK(s+1)] beside [exp(s), pack(s)]; max(s+1)
+      //   rescale(NSUB-1); PV(NSUB-1)
       // so the matrix pipe works while the VALU computes the weights.  Per
       // row the arithmetic and its order are those of online_softmax: max(s)
       // fixes the reference of sub-tile s and rescales l; O is rescaled for
-      // it after PV(s-1) and before PV(s).
+      // it after PV(s-1) and right before PV(s).  The rescale (a rare,
+      // wave-uniform branch) stays ahead of each interleaved region: inside
+      // one, it split the region in two, and the exponentials of sub-tile 0
+      // were placed after all four QK(1) instructions instead of beside them.
       auto qk = [&](int sub, f32x16_t (&acc)[QT]) {
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) acc[qt] = f32x16_t{};
@@ -939,12 +942,13 @@ void attn_fwd_kernel(AttnArgs a) {
       };
       f32x16_t sb[2][QT];          // S of sub-tiles s and s+1
       bf16x8_t pb[2][2][QT];       // P of sub-tiles s-1 and s
-      float alpha[QT];
+      float alpha[2][QT];          // O's rescale for sub-tiles s and s+1
       qk(0, sb[0]);
-      smax(0, sb[0], alpha);
+      smax(0, sb[0], alpha[0]);
 #pragma unroll
       for (int sub = 0; sub < NSUB; ++sub) {
         const int c = sub & 1;
+        if (sub >= 1) rescale(alpha[c ^ 1]);              // O for sub-tile s-1's reference
         if (sub >= 1) pv(sub - 1, pb[c ^ 1]);
         if (sub + 1 < NSUB) qk(sub + 1, sb[c ^ 1]);
         softmax_exp<QT>(sb[c], m_run, l_run, a.c_hi);
@@ -955,9 +959,9 @@ void attn_fwd_kernel(AttnArgs a) {
           interleave_mfma_valu<NKS, 12, NKS * QT, 0, 6>();
         else
           interleave_mfma_valu<2 * NDT, 12, 2 * NDT * QT, 0, 6>();
-        rescale(alpha);                                   // O for sub-tile s's reference
-        if (sub + 1 < NSUB) smax(sub + 1, sb[c ^ 1], alpha);
+        if (sub + 1 < NSUB) smax(sub + 1, sb[c ^ 1], alpha[c ^ 1]);
       }
+      rescale(alpha[(NSUB - 1) & 1]);
       pv(NSUB - 1, pb[(NSUB - 1) & 1]);
       return;
     }
