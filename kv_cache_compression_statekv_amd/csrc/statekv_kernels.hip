@@ -843,14 +843,25 @@ void attn_fwd_kernel(AttnArgs a) {
 
   typename M::Frag qf[QT][NKS];
   int qrow[QT], lim[QT];
+  // bf16: buffer loads through a resource that ends at row R (rows past it
+  // read as zero), so no load sits behind a branch and the compiler's wait
+  // counts stay exact.
+  const __amdgpu_buffer_rsrc_t qres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<T*>(qbase), (short)0, a.R * D * (int)sizeof(T), 0x00020000);
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     const int r = row_wg + (wave * QT + qt) * 32 + col;
     qrow[qt] = r;
     lim[qt] = min(kend, a.k0 + (r < a.R ? r / a.G : -1) + 1);
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-      qf[qt][ks] = r < a.R ? M::ld(qbase + (size_t)r * D + ks * M::KS + hh * M::KL) : M::zero();
+    for (int ks = 0; ks < NKS; ++ks) {
+      if constexpr (sizeof(T) == 2) {
+        const uint32_t off = (uint32_t)((r * D + ks * M::KS + hh * M::KL) * (int)sizeof(T));
+        qf[qt][ks] = __builtin_bit_cast(typename M::Frag, __builtin_amdgcn_raw_buffer_load_b128(qres, off, 0, 0));
+      } else {
+        qf[qt][ks] = r < a.R ? M::ld(qbase + (size_t)r * D + ks * M::KS + hh * M::KL) : M::zero();
+      }
+    }
   }
 
   f32x16_t o[QT][NDT];
@@ -865,20 +876,31 @@ void attn_fwd_kernel(AttnArgs a) {
   }
 
   // NPF register stages: block b's loads are issued NPF blocks ahead of its
-  // compute, so short splits (a few blocks per work-group) have all their
-  // loads in flight at once.  Blocks pass through two LDS buffers.
+  // compute and it is stored to LDS after block b-1's compute, so a load has
+  // NPF blocks of compute to arrive in, and short splits (a few blocks per
+  // work-group) have all their loads in flight at once.  Blocks pass through
+  // two LDS buffers.  Loads past the last block repeat it (every stage is
+  // loaded on every path, so the compiler's wait counts are exact); they are
+  // never stored.
   Stage st[NPF];
   typename Stage::Offsets so;
   Stage::off_uniform(so, rs, tid);
   const int nblk = kend > kbeg ? (kend - kbeg + BN - 1) / BN : 0;
+  const int kb_last = kbeg + max(nblk - 1, 0) * BN;
+  // A work-group without keys (nblk = 0) loads the pool's first rows instead
+  // (valid rows, never used).
+  const int kend_ld = nblk > 0 ? kend : a.P;
 #pragma unroll
   for (int i = 0; i < NPF; ++i)
-    if (i < nblk) st[i].load(kbase, vbase, kbeg + i * BN, kend, a.k0, a.foff, rs, so, tid);
-  if (nblk > 0) st[0].store(Ks[0], Vt[0], tid);
-  // Every load issued so far (the query fragments and block 0) has arrived
-  // here on every path; saying so keeps the compiler from waiting for the
-  // loop's own prefetch loads before the first matrix instruction of a block.
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    st[i].load(kbase, vbase, nblk > 0 ? min(kbeg + i * BN, kb_last) : 0, kend_ld, a.k0, a.foff, rs, so, tid);
+  st[0].store(Ks[0], Vt[0], tid);
+  // The query fragments and block 0 have arrived here on every path (at most
+  // the later stages' loads are outstanding); saying so keeps the compiler
+  // from waiting for the loop's own prefetch loads before the first matrix
+  // instruction of a block.
+  constexpr int kStageLoads = Stage::KCH + Stage::VCH;   // buffer loads per stage and thread
+  static_assert(kStageLoads * (NPF - 1) < 16, "wait count fits the low vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (kStageLoads * (NPF - 1)));
   __syncthreads();
 
   auto compute = [&](int kb, int buf) {
@@ -1025,26 +1047,38 @@ void attn_fwd_kernel(AttnArgs a) {
 
   };
 
-  for (int b0 = 0; b0 < nblk; b0 += NPF) {
+  if (nblk <= NPF) {
+    // Every block was loaded in the prologue: straight-line code, so that
+    // each block waits only for its own loads (across a loop's back edge the
+    // compiler waits for every outstanding load at the top of the loop).
 #pragma unroll
-    for (int i = 0; i < NPF; ++i) {
-      const int b = b0 + i;
-      if (b < nblk) {
-        const int kb = kbeg + b * BN;
-        const int buf = b & 1;
-        if constexpr (NPF >= 2) {
-          // Stage b+1 (loaded NPF-1 blocks ago) goes to the other buffer first,
-          // beside this block's compute: that buffer was last read before the
-          // previous barrier, and the barrier below publishes it.
-          if (b + 1 < nblk) st[(i + 1) % NPF].store(Ks[buf ^ 1], Vt[buf ^ 1], tid);
-          if (b + NPF < nblk) st[i].load(kbase, vbase, kb + NPF * BN, kend, a.k0, a.foff, rs, so, tid);
-          compute(kb, buf);
-        } else {
-          if (b + NPF < nblk) st[i].load(kbase, vbase, kb + NPF * BN, kend, a.k0, a.foff, rs, so, tid);
-          compute(kb, buf);
-          if (b + 1 < nblk) st[(i + 1) % NPF].store(Ks[buf ^ 1], Vt[buf ^ 1], tid);
-        }
+    for (int b = 0; b < NPF; ++b) {
+      const int buf = b & 1;
+      if (b < nblk) compute(kbeg + b * BN, buf);
+      if (b + 1 < NPF) {
+        // Stored on every path (a stage past the last block is never read).
+        st[b + 1].store(Ks[buf ^ 1], Vt[buf ^ 1], tid);
         __syncthreads();
+      }
+    }
+  } else {
+    for (int b0 = 0; b0 < nblk; b0 += NPF) {
+#pragma unroll
+      for (int i = 0; i < NPF; ++i) {
+        const int b = b0 + i;
+        if (b < nblk) {
+          const int kb = kbeg + b * BN;
+          const int buf = b & 1;
+          // Stage i held block b (stored after the previous block); it takes
+          // block b + NPF.  Block b+1 (loaded NPF blocks ago) goes to the
+          // other buffer after this block's compute: that buffer was last
+          // read before the previous barrier, and the barrier below
+          // publishes it.
+          st[i].load(kbase, vbase, min(kb + NPF * BN, kb_last), kend, a.k0, a.foff, rs, so, tid);
+          compute(kb, buf);
+          if (b + 1 < nblk) st[(i + 1) % NPF].store(Ks[buf ^ 1], Vt[buf ^ 1], tid);
+          __syncthreads();
+        }
       }
     }
   }
@@ -2362,9 +2396,12 @@ __global__ __launch_bounds__(256) void score_view_kernel(ScoreViewArgs a) {
 static constexpr int kKtBf16 = 2;  // key tiles per wave in the score pass
 static constexpr int kKtF32 = 1;
 
-// Register stages of pass 1's block prefetch: 2 for d = 128 (measured a few
-// percent faster on the long-pool shapes), 1 for d = 64 (no gain).
-static constexpr int attn_prefetch(int d) { return d == 128 ? 2 : 1; }
+// Register stages of pass 1's block prefetch (a block's loads are issued
+// NPF blocks ahead of its compute): 4 for d = 64, so that the 4-block splits
+// of a single layer at B = 4096 load every block in the prologue (pass 1
+// 11.4 -> 10.6 us at ivl3_1b); 2 for d = 128, the most its registers allow
+// without spills.
+static constexpr int attn_prefetch(int d) { return d == 128 ? 2 : 4; }
 
 // Compute units of the current device (0 if unknown).
 static int device_cus() {
