@@ -1047,17 +1047,21 @@ void attn_fwd_kernel(AttnArgs a) {
 
   };
 
-  if (nblk <= NPF) {
-    // Every block was loaded in the prologue: straight-line code, so that
-    // each block waits only for its own loads (across a loop's back edge the
-    // compiler waits for every outstanding load at the top of the loop).
+  // Splits of at most SLN blocks (a single layer's short splits) run as
+  // straight-line code, so that each block waits only for its own loads (a
+  // loop makes the compiler wait for the prologue's stages before entering
+  // it, and copy them into the loop's registers).
+  constexpr int SLN = NPF > 4 ? NPF : 4;
+  if (nblk <= SLN) {
 #pragma unroll
-    for (int b = 0; b < NPF; ++b) {
+    for (int b = 0; b < SLN; ++b) {
       const int buf = b & 1;
+      // Stage b % NPF held block b (stored after the previous block).
+      if (b + NPF < SLN) st[b % NPF].load(kbase, vbase, min(kbeg + (b + NPF) * BN, kb_last), kend_ld, a.k0, a.foff, rs, so, tid);
       if (b < nblk) compute(kbeg + b * BN, buf);
-      if (b + 1 < NPF) {
+      if (b + 1 < SLN) {
         // Stored on every path (a stage past the last block is never read).
-        st[b + 1].store(Ks[buf ^ 1], Vt[buf ^ 1], tid);
+        st[(b + 1) % NPF].store(Ks[buf ^ 1], Vt[buf ^ 1], tid);
         __syncthreads();
       }
     }
