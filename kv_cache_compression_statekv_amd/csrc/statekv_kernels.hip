@@ -1059,8 +1059,7 @@ void attn_fwd_kernel(AttnArgs a) {
       // Stage b % NPF held block b (stored after the previous block).
       if (b + NPF < SLN) st[b % NPF].load(kbase, vbase, min(kbeg + (b + NPF) * BN, kb_last), kend_ld, a.k0, a.foff, rs, so, tid);
       if (b < nblk) compute(kbeg + b * BN, buf);
-      if (b + 1 < SLN) {
-        // Stored on every path (a stage past the last block is never read).
+      if (b + 1 < nblk) {   // every load above is issued on every path, so the waits stay exact
         st[(b + 1) % NPF].store(Ks[buf ^ 1], Vt[buf ^ 1], tid);
         __syncthreads();
       }
