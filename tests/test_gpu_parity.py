@@ -68,11 +68,14 @@ SHAPES = [
     ("ragged_bf16_d64", {"STATEKV_ATTN_SPLITS": "1"}),
     ("ragged_bf16_d64", {"STATEKV_ATTN_SPLITS": "3", "STATEKV_SCORE_RSPLITS": "1"}),
     ("ragged_bf16_d128_yarn", {"STATEKV_SCORE_SLOTS": "8", "STATEKV_SCORE_RSPLITS": "64"}),
+    # one split of up to 7 key blocks at d=128: the long-split loop, its
+    # prefetch groups ending inside the last group (7 is not a multiple of 2)
+    ("ragged_bf16_d128_yarn", {"STATEKV_ATTN_SPLITS": "1"}),
 ]
 
 
 @pytest.mark.parametrize("name,env", SHAPES, ids=["one_split", "three_splits_one_rsplit",
-                                                  "few_score_slots"])
+                                                  "few_score_slots", "d128_one_split"])
 def test_launch_shape_overrides(name, env, monkeypatch):
     for k, v in env.items():
         monkeypatch.setenv(k, v)
