@@ -2063,19 +2063,31 @@ __device__ void select_top_b(const SelArgs& a, SelectShared& sh, uint32_t* val) 
     }
   }
 
-  // Without the eviction steps, the barrier that publishes the loaded rows.
-  if (a.mode != kSelEvict) __syncthreads();
-  // Move list from the flags: every thread scans a contiguous range of rows so
-  // that holes (evicted slots below B) and movers (kept rows at or beyond B)
-  // come out ascending.
+  // Without the eviction steps nothing is evicted and nothing moves.
+  if (a.mode != kSelEvict) {
+    if (tid == 0) *a.move_count = 0;
+    return;
+  }
+  // Move list from the flags: every thread takes a contiguous range of C rows
+  // (at most 32: P <= kMaxPool) so that holes (evicted slots below B) and
+  // movers (kept rows at or beyond B) come out ascending.  Its holes and
+  // movers are kept as bit masks, so the list writes below visit only them.
+  static_assert(kMaxPool <= 32 * kSelectThreads, "a thread's rows fit a 32-bit mask");
   const int i0 = tid * C;
   const int i1 = min(a.P, i0 + C);
-  int holes = 0, movers = 0;
-  for (int idx = i0; idx < i1; ++idx) {
-    const uint32_t ev = val[idx] >> 31;
-    holes += (idx < a.B && ev) ? 1 : 0;
-    movers += (idx >= a.B && !ev) ? 1 : 0;
+  uint32_t hmask = 0u, mmask = 0u;
+  for (int j0 = 0; j0 < C; j0 += kChunk) {
+#pragma unroll
+    for (int j = j0; j < j0 + kChunk; ++j) {
+      const int idx = i0 + j;
+      if (j < C && idx < i1) {
+        const uint32_t ev = val[idx] >> 31;
+        hmask |= (idx < a.B && ev) ? (1u << j) : 0u;
+        mmask |= (idx >= a.B && !ev) ? (1u << j) : 0u;
+      }
+    }
   }
+  const int holes = __popc(hmask), movers = __popc(mmask);
   int total;
   const int base = block_excl_scan(holes | (movers << 16), sh.scan, &total);
 
@@ -2090,21 +2102,19 @@ __device__ void select_top_b(const SelArgs& a, SelectShared& sh, uint32_t* val) 
   const bool lds_list = a.list_stride <= kSelListMax;
   int* l_dst = sh.hist;
   int* l_src = sh.hist + kSelListMax;
-  if (holes | movers) {
+  {
     int bh = base & 0xffff, bm = base >> 16;
-    for (int idx = i0; idx < i1; ++idx) {
-      const uint32_t ev = val[idx] >> 31;
-      if (idx < a.B && ev && bh < a.list_stride) {
-        if (lds_list) l_dst[bh] = idx;
-        else a.move_dst[bh] = idx;
-        ++bh;
-      }
-      if (idx >= a.B && !ev && bm < a.list_stride) {
-        const int row = pool_row(idx, a.k0, a.foff);
-        if (lds_list) l_src[bm] = row;
-        else a.move_src[bm] = row;
-        ++bm;
-      }
+    for (; hmask != 0u && bh < a.list_stride; ++bh) {
+      const int idx = i0 + __builtin_ctz(hmask);
+      hmask &= hmask - 1u;
+      if (lds_list) l_dst[bh] = idx;
+      else a.move_dst[bh] = idx;
+    }
+    for (; mmask != 0u && bm < a.list_stride; ++bm) {
+      const int row = pool_row(i0 + __builtin_ctz(mmask), a.k0, a.foff);
+      mmask &= mmask - 1u;
+      if (lds_list) l_src[bm] = row;
+      else a.move_src[bm] = row;
     }
   }
   const int moves = min(min(total & 0xffff, total >> 16), a.list_stride);
