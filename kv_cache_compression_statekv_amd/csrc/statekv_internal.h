@@ -112,6 +112,7 @@ struct AttnArgs {
   int32_t R, G, cap, P, k0, foff, kps, Hkv;   // Hkv: KV heads of all layers
   int32_t ss;             // split stride of the statistics (maximum splits)
   int32_t lh;             // KV heads per layer
+  int32_t head_major;     // work-group order: 1 = (row tile, split, KV head), 0 = (row tile, KV head, split)
   // Element strides of the key / value rows: between KV heads and between
   // rows.  The pool is [Hkv][cap][d] (cap*d, d); the detailed cache, read by
   // text chunks, is [positions][Hkv][d] (d, Hkv*d).

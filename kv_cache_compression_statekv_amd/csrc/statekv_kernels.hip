@@ -818,13 +818,16 @@ void attn_fwd_kernel(AttnArgs a) {
       return *reinterpret_cast<const bf16x8_t*>(&vt_[dt * 32 * VSTR + key0 + vlane]);
     }
   };
-  // Logical (row tile, KV head, split); the row tiles of one (head, split)
-  // share its K/V blocks and run on one XCD.  Heaviest row tiles first (later
-  // tokens see more keys).
+  // Logical (row tile, KV head, split), or (row tile, split, KV head) with
+  // head_major; the row tiles of one (head, split) share its K/V blocks and
+  // run on one XCD.  Head-major order gives each XCD the query rows of few
+  // heads (many KV heads: each XCD would otherwise read every head's queries).
+  // Heaviest row tiles first (later tokens see more keys).
   const int wl = xcd_remap(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z),
                            gridDim.x * gridDim.y * gridDim.z);
   const int tile = wl % gridDim.x, wrest = wl / gridDim.x;
-  const int g = wrest % gridDim.y, split = wrest / gridDim.y;
+  const int g = a.head_major ? (int)(wrest / gridDim.z) : (int)(wrest % gridDim.y);
+  const int split = a.head_major ? (int)(wrest % gridDim.z) : (int)(wrest / gridDim.y);
   const int row_wg = (gridDim.x - 1 - tile) * BM;
   const int row_last = min(a.R, row_wg + BM) - 1;
   const int tok_min = row_wg / a.G;
