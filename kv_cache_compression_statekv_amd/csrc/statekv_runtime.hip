@@ -261,7 +261,7 @@ int resolve_static_scratch(int device) {
 // Pass 1 runs best with one work-group (8 waves) per compute unit: about 256
 // work-groups; the score pass with about 8 waves per compute unit.
 constexpr int kAttnTargetWGs = 256;
-constexpr int kAttnHeadMajorMin = 4;   // KV heads (all layers) from which pass 1 runs head-major
+constexpr int kAttnHeadMajorMin = 4;   // KV heads from which a single layer's pass 1 runs head-major
 constexpr int kScoreTargetWaves = 256 * 8;
 
 // Key splits of pass 1 for a pool of P keys: enough work-groups to fill the
@@ -784,9 +784,11 @@ int frame_step(statekv_state* s, const void* Q, const void* K, const void* V, in
     a.ss = s->stat_ss;
     a.Hkv = s->HkvAll;
     a.lh = s->Hkv;
-    // Head-major work-group order with many KV heads: measured faster at 8
-    // heads (qwen3vl_2b-like and stress shapes), slower at 2 (ivl3_1b-like).
-    a.head_major = s->HkvAll >= kAttnHeadMajorMin ? 1 : 0;
+    // Head-major work-group order for a single layer with many KV heads:
+    // measured faster at 8 heads (qwen3vl_2b-like and stress shapes), slower
+    // at 2 (ivl3_1b-like); on 28-layer stacks it left pass 1 unchanged and
+    // made the next frame launch slower.
+    a.head_major = s->L == 1 && s->HkvAll >= kAttnHeadMajorMin ? 1 : 0;
     a.kv_hs = (int64_t)s->cap * s->D;
     a.kv_rs = s->D;
     a.kv_ls = (int64_t)s->Hkv * s->cap * s->D;
